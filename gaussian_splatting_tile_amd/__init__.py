@@ -1,0 +1,14 @@
+"""MI355X-native tile-based 3D Gaussian Splatting rasterizer (forward + backward).
+
+The compute path is libgs.so (HIP kernels for gfx950 behind the C ABI in
+include/gs.h); this package is its thin torch binding. The library is loaded
+on first use; every entry point raises ImportError if it has not been built
+(there is no fallback path).
+"""
+from ._lib import EXPORTS, GsError, LIB_PATH
+from .rasterizer import (BinBuffers, Rasterizer, Scene, bin_and_sort, camera, composite_bwd,
+                         composite_fwd, constants, preprocess, tile_ranges, tiles_xy, version)
+
+__all__ = ["EXPORTS", "GsError", "LIB_PATH", "BinBuffers", "Rasterizer", "Scene", "bin_and_sort",
+           "camera", "composite_bwd", "composite_fwd", "constants", "preprocess", "tile_ranges",
+           "tiles_xy", "version"]

@@ -1,0 +1,206 @@
+// C ABI of libgs (include/gs.h): host-side argument validation, scratch
+// layout, launch sequencing and error reporting. No C++ exception crosses
+// this boundary; no device memory is allocated here.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "gs_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+gs_status fail(gs_status code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+gs_status hip_check(hipError_t e, const char* what) {
+    if (e == hipSuccess) return GS_OK;
+    return fail(GS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+gs_status check_camera(const gs_camera* cam) {
+    if (!cam) return fail(GS_ERR_INVALID, "camera is NULL");
+    if (cam->width < 1 || cam->height < 1 || cam->width > GS_MAX_DIM || cam->height > GS_MAX_DIM)
+        return fail(GS_ERR_INVALID, "image size %dx%d outside [1, %d]", cam->width, cam->height,
+                    GS_MAX_DIM);
+    if (!(cam->fx > 0.0f) || !(cam->fy > 0.0f) || !std::isfinite(cam->fx) || !std::isfinite(cam->fy))
+        return fail(GS_ERR_INVALID, "focal lengths must be finite and positive");
+    if (!std::isfinite(cam->cx) || !std::isfinite(cam->cy))
+        return fail(GS_ERR_INVALID, "principal point must be finite");
+    for (int i = 0; i < 9; ++i)
+        if (!std::isfinite(cam->R[i])) return fail(GS_ERR_INVALID, "R must be finite");
+    for (int i = 0; i < 3; ++i)
+        if (!std::isfinite(cam->t[i]) || !std::isfinite(cam->campos[i]))
+            return fail(GS_ERR_INVALID, "t and campos must be finite");
+    return GS_OK;
+}
+
+int tile_bits(const gs_camera& cam) {
+    const int n_tiles = gs::tiles_x(cam) * gs::tiles_y(cam);
+    int b = 0;
+    while ((1 << b) < n_tiles) ++b;
+    return b;
+}
+
+}  // namespace
+
+extern "C" {
+
+void gs_constants(float out[9]) {
+    out[0] = (float)gs::kTile;
+    out[1] = gs::kDilation;
+    out[2] = gs::kZNear;
+    out[3] = gs::kFrustumClamp;
+    out[4] = gs::kDiscFloor;
+    out[5] = gs::kSigma;
+    out[6] = gs::kAlphaMin;
+    out[7] = gs::kAlphaMax;
+    out[8] = gs::kTStop;
+}
+
+const char* gs_last_error(void) { return g_last_error.c_str(); }
+
+void gs_version(int32_t out[3]) {
+    out[0] = 0;
+    out[1] = 1;
+    out[2] = 0;
+}
+
+gs_status gs_preprocess(const gs_camera* cam, int32_t n, const float* means, const float* scales,
+                        const float* quats, const float* opacity, const float* sh,
+                        int32_t sh_degree, const float* rgb_in, float* xy_depth, float* conic_op,
+                        float* rgb, uint32_t* tiles_touched, void* stream) {
+    g_last_error.clear();
+    if (gs_status s = check_camera(cam)) return s;
+    if (n < 0 || n > GS_MAX_GAUSSIANS) return fail(GS_ERR_INVALID, "n = %d outside [0, %d]", n, GS_MAX_GAUSSIANS);
+    if (n == 0) return GS_OK;
+    if (!means || !scales || !quats || !opacity || !xy_depth || !conic_op || !rgb || !tiles_touched)
+        return fail(GS_ERR_INVALID, "gs_preprocess: a required pointer is NULL");
+    if (sh) {
+        if (sh_degree < 0 || sh_degree > 3) return fail(GS_ERR_INVALID, "sh_degree %d outside 0..3", sh_degree);
+    } else if (!rgb_in) {
+        return fail(GS_ERR_INVALID, "gs_preprocess: rgb_in is required when sh is NULL");
+    }
+    if (((uintptr_t)xy_depth | (uintptr_t)conic_op | (uintptr_t)rgb) & 15)
+        return fail(GS_ERR_INVALID, "gs_preprocess: float4 outputs must be 16-byte aligned");
+    return hip_check(gs::launch_preprocess(*cam, n, means, scales, quats, opacity, sh, sh_degree,
+                                           rgb_in, (float4*)xy_depth, (float4*)conic_op,
+                                           (float4*)rgb, tiles_touched, (hipStream_t)stream),
+                     "gs_preprocess launch");
+}
+
+gs_status gs_bin_and_sort(const gs_camera* cam, int32_t n, const float* xy_depth,
+                          const uint32_t* tiles_touched, uint64_t* keys, uint32_t* point_list,
+                          int64_t capacity, void* scratch, size_t* scratch_bytes,
+                          int64_t* n_entries, void* stream) {
+    g_last_error.clear();
+    if (gs_status s = check_camera(cam)) return s;
+    if (n < 0 || n > GS_MAX_GAUSSIANS) return fail(GS_ERR_INVALID, "n = %d outside [0, %d]", n, GS_MAX_GAUSSIANS);
+    if (capacity < 0 || capacity > (int64_t)UINT32_MAX)
+        return fail(GS_ERR_INVALID, "capacity %lld outside [0, 2^32 - 1]", (long long)capacity);
+    if (!scratch_bytes) return fail(GS_ERR_INVALID, "scratch_bytes is NULL");
+    gs::BinScratch s{};
+    const size_t need = gs::bin_scratch_layout(n, capacity, nullptr, nullptr);
+    if (!scratch) {
+        *scratch_bytes = need;
+        return GS_OK;
+    }
+    if (!n_entries) return fail(GS_ERR_INVALID, "n_entries is NULL");
+    if (*scratch_bytes < need)
+        return fail(GS_ERR_INVALID, "scratch of %zu bytes is smaller than the %zu required",
+                    *scratch_bytes, need);
+    if ((uintptr_t)scratch & 255) return fail(GS_ERR_INVALID, "scratch must be 256-byte aligned");
+    *n_entries = 0;
+    if (n == 0) return GS_OK;
+    if (!xy_depth || !tiles_touched || (capacity > 0 && (!keys || !point_list)))
+        return fail(GS_ERR_INVALID, "gs_bin_and_sort: a required pointer is NULL");
+    gs::bin_scratch_layout(n, capacity, &s, scratch);
+    hipStream_t st = (hipStream_t)stream;
+
+    const int key_bits = 32 + tile_bits(*cam);
+    const bool in_tmp = gs::radix_input_in_tmp(key_bits);
+    if (gs_status e = hip_check(
+            gs::launch_scan_and_duplicate(*cam, n, (const float4*)xy_depth, tiles_touched, s,
+                                          in_tmp ? s.keys_tmp : keys, in_tmp ? s.vals_tmp : point_list,
+                                          (uint64_t)capacity, st),
+            "scan/duplicate launch"))
+        return e;
+    uint64_t total = 0;
+    if (gs_status e = hip_check(hipMemcpyAsync(&total, s.total, sizeof(total), hipMemcpyDeviceToHost, st),
+                                "entry count copy"))
+        return e;
+    if (gs_status e = hip_check(hipStreamSynchronize(st), "entry count sync")) return e;
+    *n_entries = (int64_t)total;
+    if (total > (uint64_t)UINT32_MAX)
+        return fail(GS_ERR_OVERFLOW, "%llu entries do not fit in 32 bits", (unsigned long long)total);
+    if ((int64_t)total > capacity)
+        return fail(GS_ERR_CAPACITY, "%llu entries exceed the capacity %lld",
+                    (unsigned long long)total, (long long)capacity);
+    return hip_check(gs::launch_radix_sort(keys, point_list, (uint32_t)total, key_bits, s, st),
+                     "radix sort launch");
+}
+
+gs_status gs_tile_ranges(const gs_camera* cam, const uint64_t* keys, int64_t n_entries,
+                         uint32_t* ranges, void* stream) {
+    g_last_error.clear();
+    if (gs_status s = check_camera(cam)) return s;
+    if (n_entries < 0 || n_entries > (int64_t)UINT32_MAX)
+        return fail(GS_ERR_INVALID, "n_entries %lld outside [0, 2^32 - 1]", (long long)n_entries);
+    if (!ranges || (n_entries > 0 && !keys)) return fail(GS_ERR_INVALID, "gs_tile_ranges: NULL pointer");
+    const int n_tiles = gs::tiles_x(*cam) * gs::tiles_y(*cam);
+    return hip_check(gs::launch_tile_ranges(keys, (uint32_t)n_entries, n_tiles, ranges, (hipStream_t)stream),
+                     "tile ranges launch");
+}
+
+gs_status gs_composite_fwd(const gs_camera* cam, const uint32_t* ranges, const uint32_t* point_list,
+                           const float* xy_depth, const float* conic_op, const float* rgb,
+                           const float bg[3], float* image, float* final_T, uint32_t* n_contrib,
+                           uint32_t* n_examined, void* stream) {
+    g_last_error.clear();
+    if (gs_status s = check_camera(cam)) return s;
+    if (!ranges || !bg || !image || !final_T || !n_contrib)
+        return fail(GS_ERR_INVALID, "gs_composite_fwd: a required pointer is NULL");
+    if (((uintptr_t)xy_depth | (uintptr_t)conic_op | (uintptr_t)rgb) & 15)
+        return fail(GS_ERR_INVALID, "gs_composite_fwd: float4 inputs must be 16-byte aligned");
+    const float3 b = make_float3(bg[0], bg[1], bg[2]);
+    return hip_check(gs::launch_composite_fwd(*cam, ranges, point_list, (const float4*)xy_depth,
+                                              (const float4*)conic_op, (const float4*)rgb, b, image,
+                                              final_T, n_contrib, n_examined, (hipStream_t)stream),
+                     "composite fwd launch");
+}
+
+gs_status gs_composite_bwd(const gs_camera* cam, int32_t n, const uint32_t* ranges,
+                           const uint32_t* point_list, const float* xy_depth,
+                           const float* conic_op, const float* rgb, const float bg[3],
+                           const float* final_T, const uint32_t* n_contrib,
+                           const float* dL_dimage, float* grad_mean2d, float* grad_conic_op,
+                           float* grad_rgb, void* stream) {
+    g_last_error.clear();
+    if (gs_status s = check_camera(cam)) return s;
+    if (n < 0 || n > GS_MAX_GAUSSIANS) return fail(GS_ERR_INVALID, "n = %d outside [0, %d]", n, GS_MAX_GAUSSIANS);
+    if (!ranges || !bg || !final_T || !n_contrib || !dL_dimage)
+        return fail(GS_ERR_INVALID, "gs_composite_bwd: a required pointer is NULL");
+    if (n > 0 && (!grad_mean2d || !grad_conic_op || !grad_rgb))
+        return fail(GS_ERR_INVALID, "gs_composite_bwd: a gradient pointer is NULL");
+    if (((uintptr_t)xy_depth | (uintptr_t)conic_op | (uintptr_t)rgb | (uintptr_t)grad_conic_op |
+         (uintptr_t)grad_rgb) & 15 || ((uintptr_t)grad_mean2d & 7))
+        return fail(GS_ERR_INVALID, "gs_composite_bwd: misaligned vector buffer");
+    const float3 b = make_float3(bg[0], bg[1], bg[2]);
+    return hip_check(gs::launch_composite_bwd(*cam, n, ranges, point_list, (const float4*)xy_depth,
+                                              (const float4*)conic_op, (const float4*)rgb, b, final_T,
+                                              n_contrib, dL_dimage, (float2*)grad_mean2d,
+                                              (float4*)grad_conic_op, (float4*)grad_rgb,
+                                              (hipStream_t)stream),
+                     "composite bwd launch");
+}
+
+}  // extern "C"

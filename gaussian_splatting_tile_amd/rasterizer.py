@@ -1,0 +1,245 @@
+"""Thin torch binding over the libgs C ABI.
+
+torch supplies device memory and the current HIP stream; every step of the
+path runs in libgs's kernels. Function names mirror the C entry points
+(gs_preprocess -> preprocess, ...). Inputs must be contiguous float32 /
+uint32-compatible tensors on a ROCm device.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+from . import _lib
+
+TILE = 16
+
+
+def camera(cam: dict) -> _lib.GsCamera:
+    """Build the C camera struct from a dict (R [9] row-major world->camera,
+    t [3], campos [3], fx, fy, cx, cy, width, height)."""
+    c = _lib.GsCamera()
+    c.R[:] = [float(x) for x in np.asarray(cam["R"], np.float32).reshape(9)]
+    c.t[:] = [float(x) for x in np.asarray(cam["t"], np.float32).reshape(3)]
+    c.campos[:] = [float(x) for x in np.asarray(cam["campos"], np.float32).reshape(3)]
+    c.fx, c.fy = float(np.float32(cam["fx"])), float(np.float32(cam["fy"]))
+    c.cx, c.cy = float(np.float32(cam["cx"])), float(np.float32(cam["cy"]))
+    c.width, c.height = int(cam["width"]), int(cam["height"])
+    return c
+
+
+def tiles_xy(cam: dict):
+    return (int(cam["width"]) + TILE - 1) // TILE, (int(cam["height"]) + TILE - 1) // TILE
+
+
+def _cam(cam):
+    return cam if isinstance(cam, _lib.GsCamera) else camera(cam)
+
+
+def _ptr(t, dtype=None, name="tensor"):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise TypeError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def constants():
+    out = np.zeros(9, np.float32)
+    _lib.load().gs_constants(out.ctypes.data_as(ctypes.c_void_p))
+    return out
+
+
+def version():
+    out = np.zeros(3, np.int32)
+    _lib.load().gs_version(out.ctypes.data_as(ctypes.c_void_p))
+    return tuple(int(x) for x in out)
+
+
+def preprocess(cam, means, scales, quats, opacity, sh=None, sh_degree=0, rgb_in=None, out=None,
+               stream=None):
+    """gs_preprocess. Returns dict xy_depth [n,4], conic_op [n,4], rgb [n,4], tiles_touched [n]."""
+    n = int(opacity.shape[0])
+    dev = opacity.device
+    if out is None:
+        out = dict(xy_depth=torch.empty((n, 4), dtype=torch.float32, device=dev),
+                   conic_op=torch.empty((n, 4), dtype=torch.float32, device=dev),
+                   rgb=torch.empty((n, 4), dtype=torch.float32, device=dev),
+                   tiles_touched=torch.empty((n,), dtype=torch.int32, device=dev))
+    f32, i32 = torch.float32, torch.int32
+    c = _cam(cam)
+    _lib.check(_lib.load().gs_preprocess(
+        ctypes.byref(c), n, _ptr(means, f32, "means"), _ptr(scales, f32, "scales"),
+        _ptr(quats, f32, "quats"), _ptr(opacity, f32, "opacity"), _ptr(sh, f32, "sh"),
+        int(sh_degree), _ptr(rgb_in, f32, "rgb_in"), _ptr(out["xy_depth"], f32),
+        _ptr(out["conic_op"], f32), _ptr(out["rgb"], f32), _ptr(out["tiles_touched"], i32),
+        _stream(stream)))
+    return out
+
+
+class BinBuffers:
+    """Entry buffers (keys, point_list, scratch) reused across frames; grown
+    on demand when a frame needs more entries than the capacity."""
+
+    def __init__(self, device, capacity: int = 1 << 20):
+        self.device = device
+        self.capacity = 0
+        self.keys = self.point_list = self.scratch = None
+        self.n_scratch = -1
+        self._ensure(int(capacity))
+
+    def _ensure(self, capacity: int):
+        if capacity > self.capacity:
+            self.capacity = capacity
+            self.keys = torch.empty((capacity,), dtype=torch.int64, device=self.device)
+            self.point_list = torch.empty((capacity,), dtype=torch.int32, device=self.device)
+            self.scratch = None
+
+    def scratch_for(self, c, n: int):
+        need = ctypes.c_size_t(0)
+        _lib.check(_lib.load().gs_bin_and_sort(ctypes.byref(c), n, None, None, None, None,
+                                               self.capacity, None, ctypes.byref(need), None, None))
+        if self.scratch is None or self.scratch.numel() < need.value:
+            self.scratch = torch.empty((max(int(need.value), 256),), dtype=torch.uint8,
+                                       device=self.device)
+        return self.scratch
+
+
+def bin_and_sort(cam, xy_depth, tiles_touched, buffers: BinBuffers | None = None, stream=None):
+    """gs_bin_and_sort. Returns (keys int64 [E] (uint64 bits), point_list int32 [E], E).
+
+    Grows the buffers and retries once if the entry count exceeds capacity.
+    """
+    c = _cam(cam)
+    n = int(tiles_touched.shape[0])
+    if buffers is None:
+        buffers = BinBuffers(xy_depth.device, capacity=max(1024, 16 * n))
+    lib = _lib.load()
+    for attempt in range(2):
+        scratch = buffers.scratch_for(c, n)
+        nbytes = ctypes.c_size_t(scratch.numel())
+        n_entries = ctypes.c_int64(0)
+        st = lib.gs_bin_and_sort(ctypes.byref(c), n, _ptr(xy_depth, torch.float32, "xy_depth"),
+                                 _ptr(tiles_touched, torch.int32, "tiles_touched"),
+                                 _ptr(buffers.keys), _ptr(buffers.point_list), buffers.capacity,
+                                 _ptr(scratch), ctypes.byref(nbytes), ctypes.byref(n_entries),
+                                 _stream(stream))
+        if st == _lib.GS_ERR_CAPACITY and attempt == 0:
+            buffers._ensure(int(n_entries.value * 5 // 4 + 1024))
+            continue
+        _lib.check(st)
+        E = int(n_entries.value)
+        return buffers.keys[:E], buffers.point_list[:E], E
+    raise AssertionError("unreachable")
+
+
+def tile_ranges(cam, keys, n_entries: int, out=None, stream=None):
+    """gs_tile_ranges. Returns ranges int32 [TX*TY, 2] (uint32 values)."""
+    TX, TY = tiles_xy(cam if isinstance(cam, dict) else
+                      dict(width=cam.width, height=cam.height))
+    if out is None:
+        out = torch.empty((TX * TY, 2), dtype=torch.int32, device=keys.device)
+    c = _cam(cam)
+    _lib.check(_lib.load().gs_tile_ranges(ctypes.byref(c), _ptr(keys, torch.int64, "keys"),
+                                          int(n_entries), _ptr(out, torch.int32), _stream(stream)))
+    return out
+
+
+def composite_fwd(cam, ranges, point_list, xy_depth, conic_op, rgb, bg=(0.0, 0.0, 0.0),
+                  with_examined=False, out=None, stream=None):
+    """gs_composite_fwd. Returns dict image [3,H,W], final_T [H,W], n_contrib [H,W] (int32),
+    and n_examined [H,W] when requested."""
+    W, H = (cam["width"], cam["height"]) if isinstance(cam, dict) else (cam.width, cam.height)
+    dev = xy_depth.device
+    if out is None:
+        out = dict(image=torch.empty((3, H, W), dtype=torch.float32, device=dev),
+                   final_T=torch.empty((H, W), dtype=torch.float32, device=dev),
+                   n_contrib=torch.empty((H, W), dtype=torch.int32, device=dev))
+        if with_examined:
+            out["n_examined"] = torch.empty((H, W), dtype=torch.int32, device=dev)
+    bgc = (ctypes.c_float * 3)(*[float(x) for x in bg])
+    c = _cam(cam)
+    _lib.check(_lib.load().gs_composite_fwd(
+        ctypes.byref(c), _ptr(ranges, torch.int32, "ranges"), _ptr(point_list, torch.int32, "point_list"),
+        _ptr(xy_depth, torch.float32), _ptr(conic_op, torch.float32), _ptr(rgb, torch.float32),
+        ctypes.cast(bgc, ctypes.c_void_p), _ptr(out["image"]), _ptr(out["final_T"]),
+        _ptr(out["n_contrib"]), _ptr(out.get("n_examined")), _stream(stream)))
+    return out
+
+
+def composite_bwd(cam, n, ranges, point_list, xy_depth, conic_op, rgb, final_T, n_contrib,
+                  dL_dimage, bg=(0.0, 0.0, 0.0), out=None, stream=None):
+    """gs_composite_bwd. Returns dict grad_mean2d [n,2], grad_conic_op [n,4], grad_rgb [n,4]."""
+    dev = xy_depth.device
+    if out is None:
+        out = dict(grad_mean2d=torch.empty((n, 2), dtype=torch.float32, device=dev),
+                   grad_conic_op=torch.empty((n, 4), dtype=torch.float32, device=dev),
+                   grad_rgb=torch.empty((n, 4), dtype=torch.float32, device=dev))
+    bgc = (ctypes.c_float * 3)(*[float(x) for x in bg])
+    c = _cam(cam)
+    _lib.check(_lib.load().gs_composite_bwd(
+        ctypes.byref(c), int(n), _ptr(ranges, torch.int32, "ranges"),
+        _ptr(point_list, torch.int32, "point_list"), _ptr(xy_depth, torch.float32),
+        _ptr(conic_op, torch.float32), _ptr(rgb, torch.float32), ctypes.cast(bgc, ctypes.c_void_p),
+        _ptr(final_T, torch.float32, "final_T"), _ptr(n_contrib, torch.int32, "n_contrib"),
+        _ptr(dL_dimage, torch.float32, "dL_dimage"), _ptr(out["grad_mean2d"]),
+        _ptr(out["grad_conic_op"]), _ptr(out["grad_rgb"]), _stream(stream)))
+    return out
+
+
+@dataclass
+class Scene:
+    """Device-resident Gaussian parameters in the C-ABI layouts."""
+    means: torch.Tensor
+    scales: torch.Tensor
+    quats: torch.Tensor
+    opacity: torch.Tensor
+    sh: torch.Tensor | None = None
+    sh_degree: int = 0
+    rgb: torch.Tensor | None = None
+
+    @property
+    def n(self) -> int:
+        return int(self.opacity.shape[0])
+
+    @staticmethod
+    def from_numpy(d: dict, device="cuda") -> "Scene":
+        t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(device)
+        return Scene(t(d["means"]), t(d["scales"]), t(d["quats"]), t(d["opacity"]), t(d.get("sh")),
+                     int(d.get("sh_degree", 0)), t(d.get("rgb")))
+
+
+class Rasterizer:
+    """Runs the whole path for one camera at a time, reusing its buffers."""
+
+    def __init__(self, device="cuda", capacity: int = 1 << 20):
+        self.device = torch.device(device)
+        self.bins = BinBuffers(self.device, capacity)
+
+    def forward(self, cam: dict, scene: Scene, bg=(0.0, 0.0, 0.0), with_examined=False):
+        c = camera(cam)
+        pre = preprocess(c, scene.means, scene.scales, scene.quats, scene.opacity, scene.sh,
+                         scene.sh_degree, scene.rgb)
+        keys, point_list, E = bin_and_sort(c, pre["xy_depth"], pre["tiles_touched"], self.bins)
+        ranges = tile_ranges(cam, keys, E)
+        fwd = composite_fwd(cam, ranges, point_list, pre["xy_depth"], pre["conic_op"], pre["rgb"], bg,
+                            with_examined=with_examined)
+        out = dict(pre)
+        out.update(keys=keys, point_list=point_list, n_entries=E, ranges=ranges, **fwd)
+        return out
+
+    def backward(self, cam: dict, scene: Scene, fwd: dict, dL_dimage, bg=(0.0, 0.0, 0.0)):
+        return composite_bwd(cam, scene.n, fwd["ranges"], fwd["point_list"], fwd["xy_depth"],
+                             fwd["conic_op"], fwd["rgb"], fwd["final_T"], fwd["n_contrib"], dL_dimage, bg)

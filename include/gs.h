@@ -1,0 +1,230 @@
+/*
+ * gs.h - C ABI of libgs, a tile-based 3D Gaussian Splatting rasterizer for
+ * AMD Instinct MI355X (gfx950), forward and backward.
+ *
+ * The pipeline follows the pages it was built from:
+ *   - "rigel" (GitHub README), sections "Projection", "Binning",
+ *     "Rasterization", "Backward" and "Deliberate differences";
+ *   - "3D Gaussian Splatting ビューワを作る" (zenn.dev), sections 2.1-2.3
+ *     (preprocess), 4.1 (prefix scan), 4.2 (duplicate), 4.3 (radix sort),
+ *     4.4 (tile ranges) and 4.5 (tile render);
+ *   - "11 - Tiles: the actual 3DGS design" (learn-gs notebook): constants,
+ *     prep_splats, tile_spans, build_tile_lists and the tiled kernel loop.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Memory: every array argument is a DEVICE pointer unless marked (host).
+ *    The caller owns all memory; libgs never allocates device memory.
+ *    Scratch space follows a size-query protocol: call with scratch == NULL
+ *    to receive the required byte count in *scratch_bytes; nothing is
+ *    launched by such a call.
+ *  - Streams: `stream` is a hipStream_t passed as void* (NULL = the null
+ *    stream). Work is enqueued asynchronously; the only call that blocks the
+ *    host is gs_bin_and_sort, which waits once to read the entry count.
+ *  - Errors: every call returns a gs_status. Arguments are validated on the
+ *    host before anything is launched; on GS_ERR_INVALID nothing was
+ *    enqueued. gs_last_error() gives a message for the calling thread. HIP
+ *    failures are reported as GS_ERR_HIP.
+ *  - Layouts: per-Gaussian inputs are structure-of-arrays, component-major
+ *    float32: means/scales [3][n], quats [4][n] as (w, x, y, z), opacity
+ *    [n], sh [(d+1)^2][3][n]. Per-Gaussian outputs are packed float4
+ *    records [n][4]. Images are planar [3][H][W] float32; per-pixel buffers
+ *    are [H][W]. Every output is overwritten, never accumulated into.
+ *  - Tiles are 16 x 16 pixels; TX = ceil(W / 16), TY = ceil(H / 16); tile id
+ *    t = ty * TX + tx. Pixel (x, y) is sampled at the integer point (x, y).
+ *  - Limits: 0 <= n <= GS_MAX_GAUSSIANS; 1 <= width, height <= GS_MAX_DIM.
+ */
+#ifndef GS_H
+#define GS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GS_TILE 16
+#define GS_MAX_GAUSSIANS (1 << 24) /* prefix-scan capacity, 256^3 */
+#define GS_MAX_DIM 16384
+
+typedef enum {
+    GS_OK = 0,
+    GS_ERR_INVALID = 1,  /* bad argument; nothing enqueued */
+    GS_ERR_CAPACITY = 2, /* entry count exceeds the caller's capacity */
+    GS_ERR_OVERFLOW = 3, /* entry count does not fit in 32 bits */
+    GS_ERR_HIP = 4       /* a HIP runtime call failed */
+} gs_status;
+
+/* Pinhole camera, passed by host pointer. p_cam = R p + t with R row-major
+ * world-to-camera; +z looks forward, image y grows downward. campos is the
+ * camera centre in world space (-R^T t), used for the SH view direction.
+ * fx, fy, cx, cy are in pixels and must be finite with fx, fy > 0.
+ * ("rigel" README, "Deliberate differences": row-major world-to-camera
+ * matrices and explicit pinhole intrinsics.) */
+typedef struct {
+    float R[9];
+    float t[3];
+    float campos[3];
+    float fx, fy, cx, cy;
+    int32_t width, height;
+} gs_camera;
+
+/* Library constants, in this order: tile size, dilation (0.3), near plane
+ * (0.05), frustum clamp (1.3), discriminant floor (0.1), sigma (3), alpha
+ * floor (1/255), alpha cap (0.99), transmittance stop (1e-4). (learn-gs
+ * constants block; "rigel" README "Projection"; zenn section 2.3.3.)
+ * out: host array of 9 floats. */
+void gs_constants(float out[9]);
+
+/* Message describing the last failure on the calling thread ("" if none). */
+const char* gs_last_error(void);
+
+/* Library version as (major, minor, patch), written to out (host). */
+void gs_version(int32_t out[3]);
+
+/* ---------------------------------------------------------------------
+ * gs_preprocess - project every Gaussian to a screen-space splat.
+ * ("rigel" README "Projection"; zenn 2.1.1-2.1.2, 2.2.3, 2.3.1, 2.3.3;
+ * learn-gs prep_splats and tile_spans.)
+ *
+ * Per Gaussian g: camera transform; cull unless z > 0.05; pinhole centre
+ * (u, v); quaternion normalised to R(q); Sigma = R S S^T R^T; J built at the
+ * centre with x/z and y/z clamped to 1.3x the frustum half-width;
+ * Sigma_2d = (J W) Sigma (J W)^T + 0.3 I; cull unless det > 0; conic
+ * (A, B, C) = (c, -b, a) / det; radius r = ceil(3 sqrt(lambda_max)) with the
+ * discriminant floored at 0.1; tile span [x0, x1) x [y0, y1) with
+ * x0 = clamp(floor((u - r) / 16), 0, TX), x1 = clamp(floor((u + r) / 16) + 1,
+ * 0, TX) (same in y); cull if the span is empty. Colour from SH degree
+ * 0..sh_degree at the unit direction (mean - campos), or copied from rgb_in.
+ * Any non-finite intermediate or output also culls. A culled Gaussian's
+ * outputs are all zero.
+ *
+ *   cam            (host) camera
+ *   n              number of Gaussians
+ *   means, scales  [3][n] float32; scales are positive (already activated)
+ *   quats          [4][n] float32 (w, x, y, z), need not be unit
+ *   opacity        [n] float32 in (0, 1) (already activated)
+ *   sh             [(sh_degree+1)^2][3][n] float32, or NULL
+ *   sh_degree      0..3 (ignored when sh == NULL)
+ *   rgb_in         [3][n] float32; required iff sh == NULL
+ *   xy_depth       out [n][4]: (u, v, z, r)
+ *   conic_op       out [n][4]: (A, B, C, opacity)
+ *   rgb            out [n][4]: (r, g, b, 0)
+ *   tiles_touched  out [n] uint32: span area (0 = culled)
+ * Every floating-point result is computed in float32 with a fixed operation
+ * order and no contraction, so it is bit-identical to a host evaluation of
+ * the same formulas.
+ * ------------------------------------------------------------------- */
+gs_status gs_preprocess(const gs_camera* cam, int32_t n, const float* means, const float* scales,
+                        const float* quats, const float* opacity, const float* sh,
+                        int32_t sh_degree, const float* rgb_in, float* xy_depth, float* conic_op,
+                        float* rgb, uint32_t* tiles_touched, void* stream);
+
+/* ---------------------------------------------------------------------
+ * gs_bin_and_sort - duplicate splats into tile entries and sort them.
+ * ("rigel" README "Binning"; zenn 4.1-4.3; learn-gs build_tile_lists.)
+ *
+ * Exclusive prefix sum of tiles_touched gives Gaussian g the private slice
+ * [offset_g, offset_g + tiles_touched[g]) of the entry array; g writes one
+ * entry per tile of its span, ty outer and tx inner, with
+ *     key   = (uint64)(ty * TX + tx) << 32 | float_bits(z_g)
+ *     value = g.
+ * The entries are then sorted by key with a stable LSD radix sort over the
+ * key bits a tile id can occupy (32 + ceil(log2(TX*TY))), so equal keys keep
+ * Gaussian-index order. The entry count E is copied to the host: this is
+ * the call's one host synchronisation.
+ *
+ *   cam, n         as gs_preprocess; n <= GS_MAX_GAUSSIANS
+ *   xy_depth       [n][4] from gs_preprocess
+ *   tiles_touched  [n] from gs_preprocess
+ *   keys           out [capacity] uint64: sorted keys (first E valid)
+ *   point_list     out [capacity] uint32: Gaussian ids in sorted order
+ *   capacity       entries the caller allocated
+ *   scratch        device workspace of *scratch_bytes bytes (256-byte
+ *                  aligned), or NULL to query the size
+ *   scratch_bytes  (host) in: size of scratch; out: required size, which
+ *                  depends on n, capacity and the camera's tile count
+ *   n_entries      (host) out: E
+ * Returns GS_ERR_CAPACITY (with *n_entries = E, keys/point_list
+ * unspecified) when E > capacity, GS_ERR_OVERFLOW when E >= 2^32.
+ * ------------------------------------------------------------------- */
+gs_status gs_bin_and_sort(const gs_camera* cam, int32_t n, const float* xy_depth,
+                          const uint32_t* tiles_touched, uint64_t* keys, uint32_t* point_list,
+                          int64_t capacity, void* scratch, size_t* scratch_bytes,
+                          int64_t* n_entries, void* stream);
+
+/* ---------------------------------------------------------------------
+ * gs_tile_ranges - per-tile [start, end) of the sorted entries.
+ * (zenn 4.4.1-4.4.2; "rigel" README "Binning": the range kernel.)
+ *
+ *   keys       [n_entries] sorted keys from gs_bin_and_sort
+ *   n_entries  E
+ *   ranges     out [TX*TY][2] uint32: (start, end); (0, 0) for an empty tile
+ * ------------------------------------------------------------------- */
+gs_status gs_tile_ranges(const gs_camera* cam, const uint64_t* keys, int64_t n_entries,
+                         uint32_t* ranges, void* stream);
+
+/* ---------------------------------------------------------------------
+ * gs_composite_fwd - front-to-back alpha compositing per tile.
+ * ("rigel" README "Rasterization"; zenn 4.5; learn-gs "The kernel".)
+ *
+ * For pixel (x, y) in tile t, over j = start_t .. end_t - 1 with
+ * g = point_list[j]: dx = x - u_g, dy = y - v_g,
+ * power = -0.5 (A dx^2 + C dy^2) - B dx dy, alpha = min(0.99, o exp(power));
+ * alpha < 1/255 is skipped; otherwise C += c alpha T, T *= 1 - alpha, and
+ * the pixel stops once T < 1e-4 (the splat that crossed is included).
+ * image = C + T bg.
+ *
+ *   ranges, point_list     from gs_tile_ranges / gs_bin_and_sort
+ *   xy_depth, conic_op, rgb  [n][4] from gs_preprocess
+ *   bg          (host) 3 floats, background colour
+ *   image       out [3][H][W]
+ *   final_T     out [H][W]: transmittance left at the pixel
+ *   n_contrib   out [H][W] uint32: 1 + list position (within the tile) of
+ *               the last contributing splat, 0 if none
+ *   n_examined  out [H][W] uint32, or NULL: splats evaluated before the
+ *               pixel stopped (diagnostic; pixel-splat evaluations)
+ * ------------------------------------------------------------------- */
+gs_status gs_composite_fwd(const gs_camera* cam, const uint32_t* ranges, const uint32_t* point_list,
+                           const float* xy_depth, const float* conic_op, const float* rgb,
+                           const float bg[3], float* image, float* final_T, uint32_t* n_contrib,
+                           uint32_t* n_examined, void* stream);
+
+/* ---------------------------------------------------------------------
+ * gs_composite_bwd - reverse walk of the compositing, per tile.
+ * ("rigel" README "Backward" and "Deliberate differences"; learn-gs "The
+ * next live problem".)
+ *
+ * Each pixel walks its tile's list from n_contrib - 1 down to 0, undoing
+ * T_j = T_{j+1} / (1 - alpha_j) from final_T and carrying the colour behind
+ * the current splat (starting from bg). With g_pix = dL/dI:
+ *   dL/dc      += alpha T_j g_pix
+ *   dL/dalpha   = T_j sum_ch g_pix,ch (c_ch - behind_ch)
+ * and, unless the alpha was clamped (o G > 0.99, then nothing more):
+ *   dL/do += G dL/dalpha; with dp = alpha dL/dalpha:
+ *   dA += -0.5 dx^2 dp, dB += -dx dy dp, dC += -0.5 dy^2 dp,
+ *   du += (A dx + B dy) dp, dv += (B dx + C dy) dp.
+ * Sums over all pixels are formed on the device; the summation order is
+ * not fixed, so results agree with an exact sum to float32 rounding.
+ *
+ *   n                 number of Gaussians (size of the gradient arrays)
+ *   ranges, point_list, xy_depth, conic_op, rgb, bg: as gs_composite_fwd
+ *   final_T, n_contrib  from gs_composite_fwd
+ *   dL_dimage         [3][H][W] upstream gradient
+ *   grad_mean2d       out [n][2]: (du, dv)
+ *   grad_conic_op     out [n][4]: (dA, dB, dC, dopacity)
+ *   grad_rgb          out [n][4]: (dr, dg, db, 0)
+ * ------------------------------------------------------------------- */
+gs_status gs_composite_bwd(const gs_camera* cam, int32_t n, const uint32_t* ranges,
+                           const uint32_t* point_list, const float* xy_depth,
+                           const float* conic_op, const float* rgb, const float bg[3],
+                           const float* final_T, const uint32_t* n_contrib,
+                           const float* dL_dimage, float* grad_mean2d, float* grad_conic_op,
+                           float* grad_rgb, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GS_H */

@@ -1,0 +1,124 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, it
+exports every function include/gs.h declares, its constants agree with the
+oracle's, and argument validation rejects bad calls before launching."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gs.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(gs_[a-z_0-9]+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def gs():
+    import gaussian_splatting_tile_amd as pkg
+    from gaussian_splatting_tile_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libgs.so is not built: run __graft_entry__.build()")
+    return _lib.load()
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for required in ("gs_preprocess", "gs_bin_and_sort", "gs_tile_ranges", "gs_composite_fwd",
+                     "gs_composite_bwd", "gs_last_error", "gs_constants"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(gs):
+    from gaussian_splatting_tile_amd import _lib
+    names = declared_functions()
+    assert sorted(_lib.EXPORTS) == names
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (gs_[a-z_0-9]+)$", out, flags=re.M))
+    for name in names:
+        assert name in exported, name
+        assert hasattr(gs, name)
+
+
+def test_constants_match_oracle(gs, orc):
+    import gaussian_splatting_tile_amd as pkg
+    np.testing.assert_array_equal(pkg.constants(), orc.constants())
+    assert pkg.version() == (0, 1, 0)
+
+
+def _cam(**kw):
+    from gaussian_splatting_tile_amd import _lib
+    import synth
+    from gaussian_splatting_tile_amd.rasterizer import camera
+    c = synth.look_at_camera((0, 0, -4), (0, 0, 0), 64, 64, 64.0, 64.0)
+    c.update(kw)
+    return camera(c)
+
+
+def test_invalid_arguments_rejected_before_launch(gs):
+    from gaussian_splatting_tile_amd import _lib
+    P = ctypes.c_void_p
+    dummy = P(256)  # never dereferenced: validation fails first
+    c = _cam()
+    # NULL camera
+    assert gs.gs_preprocess(None, 1, dummy, dummy, dummy, dummy, None, 0, dummy, dummy, dummy,
+                            dummy, dummy, None) == _lib.GS_ERR_INVALID
+    assert b"camera" in gs.gs_last_error()
+    # negative n
+    assert gs.gs_preprocess(ctypes.byref(c), -1, dummy, dummy, dummy, dummy, None, 0, dummy, dummy,
+                            dummy, dummy, dummy, None) == _lib.GS_ERR_INVALID
+    # sh degree out of range
+    assert gs.gs_preprocess(ctypes.byref(c), 4, dummy, dummy, dummy, dummy, dummy, 4, None, dummy,
+                            dummy, dummy, dummy, None) == _lib.GS_ERR_INVALID
+    # no colour source
+    assert gs.gs_preprocess(ctypes.byref(c), 4, dummy, dummy, dummy, dummy, None, 0, None, dummy,
+                            dummy, dummy, dummy, None) == _lib.GS_ERR_INVALID
+    # bad image sizes / focal lengths
+    for bad in (_cam(width=0), _cam(height=-3), _cam(width=20000), _cam(fx=0.0),
+                _cam(fy=float("nan")), _cam(cx=float("inf"))):
+        assert gs.gs_tile_ranges(ctypes.byref(bad), None, 0, dummy, None) == _lib.GS_ERR_INVALID
+    # n == 0 is a valid no-op
+    assert gs.gs_preprocess(ctypes.byref(c), 0, None, None, None, None, None, 0, None, None, None,
+                            None, None, None) == _lib.GS_OK
+    # misaligned float4 buffer
+    assert gs.gs_composite_fwd(ctypes.byref(c), dummy, dummy, P(260), dummy, dummy,
+                               (ctypes.c_float * 3)(), dummy, dummy, dummy, None, None) == _lib.GS_ERR_INVALID
+
+
+def test_bin_scratch_size_query(gs):
+    from gaussian_splatting_tile_amd import _lib
+    c = _cam()
+    need = ctypes.c_size_t(0)
+    assert gs.gs_bin_and_sort(ctypes.byref(c), 1000, None, None, None, None, 5000, None,
+                              ctypes.byref(need), None, None) == _lib.GS_OK
+    small = need.value
+    assert small > 5000 * 12
+    assert gs.gs_bin_and_sort(ctypes.byref(c), 1000, None, None, None, None, 50000, None,
+                              ctypes.byref(need), None, None) == _lib.GS_OK
+    assert need.value > small
+    # a scratch buffer smaller than required is rejected
+    nbytes = ctypes.c_size_t(small - 1)
+    e = ctypes.c_int64(0)
+    assert gs.gs_bin_and_sort(ctypes.byref(c), 1000, ctypes.c_void_p(256), ctypes.c_void_p(256),
+                              ctypes.c_void_p(256), ctypes.c_void_p(256), 5000, ctypes.c_void_p(256),
+                              ctypes.byref(nbytes), ctypes.byref(e), None) == _lib.GS_ERR_INVALID
+    # capacity beyond 32-bit entry indices is rejected
+    assert gs.gs_bin_and_sort(ctypes.byref(c), 10, None, None, None, None, 1 << 33, None,
+                              ctypes.byref(need), None, None) == _lib.GS_ERR_INVALID
+
+
+def test_binding_refuses_host_tensors(gs):
+    import torch
+    import gaussian_splatting_tile_amd as pkg
+    import synth
+    cam = synth.look_at_camera((0, 0, -4), (0, 0, 0), 64, 64, 64.0, 64.0)
+    x = torch.zeros((3, 4))
+    with pytest.raises(TypeError):
+        pkg.preprocess(cam, x, x, torch.zeros((4, 4)), torch.zeros(4), rgb_in=x)
