@@ -379,6 +379,13 @@ void orc_tile_ranges(const orc_camera* cam, const uint64_t* keys, int64_t n_entr
 
 namespace {
 
+// The exponential of the compositing step. The pages leave its precision
+// open; in fp32 it is the correctly rounded value (evaluated in double and
+// rounded once), so the alpha-floor and stop decisions are taken on an
+// exactly defined number. In fp64 it is the double exponential.
+inline float exp_rn(float x) { return (float)std::exp((double)x); }
+inline double exp_rn(double x) { return std::exp(x); }
+
 // Forward compositing of one image, front to back per pixel over its tile's
 // depth-sorted list.
 //   [rigel] "Rasterization": power = -0.5 (A dx^2 + C dy^2) - B dx dy,
@@ -408,7 +415,7 @@ void composite_fwd(const orc_camera* cam, const uint32_t* ranges, const uint32_t
                 const F dx = (F)x - xy_depth[4 * (size_t)g + 0];
                 const F dy = (F)y - xy_depth[4 * (size_t)g + 1];
                 const F power = (F)(-0.5) * ((co[0] * dx) * dx + (co[2] * dy) * dy) - (co[1] * dx) * dy;
-                const F G = std::exp(power);
+                const F G = exp_rn(power);
                 const F alpha = std::min(alpha_max, co[3] * G);
                 examined = j - start + 1;
                 if (alpha < alpha_min) continue;
@@ -466,7 +473,7 @@ void composite_bwd(const orc_camera* cam, int32_t n, const uint32_t* ranges,
                 const F dx = (F)x - xy_depth[4 * (size_t)g + 0];
                 const F dy = (F)y - xy_depth[4 * (size_t)g + 1];
                 const F power = (F)(-0.5) * ((co[0] * dx) * dx + (co[2] * dy) * dy) - (co[1] * dx) * dy;
-                const F G = std::exp(power);
+                const F G = exp_rn(power);
                 const F a_raw = co[3] * G;
                 const F a = std::min(alpha_max, a_raw);
                 if (a < alpha_min) continue;
