@@ -12,12 +12,16 @@
 // and "Deliberate differences" (no gradient through a saturated alpha).
 //
 // MI355X design:
-//  * Splat records are staged in LDS in a prescaled form so the inner loop
-//    is 8 VALU ops for the exponent and one v_exp_f32 (base 2): the conic
-//    is multiplied by -0.5 log2(e) (off-diagonal by -log2(e)) once per tile.
-//  * The exponent is computed with explicit FMAs in the same instruction
-//    sequence in both kernels, so the backward re-derives exactly the
-//    alphas, skips and clamps the forward saw on the GPU.
+//  * The exponent -0.5 (A dx^2 + C dy^2) - B dx dy is evaluated in fp32 in
+//    exactly the written order with no contraction, so it is bit-identical
+//    to a host evaluation (this matters: for elongated splats the terms
+//    cancel and any other order drifts by more than the image tolerance).
+//    exp(power) uses the native base-2 v_exp_f32; only when the resulting
+//    alpha lies within a relative 4e-6 of the 1/255 floor (the fast value's
+//    error is below 1e-6 there) is the correctly rounded exponential taken
+//    (in double), so the skip decision is the exactly defined one.
+//  * Both kernels call the same alpha routine, so the backward re-derives
+//    exactly the alphas, skips and clamps the forward saw.
 //  * Workgroup ids are remapped so each XCD renders a contiguous band of
 //    tiles (neighbouring tiles share splats; L2 is per XCD).
 //  * Backward: per splat, each wave sums its 64 pixels' nine gradient terms
@@ -32,13 +36,20 @@ namespace {
 constexpr int kBatch = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Prescaled exponent in base 2: log2(e) * (-0.5 (A dx^2 + C dy^2) - B dx dy)
-// with ap = -0.5 log2e A, bp = -log2e B, cp = -0.5 log2e C.
-__device__ __forceinline__ float power2(float ap, float bp, float cp, float dx, float dy) {
-    return __builtin_fmaf(ap * dx, dx, __builtin_fmaf(cp * dy, dy, (bp * dx) * dy));
+// Gaussian weight and alpha of a splat with conic (A, B, C) and opacity o at
+// offset (dx, dy) from its centre:
+//   power = -0.5 (A dx^2 + C dy^2) - B dx dy,  G = exp(power),
+//   alpha = min(0.99, o G).
+__device__ __forceinline__ void splat_alpha(float A, float B, float C, float o, float dx, float dy,
+                                            float& G, float& alpha) {
+    const float power = -0.5f * ((A * dx) * dx + (C * dy) * dy) - (B * dx) * dy;
+    G = __builtin_amdgcn_exp2f(power * kLog2e);
+    alpha = fminf(kAlphaMax, o * G);
+    if (fabsf(alpha - kAlphaMin) <= kAlphaMin * 4e-6f) {
+        G = (float)exp((double)power);
+        alpha = fminf(kAlphaMax, o * G);
+    }
 }
-
-__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __global__ __launch_bounds__(256) void k_composite_fwd(
     const int W, const int H, const int TX, const uint32_t* __restrict__ ranges,
@@ -46,8 +57,8 @@ __global__ __launch_bounds__(256) void k_composite_fwd(
     const float4* __restrict__ conic_op, const float4* __restrict__ rgb, const float3 bg,
     float* __restrict__ image, float* __restrict__ final_T, uint32_t* __restrict__ n_contrib,
     uint32_t* __restrict__ n_examined) {
-    __shared__ float4 s_geo[kBatch];  // u, v, ap, bp
-    __shared__ float4 s_app[kBatch];  // cp, opacity, r, g
+    __shared__ float4 s_conic[kBatch];  // A, B, C, opacity
+    __shared__ float4 s_xyc[kBatch];    // u, v, r, g
     __shared__ float s_blue[kBatch];
 
     const int tile = xcd_contiguous(blockIdx.x, gridDim.x);
@@ -71,8 +82,8 @@ __global__ __launch_bounds__(256) void k_composite_fwd(
             const float4 xy = xy_depth[g];
             const float4 co = conic_op[g];
             const float4 c = rgb[g];
-            s_geo[tid] = make_float4(xy.x, xy.y, -0.5f * kLog2e * co.x, -kLog2e * co.y);
-            s_app[tid] = make_float4(-0.5f * kLog2e * co.z, co.w, c.x, c.y);
+            s_conic[tid] = co;
+            s_xyc[tid] = make_float4(xy.x, xy.y, c.x, c.y);
             s_blue[tid] = c.z;
         }
         __syncthreads();
@@ -80,16 +91,15 @@ __global__ __launch_bounds__(256) void k_composite_fwd(
             const int cnt = (int)min((uint32_t)kBatch, end - base);
             const uint32_t pos0 = base - start;
             for (int k = 0; k < cnt; ++k) {
-                const float4 gq = s_geo[k];
-                const float4 ap = s_app[k];
-                const float dx = fx - gq.x, dy = fy - gq.y;
-                const float G = exp2_fast(power2(gq.z, gq.w, ap.x, dx, dy));
-                const float alpha = fminf(kAlphaMax, ap.y * G);
+                const float4 co = s_conic[k];
+                const float4 xc = s_xyc[k];
+                float G, alpha;
+                splat_alpha(co.x, co.y, co.z, co.w, fx - xc.x, fy - xc.y, G, alpha);
                 examined = pos0 + k + 1;
                 if (alpha < kAlphaMin) continue;
                 const float w = alpha * T;
-                C0 = __builtin_fmaf(ap.z, w, C0);
-                C1 = __builtin_fmaf(ap.w, w, C1);
+                C0 = __builtin_fmaf(xc.z, w, C0);
+                C1 = __builtin_fmaf(xc.w, w, C1);
                 C2 = __builtin_fmaf(s_blue[k], w, C2);
                 T = T * (1.0f - alpha);
                 last = pos0 + k + 1;
@@ -131,9 +141,9 @@ __global__ __launch_bounds__(256) void k_composite_bwd(
     const float* __restrict__ final_T, const uint32_t* __restrict__ n_contrib,
     const float* __restrict__ dL_dimage, float* __restrict__ grad_mean2d,
     float* __restrict__ grad_conic_op, float* __restrict__ grad_rgb) {
-    __shared__ float4 s_geo[kBatch];   // u, v, ap, bp
-    __shared__ float4 s_app[kBatch];   // cp, opacity, r, g
-    __shared__ float4 s_raw[kBatch];   // b, A, B, C
+    __shared__ float4 s_conic[kBatch];  // A, B, C, opacity
+    __shared__ float4 s_xyc[kBatch];    // u, v, r, g
+    __shared__ float s_blue[kBatch];
     __shared__ uint32_t s_gid[kBatch];
     __shared__ float s_grad[kBatch][9];
     __shared__ uint32_t s_maxnc;
@@ -176,9 +186,9 @@ __global__ __launch_bounds__(256) void k_composite_bwd(
             const float4 xy = xy_depth[g];
             const float4 co = conic_op[g];
             const float4 c = rgb[g];
-            s_geo[tid] = make_float4(xy.x, xy.y, -0.5f * kLog2e * co.x, -kLog2e * co.y);
-            s_app[tid] = make_float4(-0.5f * kLog2e * co.z, co.w, c.x, c.y);
-            s_raw[tid] = make_float4(c.z, co.x, co.y, co.z);
+            s_conic[tid] = co;
+            s_xyc[tid] = make_float4(xy.x, xy.y, c.x, c.y);
+            s_blue[tid] = c.z;
             s_gid[tid] = g;
 #pragma unroll
             for (int v = 0; v < 9; ++v) s_grad[tid][v] = 0.0f;
@@ -189,33 +199,32 @@ __global__ __launch_bounds__(256) void k_composite_bwd(
             float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f, d4 = 0.f, d5 = 0.f, d6 = 0.f, d7 = 0.f, d8 = 0.f;
             bool any = false;
             if (bstart + k < (int)nc) {
-                const float4 gq = s_geo[k];
-                const float4 ap = s_app[k];
-                const float dx = fx - gq.x, dy = fy - gq.y;
-                const float G = exp2_fast(power2(gq.z, gq.w, ap.x, dx, dy));
-                const float a_raw = ap.y * G;
-                const float alpha = fminf(kAlphaMax, a_raw);
+                const float4 co = s_conic[k];
+                const float4 xc = s_xyc[k];
+                const float dx = fx - xc.x, dy = fy - xc.y;
+                float G, alpha;
+                splat_alpha(co.x, co.y, co.z, co.w, dx, dy, G, alpha);
                 if (alpha >= kAlphaMin) {
-                    const float4 rw = s_raw[k];
+                    const float cb = s_blue[k];
                     const float Tj = T / (1.0f - alpha);
                     const float w = alpha * Tj;
                     d6 = w * g0;
                     d7 = w * g1;
                     d8 = w * g2;
-                    const float dL_da = ((g0 * (ap.z - B0) + g1 * (ap.w - B1)) + g2 * (rw.x - B2)) * Tj;
+                    const float dL_da = ((g0 * (xc.z - B0) + g1 * (xc.w - B1)) + g2 * (cb - B2)) * Tj;
                     const float om = 1.0f - alpha;
-                    B0 = alpha * ap.z + om * B0;
-                    B1 = alpha * ap.w + om * B1;
-                    B2 = alpha * rw.x + om * B2;
+                    B0 = alpha * xc.z + om * B0;
+                    B1 = alpha * xc.w + om * B1;
+                    B2 = alpha * cb + om * B2;
                     T = Tj;
-                    if (a_raw <= kAlphaMax) {
+                    if (co.w * G <= kAlphaMax) {  // not saturated
                         const float dp = alpha * dL_da;
                         d5 = G * dL_da;
                         d2 = -0.5f * dx * dx * dp;
                         d3 = -dx * dy * dp;
                         d4 = -0.5f * dy * dy * dp;
-                        d0 = (rw.y * dx + rw.z * dy) * dp;
-                        d1 = (rw.z * dx + rw.w * dy) * dp;
+                        d0 = (co.x * dx + co.y * dy) * dp;
+                        d1 = (co.y * dx + co.z * dy) * dp;
                     }
                     any = true;
                 }

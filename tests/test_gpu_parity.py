@@ -176,7 +176,8 @@ def test_equal_depth_ties_keep_index_order(orc):
                  opacity=rng.uniform(0.1, 0.9, n).astype(np.float32),
                  rgb=rng.uniform(0, 1, (3, n)).astype(np.float32), sh=None, sh_degree=0)
     ofwd = oracle_forward(orc, cam, scene)
-    assert (ofwd["xy_depth"][:, 2] == 1.0).all()
+    vis = ofwd["tiles_touched"] > 0
+    assert vis.sum() > 2000 and (ofwd["xy_depth"][vis, 2] == 1.0).all()
     g, out, sc, _ = gpu_forward(cam, scene)
     assert_binning_equal(g, ofwd)
     compare_forward(g, ofwd)
