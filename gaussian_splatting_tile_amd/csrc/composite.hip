@@ -36,6 +36,10 @@ namespace {
 constexpr int kBatch = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Correctly rounded fp32 exponential (double evaluation, one rounding); the
+// rare slow path of splat_alpha, kept out of line.
+__device__ __noinline__ float exp_rn(float x) { return (float)exp((double)x); }
+
 // Gaussian weight and alpha of a splat with conic (A, B, C) and opacity o at
 // offset (dx, dy) from its centre:
 //   power = -0.5 (A dx^2 + C dy^2) - B dx dy,  G = exp(power),
@@ -46,9 +50,57 @@ __device__ __forceinline__ void splat_alpha(float A, float B, float C, float o, 
     G = __builtin_amdgcn_exp2f(power * kLog2e);
     alpha = fminf(kAlphaMax, o * G);
     if (fabsf(alpha - kAlphaMin) <= kAlphaMin * 4e-6f) {
-        G = (float)exp((double)power);
+        G = exp_rn(power);
         alpha = fminf(kAlphaMax, o * G);
     }
+}
+
+// ---- which waves can a splat reach? ----
+//
+// A workgroup's four waves each own a 16 x 4 strip of the tile (rows
+// 4w .. 4w+3). A splat can only change a pixel if alpha >= 1/255, i.e. if
+// Q(d) = A dx^2 + 2B dx dy + C dy^2 <= 2 ln(255 o). live_mask() computes, in
+// double, the exact minimum of Q over each strip's pixel rectangle (Q is
+// convex along every edge, so off the centre the minimum lies on an edge)
+// and keeps the strip unless that minimum exceeds the threshold by more than
+// a bound on the fp32 rounding of Q and of the exponential. A culled
+// (splat, strip) pair therefore has alpha < 1/255 at every pixel of the
+// strip in the fp32 evaluation as well: skipping it changes no result.
+__device__ __forceinline__ double edge_min_q(double A, double B, double C, double fixed, double lo,
+                                             double hi, bool fixed_is_x) {
+    // minimise Q along the segment where one offset is `fixed`
+    if (fixed_is_x) {
+        double t = fmin(fmax(-B * fixed / C, lo), hi);
+        return (A * fixed + 2.0 * B * t) * fixed + C * t * t;
+    }
+    double t = fmin(fmax(-B * fixed / A, lo), hi);
+    return A * t * t + (2.0 * B * t + C * fixed) * fixed;
+}
+
+__device__ __noinline__ uint32_t live_mask(float4 co, float u, float v, int x0, int y0) {
+    const double A = co.x, B = co.y, C = co.z, o = co.w;
+    if (!(o > 0.0)) return 0u;  // alpha = o G <= 0 never reaches the floor
+    const double thr = 2.0 * log(255.0 * o) * (1.0 + 1e-6) + 1e-4;
+    const double bound = 16.0 * 5.96e-8 * (fabs(A) + fabs(C) + 2.0 * fabs(B));
+    uint32_t mask = 0;
+#pragma unroll 1
+    for (int w = 0; w < 4; ++w) {
+        const double dx0 = (double)x0 - u, dx1 = (double)(x0 + 15) - u;
+        const double dy0 = (double)(y0 + 4 * w) - v, dy1 = (double)(y0 + 4 * w + 3) - v;
+        bool live;
+        if (dx0 <= 0.0 && dx1 >= 0.0 && dy0 <= 0.0 && dy1 >= 0.0) {
+            live = true;
+        } else {
+            double q = edge_min_q(A, B, C, dx0, dy0, dy1, true);
+            q = fmin(q, edge_min_q(A, B, C, dx1, dy0, dy1, true));
+            q = fmin(q, edge_min_q(A, B, C, dy0, dx0, dx1, false));
+            q = fmin(q, edge_min_q(A, B, C, dy1, dx0, dx1, false));
+            const double dmax2 = fmax(dx0 * dx0, dx1 * dx1) + fmax(dy0 * dy0, dy1 * dy1);
+            live = q - bound * dmax2 <= thr;
+        }
+        mask |= (live ? 1u : 0u) << w;
+    }
+    return mask;
 }
 
 __global__ __launch_bounds__(256) void k_composite_fwd(
@@ -60,9 +112,12 @@ __global__ __launch_bounds__(256) void k_composite_fwd(
     __shared__ float4 s_conic[kBatch];  // A, B, C, opacity
     __shared__ float4 s_xyc[kBatch];    // u, v, r, g
     __shared__ float s_blue[kBatch];
+    __shared__ uint32_t s_live[kBatch];
 
     const int tile = xcd_contiguous(blockIdx.x, gridDim.x);
     const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
     const int tx = tile % TX, ty = tile / TX;
     const int px = tx * kTile + (tid & 15);
     const int py = ty * kTile + (tid >> 4);
@@ -71,8 +126,8 @@ __global__ __launch_bounds__(256) void k_composite_fwd(
     const uint32_t start = ranges[2 * tile], end = ranges[2 * tile + 1];
 
     float T = 1.0f, C0 = 0.0f, C1 = 0.0f, C2 = 0.0f;
-    uint32_t last = 0, examined = 0;
-    bool done = !inside;
+    uint32_t last = 0;
+    bool done = !inside, stopped = false;
 
     for (uint32_t base = start; base < end; base += kBatch) {
         if (__syncthreads_count(done) == 256) break;
@@ -85,27 +140,42 @@ __global__ __launch_bounds__(256) void k_composite_fwd(
             s_conic[tid] = co;
             s_xyc[tid] = make_float4(xy.x, xy.y, c.x, c.y);
             s_blue[tid] = c.z;
+            s_live[tid] = live_mask(co, xy.x, xy.y, tx * kTile, ty * kTile);
         }
         __syncthreads();
-        if (!done) {
-            const int cnt = (int)min((uint32_t)kBatch, end - base);
-            const uint32_t pos0 = base - start;
-            for (int k = 0; k < cnt; ++k) {
-                const float4 co = s_conic[k];
-                const float4 xc = s_xyc[k];
-                float G, alpha;
-                splat_alpha(co.x, co.y, co.z, co.w, fx - xc.x, fy - xc.y, G, alpha);
-                examined = pos0 + k + 1;
-                if (alpha < kAlphaMin) continue;
-                const float w = alpha * T;
-                C0 = __builtin_fmaf(xc.z, w, C0);
-                C1 = __builtin_fmaf(xc.w, w, C1);
-                C2 = __builtin_fmaf(s_blue[k], w, C2);
-                T = T * (1.0f - alpha);
-                last = pos0 + k + 1;
-                if (T < kTStop) {
-                    done = true;
-                    break;
+        const int cnt = (int)min((uint32_t)kBatch, end - base);
+        const uint32_t pos0 = base - start;
+        // this wave's live splats of the batch, as four 64-bit masks
+        uint64_t m[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int k = q * 64 + lane;
+            m[q] = __ballot(k < cnt && ((s_live[k] >> wave) & 1u));
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            uint64_t mq = m[q];
+            while (mq != 0ull) {
+                if (__ballot(!done) == 0ull) { mq = 0ull; break; }
+                const int k = q * 64 + (__ffsll((unsigned long long)mq) - 1);
+                mq &= mq - 1ull;
+                if (!done) {
+                    const float4 co = s_conic[k];
+                    const float4 xc = s_xyc[k];
+                    float G, alpha;
+                    splat_alpha(co.x, co.y, co.z, co.w, fx - xc.x, fy - xc.y, G, alpha);
+                    if (alpha >= kAlphaMin) {
+                        const float w = alpha * T;
+                        C0 = __builtin_fmaf(xc.z, w, C0);
+                        C1 = __builtin_fmaf(xc.w, w, C1);
+                        C2 = __builtin_fmaf(s_blue[k], w, C2);
+                        T = T * (1.0f - alpha);
+                        last = pos0 + k + 1;
+                        if (T < kTStop) {
+                            done = true;
+                            stopped = true;
+                        }
+                    }
                 }
             }
         }
@@ -119,13 +189,20 @@ __global__ __launch_bounds__(256) void k_composite_fwd(
         image[2 * plane + p] = __builtin_fmaf(T, bg.z, C2);
         final_T[p] = T;
         n_contrib[p] = last;
-        if (n_examined) n_examined[p] = examined;
+        // a pixel that stopped examined up to its last contributor; one that
+        // did not examined the whole list
+        if (n_examined) n_examined[p] = stopped ? last : end - start;
     }
 }
 
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+// Sum over the 16 lanes of each row of the wave with DPP lane permutes
+// (quad swaps, then half-row and row mirrors); every lane of a row ends
+// with the row's sum. Must be called with all 64 lanes active.
+__device__ __forceinline__ float dpp_row_sum(float x) {
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));   // [1,0,3,2]
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));   // [2,3,0,1]
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false));  // half mirror
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, false));  // mirror
     return x;
 }
 
@@ -134,6 +211,9 @@ __global__ void k_zero(float* __restrict__ p, size_t n) {
     if (i < n) p[i] = 0.0f;
 }
 
+constexpr int kBwdBatch = 32;
+constexpr int kParts = 16;  // 4 waves x 4 rows of 16 lanes
+
 __global__ __launch_bounds__(256) void k_composite_bwd(
     const int W, const int H, const int TX, const uint32_t* __restrict__ ranges,
     const uint32_t* __restrict__ point_list, const float4* __restrict__ xy_depth,
@@ -141,16 +221,18 @@ __global__ __launch_bounds__(256) void k_composite_bwd(
     const float* __restrict__ final_T, const uint32_t* __restrict__ n_contrib,
     const float* __restrict__ dL_dimage, float* __restrict__ grad_mean2d,
     float* __restrict__ grad_conic_op, float* __restrict__ grad_rgb) {
-    __shared__ float4 s_conic[kBatch];  // A, B, C, opacity
-    __shared__ float4 s_xyc[kBatch];    // u, v, r, g
-    __shared__ float s_blue[kBatch];
-    __shared__ uint32_t s_gid[kBatch];
-    __shared__ float s_grad[kBatch][9];
-    __shared__ uint32_t s_maxnc;
+    __shared__ float4 s_conic[kBwdBatch];  // A, B, C, opacity
+    __shared__ float4 s_xyc[kBwdBatch];    // u, v, r, g
+    __shared__ float s_blue[kBwdBatch];
+    __shared__ uint32_t s_gid[kBwdBatch];
+    __shared__ uint32_t s_live[kBwdBatch];
+    __shared__ float s_part[kBwdBatch][9][kParts];  // per-row partial sums
+    __shared__ uint32_t s_maxnc[4];
 
     const int tile = xcd_contiguous(blockIdx.x, gridDim.x);
     const int tid = threadIdx.x;
     const int lane = tid & 63;
+    const int wave = tid >> 6;
     const int tx = tile % TX, ty = tile / TX;
     const int px = tx * kTile + (tid & 15);
     const int py = ty * kTile + (tid >> 4);
@@ -171,16 +253,20 @@ __global__ __launch_bounds__(256) void k_composite_bwd(
     }
     float B0 = bg.x, B1 = bg.y, B2 = bg.z;
 
-    if (tid == 0) s_maxnc = 0;
+    // per-wave and per-tile maximum of n_contrib
+    uint32_t wmax = nc;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) wmax = max(wmax, (uint32_t)__shfl_xor((int)wmax, off, 64));
+    if (lane == 0) s_maxnc[wave] = wmax;
     __syncthreads();
-    if (nc > 0) atomicMax(&s_maxnc, nc);
-    __syncthreads();
-    const int maxnc = (int)s_maxnc;
+    const int maxnc = (int)max(max(s_maxnc[0], s_maxnc[1]), max(s_maxnc[2], s_maxnc[3]));
+    const int wave_maxnc = (int)wmax;
 
-    for (int bend = maxnc; bend > 0; bend -= kBatch) {
-        const int bstart = bend > kBatch ? bend - kBatch : 0;
+    for (int bend = maxnc; bend > 0; bend -= kBwdBatch) {
+        const int bstart = bend > kBwdBatch ? bend - kBwdBatch : 0;
         const int cnt = bend - bstart;
         __syncthreads();  // the previous batch is fully consumed
+        for (int i = tid; i < kBwdBatch * 9 * kParts; i += 256) (&s_part[0][0][0])[i] = 0.0f;
         if (tid < cnt) {
             const uint32_t g = point_list[start + bstart + tid];
             const float4 xy = xy_depth[g];
@@ -190,12 +276,15 @@ __global__ __launch_bounds__(256) void k_composite_bwd(
             s_xyc[tid] = make_float4(xy.x, xy.y, c.x, c.y);
             s_blue[tid] = c.z;
             s_gid[tid] = g;
-#pragma unroll
-            for (int v = 0; v < 9; ++v) s_grad[tid][v] = 0.0f;
+            s_live[tid] = live_mask(co, xy.x, xy.y, tx * kTile, ty * kTile);
         }
         __syncthreads();
 
-        for (int k = cnt - 1; k >= 0; --k) {
+        // live splats of this wave below its largest n_contrib, walked back to front
+        uint64_t mk = __ballot(lane < cnt && bstart + lane < wave_maxnc && ((s_live[lane & 31] >> wave) & 1u));
+        while (mk != 0ull) {
+            const int k = 63 - __clzll((long long)mk);
+            mk &= ~(1ull << k);
             float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f, d4 = 0.f, d5 = 0.f, d6 = 0.f, d7 = 0.f, d8 = 0.f;
             bool any = false;
             if (bstart + k < (int)nc) {
@@ -230,34 +319,32 @@ __global__ __launch_bounds__(256) void k_composite_bwd(
                 }
             }
             if (__ballot(any) != 0ull) {
-                d0 = wave_sum(d0); d1 = wave_sum(d1); d2 = wave_sum(d2);
-                d3 = wave_sum(d3); d4 = wave_sum(d4); d5 = wave_sum(d5);
-                d6 = wave_sum(d6); d7 = wave_sum(d7); d8 = wave_sum(d8);
-                if (lane == 0) {
-                    atomicAdd(&s_grad[k][0], d0); atomicAdd(&s_grad[k][1], d1);
-                    atomicAdd(&s_grad[k][2], d2); atomicAdd(&s_grad[k][3], d3);
-                    atomicAdd(&s_grad[k][4], d4); atomicAdd(&s_grad[k][5], d5);
-                    atomicAdd(&s_grad[k][6], d6); atomicAdd(&s_grad[k][7], d7);
-                    atomicAdd(&s_grad[k][8], d8);
+                d0 = dpp_row_sum(d0); d1 = dpp_row_sum(d1); d2 = dpp_row_sum(d2);
+                d3 = dpp_row_sum(d3); d4 = dpp_row_sum(d4); d5 = dpp_row_sum(d5);
+                d6 = dpp_row_sum(d6); d7 = dpp_row_sum(d7); d8 = dpp_row_sum(d8);
+                if ((lane & 15) == 0) {
+                    const int slot = wave * 4 + (lane >> 4);
+                    s_part[k][0][slot] = d0; s_part[k][1][slot] = d1; s_part[k][2][slot] = d2;
+                    s_part[k][3][slot] = d3; s_part[k][4][slot] = d4; s_part[k][5][slot] = d5;
+                    s_part[k][6][slot] = d6; s_part[k][7][slot] = d7; s_part[k][8][slot] = d8;
                 }
             }
         }
         __syncthreads();
-        if (tid < cnt) {
-            const uint32_t g = s_gid[tid];
-            const float* sg = s_grad[tid];
-            float* gm = grad_mean2d + 2 * (size_t)g;
-            float* gc = grad_conic_op + 4 * (size_t)g;
-            float* gr = grad_rgb + 4 * (size_t)g;
-            if (sg[0] != 0.0f) unsafeAtomicAdd(gm + 0, sg[0]);
-            if (sg[1] != 0.0f) unsafeAtomicAdd(gm + 1, sg[1]);
-            if (sg[2] != 0.0f) unsafeAtomicAdd(gc + 0, sg[2]);
-            if (sg[3] != 0.0f) unsafeAtomicAdd(gc + 1, sg[3]);
-            if (sg[4] != 0.0f) unsafeAtomicAdd(gc + 2, sg[4]);
-            if (sg[5] != 0.0f) unsafeAtomicAdd(gc + 3, sg[5]);
-            if (sg[6] != 0.0f) unsafeAtomicAdd(gr + 0, sg[6]);
-            if (sg[7] != 0.0f) unsafeAtomicAdd(gr + 1, sg[7]);
-            if (sg[8] != 0.0f) unsafeAtomicAdd(gr + 2, sg[8]);
+        // one thread per (splat, value): sum the 16 partials, one atomic
+        for (int i = tid; i < cnt * 9; i += 256) {
+            const int k = i / 9, v = i - 9 * (i / 9);
+            const float* pp = s_part[k][v];
+            float sum = 0.0f;
+#pragma unroll
+            for (int r = 0; r < kParts; ++r) sum += pp[r];
+            if (sum != 0.0f) {
+                const uint32_t g = s_gid[k];
+                float* dst = v < 2 ? grad_mean2d + 2 * (size_t)g + v
+                           : v < 6 ? grad_conic_op + 4 * (size_t)g + (v - 2)
+                                   : grad_rgb + 4 * (size_t)g + (v - 6);
+                unsafeAtomicAdd(dst, sum);
+            }
         }
     }
 }
