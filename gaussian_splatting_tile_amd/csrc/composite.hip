@@ -44,14 +44,19 @@ __device__ __noinline__ float exp_rn(float x) { return (float)exp((double)x); }
 // offset (dx, dy) from its centre:
 //   power = -0.5 (A dx^2 + C dy^2) - B dx dy,  G = exp(power),
 //   alpha = min(0.99, o G).
+// Must be called with the whole wave active (the rare exact path is behind
+// a wave-uniform test).
 __device__ __forceinline__ void splat_alpha(float A, float B, float C, float o, float dx, float dy,
                                             float& G, float& alpha) {
     const float power = -0.5f * ((A * dx) * dx + (C * dy) * dy) - (B * dx) * dy;
     G = __builtin_amdgcn_exp2f(power * kLog2e);
     alpha = fminf(kAlphaMax, o * G);
-    if (fabsf(alpha - kAlphaMin) <= kAlphaMin * 4e-6f) {
-        G = exp_rn(power);
-        alpha = fminf(kAlphaMax, o * G);
+    const bool near = fabsf(alpha - kAlphaMin) <= kAlphaMin * 4e-6f;
+    if (__builtin_expect(__ballot(near) != 0ull, 0)) {
+        if (near) {
+            G = exp_rn(power);
+            alpha = fminf(kAlphaMax, o * G);
+        }
     }
 }
 
@@ -125,12 +130,14 @@ __global__ __launch_bounds__(256) void k_composite_fwd(
     const float fx = (float)px, fy = (float)py;
     const uint32_t start = ranges[2 * tile], end = ranges[2 * tile + 1];
 
+    // A pixel has stopped exactly when its transmittance is below the stop
+    // threshold (T only decreases, and compositing ends at the first splat
+    // that takes it there), so no separate flag is carried.
     float T = 1.0f, C0 = 0.0f, C1 = 0.0f, C2 = 0.0f;
     uint32_t last = 0;
-    bool done = !inside, stopped = false;
 
     for (uint32_t base = start; base < end; base += kBatch) {
-        if (__syncthreads_count(done) == 256) break;
+        if (__syncthreads_count(!inside || T < kTStop) == 256) break;
         const uint32_t j = base + tid;
         if (j < end) {
             const uint32_t g = point_list[j];
@@ -156,27 +163,22 @@ __global__ __launch_bounds__(256) void k_composite_fwd(
         for (int q = 0; q < 4; ++q) {
             uint64_t mq = m[q];
             while (mq != 0ull) {
-                if (__ballot(!done) == 0ull) { mq = 0ull; break; }
+                if (__ballot(inside && T >= kTStop) == 0ull) { mq = 0ull; break; }
                 const int k = q * 64 + (__ffsll((unsigned long long)mq) - 1);
                 mq &= mq - 1ull;
-                if (!done) {
-                    const float4 co = s_conic[k];
-                    const float4 xc = s_xyc[k];
-                    float G, alpha;
-                    splat_alpha(co.x, co.y, co.z, co.w, fx - xc.x, fy - xc.y, G, alpha);
-                    if (alpha >= kAlphaMin) {
-                        const float w = alpha * T;
-                        C0 = __builtin_fmaf(xc.z, w, C0);
-                        C1 = __builtin_fmaf(xc.w, w, C1);
-                        C2 = __builtin_fmaf(s_blue[k], w, C2);
-                        T = T * (1.0f - alpha);
-                        last = pos0 + k + 1;
-                        if (T < kTStop) {
-                            done = true;
-                            stopped = true;
-                        }
-                    }
-                }
+                const float4 co = s_conic[k];
+                const float4 xc = s_xyc[k];
+                const float cb = s_blue[k];
+                float G, alpha;
+                splat_alpha(co.x, co.y, co.z, co.w, fx - xc.x, fy - xc.y, G, alpha);
+                // branch-free update; stopped lanes and alphas below the floor change nothing
+                const bool use = inside && T >= kTStop && alpha >= kAlphaMin;
+                const float w = use ? alpha * T : 0.0f;
+                C0 = __builtin_fmaf(xc.z, w, C0);
+                C1 = __builtin_fmaf(xc.w, w, C1);
+                C2 = __builtin_fmaf(cb, w, C2);
+                T = use ? T * (1.0f - alpha) : T;
+                last = use ? pos0 + k + 1 : last;
             }
         }
     }
@@ -191,18 +193,22 @@ __global__ __launch_bounds__(256) void k_composite_fwd(
         n_contrib[p] = last;
         // a pixel that stopped examined up to its last contributor; one that
         // did not examined the whole list
-        if (n_examined) n_examined[p] = stopped ? last : end - start;
+        if (n_examined) n_examined[p] = T < kTStop ? last : end - start;
     }
 }
 
 // Sum over the 16 lanes of each row of the wave with DPP lane permutes
 // (quad swaps, then half-row and row mirrors); every lane of a row ends
 // with the row's sum. Must be called with all 64 lanes active.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_add(float x) {
+    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, true));
+}
 __device__ __forceinline__ float dpp_row_sum(float x) {
-    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));   // [1,0,3,2]
-    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));   // [2,3,0,1]
-    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false));  // half mirror
-    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, false));  // mirror
+    x = dpp_add<0xB1>(x);   // quad_perm [1,0,3,2]
+    x = dpp_add<0x4E>(x);   // quad_perm [2,3,0,1]
+    x = dpp_add<0x141>(x);  // row_half_mirror
+    x = dpp_add<0x140>(x);  // row_mirror
     return x;
 }
 
@@ -285,48 +291,41 @@ __global__ __launch_bounds__(256) void k_composite_bwd(
         while (mk != 0ull) {
             const int k = 63 - __clzll((long long)mk);
             mk &= ~(1ull << k);
-            float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f, d4 = 0.f, d5 = 0.f, d6 = 0.f, d7 = 0.f, d8 = 0.f;
-            bool any = false;
-            if (bstart + k < (int)nc) {
-                const float4 co = s_conic[k];
-                const float4 xc = s_xyc[k];
-                const float dx = fx - xc.x, dy = fy - xc.y;
-                float G, alpha;
-                splat_alpha(co.x, co.y, co.z, co.w, dx, dy, G, alpha);
-                if (alpha >= kAlphaMin) {
-                    const float cb = s_blue[k];
-                    const float Tj = T / (1.0f - alpha);
-                    const float w = alpha * Tj;
-                    d6 = w * g0;
-                    d7 = w * g1;
-                    d8 = w * g2;
-                    const float dL_da = ((g0 * (xc.z - B0) + g1 * (xc.w - B1)) + g2 * (cb - B2)) * Tj;
-                    const float om = 1.0f - alpha;
-                    B0 = alpha * xc.z + om * B0;
-                    B1 = alpha * xc.w + om * B1;
-                    B2 = alpha * cb + om * B2;
-                    T = Tj;
-                    if (co.w * G <= kAlphaMax) {  // not saturated
-                        const float dp = alpha * dL_da;
-                        d5 = G * dL_da;
-                        d2 = -0.5f * dx * dx * dp;
-                        d3 = -dx * dy * dp;
-                        d4 = -0.5f * dy * dy * dp;
-                        d0 = (co.x * dx + co.y * dy) * dp;
-                        d1 = (co.y * dx + co.z * dy) * dp;
-                    }
-                    any = true;
-                }
-            }
+            const float4 co = s_conic[k];
+            const float4 xc = s_xyc[k];
+            const float cb = s_blue[k];
+            const float dx = fx - xc.x, dy = fy - xc.y;
+            float G, alpha;
+            splat_alpha(co.x, co.y, co.z, co.w, dx, dy, G, alpha);
+            // branch-free: lanes past their n_contrib or below the floor add nothing
+            const bool use = bstart + k < (int)nc && alpha >= kAlphaMin;
+            const float om = 1.0f - alpha;
+            const float Tj = T * __builtin_amdgcn_rcpf(om);  // transmittance in front of k
+            const float w = use ? alpha * Tj : 0.0f;
+            const float d6 = w * g0, d7 = w * g1, d8 = w * g2;
+            const float dL_da = ((g0 * (xc.z - B0) + g1 * (xc.w - B1)) + g2 * (cb - B2)) * Tj;
+            B0 = use ? alpha * xc.z + om * B0 : B0;
+            B1 = use ? alpha * xc.w + om * B1 : B1;
+            B2 = use ? alpha * cb + om * B2 : B2;
+            T = use ? Tj : T;
+            const bool geo = use && co.w * G <= kAlphaMax;  // not saturated
+            const float dp = geo ? alpha * dL_da : 0.0f;
+            const float d5 = geo ? G * dL_da : 0.0f;
+            const float d2 = -0.5f * dx * dx * dp;
+            const float d3 = -dx * dy * dp;
+            const float d4 = -0.5f * dy * dy * dp;
+            const float d0 = (co.x * dx + co.y * dy) * dp;
+            const float d1 = (co.y * dx + co.z * dy) * dp;
+            const bool any = use;
             if (__ballot(any) != 0ull) {
-                d0 = dpp_row_sum(d0); d1 = dpp_row_sum(d1); d2 = dpp_row_sum(d2);
-                d3 = dpp_row_sum(d3); d4 = dpp_row_sum(d4); d5 = dpp_row_sum(d5);
-                d6 = dpp_row_sum(d6); d7 = dpp_row_sum(d7); d8 = dpp_row_sum(d8);
+                const float r0 = dpp_row_sum(d0), r1 = dpp_row_sum(d1), r2 = dpp_row_sum(d2);
+                const float r3 = dpp_row_sum(d3), r4 = dpp_row_sum(d4), r5 = dpp_row_sum(d5);
+                const float r6 = dpp_row_sum(d6), r7 = dpp_row_sum(d7), r8 = dpp_row_sum(d8);
                 if ((lane & 15) == 0) {
                     const int slot = wave * 4 + (lane >> 4);
-                    s_part[k][0][slot] = d0; s_part[k][1][slot] = d1; s_part[k][2][slot] = d2;
-                    s_part[k][3][slot] = d3; s_part[k][4][slot] = d4; s_part[k][5][slot] = d5;
-                    s_part[k][6][slot] = d6; s_part[k][7][slot] = d7; s_part[k][8][slot] = d8;
+                    s_part[k][0][slot] = r0; s_part[k][1][slot] = r1; s_part[k][2][slot] = r2;
+                    s_part[k][3][slot] = r3; s_part[k][4][slot] = r4; s_part[k][5][slot] = r5;
+                    s_part[k][6][slot] = r6; s_part[k][7][slot] = r7; s_part[k][8][slot] = r8;
                 }
             }
         }
