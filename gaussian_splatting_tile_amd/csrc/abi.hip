@@ -128,12 +128,7 @@ gs_status gs_bin_and_sort(const gs_camera* cam, int32_t n, const float* xy_depth
 
     const int key_bits = 32 + tile_bits(*cam);
     const bool in_tmp = gs::radix_input_in_tmp(key_bits);
-    if (gs_status e = hip_check(
-            gs::launch_scan_and_duplicate(*cam, n, (const float4*)xy_depth, tiles_touched, s,
-                                          in_tmp ? s.keys_tmp : keys, in_tmp ? s.vals_tmp : point_list,
-                                          (uint64_t)capacity, st),
-            "scan/duplicate launch"))
-        return e;
+    if (gs_status e = hip_check(gs::launch_scan(n, tiles_touched, s, st), "scan launch")) return e;
     uint64_t total = 0;
     if (gs_status e = hip_check(hipMemcpyAsync(&total, s.total, sizeof(total), hipMemcpyDeviceToHost, st),
                                 "entry count copy"))
@@ -145,6 +140,11 @@ gs_status gs_bin_and_sort(const gs_camera* cam, int32_t n, const float* xy_depth
     if ((int64_t)total > capacity)
         return fail(GS_ERR_CAPACITY, "%llu entries exceed the capacity %lld",
                     (unsigned long long)total, (long long)capacity);
+    if (gs_status e = hip_check(gs::launch_duplicate(*cam, n, (uint32_t)total, (const float4*)xy_depth, s,
+                                                     in_tmp ? s.keys_tmp : keys,
+                                                     in_tmp ? s.vals_tmp : point_list, st),
+                                "duplicate launch"))
+        return e;
     return hip_check(gs::launch_radix_sort(keys, point_list, (uint32_t)total, key_bits, s, st),
                      "radix sort launch");
 }

@@ -10,12 +10,12 @@
 // cleared); learn-gs build_tile_lists (span order, ty outer, tx inner).
 //
 // MI355X design:
-//  * The scan is reduce / scan-of-block-sums / rescan. The rescan is fused
-//    with the duplication: every workgroup holds the exclusive offsets of
-//    its 2048 Gaussians in LDS and expands its entries cooperatively, one
-//    entry per lane (owner found by binary search in LDS), so a Gaussian
-//    covering hundreds of tiles does not serialise a lane, and the key and
-//    value stores are fully coalesced.
+//  * The scan is reduce / scan-of-block-sums / rescan into per-Gaussian
+//    offsets. The duplication is entry-parallel: each workgroup takes 2048
+//    consecutive entries, finds the Gaussians that own them, stages their
+//    offsets in LDS and gives every lane one entry (owner by binary search),
+//    so the work is balanced however many tiles a Gaussian covers, and the
+//    key and value stores are fully coalesced.
 //  * The sort's in-workgroup rank uses 64-lane ballots: eight ballots, one
 //    per digit bit, give every lane the mask of lanes holding its digit;
 //    popcount below the lane is its rank (the zenn flag-bit rank, done on
@@ -122,66 +122,111 @@ __global__ __launch_bounds__(1024) void k_scan_block_sums(const uint32_t* __rest
     if (tid == 1023) *total = sum;
 }
 
-// Rescan each workgroup's 2048 counts, then expand the entries. Entry e of
-// the workgroup (0 <= e < its total) belongs to the last Gaussian whose
-// local offset is <= e; its position inside that Gaussian's span is
-// k = e - offset, giving tx = x0 + k % width, ty = y0 + k / width.
-__global__ __launch_bounds__(kScanThreads) void k_scan_duplicate(
-    const float4* __restrict__ xy_depth, const uint32_t* __restrict__ counts, int n, int TX, int TY,
-    const uint64_t* __restrict__ block_offsets, uint64_t* __restrict__ keys,
-    uint32_t* __restrict__ values, uint64_t capacity) {
-    __shared__ uint32_t s_off[kScanTile + 1];
+// Rescan each workgroup's 2048 counts with its global offset: offsets[g]
+// is the first entry of Gaussian g.
+__global__ __launch_bounds__(kScanThreads) void k_scan_offsets(const uint32_t* __restrict__ counts, int n,
+                                                               const uint64_t* __restrict__ block_offsets,
+                                                               uint32_t* __restrict__ offsets) {
+    __shared__ uint32_t s_c[kScanTile];
     __shared__ uint32_t s_tmp[kScanThreads];
     const int tid = threadIdx.x;
     const int base = blockIdx.x * kScanTile;
-    // coalesced load into LDS
 #pragma unroll
     for (int i = 0; i < kScanItems; ++i) {
         const int idx = i * kScanThreads + tid;
         const int g = base + idx;
-        s_off[idx] = g < n ? counts[g] : 0u;
+        s_c[idx] = g < n ? counts[g] : 0u;
     }
     __syncthreads();
-    // each thread scans 8 contiguous counts
     uint32_t c[kScanItems];
     uint32_t sum = 0;
 #pragma unroll
     for (int i = 0; i < kScanItems; ++i) {
-        c[i] = s_off[tid * kScanItems + i];
+        c[i] = s_c[tid * kScanItems + i];
         sum += c[i];
     }
     uint32_t total;
     const uint32_t incl = block_inclusive_scan_256<uint32_t>(sum, s_tmp, &total);
-    uint32_t run = incl - sum;
+    uint32_t run = (uint32_t)block_offsets[blockIdx.x] + (incl - sum);
 #pragma unroll
     for (int i = 0; i < kScanItems; ++i) {
-        s_off[tid * kScanItems + i] = run;
+        s_c[tid * kScanItems + i] = run;
         run += c[i];
     }
-    if (tid == 0) s_off[kScanTile] = total;
     __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kScanItems; ++i) {
+        const int idx = i * kScanThreads + tid;
+        if (base + idx < n) offsets[base + idx] = s_c[idx];
+    }
+}
 
-    const uint64_t gbase = block_offsets[blockIdx.x];
-    for (uint32_t e = tid; e < total; e += kScanThreads) {
-        // upper_bound over s_off[0 .. kScanTile] (s_off[kScanTile] = total > e)
-        int lo = 0, hi = kScanTile;  // answer in [lo, hi)
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (s_off[mid] <= e) lo = mid; else hi = mid;
+// Last index g in [lo, hi] with offsets[g] <= e (offsets is nondecreasing;
+// the answer is the Gaussian owning entry e, never a zero-count one).
+__device__ __forceinline__ int owner_search(const uint32_t* __restrict__ offsets, int lo, int hi, uint32_t e) {
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (offsets[mid] <= e) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// Duplication, one entry per lane: entry e of Gaussian g (its k-th tile,
+// k = e - offsets[g]) is the tile (x0 + k % w, y0 + k / w) of g's span.
+// Each workgroup covers 2048 consecutive entries; it finds the range of
+// Gaussians owning them, stages their offsets in LDS, and searches there.
+constexpr int kDupThreads = 256;
+constexpr int kDupItems = 8;
+constexpr int kDupTile = kDupThreads * kDupItems;
+constexpr int kDupWindow = 2048;  // staged offsets; longer owner ranges search global memory
+
+__global__ __launch_bounds__(kDupThreads) void k_duplicate(
+    const float4* __restrict__ xy_depth, const uint32_t* __restrict__ offsets, int n, uint32_t n_entries,
+    int TX, int TY, uint64_t* __restrict__ keys, uint32_t* __restrict__ values) {
+    __shared__ uint32_t s_off[kDupWindow];
+    __shared__ int s_range[2];
+    const int tid = threadIdx.x;
+    const uint32_t e0 = blockIdx.x * kDupTile;
+    const uint32_t e1 = min(e0 + (uint32_t)kDupTile, n_entries);
+    if (tid < 2) s_range[tid] = owner_search(offsets, 0, n - 1, tid == 0 ? e0 : e1 - 1);
+    __syncthreads();
+    const int g_lo = s_range[0], g_hi = s_range[1];
+    const int span = g_hi - g_lo + 1;
+    const bool staged = span <= kDupWindow;
+    if (staged)
+        for (int i = tid; i < span; i += kDupThreads) s_off[i] = offsets[g_lo + i];
+    __syncthreads();
+#pragma unroll 2
+    for (int it = 0; it < kDupItems; ++it) {
+        const uint32_t e = e0 + it * kDupThreads + tid;
+        if (e >= e1) break;
+        int g;
+        uint32_t off;
+        if (staged) {
+            int lo = 0, hi = span - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (s_off[mid] <= e) lo = mid; else hi = mid - 1;
+            }
+            g = g_lo + lo;
+            off = s_off[lo];
+        } else {
+            g = owner_search(offsets, g_lo, g_hi, e);
+            off = offsets[g];
         }
-        const int g = base + lo;
-        const uint32_t k = e - s_off[lo];
+        const uint32_t k = e - off;
         const float4 rec = xy_depth[g];
         const Span sp = tile_span(rec.x, rec.y, rec.w, TX, TY);
         const uint32_t w = (uint32_t)(sp.x1 - sp.x0);
-        const uint32_t tx = (uint32_t)sp.x0 + k % w;
-        const uint32_t ty = (uint32_t)sp.y0 + k / w;
-        const uint64_t key = ((uint64_t)(ty * (uint32_t)TX + tx) << 32) | (uint64_t)__float_as_uint(rec.z);
-        const uint64_t out = gbase + e;
-        if (out < capacity) {
-            keys[out] = key;
-            values[out] = (uint32_t)g;
-        }
+        // k / w and k % w: float quotient (k < 2^21) fixed up by one step
+        uint32_t q = (uint32_t)((float)k * __builtin_amdgcn_rcpf((float)w));
+        int r = (int)k - (int)(q * w);
+        if (r < 0) { --q; r += (int)w; }
+        if (r >= (int)w) { ++q; r -= (int)w; }
+        const uint32_t tx = (uint32_t)sp.x0 + (uint32_t)r;
+        const uint32_t ty = (uint32_t)sp.y0 + q;
+        keys[e] = ((uint64_t)(ty * (uint32_t)TX + tx) << 32) | (uint64_t)__float_as_uint(rec.z);
+        values[e] = (uint32_t)g;
     }
 }
 
@@ -361,6 +406,7 @@ size_t bin_scratch_layout(int n, int64_t capacity, BinScratch* out, void* base) 
     const size_t o_bs = take(nb_scan * 4);
     const size_t o_bo = take(nb_scan * 8);
     const size_t o_tot = take(8);
+    const size_t o_off = take((size_t)n * 4);
     const size_t o_kt = take((size_t)capacity * 8);
     const size_t o_vt = take((size_t)capacity * 4);
     const size_t o_cnt = take((size_t)kRadix * nb_sort * 4);
@@ -370,6 +416,7 @@ size_t bin_scratch_layout(int n, int64_t capacity, BinScratch* out, void* base) 
         out->block_sums = (uint32_t*)(b + o_bs);
         out->block_offsets = (uint64_t*)(b + o_bo);
         out->total = (uint64_t*)(b + o_tot);
+        out->offsets = (uint32_t*)(b + o_off);
         out->keys_tmp = (uint64_t*)(b + o_kt);
         out->vals_tmp = (uint32_t*)(b + o_vt);
         out->counts = (uint32_t*)(b + o_cnt);
@@ -378,18 +425,23 @@ size_t bin_scratch_layout(int n, int64_t capacity, BinScratch* out, void* base) 
     return off;
 }
 
-hipError_t launch_scan_and_duplicate(const gs_camera& cam, int n, const float4* xy_depth,
-                                     const uint32_t* tiles_touched, const BinScratch& s,
-                                     uint64_t* keys, uint32_t* values, uint64_t capacity,
-                                     hipStream_t stream) {
+hipError_t launch_scan(int n, const uint32_t* tiles_touched, const BinScratch& s, hipStream_t stream) {
     const int nb = (n + kScanTile - 1) / kScanTile;
     hipLaunchKernelGGL(k_scan_reduce, dim3(nb), dim3(kScanThreads), 0, stream, tiles_touched, n,
                        s.block_sums);
     hipLaunchKernelGGL(k_scan_block_sums, dim3(1), dim3(1024), 0, stream, s.block_sums, nb,
                        s.block_offsets, s.total);
-    hipLaunchKernelGGL(k_scan_duplicate, dim3(nb), dim3(kScanThreads), 0, stream, xy_depth,
-                       tiles_touched, n, tiles_x(cam), tiles_y(cam), s.block_offsets, keys, values,
-                       capacity);
+    hipLaunchKernelGGL(k_scan_offsets, dim3(nb), dim3(kScanThreads), 0, stream, tiles_touched, n,
+                       s.block_offsets, s.offsets);
+    return hipGetLastError();
+}
+
+hipError_t launch_duplicate(const gs_camera& cam, int n, uint32_t n_entries, const float4* xy_depth,
+                            const BinScratch& s, uint64_t* keys, uint32_t* values, hipStream_t stream) {
+    if (n_entries == 0) return hipSuccess;
+    const unsigned blocks = (n_entries + kDupTile - 1) / kDupTile;
+    hipLaunchKernelGGL(k_duplicate, dim3(blocks), dim3(kDupThreads), 0, stream, xy_depth, s.offsets, n,
+                       n_entries, tiles_x(cam), tiles_y(cam), keys, values);
     return hipGetLastError();
 }
 

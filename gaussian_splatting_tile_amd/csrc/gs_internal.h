@@ -69,6 +69,7 @@ struct BinScratch {
     uint32_t* block_sums;     // [nb_scan]
     uint64_t* block_offsets;  // [nb_scan]
     uint64_t* total;          // [1]
+    uint32_t* offsets;        // [n] first entry of each Gaussian
     uint64_t* keys_tmp;       // [capacity]
     uint32_t* vals_tmp;       // [capacity]
     uint32_t* counts;         // [256][nb_sort]
@@ -76,10 +77,11 @@ struct BinScratch {
 };
 size_t bin_scratch_layout(int n, int64_t capacity, BinScratch* out, void* base);
 
-hipError_t launch_scan_and_duplicate(const gs_camera& cam, int n, const float4* xy_depth,
-                                     const uint32_t* tiles_touched, const BinScratch& s,
-                                     uint64_t* keys, uint32_t* values, uint64_t capacity,
-                                     hipStream_t stream);
+// Exclusive scan of tiles_touched into s.offsets and s.total (entry count).
+hipError_t launch_scan(int n, const uint32_t* tiles_touched, const BinScratch& s, hipStream_t stream);
+// One (key, value) per entry, n_entries = *s.total, written to keys/values.
+hipError_t launch_duplicate(const gs_camera& cam, int n, uint32_t n_entries, const float4* xy_depth,
+                            const BinScratch& s, uint64_t* keys, uint32_t* values, hipStream_t stream);
 
 // Stable LSD radix sort, 8-bit digits, of n (key, value) pairs on key bits
 // [0, key_bits). (keys_tmp, vals_tmp) in the scratch is the ping-pong
