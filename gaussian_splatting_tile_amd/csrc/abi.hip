@@ -109,7 +109,8 @@ gs_status gs_bin_and_sort(const gs_camera* cam, int32_t n, const float* xy_depth
         return fail(GS_ERR_INVALID, "capacity %lld outside [0, 2^32 - 1]", (long long)capacity);
     if (!scratch_bytes) return fail(GS_ERR_INVALID, "scratch_bytes is NULL");
     gs::BinScratch s{};
-    const size_t need = gs::bin_scratch_layout(n, capacity, nullptr, nullptr);
+    const int n_tiles = gs::tiles_x(*cam) * gs::tiles_y(*cam);
+    const size_t need = gs::bin_scratch_layout(n, capacity, n_tiles, nullptr, nullptr);
     if (!scratch) {
         *scratch_bytes = need;
         return GS_OK;
@@ -123,11 +124,11 @@ gs_status gs_bin_and_sort(const gs_camera* cam, int32_t n, const float* xy_depth
     if (n == 0) return GS_OK;
     if (!xy_depth || !tiles_touched || (capacity > 0 && (!keys || !point_list)))
         return fail(GS_ERR_INVALID, "gs_bin_and_sort: a required pointer is NULL");
-    gs::bin_scratch_layout(n, capacity, &s, scratch);
+    gs::bin_scratch_layout(n, capacity, n_tiles, &s, scratch);
     hipStream_t st = (hipStream_t)stream;
 
-    const int key_bits = 32 + tile_bits(*cam);
-    const bool in_tmp = gs::radix_input_in_tmp(key_bits);
+    const int tbits = tile_bits(*cam);
+    const bool in_tmp = gs::dup_writes_tmp(tbits);
     if (gs_status e = hip_check(gs::launch_scan(n, tiles_touched, s, st), "scan launch")) return e;
     uint64_t total = 0;
     if (gs_status e = hip_check(hipMemcpyAsync(&total, s.total, sizeof(total), hipMemcpyDeviceToHost, st),
@@ -145,8 +146,8 @@ gs_status gs_bin_and_sort(const gs_camera* cam, int32_t n, const float* xy_depth
                                                      in_tmp ? s.vals_tmp : point_list, st),
                                 "duplicate launch"))
         return e;
-    return hip_check(gs::launch_radix_sort(keys, point_list, (uint32_t)total, key_bits, s, st),
-                     "radix sort launch");
+    return hip_check(gs::launch_sort(keys, point_list, (uint32_t)total, tbits, n_tiles, s, st),
+                     "sort launch");
 }
 
 gs_status gs_tile_ranges(const gs_camera* cam, const uint64_t* keys, int64_t n_entries,

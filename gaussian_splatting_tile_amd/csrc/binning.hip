@@ -16,7 +16,12 @@
 //    offsets in LDS and gives every lane one entry (owner by binary search),
 //    so the work is balanced however many tiles a Gaussian covers, and the
 //    key and value stores are fully coalesced.
-//  * The sort's in-workgroup rank uses 64-lane ballots: eight ballots, one
+//  * The sort is split in two, with the same final order as one stable sort
+//    of the 64-bit keys: a stable LSD sort on the tile-id bits only (two
+//    8-bit passes at 1080p), then one workgroup per tile sorting its
+//    segment by the 32 depth bits in LDS. Passes over digits that every
+//    element of a segment shares are skipped.
+//  * The in-workgroup rank uses 64-lane ballots: eight ballots, one
 //    per digit bit, give every lane the mask of lanes holding its digit;
 //    popcount below the lane is its rank (the zenn flag-bit rank, done on
 //    wave64 without a match instruction). Per-wave digit counters in LDS
@@ -377,6 +382,372 @@ __global__ __launch_bounds__(kSortThreads) void k_scatter(
     }
 }
 
+// ---- per-tile depth sort ----
+//
+// After the tile-id passes, each tile's entries are contiguous and in
+// Gaussian-index order. Each tile's segment is then sorted by its 32 depth
+// bits with a stable 8-bit LSD radix sort (passes over a digit that every
+// element shares are skipped), so the final order is (tile, depth bits,
+// Gaussian index): the order of one stable sort on the whole 64-bit key.
+// Segment sizes vary by orders of magnitude, so there are size classes:
+//   n <= 512      one wave per tile, no barriers (four tiles per workgroup)
+//   n <= 2048     a 256-lane workgroup
+//   n <= 8192     a 1024-lane workgroup with a 128 KB LDS arena
+//   larger        the 1024-lane workgroup, chunked through global scratch
+// Each class's kernel runs over all tiles and skips the others.
+constexpr int kSegWaveCap = 512;
+constexpr int kSegRounds = 8;  // 64-key rounds per wave
+
+// --- one wave per tile ---
+
+// Orders this wave's LDS accesses across lanes at a phase boundary (the
+// wave's LDS operations complete in order; this keeps the compiler from
+// moving them across the boundary).
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
+__global__ __launch_bounds__(256) void k_segment_sort_wave(
+    const uint32_t* __restrict__ seg_ranges, int n_tiles, const uint64_t* __restrict__ keys_in,
+    const uint32_t* __restrict__ vals_in, uint64_t* __restrict__ keys_out, uint32_t* __restrict__ vals_out) {
+    __shared__ uint32_t s_k[4][kSegWaveCap];
+    __shared__ uint32_t s_v[4][kSegWaveCap];
+    __shared__ uint32_t s_cnt[4][kRadix];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int t = blockIdx.x * 4 + wave;
+    if (t >= n_tiles) return;
+    const uint32_t start = seg_ranges[2 * t], end = seg_ranges[2 * t + 1];
+    const int n = (int)(end - start);
+    if (n <= 0 || n > kSegWaveCap) return;
+    if (n == 1) {
+        if (lane == 0) {
+            keys_out[start] = keys_in[start];
+            vals_out[start] = vals_in[start];
+        }
+        return;
+    }
+    const uint64_t hi = keys_in[start] & 0xFFFFFFFF00000000ull;
+    uint32_t* cnt = s_cnt[wave];
+    const int rounds = (n + 63) / 64;
+    // keys and values live in registers between passes; LDS only stages the scatter
+    uint32_t key[kSegRounds], val[kSegRounds];
+#pragma unroll
+    for (int r = 0; r < kSegRounds; ++r) {
+        const int i = r * 64 + lane;
+        key[r] = (r < rounds && i < n) ? (uint32_t)keys_in[start + i] : 0u;
+        val[r] = (r < rounds && i < n) ? vals_in[start + i] : 0u;
+    }
+    uint32_t* dk = s_k[wave];
+    uint32_t* dv = s_v[wave];
+    for (int p = 0; p < 4; ++p) {
+        const int shift = 8 * p;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) cnt[4 * lane + j] = 0u;
+        wave_sync();
+        uint32_t rank[kSegRounds];
+#pragma unroll
+        for (int r = 0; r < kSegRounds; ++r) {
+            rank[r] = 0u;
+            if (r < rounds) {
+                const bool valid = r * 64 + lane < n;
+                const uint32_t d = (key[r] >> shift) & (kRadix - 1);
+                const uint64_t peers = match_digit(d, valid);
+                const uint64_t below = peers & ((1ull << lane) - 1ull);
+                uint32_t before = 0;
+                if (valid) before = cnt[d];
+                rank[r] = before + (uint32_t)__popcll(below);
+                if (valid && below == 0ull) cnt[d] = before + (uint32_t)__popcll(peers);
+            }
+        }
+        wave_sync();
+        // digit starts: lane owns digits 4 lane .. 4 lane + 3
+        const uint32_t c0 = cnt[4 * lane], c1 = cnt[4 * lane + 1], c2 = cnt[4 * lane + 2], c3 = cnt[4 * lane + 3];
+        if (__ballot(c0 == (uint32_t)n || c1 == (uint32_t)n || c2 == (uint32_t)n || c3 == (uint32_t)n) != 0ull)
+            continue;  // one digit holds everything: this pass is the identity
+        const uint32_t local = (c0 + c1) + (c2 + c3);
+        uint32_t v = local;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t y = (uint32_t)__shfl_up((int)v, off, 64);
+            if (lane >= off) v += y;
+        }
+        const uint32_t b0 = v - local;
+        cnt[4 * lane] = b0;
+        cnt[4 * lane + 1] = b0 + c0;
+        cnt[4 * lane + 2] = b0 + c0 + c1;
+        cnt[4 * lane + 3] = b0 + c0 + c1 + c2;
+        wave_sync();
+#pragma unroll
+        for (int r = 0; r < kSegRounds; ++r) {
+            if (r < rounds && r * 64 + lane < n) {
+                const uint32_t d = (key[r] >> shift) & (kRadix - 1);
+                const uint32_t pos = cnt[d] + rank[r];
+                dk[pos] = key[r];
+                dv[pos] = val[r];
+            }
+        }
+        wave_sync();
+#pragma unroll
+        for (int r = 0; r < kSegRounds; ++r) {
+            const int i = r * 64 + lane;
+            if (r < rounds && i < n) {
+                key[r] = dk[i];
+                val[r] = dv[i];
+            }
+        }
+        wave_sync();
+    }
+#pragma unroll
+    for (int r = 0; r < kSegRounds; ++r) {
+        const int i = r * 64 + lane;
+        if (r < rounds && i < n) {
+            keys_out[start + i] = hi | key[r];
+            vals_out[start + i] = val[r];
+        }
+    }
+}
+
+// --- one workgroup per tile ---
+
+template <int NW>
+struct SegShared {
+    uint32_t wc[NW][kRadix];  // per-wave digit counts / prefixes
+    uint32_t base[kRadix];    // digit start (+ elements already placed)
+    uint32_t wsum[4];
+    uint32_t flag[4];         // pass p: every element has the same digit
+};
+
+// Exclusive scan of one value per thread over threads 0..255 (all threads
+// of the workgroup must call it: it contains a barrier).
+__device__ __forceinline__ uint32_t block_exclusive_scan_fast(uint32_t x, uint32_t* wsum) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t v = x;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = (uint32_t)__shfl_up((int)v, off, 64);
+        if (lane >= off) v += y;
+    }
+    if (lane == 63 && wave < 4) wsum[wave] = v;
+    __syncthreads();
+    uint32_t pre = 0;
+    for (int w = 0; w < wave && w < 4; ++w) pre += wsum[w];
+    return pre + v - x;
+}
+
+// One stable counting pass over n <= NW * 64 * kSegRounds elements,
+// src -> dst. Wave w ranks the contiguous elements [w q, (w + 1) q) (q a
+// multiple of 64) in rounds of 64 against its own digit counters, keeping
+// keys and ranks in registers; the per-wave counts give the wave prefixes
+// and the histogram. Returns false (moving nothing) when all elements share
+// the digit.
+template <int NW>
+__device__ __forceinline__ bool seg_pass_reg(const uint32_t* sk, const uint32_t* sv, uint32_t* dk,
+                                             uint32_t* dv, int n, int pass, SegShared<NW>& L) {
+    constexpr int NT = NW * 64;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int shift = 8 * pass;
+    const int q = ((n + NT - 1) / NT) * 64;
+    if (tid < kRadix)
+#pragma unroll
+        for (int w = 0; w < NW; ++w) L.wc[w][tid] = 0;
+    __syncthreads();
+    uint32_t key[kSegRounds], val[kSegRounds], rank[kSegRounds];
+#pragma unroll
+    for (int r = 0; r < kSegRounds; ++r) {
+        key[r] = 0u; val[r] = 0u; rank[r] = 0u;
+        if (r * 64 < q) {
+            const int i = wave * q + r * 64 + lane;
+            const bool valid = i < n;
+            key[r] = valid ? sk[i] : 0u;
+            val[r] = valid ? sv[i] : 0u;
+            const uint32_t d = (key[r] >> shift) & (kRadix - 1);
+            const uint64_t peers = match_digit(d, valid);
+            const uint64_t below = peers & ((1ull << lane) - 1ull);
+            uint32_t before = 0;
+            if (valid) before = L.wc[wave][d];
+            rank[r] = before + (uint32_t)__popcll(below);
+            if (valid && below == 0ull) L.wc[wave][d] = before + (uint32_t)__popcll(peers);
+        }
+    }
+    __syncthreads();
+    uint32_t acc = 0;
+    if (tid < kRadix) {
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const uint32_t c = L.wc[w][tid];
+            L.wc[w][tid] = acc;
+            acc += c;
+        }
+        if (acc == (uint32_t)n) L.flag[pass] = 1u;
+    }
+    const uint32_t b = block_exclusive_scan_fast(acc, L.wsum);
+    if (tid < kRadix) L.base[tid] = b;
+    __syncthreads();
+    if (L.flag[pass]) return false;
+#pragma unroll
+    for (int r = 0; r < kSegRounds; ++r) {
+        const int i = wave * q + r * 64 + lane;
+        if (r * 64 < q && i < n) {
+            const uint32_t d = (key[r] >> shift) & (kRadix - 1);
+            const uint32_t pos = L.base[d] + L.wc[wave][d] + rank[r];
+            dk[pos] = key[r];
+            dv[pos] = val[r];
+        }
+    }
+    __syncthreads();
+    return true;
+}
+
+// The same pass for any n, chunk by chunk (a histogram sweep gives the
+// digit starts; a running count per digit carries the order across chunks).
+template <int NW>
+__device__ __forceinline__ bool seg_pass_chunked(const uint32_t* sk, const uint32_t* sv, uint32_t* dk,
+                                                 uint32_t* dv, int n, int pass, SegShared<NW>& L) {
+    constexpr int NT = NW * 64;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int shift = 8 * pass;
+    if (tid < kRadix) L.base[tid] = 0;
+    __syncthreads();
+    for (int c = 0; c < n; c += NT) {
+        const int i = c + tid;
+        const bool valid = i < n;
+        const uint32_t d = valid ? (sk[i] >> shift) & (kRadix - 1) : 0u;
+        const uint64_t peers = match_digit(d, valid);
+        if (valid && lane == __ffsll((unsigned long long)peers) - 1) atomicAdd(&L.base[d], (uint32_t)__popcll(peers));
+    }
+    __syncthreads();
+    const uint32_t h = tid < kRadix ? L.base[tid] : 0u;
+    if (tid < kRadix && h == (uint32_t)n) L.flag[pass] = 1u;
+    const uint32_t b = block_exclusive_scan_fast(h, L.wsum);
+    if (tid < kRadix) {
+        L.base[tid] = b;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) L.wc[w][tid] = 0;
+    }
+    __syncthreads();
+    if (L.flag[pass]) return false;
+    for (int c = 0; c < n; c += NT) {
+        const int i = c + tid;
+        const bool valid = i < n;
+        const uint32_t key = valid ? sk[i] : 0u, val = valid ? sv[i] : 0u;
+        const uint32_t d = (key >> shift) & (kRadix - 1);
+        const uint64_t peers = match_digit(d, valid);
+        const uint64_t below = peers & ((1ull << lane) - 1ull);
+        if (valid && below == 0ull) L.wc[wave][d] = (uint32_t)__popcll(peers);
+        __syncthreads();
+        if (valid) {
+            uint32_t pre = 0;
+            for (int w = 0; w < wave; ++w) pre += L.wc[w][d];
+            const uint32_t pos = L.base[d] + pre + (uint32_t)__popcll(below);
+            dk[pos] = key;
+            dv[pos] = val;
+        }
+        __syncthreads();
+        if (tid < kRadix) {
+            uint32_t placed = 0;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                placed += L.wc[w][tid];
+                L.wc[w][tid] = 0;
+            }
+            L.base[tid] += placed;
+        }
+        __syncthreads();
+    }
+    return true;
+}
+
+// Four passes; the result ends in (xk, xv) whichever passes were skipped.
+template <int NW, bool kReg>
+__device__ __forceinline__ void seg_sort(uint32_t* xk, uint32_t* xv, uint32_t* yk, uint32_t* yv, int n,
+                                         SegShared<NW>& L) {
+    bool in_x = true;
+    for (int p = 0; p < 4; ++p) {
+        bool moved;
+        if (kReg)
+            moved = in_x ? seg_pass_reg<NW>(xk, xv, yk, yv, n, p, L) : seg_pass_reg<NW>(yk, yv, xk, xv, n, p, L);
+        else
+            moved = in_x ? seg_pass_chunked<NW>(xk, xv, yk, yv, n, p, L)
+                         : seg_pass_chunked<NW>(yk, yv, xk, xv, n, p, L);
+        if (moved) in_x = !in_x;
+    }
+    if (!in_x) {
+        for (int i = threadIdx.x; i < n; i += NW * 64) {
+            xk[i] = yk[i];
+            xv[i] = yv[i];
+        }
+        __syncthreads();
+    }
+}
+
+template <int NW, int kLo, int kCap, bool kGlobalBeyond>
+__device__ __forceinline__ void segment_sort_block(const uint32_t* __restrict__ seg_ranges,
+                                                   const uint64_t* __restrict__ keys_in,
+                                                   const uint32_t* __restrict__ vals_in,
+                                                   uint64_t* __restrict__ keys_out, uint32_t* __restrict__ vals_out,
+                                                   uint32_t* gk0, uint32_t* gv0, uint32_t* gk1, uint32_t* gv1,
+                                                   SegShared<NW>& L, uint32_t (*s_k)[kCap],
+                                                   uint32_t (*s_v)[kCap]) {
+    constexpr int NT = NW * 64;
+    const int t = blockIdx.x;
+    const uint32_t start = seg_ranges[2 * t], end = seg_ranges[2 * t + 1];
+    const int n = (int)(end - start);
+    if (n <= kLo || (!kGlobalBeyond && n > kCap)) return;
+    const uint64_t hi = keys_in[start] & 0xFFFFFFFF00000000ull;
+    if (threadIdx.x < 4) L.flag[threadIdx.x] = 0u;
+    if (n <= kCap) {
+        for (int i = threadIdx.x; i < n; i += NT) {
+            s_k[0][i] = (uint32_t)keys_in[start + i];
+            s_v[0][i] = vals_in[start + i];
+        }
+        __syncthreads();
+        seg_sort<NW, true>(s_k[0], s_v[0], s_k[1], s_v[1], n, L);
+        for (int i = threadIdx.x; i < n; i += NT) {
+            keys_out[start + i] = hi | s_k[0][i];
+            vals_out[start + i] = s_v[0][i];
+        }
+    } else {
+        uint32_t* xk = gk0 + start; uint32_t* xv = gv0 + start;
+        uint32_t* yk = gk1 + start; uint32_t* yv = gv1 + start;
+        for (int i = threadIdx.x; i < n; i += NT) {
+            xk[i] = (uint32_t)keys_in[start + i];
+            xv[i] = vals_in[start + i];
+        }
+        __syncthreads();
+        seg_sort<NW, false>(xk, xv, yk, yv, n, L);
+        for (int i = threadIdx.x; i < n; i += NT) {
+            keys_out[start + i] = hi | xk[i];
+            vals_out[start + i] = xv[i];
+        }
+    }
+}
+
+constexpr int kSegMidCap = 4 * 64 * kSegRounds;    // 2048
+constexpr int kSegBigCap = 16 * 64 * kSegRounds;   // 8192
+
+__global__ __launch_bounds__(256) void k_segment_sort_mid(
+    const uint32_t* __restrict__ seg_ranges, const uint64_t* __restrict__ keys_in,
+    const uint32_t* __restrict__ vals_in, uint64_t* __restrict__ keys_out, uint32_t* __restrict__ vals_out) {
+    __shared__ SegShared<4> L;
+    __shared__ uint32_t s_k[2][kSegMidCap];
+    __shared__ uint32_t s_v[2][kSegMidCap];
+    segment_sort_block<4, kSegWaveCap, kSegMidCap, false>(seg_ranges, keys_in, vals_in, keys_out, vals_out,
+                                                          nullptr, nullptr, nullptr, nullptr, L, s_k, s_v);
+}
+
+__global__ __launch_bounds__(1024) void k_segment_sort_big(
+    const uint32_t* __restrict__ seg_ranges, const uint64_t* __restrict__ keys_in,
+    const uint32_t* __restrict__ vals_in, uint64_t* __restrict__ keys_out, uint32_t* __restrict__ vals_out,
+    uint32_t* __restrict__ gk0, uint32_t* __restrict__ gv0, uint32_t* __restrict__ gk1,
+    uint32_t* __restrict__ gv1) {
+    __shared__ SegShared<16> L;
+    __shared__ uint32_t s_k[2][kSegBigCap];
+    __shared__ uint32_t s_v[2][kSegBigCap];
+    segment_sort_block<16, kSegMidCap, kSegBigCap, true>(seg_ranges, keys_in, vals_in, keys_out, vals_out,
+                                                         gk0, gv0, gk1, gv1, L, s_k, s_v);
+}
+
 // ---- tile ranges ----
 
 __global__ void k_fill_u32(uint32_t* __restrict__ p, size_t n, uint32_t v) {
@@ -394,7 +765,7 @@ __global__ void k_ranges(const uint64_t* __restrict__ keys, uint32_t n, uint32_t
 
 }  // namespace
 
-size_t bin_scratch_layout(int n, int64_t capacity, BinScratch* out, void* base) {
+size_t bin_scratch_layout(int n, int64_t capacity, int n_tiles, BinScratch* out, void* base) {
     const size_t nb_scan = (size_t)(n + kScanTile - 1) / kScanTile;
     const size_t nb_sort = (size_t)((capacity + kSortTile - 1) / kSortTile);
     size_t off = 0;
@@ -411,6 +782,11 @@ size_t bin_scratch_layout(int n, int64_t capacity, BinScratch* out, void* base) 
     const size_t o_vt = take((size_t)capacity * 4);
     const size_t o_cnt = take((size_t)kRadix * nb_sort * 4);
     const size_t o_dt = take((size_t)kRadix * 4);
+    const size_t o_sr = take((size_t)n_tiles * 8);
+    const size_t o_k0 = take((size_t)capacity * 4);
+    const size_t o_v0 = take((size_t)capacity * 4);
+    const size_t o_k1 = take((size_t)capacity * 4);
+    const size_t o_v1 = take((size_t)capacity * 4);
     if (out && base) {
         char* b = (char*)base;
         out->block_sums = (uint32_t*)(b + o_bs);
@@ -421,6 +797,11 @@ size_t bin_scratch_layout(int n, int64_t capacity, BinScratch* out, void* base) 
         out->vals_tmp = (uint32_t*)(b + o_vt);
         out->counts = (uint32_t*)(b + o_cnt);
         out->digit_totals = (uint32_t*)(b + o_dt);
+        out->seg_ranges = (uint32_t*)(b + o_sr);
+        out->seg_k0 = (uint32_t*)(b + o_k0);
+        out->seg_v0 = (uint32_t*)(b + o_v0);
+        out->seg_k1 = (uint32_t*)(b + o_k1);
+        out->seg_v1 = (uint32_t*)(b + o_v1);
     }
     return off;
 }
@@ -445,29 +826,22 @@ hipError_t launch_duplicate(const gs_camera& cam, int n, uint32_t n_entries, con
     return hipGetLastError();
 }
 
-int radix_pass_count(int key_bits) { return (key_bits + 7) / 8; }
+int tile_pass_count(int tile_bits) { return (tile_bits + 7) / 8; }
 
-bool radix_input_in_tmp(int key_bits) { return (radix_pass_count(key_bits) & 1) != 0; }
+bool dup_writes_tmp(int tile_bits) { return (tile_pass_count(tile_bits) & 1) == 0; }
 
-hipError_t launch_radix_sort(uint64_t* keys, uint32_t* values, uint32_t n, int key_bits,
-                             const BinScratch& s, hipStream_t stream) {
-    const int passes = radix_pass_count(key_bits);
-    const bool in_tmp = (passes & 1) != 0;
-    uint64_t* kin = in_tmp ? s.keys_tmp : keys;
-    uint32_t* vin = in_tmp ? s.vals_tmp : values;
-    uint64_t* kout = in_tmp ? keys : s.keys_tmp;
-    uint32_t* vout = in_tmp ? values : s.vals_tmp;
-    if (n <= 1) {
-        if (in_tmp && n == 1) {
-            hipError_t e = hipMemcpyAsync(keys, kin, 8, hipMemcpyDeviceToDevice, stream);
-            if (e == hipSuccess) e = hipMemcpyAsync(values, vin, 4, hipMemcpyDeviceToDevice, stream);
-            return e;
-        }
-        return hipSuccess;
-    }
+hipError_t launch_sort(uint64_t* keys, uint32_t* values, uint32_t n, int tile_bits, int n_tiles,
+                       const BinScratch& s, hipStream_t stream) {
+    if (n == 0) return hipSuccess;
+    const int passes = tile_pass_count(tile_bits);
+    // the tile-id passes end in the tmp pair; the per-tile sort writes (keys, values)
+    uint64_t* kin = (passes & 1) ? keys : s.keys_tmp;
+    uint32_t* vin = (passes & 1) ? values : s.vals_tmp;
+    uint64_t* kout = (passes & 1) ? s.keys_tmp : keys;
+    uint32_t* vout = (passes & 1) ? s.vals_tmp : values;
     const int nblk = (int)((n + kSortTile - 1) / kSortTile);
     for (int p = 0; p < passes; ++p) {
-        const int shift = 8 * p;
+        const int shift = 32 + 8 * p;
         hipLaunchKernelGGL(k_digit_count, dim3(nblk), dim3(kSortThreads), 0, stream, kin, n, shift,
                            nblk, s.counts);
         hipLaunchKernelGGL(k_digit_scan, dim3(kRadix), dim3(256), 0, stream, s.counts, nblk,
@@ -477,11 +851,23 @@ hipError_t launch_radix_sort(uint64_t* keys, uint32_t* values, uint32_t n, int k
         uint64_t* tk = kin; kin = kout; kout = tk;
         uint32_t* tv = vin; vin = vout; vout = tv;
     }
+    // kin/vin now is the tmp pair, grouped by tile
+    hipError_t e = launch_tile_ranges(s.keys_tmp, n, n_tiles, s.seg_ranges, stream);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_segment_sort_wave, dim3((n_tiles + 3) / 4), dim3(256), 0, stream, s.seg_ranges,
+                       n_tiles, s.keys_tmp, s.vals_tmp, keys, values);
+    if (n > (uint32_t)kSegWaveCap)  // only then can a tile exceed the wave class
+        hipLaunchKernelGGL(k_segment_sort_mid, dim3(n_tiles), dim3(256), 0, stream, s.seg_ranges,
+                           s.keys_tmp, s.vals_tmp, keys, values);
+    if (n > (uint32_t)kSegMidCap)
+        hipLaunchKernelGGL(k_segment_sort_big, dim3(n_tiles), dim3(1024), 0, stream, s.seg_ranges,
+                           s.keys_tmp, s.vals_tmp, keys, values, s.seg_k0, s.seg_v0, s.seg_k1, s.seg_v1);
     return hipGetLastError();
 }
 
 hipError_t launch_tile_ranges(const uint64_t* keys, uint32_t n_entries, int n_tiles,
                               uint32_t* ranges, hipStream_t stream) {
+    // clear every tile (empty tiles keep (0, 0)), then mark the run boundaries
     const size_t words = 2 * (size_t)n_tiles;
     hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, stream,
                        ranges, words, 0u);

@@ -64,44 +64,45 @@ __device__ __forceinline__ void splat_alpha(float A, float B, float C, float o, 
 //
 // A workgroup's four waves each own a 16 x 4 strip of the tile (rows
 // 4w .. 4w+3). A splat can only change a pixel if alpha >= 1/255, i.e. if
-// Q(d) = A dx^2 + 2B dx dy + C dy^2 <= 2 ln(255 o). live_mask() computes, in
-// double, the exact minimum of Q over each strip's pixel rectangle (Q is
-// convex along every edge, so off the centre the minimum lies on an edge)
-// and keeps the strip unless that minimum exceeds the threshold by more than
-// a bound on the fp32 rounding of Q and of the exponential. A culled
-// (splat, strip) pair therefore has alpha < 1/255 at every pixel of the
-// strip in the fp32 evaluation as well: skipping it changes no result.
-__device__ __forceinline__ double edge_min_q(double A, double B, double C, double fixed, double lo,
-                                             double hi, bool fixed_is_x) {
+// Q(d) = A dx^2 + 2B dx dy + C dy^2 <= 2 ln(255 o). live_mask() computes the
+// minimum of Q over each strip's pixel rectangle (Q is convex along every
+// edge, so off the centre the minimum lies on an edge) and keeps the strip
+// unless that minimum exceeds the threshold by more than a bound on the
+// rounding of Q (in the kernels' fp32 evaluation and in this one) and of
+// the exponential. A culled (splat, strip) pair therefore has
+// alpha < 1/255 at every pixel of the strip: skipping it changes no result.
+__device__ __forceinline__ float edge_min_q(float A, float B, float C, float fixed, float lo, float hi,
+                                            bool fixed_is_x) {
     // minimise Q along the segment where one offset is `fixed`
     if (fixed_is_x) {
-        double t = fmin(fmax(-B * fixed / C, lo), hi);
-        return (A * fixed + 2.0 * B * t) * fixed + C * t * t;
+        const float t = fminf(fmaxf(-B * fixed * __builtin_amdgcn_rcpf(C), lo), hi);
+        return (A * fixed + 2.0f * B * t) * fixed + C * t * t;
     }
-    double t = fmin(fmax(-B * fixed / A, lo), hi);
-    return A * t * t + (2.0 * B * t + C * fixed) * fixed;
+    const float t = fminf(fmaxf(-B * fixed * __builtin_amdgcn_rcpf(A), lo), hi);
+    return A * t * t + (2.0f * B * t + C * fixed) * fixed;
 }
 
-__device__ __noinline__ uint32_t live_mask(float4 co, float u, float v, int x0, int y0) {
-    const double A = co.x, B = co.y, C = co.z, o = co.w;
-    if (!(o > 0.0)) return 0u;  // alpha = o G <= 0 never reaches the floor
-    const double thr = 2.0 * log(255.0 * o) * (1.0 + 1e-6) + 1e-4;
-    const double bound = 16.0 * 5.96e-8 * (fabs(A) + fabs(C) + 2.0 * fabs(B));
+__device__ __forceinline__ uint32_t live_mask(float4 co, float u, float v, int x0, int y0) {
+    const float A = co.x, B = co.y, C = co.z, o = co.w;
+    if (!(o > 0.0f)) return 0u;  // alpha = o G <= 0 never reaches the floor
+    const float thr = 2.0f * __logf(255.0f * o) * (1.0f + 1e-5f) + 1e-3f;
+    // 64 ulp of |A| dx^2 + |C| dy^2 + 2|B dx dy| covers both evaluations
+    const float bound = 64.0f * 5.96e-8f * (fabsf(A) + fabsf(C) + 2.0f * fabsf(B));
     uint32_t mask = 0;
-#pragma unroll 1
+#pragma unroll
     for (int w = 0; w < 4; ++w) {
-        const double dx0 = (double)x0 - u, dx1 = (double)(x0 + 15) - u;
-        const double dy0 = (double)(y0 + 4 * w) - v, dy1 = (double)(y0 + 4 * w + 3) - v;
+        const float dx0 = (float)x0 - u, dx1 = (float)(x0 + 15) - u;
+        const float dy0 = (float)(y0 + 4 * w) - v, dy1 = (float)(y0 + 4 * w + 3) - v;
         bool live;
-        if (dx0 <= 0.0 && dx1 >= 0.0 && dy0 <= 0.0 && dy1 >= 0.0) {
+        if (dx0 <= 0.0f && dx1 >= 0.0f && dy0 <= 0.0f && dy1 >= 0.0f) {
             live = true;
         } else {
-            double q = edge_min_q(A, B, C, dx0, dy0, dy1, true);
-            q = fmin(q, edge_min_q(A, B, C, dx1, dy0, dy1, true));
-            q = fmin(q, edge_min_q(A, B, C, dy0, dx0, dx1, false));
-            q = fmin(q, edge_min_q(A, B, C, dy1, dx0, dx1, false));
-            const double dmax2 = fmax(dx0 * dx0, dx1 * dx1) + fmax(dy0 * dy0, dy1 * dy1);
-            live = q - bound * dmax2 <= thr;
+            float q = edge_min_q(A, B, C, dx0, dy0, dy1, true);
+            q = fminf(q, edge_min_q(A, B, C, dx1, dy0, dy1, true));
+            q = fminf(q, edge_min_q(A, B, C, dy0, dx0, dx1, false));
+            q = fminf(q, edge_min_q(A, B, C, dy1, dx0, dx1, false));
+            const float dmax2 = fmaxf(dx0 * dx0, dx1 * dx1) + fmaxf(dy0 * dy0, dy1 * dy1);
+            live = !(q - bound * dmax2 > thr);  // a NaN anywhere keeps the strip
         }
         mask |= (live ? 1u : 0u) << w;
     }
@@ -212,9 +213,14 @@ __device__ __forceinline__ float dpp_row_sum(float x) {
     return x;
 }
 
-__global__ void k_zero(float* __restrict__ p, size_t n) {
-    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) p[i] = 0.0f;
+// Clears the three gradient arrays (n x 2, n x 4, n x 4 floats) in one launch.
+__global__ void k_zero_grads(float2* __restrict__ gm, float4* __restrict__ gc, float4* __restrict__ gr, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) {
+        gm[i] = make_float2(0.f, 0.f);
+        gc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        gr[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
 }
 
 constexpr int kBwdBatch = 32;
@@ -368,15 +374,9 @@ hipError_t launch_composite_bwd(const gs_camera& cam, int n, const uint32_t* ran
                                 const float* final_T, const uint32_t* n_contrib,
                                 const float* dL_dimage, float2* grad_mean2d,
                                 float4* grad_conic_op, float4* grad_rgb, hipStream_t stream) {
-    if (n > 0) {
-        const size_t nm = 2 * (size_t)n, nc = 4 * (size_t)n;
-        hipLaunchKernelGGL(k_zero, dim3((unsigned)((nm + 255) / 256)), dim3(256), 0, stream,
-                           (float*)grad_mean2d, nm);
-        hipLaunchKernelGGL(k_zero, dim3((unsigned)((nc + 255) / 256)), dim3(256), 0, stream,
-                           (float*)grad_conic_op, nc);
-        hipLaunchKernelGGL(k_zero, dim3((unsigned)((nc + 255) / 256)), dim3(256), 0, stream,
-                           (float*)grad_rgb, nc);
-    }
+    if (n > 0)
+        hipLaunchKernelGGL(k_zero_grads, dim3((n + 255) / 256), dim3(256), 0, stream, grad_mean2d,
+                           grad_conic_op, grad_rgb, n);
     const int TX = tiles_x(cam), TY = tiles_y(cam);
     hipLaunchKernelGGL(k_composite_bwd, dim3(TX * TY), dim3(256), 0, stream, cam.width, cam.height,
                        TX, ranges, point_list, xy_depth, conic_op, rgb, bg, final_T, n_contrib,

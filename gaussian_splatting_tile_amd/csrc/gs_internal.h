@@ -74,8 +74,13 @@ struct BinScratch {
     uint32_t* vals_tmp;       // [capacity]
     uint32_t* counts;         // [256][nb_sort]
     uint32_t* digit_totals;   // [256]
+    uint32_t* seg_ranges;     // [n_tiles][2] tile segments after the tile-id passes
+    uint32_t* seg_k0;         // [capacity] global ping-pong of the per-tile sort
+    uint32_t* seg_v0;
+    uint32_t* seg_k1;
+    uint32_t* seg_v1;
 };
-size_t bin_scratch_layout(int n, int64_t capacity, BinScratch* out, void* base);
+size_t bin_scratch_layout(int n, int64_t capacity, int n_tiles, BinScratch* out, void* base);
 
 // Exclusive scan of tiles_touched into s.offsets and s.total (entry count).
 hipError_t launch_scan(int n, const uint32_t* tiles_touched, const BinScratch& s, hipStream_t stream);
@@ -83,15 +88,14 @@ hipError_t launch_scan(int n, const uint32_t* tiles_touched, const BinScratch& s
 hipError_t launch_duplicate(const gs_camera& cam, int n, uint32_t n_entries, const float4* xy_depth,
                             const BinScratch& s, uint64_t* keys, uint32_t* values, hipStream_t stream);
 
-// Stable LSD radix sort, 8-bit digits, of n (key, value) pairs on key bits
-// [0, key_bits). (keys_tmp, vals_tmp) in the scratch is the ping-pong
-// partner; the input must sit in the tmp pair when the pass count is odd
-// (radix_input_in_tmp), in (keys, values) otherwise, so the last pass always
-// writes into (keys, values).
-int radix_pass_count(int key_bits);
-bool radix_input_in_tmp(int key_bits);
-hipError_t launch_radix_sort(uint64_t* keys, uint32_t* values, uint32_t n, int key_bits,
-                             const BinScratch& s, hipStream_t stream);
+// Sort n entries by the whole key (tile id << 32 | depth bits), stably.
+// The duplication must have written the entries into the tmp pair when
+// dup_writes_tmp(tile_bits), into (keys, values) otherwise; the result is in
+// (keys, values).
+int tile_pass_count(int tile_bits);
+bool dup_writes_tmp(int tile_bits);
+hipError_t launch_sort(uint64_t* keys, uint32_t* values, uint32_t n, int tile_bits, int n_tiles,
+                       const BinScratch& s, hipStream_t stream);
 
 hipError_t launch_tile_ranges(const uint64_t* keys, uint32_t n_entries, int n_tiles,
                               uint32_t* ranges, hipStream_t stream);
