@@ -24,10 +24,12 @@
 //    exactly the alphas, skips and clamps the forward saw.
 //  * Workgroup ids are remapped so each XCD renders a contiguous band of
 //    tiles (neighbouring tiles share splats; L2 is per XCD).
-//  * Backward: per splat, each wave sums its 64 pixels' nine gradient terms
-//    with cross-lane adds (skipped when no lane contributed), the four
-//    waves combine in LDS, and one global atomic per value per tile entry
-//    lands in the per-Gaussian gradient.
+//  * Backward: per splat, each wave sums nine per-pixel terms over its 16-lane
+//    rows with DPP adds (skipped when no lane contributed) into LDS; the
+//    terms are the colour gradient, dL/do, and the moments of dL/dpower
+//    (dx, dy, dx^2, dx dy, dy^2 times it), from which the conic and mean
+//    gradients follow once per (splat, tile). One global atomic per value
+//    per tile entry lands in the per-Gaussian gradient.
 #include "gs_internal.h"
 
 namespace gs {
@@ -120,7 +122,7 @@ __global__ __launch_bounds__(256) void k_composite_fwd(
     __shared__ float s_blue[kBatch];
     __shared__ uint32_t s_live[kBatch];
 
-    const int tile = xcd_contiguous(blockIdx.x, gridDim.x);
+    const int tile = blockIdx.x;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -213,6 +215,18 @@ __device__ __forceinline__ float dpp_row_sum(float x) {
     return x;
 }
 
+// Sum of the 16 row partials of one term.
+__device__ __forceinline__ float part_sum(const float* p) {
+    const float4* pv = reinterpret_cast<const float4*>(p);
+    const float4 a = pv[0], b = pv[1], c = pv[2], d = pv[3];
+    return (((a.x + a.y) + (a.z + a.w)) + ((b.x + b.y) + (b.z + b.w))) +
+           (((c.x + c.y) + (c.z + c.w)) + ((d.x + d.y) + (d.z + d.w)));
+}
+
+__device__ __forceinline__ void atomic_add_nz(float* p, float v) {
+    if (v != 0.0f) unsafeAtomicAdd(p, v);
+}
+
 // Clears the three gradient arrays (n x 2, n x 4, n x 4 floats) in one launch.
 __global__ void k_zero_grads(float2* __restrict__ gm, float4* __restrict__ gc, float4* __restrict__ gr, int n) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -223,8 +237,10 @@ __global__ void k_zero_grads(float2* __restrict__ gm, float4* __restrict__ gc, f
     }
 }
 
+// Per (splat, wave) the nine terms are summed over each 16-lane row with
+// DPP; the four row sums of each wave go to LDS (16 partials per splat).
 constexpr int kBwdBatch = 32;
-constexpr int kParts = 16;  // 4 waves x 4 rows of 16 lanes
+constexpr int kParts = 16;  // 4 waves x 4 rows
 
 __global__ __launch_bounds__(256) void k_composite_bwd(
     const int W, const int H, const int TX, const uint32_t* __restrict__ ranges,
@@ -241,7 +257,7 @@ __global__ __launch_bounds__(256) void k_composite_bwd(
     __shared__ float s_part[kBwdBatch][9][kParts];  // per-row partial sums
     __shared__ uint32_t s_maxnc[4];
 
-    const int tile = xcd_contiguous(blockIdx.x, gridDim.x);
+    const int tile = blockIdx.x;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -293,7 +309,8 @@ __global__ __launch_bounds__(256) void k_composite_bwd(
         __syncthreads();
 
         // live splats of this wave below its largest n_contrib, walked back to front
-        uint64_t mk = __ballot(lane < cnt && bstart + lane < wave_maxnc && ((s_live[lane & 31] >> wave) & 1u));
+        static_assert(kBwdBatch <= 64, "one 64-bit live mask");
+        uint64_t mk = __ballot(lane < cnt && bstart + lane < wave_maxnc && ((s_live[lane] >> wave) & 1u));
         while (mk != 0ull) {
             const int k = 63 - __clzll((long long)mk);
             mk &= ~(1ull << k);
@@ -305,23 +322,22 @@ __global__ __launch_bounds__(256) void k_composite_bwd(
             splat_alpha(co.x, co.y, co.z, co.w, dx, dy, G, alpha);
             // branch-free: lanes past their n_contrib or below the floor add nothing
             const bool use = bstart + k < (int)nc && alpha >= kAlphaMin;
-            const float om = 1.0f - alpha;
-            const float Tj = T * __builtin_amdgcn_rcpf(om);  // transmittance in front of k
+            const float Tj = T * __builtin_amdgcn_rcpf(1.0f - alpha);  // transmittance in front of k
             const float w = use ? alpha * Tj : 0.0f;
-            const float d6 = w * g0, d7 = w * g1, d8 = w * g2;
-            const float dL_da = ((g0 * (xc.z - B0) + g1 * (xc.w - B1)) + g2 * (cb - B2)) * Tj;
-            B0 = use ? alpha * xc.z + om * B0 : B0;
-            B1 = use ? alpha * xc.w + om * B1 : B1;
-            B2 = use ? alpha * cb + om * B2 : B2;
+            const float d6 = w * g0, d7 = w * g1, d8 = w * g2;          // dL/dc
+            const float e0 = xc.z - B0, e1 = xc.w - B1, e2 = cb - B2;     // colour minus colour behind
+            const float dL_da = __builtin_fmaf(g2, e2, __builtin_fmaf(g1, e1, g0 * e0)) * Tj;
+            B0 = use ? __builtin_fmaf(alpha, e0, B0) : B0;                 // B + a (c - B)
+            B1 = use ? __builtin_fmaf(alpha, e1, B1) : B1;
+            B2 = use ? __builtin_fmaf(alpha, e2, B2) : B2;
             T = use ? Tj : T;
-            const bool geo = use && co.w * G <= kAlphaMax;  // not saturated
-            const float dp = geo ? alpha * dL_da : 0.0f;
+            // unsaturated alpha = o G: dL/do = G dL/da, dL/dpower = o G dL/da
+            const bool geo = use && co.w * G <= kAlphaMax;
             const float d5 = geo ? G * dL_da : 0.0f;
-            const float d2 = -0.5f * dx * dx * dp;
-            const float d3 = -dx * dy * dp;
-            const float d4 = -0.5f * dy * dy * dp;
-            const float d0 = (co.x * dx + co.y * dy) * dp;
-            const float d1 = (co.y * dx + co.z * dy) * dp;
+            const float dp = co.w * d5;
+            // moments of dL/dpower; the conic is applied once per splat afterwards
+            const float d0 = dx * dp, d1 = dy * dp;         // sum dx dp, sum dy dp
+            const float d2 = dx * d0, d3 = dy * d0, d4 = dy * d1;  // dx^2 dp, dx dy dp, dy^2 dp
             const bool any = use;
             if (__ballot(any) != 0ull) {
                 const float r0 = dpp_row_sum(d0), r1 = dpp_row_sum(d1), r2 = dpp_row_sum(d2);
@@ -336,20 +352,25 @@ __global__ __launch_bounds__(256) void k_composite_bwd(
             }
         }
         __syncthreads();
-        // one thread per (splat, value): sum the 16 partials, one atomic
-        for (int i = tid; i < cnt * 9; i += 256) {
-            const int k = i / 9, v = i - 9 * (i / 9);
-            const float* pp = s_part[k][v];
-            float sum = 0.0f;
-#pragma unroll
-            for (int r = 0; r < kParts; ++r) sum += pp[r];
-            if (sum != 0.0f) {
-                const uint32_t g = s_gid[k];
-                float* dst = v < 2 ? grad_mean2d + 2 * (size_t)g + v
-                           : v < 6 ? grad_conic_op + 4 * (size_t)g + (v - 2)
-                                   : grad_rgb + 4 * (size_t)g + (v - 6);
-                unsafeAtomicAdd(dst, sum);
-            }
+        // one thread per splat: sum the 16 row partials of each term, turn
+        // the moments into gradients, one atomic per output
+        //   d(u, v) = (A Sx + B Sy, B Sx + C Sy); dA = -Sxx / 2; dB = -Sxy; dC = -Syy / 2
+        if (tid < cnt) {
+            const float4 co = s_conic[tid];
+            const uint32_t g = s_gid[tid];
+            float* gm = grad_mean2d + 2 * (size_t)g;
+            float* gc = grad_conic_op + 4 * (size_t)g;
+            float* gr = grad_rgb + 4 * (size_t)g;
+            const float Sx = part_sum(s_part[tid][0]), Sy = part_sum(s_part[tid][1]);
+            atomic_add_nz(gm + 0, co.x * Sx + co.y * Sy);
+            atomic_add_nz(gm + 1, co.y * Sx + co.z * Sy);
+            atomic_add_nz(gc + 0, -0.5f * part_sum(s_part[tid][2]));
+            atomic_add_nz(gc + 1, -part_sum(s_part[tid][3]));
+            atomic_add_nz(gc + 2, -0.5f * part_sum(s_part[tid][4]));
+            atomic_add_nz(gc + 3, part_sum(s_part[tid][5]));
+            atomic_add_nz(gr + 0, part_sum(s_part[tid][6]));
+            atomic_add_nz(gr + 1, part_sum(s_part[tid][7]));
+            atomic_add_nz(gr + 2, part_sum(s_part[tid][8]));
         }
     }
 }
