@@ -13,7 +13,10 @@ STATUS_NAMES = {0: "GS_OK", 1: "GS_ERR_INVALID", 2: "GS_ERR_CAPACITY", 3: "GS_ER
 
 # Every symbol include/gs.h declares.
 EXPORTS = ("gs_constants", "gs_last_error", "gs_version", "gs_preprocess", "gs_bin_and_sort",
-           "gs_tile_ranges", "gs_composite_fwd", "gs_composite_bwd")
+           "gs_bin_and_sort_async", "gs_tile_ranges", "gs_tile_ranges_async", "gs_composite_fwd",
+           "gs_composite_bwd")
+# entry count stored by the asynchronous binning when a bounded wait gave up
+ENTRIES_FAILED = (1 << 64) - 1
 
 
 class GsCamera(ctypes.Structure):
@@ -55,8 +58,12 @@ def load() -> ctypes.CDLL:
     lib.gs_bin_and_sort.restype = ctypes.c_int
     lib.gs_bin_and_sort.argtypes = [CAM, I32, P, P, P, P, I64, P, ctypes.POINTER(ctypes.c_size_t),
                                     ctypes.POINTER(ctypes.c_int64), P]
+    lib.gs_bin_and_sort_async.restype = ctypes.c_int
+    lib.gs_bin_and_sort_async.argtypes = [CAM, I32, P, P, P, P, I64, P, ctypes.POINTER(ctypes.c_size_t), P, P]
     lib.gs_tile_ranges.restype = ctypes.c_int
     lib.gs_tile_ranges.argtypes = [CAM, P, I64, P, P]
+    lib.gs_tile_ranges_async.restype = ctypes.c_int
+    lib.gs_tile_ranges_async.argtypes = [CAM, P, P, I64, P, P]
     lib.gs_composite_fwd.restype = ctypes.c_int
     lib.gs_composite_fwd.argtypes = [CAM, P, P, P, P, P, P, P, P, P, P, P]
     lib.gs_composite_bwd.restype = ctypes.c_int

@@ -44,13 +44,6 @@ gs_status check_camera(const gs_camera* cam) {
     return GS_OK;
 }
 
-int tile_bits(const gs_camera& cam) {
-    const int n_tiles = gs::tiles_x(cam) * gs::tiles_y(cam);
-    int b = 0;
-    while ((1 << b) < n_tiles) ++b;
-    return b;
-}
-
 }  // namespace
 
 extern "C" {
@@ -98,56 +91,92 @@ gs_status gs_preprocess(const gs_camera* cam, int32_t n, const float* means, con
                      "gs_preprocess launch");
 }
 
+namespace {
+
+// Checks shared by the blocking and the asynchronous binning entry points;
+// on GS_OK with scratch != NULL, *s is laid out in scratch.
+gs_status bin_args(const char* fn, const gs_camera* cam, int32_t n, const float* xy_depth,
+                   const uint32_t* tiles_touched, const uint64_t* keys, const uint32_t* point_list,
+                   int64_t capacity, void* scratch, size_t* scratch_bytes, bool* size_query, gs::BinScratch* s) {
+    if (gs_status st = check_camera(cam)) return st;
+    if (n < 0 || n > GS_MAX_GAUSSIANS) return fail(GS_ERR_INVALID, "n = %d outside [0, %d]", n, GS_MAX_GAUSSIANS);
+    if (capacity < 0 || capacity > (int64_t)UINT32_MAX)
+        return fail(GS_ERR_INVALID, "capacity %lld outside [0, 2^32 - 1]", (long long)capacity);
+    if (!scratch_bytes) return fail(GS_ERR_INVALID, "%s: scratch_bytes is NULL", fn);
+    const size_t need = gs::bin_scratch_layout(n, capacity, nullptr, nullptr);
+    *size_query = scratch == nullptr;
+    if (*size_query) {
+        *scratch_bytes = need;
+        return GS_OK;
+    }
+    if (*scratch_bytes < need)
+        return fail(GS_ERR_INVALID, "%s: scratch of %zu bytes is smaller than the %zu required", fn,
+                    *scratch_bytes, need);
+    if ((uintptr_t)scratch & 255) return fail(GS_ERR_INVALID, "%s: scratch must be 256-byte aligned", fn);
+    if (n > 0 && (!xy_depth || !tiles_touched || (capacity > 0 && (!keys || !point_list))))
+        return fail(GS_ERR_INVALID, "%s: a required pointer is NULL", fn);
+    if (n > 0 && ((uintptr_t)xy_depth & 15)) return fail(GS_ERR_INVALID, "%s: xy_depth must be 16-byte aligned", fn);
+    gs::bin_scratch_layout(n, capacity, s, scratch);
+    return GS_OK;
+}
+
+}  // namespace
+
 gs_status gs_bin_and_sort(const gs_camera* cam, int32_t n, const float* xy_depth,
                           const uint32_t* tiles_touched, uint64_t* keys, uint32_t* point_list,
                           int64_t capacity, void* scratch, size_t* scratch_bytes,
                           int64_t* n_entries, void* stream) {
     g_last_error.clear();
-    if (gs_status s = check_camera(cam)) return s;
-    if (n < 0 || n > GS_MAX_GAUSSIANS) return fail(GS_ERR_INVALID, "n = %d outside [0, %d]", n, GS_MAX_GAUSSIANS);
-    if (capacity < 0 || capacity > (int64_t)UINT32_MAX)
-        return fail(GS_ERR_INVALID, "capacity %lld outside [0, 2^32 - 1]", (long long)capacity);
-    if (!scratch_bytes) return fail(GS_ERR_INVALID, "scratch_bytes is NULL");
     gs::BinScratch s{};
-    const int n_tiles = gs::tiles_x(*cam) * gs::tiles_y(*cam);
-    const size_t need = gs::bin_scratch_layout(n, capacity, n_tiles, nullptr, nullptr);
-    if (!scratch) {
-        *scratch_bytes = need;
-        return GS_OK;
-    }
-    if (!n_entries) return fail(GS_ERR_INVALID, "n_entries is NULL");
-    if (*scratch_bytes < need)
-        return fail(GS_ERR_INVALID, "scratch of %zu bytes is smaller than the %zu required",
-                    *scratch_bytes, need);
-    if ((uintptr_t)scratch & 255) return fail(GS_ERR_INVALID, "scratch must be 256-byte aligned");
+    bool query = false;
+    if (gs_status e = bin_args("gs_bin_and_sort", cam, n, xy_depth, tiles_touched, keys, point_list, capacity,
+                               scratch, scratch_bytes, &query, &s))
+        return e;
+    if (query) return GS_OK;
+    if (!n_entries) return fail(GS_ERR_INVALID, "gs_bin_and_sort: n_entries is NULL");
     *n_entries = 0;
     if (n == 0) return GS_OK;
-    if (!xy_depth || !tiles_touched || (capacity > 0 && (!keys || !point_list)))
-        return fail(GS_ERR_INVALID, "gs_bin_and_sort: a required pointer is NULL");
-    gs::bin_scratch_layout(n, capacity, n_tiles, &s, scratch);
     hipStream_t st = (hipStream_t)stream;
-
-    const int tbits = tile_bits(*cam);
-    const bool in_tmp = gs::dup_writes_tmp(tbits);
-    if (gs_status e = hip_check(gs::launch_scan(n, tiles_touched, s, st), "scan launch")) return e;
-    uint64_t total = 0;
-    if (gs_status e = hip_check(hipMemcpyAsync(&total, s.total, sizeof(total), hipMemcpyDeviceToHost, st),
+    if (gs_status e = hip_check(gs::launch_bin_and_sort(*cam, n, (const float4*)xy_depth, tiles_touched, keys,
+                                                        point_list, (uint32_t)capacity, s, nullptr, st),
+                                "bin_and_sort launch"))
+        return e;
+    // the error word and the entry count, in one copy, once everything is enqueued
+    uint32_t flags[3] = {0, 0, 0};
+    if (gs_status e = hip_check(hipMemcpyAsync(flags, s.err, sizeof(flags), hipMemcpyDeviceToHost, st),
                                 "entry count copy"))
         return e;
     if (gs_status e = hip_check(hipStreamSynchronize(st), "entry count sync")) return e;
+    if (flags[0] != 0) return fail(GS_ERR_HIP, "gs_bin_and_sort: a radix pass's bounded wait gave up");
+    const uint64_t total = (uint64_t)flags[1] | ((uint64_t)flags[2] << 32);
     *n_entries = (int64_t)total;
     if (total > (uint64_t)UINT32_MAX)
         return fail(GS_ERR_OVERFLOW, "%llu entries do not fit in 32 bits", (unsigned long long)total);
     if ((int64_t)total > capacity)
-        return fail(GS_ERR_CAPACITY, "%llu entries exceed the capacity %lld",
-                    (unsigned long long)total, (long long)capacity);
-    if (gs_status e = hip_check(gs::launch_duplicate(*cam, n, (uint32_t)total, (const float4*)xy_depth, s,
-                                                     in_tmp ? s.keys_tmp : keys,
-                                                     in_tmp ? s.vals_tmp : point_list, st),
-                                "duplicate launch"))
+        return fail(GS_ERR_CAPACITY, "%llu entries exceed the capacity %lld", (unsigned long long)total,
+                    (long long)capacity);
+    return GS_OK;
+}
+
+gs_status gs_bin_and_sort_async(const gs_camera* cam, int32_t n, const float* xy_depth,
+                                const uint32_t* tiles_touched, uint64_t* keys, uint32_t* point_list,
+                                int64_t capacity, void* scratch, size_t* scratch_bytes,
+                                uint64_t* n_entries_dev, void* stream) {
+    g_last_error.clear();
+    gs::BinScratch s{};
+    bool query = false;
+    if (gs_status e = bin_args("gs_bin_and_sort_async", cam, n, xy_depth, tiles_touched, keys, point_list,
+                               capacity, scratch, scratch_bytes, &query, &s))
         return e;
-    return hip_check(gs::launch_sort(keys, point_list, (uint32_t)total, tbits, n_tiles, s, st),
-                     "sort launch");
+    if (query) return GS_OK;
+    if (!n_entries_dev || ((uintptr_t)n_entries_dev & 7))
+        return fail(GS_ERR_INVALID, "gs_bin_and_sort_async: n_entries_dev must be an 8-byte aligned device pointer");
+    hipStream_t st = (hipStream_t)stream;
+    if (n == 0)
+        return hip_check(gs::launch_fill_u32((uint32_t*)n_entries_dev, 2, 0u, st), "entry count clear");
+    return hip_check(gs::launch_bin_and_sort(*cam, n, (const float4*)xy_depth, tiles_touched, keys, point_list,
+                                             (uint32_t)capacity, s, n_entries_dev, st),
+                     "bin_and_sort launch");
 }
 
 gs_status gs_tile_ranges(const gs_camera* cam, const uint64_t* keys, int64_t n_entries,
@@ -158,7 +187,22 @@ gs_status gs_tile_ranges(const gs_camera* cam, const uint64_t* keys, int64_t n_e
         return fail(GS_ERR_INVALID, "n_entries %lld outside [0, 2^32 - 1]", (long long)n_entries);
     if (!ranges || (n_entries > 0 && !keys)) return fail(GS_ERR_INVALID, "gs_tile_ranges: NULL pointer");
     const int n_tiles = gs::tiles_x(*cam) * gs::tiles_y(*cam);
-    return hip_check(gs::launch_tile_ranges(keys, (uint32_t)n_entries, n_tiles, ranges, (hipStream_t)stream),
+    return hip_check(gs::launch_tile_ranges(keys, (uint32_t)n_entries, nullptr, 0u, n_tiles, ranges,
+                                            (hipStream_t)stream),
+                     "tile ranges launch");
+}
+
+gs_status gs_tile_ranges_async(const gs_camera* cam, const uint64_t* keys, const uint64_t* n_entries_dev,
+                               int64_t capacity, uint32_t* ranges, void* stream) {
+    g_last_error.clear();
+    if (gs_status s = check_camera(cam)) return s;
+    if (capacity < 0 || capacity > (int64_t)UINT32_MAX)
+        return fail(GS_ERR_INVALID, "capacity %lld outside [0, 2^32 - 1]", (long long)capacity);
+    if (!ranges || !n_entries_dev || ((uintptr_t)n_entries_dev & 7) || (capacity > 0 && !keys))
+        return fail(GS_ERR_INVALID, "gs_tile_ranges_async: NULL or misaligned pointer");
+    const int n_tiles = gs::tiles_x(*cam) * gs::tiles_y(*cam);
+    return hip_check(gs::launch_tile_ranges(keys, 0u, n_entries_dev, (uint32_t)capacity, n_tiles, ranges,
+                                            (hipStream_t)stream),
                      "tile ranges launch");
 }
 

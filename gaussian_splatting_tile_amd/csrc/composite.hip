@@ -22,8 +22,10 @@
 //    (in double), so the skip decision is the exactly defined one.
 //  * Both kernels call the same alpha routine, so the backward re-derives
 //    exactly the alphas, skips and clamps the forward saw.
-//  * Workgroup ids are remapped so each XCD renders a contiguous band of
-//    tiles (neighbouring tiles share splats; L2 is per XCD).
+//  * Tiles are taken in workgroup-id order, which the dispatcher deals out
+//    round-robin over the 8 XCDs, so the dense middle rows of the image are
+//    spread over all of them (contiguous bands per XCD left some XCDs with
+//    most of the work).
 //  * Backward: per splat, each wave sums nine per-pixel terms over its 16-lane
 //    rows with DPP adds (skipped when no lane contributed) into LDS; the
 //    terms are the colour gradient, dL/do, and the moments of dL/dpower

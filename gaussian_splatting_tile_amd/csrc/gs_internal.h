@@ -22,6 +22,9 @@ constexpr float kAlphaMin = 1.0f / 255.0f;
 constexpr float kAlphaMax = 0.99f;
 constexpr float kTStop = 1e-4f;
 
+// Entry count reported when a radix pass gave up one of its bounded waits.
+constexpr uint64_t kCountFailed = ~0ull;
+
 inline int tiles_x(const gs_camera& c) { return (c.width + kTile - 1) / kTile; }
 inline int tiles_y(const gs_camera& c) { return (c.height + kTile - 1) / kTile; }
 
@@ -47,15 +50,6 @@ __device__ __forceinline__ Span tile_span(float u, float v, float r, int TX, int
     return Span{(int)x0, (int)x1, (int)y0, (int)y1};
 }
 
-// Workgroups are handed to the 8 XCDs round-robin by workgroup id. Remap
-// the id so each XCD walks one contiguous run of tiles: neighbouring tiles
-// share most of their splats, and each XCD has its own L2.
-__device__ __forceinline__ int xcd_contiguous(int bid, int nblocks) {
-    const int q = nblocks / 8, rem = nblocks % 8;
-    const int x = bid % 8, i = bid / 8;
-    return x * q + (x < rem ? x : rem) + i;
-}
-
 // ---- launchers (each returns the launch's hipError_t) ----
 
 hipError_t launch_preprocess(const gs_camera& cam, int n, const float* means, const float* scales,
@@ -64,41 +58,44 @@ hipError_t launch_preprocess(const gs_camera& cam, int n, const float* means, co
                              float4* conic_op, float4* rgb, uint32_t* tiles_touched,
                              hipStream_t stream);
 
-// Binning workspace, carved from the caller's scratch buffer.
+// Binning workspace, carved from the caller's scratch buffer. The first
+// kernel of every call clears the tickets and the error word, the counting
+// kernels clear the look-back words they will need; nothing else needs
+// initialisation.
 struct BinScratch {
+    uint32_t* tickets;        // [16] workgroup tickets of each pass
+    uint32_t* err;            // = tickets + 15, set if a look-back wait gave up
+    uint64_t* total;          // [1] entry count, right after err
+    uint32_t* gauss_hist;     // [4][256] digit totals of the depth passes
+    uint32_t* entry_hist;     // [3][256] digit totals of the tile-id passes
+    uint32_t* gauss_counts;   // [4][256][nb_gauss] per-tile digit counts
+    uint32_t* entry_counts;   // [3][256][nb_entry]
+    uint64_t* gauss_status;   // [3][nb_gauss][256] look-back words of passes 1..3
+    uint64_t* entry_status;   // [2][nb_entry][256]
     uint32_t* block_sums;     // [nb_scan]
     uint64_t* block_offsets;  // [nb_scan]
-    uint64_t* total;          // [1]
-    uint32_t* offsets;        // [n] first entry of each Gaussian
+    uint32_t* offsets;        // [n] first entry of the i-th splat in depth order
+    uint32_t* gk[2];          // [n] depth keys, ping-pong
+    uint32_t* gv[2];          // [n] splat ids, ping-pong; gv[0] ends as the depth order
     uint64_t* keys_tmp;       // [capacity]
     uint32_t* vals_tmp;       // [capacity]
-    uint32_t* counts;         // [256][nb_sort]
-    uint32_t* digit_totals;   // [256]
-    uint32_t* seg_ranges;     // [n_tiles][2] tile segments after the tile-id passes
-    uint32_t* seg_k0;         // [capacity] global ping-pong of the per-tile sort
-    uint32_t* seg_v0;
-    uint32_t* seg_k1;
-    uint32_t* seg_v1;
 };
-size_t bin_scratch_layout(int n, int64_t capacity, int n_tiles, BinScratch* out, void* base);
+size_t bin_scratch_layout(int n, int64_t capacity, BinScratch* out, void* base);
 
-// Exclusive scan of tiles_touched into s.offsets and s.total (entry count).
-hipError_t launch_scan(int n, const uint32_t* tiles_touched, const BinScratch& s, hipStream_t stream);
-// One (key, value) per entry, n_entries = *s.total, written to keys/values.
-hipError_t launch_duplicate(const gs_camera& cam, int n, uint32_t n_entries, const float4* xy_depth,
-                            const BinScratch& s, uint64_t* keys, uint32_t* values, hipStream_t stream);
+// The whole binning: stable depth order of the splats, scan of their tile
+// counts in that order (E -> *s.total, and *n_dev if given), duplication,
+// stable sort on the tile-id bits into (keys, values). Never waits on the
+// host. When E > capacity nothing is written to keys/values.
+hipError_t launch_bin_and_sort(const gs_camera& cam, int n, const float4* xy_depth,
+                               const uint32_t* tiles_touched, uint64_t* keys, uint32_t* values,
+                               uint32_t capacity, const BinScratch& s, uint64_t* n_dev, hipStream_t stream);
 
-// Sort n entries by the whole key (tile id << 32 | depth bits), stably.
-// The duplication must have written the entries into the tmp pair when
-// dup_writes_tmp(tile_bits), into (keys, values) otherwise; the result is in
-// (keys, values).
-int tile_pass_count(int tile_bits);
-bool dup_writes_tmp(int tile_bits);
-hipError_t launch_sort(uint64_t* keys, uint32_t* values, uint32_t n, int tile_bits, int n_tiles,
-                       const BinScratch& s, hipStream_t stream);
+hipError_t launch_fill_u32(uint32_t* p, size_t words, uint32_t v, hipStream_t stream);
 
-hipError_t launch_tile_ranges(const uint64_t* keys, uint32_t n_entries, int n_tiles,
-                              uint32_t* ranges, hipStream_t stream);
+// Per-tile ranges. The entry count is n_entries, or, when n_dev is given,
+// *n_dev if it does not exceed capacity and 0 otherwise.
+hipError_t launch_tile_ranges(const uint64_t* keys, uint32_t n_entries, const uint64_t* n_dev, uint32_t capacity,
+                              int n_tiles, uint32_t* ranges, hipStream_t stream);
 
 hipError_t launch_composite_fwd(const gs_camera& cam, const uint32_t* ranges,
                                 const uint32_t* point_list, const float4* xy_depth,

@@ -90,14 +90,16 @@ def preprocess(cam, means, scales, quats, opacity, sh=None, sh_degree=0, rgb_in=
 
 
 class BinBuffers:
-    """Entry buffers (keys, point_list, scratch) reused across frames; grown
-    on demand when a frame needs more entries than the capacity."""
+    """Entry buffers (keys, point_list, scratch, the device entry count)
+    reused across frames; grown on demand when a frame needs more entries
+    than the capacity."""
 
     def __init__(self, device, capacity: int = 1 << 20):
         self.device = device
         self.capacity = 0
         self.keys = self.point_list = self.scratch = None
-        self.n_scratch = -1
+        self.n_entries_dev = torch.zeros((1,), dtype=torch.int64, device=device)
+        self._need = {}
         self._ensure(int(capacity))
 
     def _ensure(self, capacity: int):
@@ -106,15 +108,27 @@ class BinBuffers:
             self.keys = torch.empty((capacity,), dtype=torch.int64, device=self.device)
             self.point_list = torch.empty((capacity,), dtype=torch.int32, device=self.device)
             self.scratch = None
+            self._need = {}
 
     def scratch_for(self, c, n: int):
-        need = ctypes.c_size_t(0)
-        _lib.check(_lib.load().gs_bin_and_sort(ctypes.byref(c), n, None, None, None, None,
-                                               self.capacity, None, ctypes.byref(need), None, None))
-        if self.scratch is None or self.scratch.numel() < need.value:
-            self.scratch = torch.empty((max(int(need.value), 256),), dtype=torch.uint8,
-                                       device=self.device)
+        need = self._need.get(n)
+        if need is None:
+            q = ctypes.c_size_t(0)
+            _lib.check(_lib.load().gs_bin_and_sort(ctypes.byref(c), n, None, None, None, None,
+                                                   self.capacity, None, ctypes.byref(q), None, None))
+            need = self._need[n] = int(q.value)
+        if self.scratch is None or self.scratch.numel() < need:
+            self.scratch = torch.empty((max(need, 256),), dtype=torch.uint8, device=self.device)
         return self.scratch
+
+    def entries(self) -> int:
+        """E of the last asynchronous binning (waits for the stream). Raises
+        GsError if a bounded wait gave up; E > capacity means the frame
+        rendered nothing and must be redone after _ensure(E)."""
+        e = int(self.n_entries_dev.item()) & ((1 << 64) - 1)
+        if e == _lib.ENTRIES_FAILED:
+            raise _lib.GsError(_lib.GS_ERR_HIP, "a radix pass's bounded wait gave up")
+        return e
 
 
 def bin_and_sort(cam, xy_depth, tiles_touched, buffers: BinBuffers | None = None, stream=None):
@@ -143,6 +157,31 @@ def bin_and_sort(cam, xy_depth, tiles_touched, buffers: BinBuffers | None = None
         E = int(n_entries.value)
         return buffers.keys[:E], buffers.point_list[:E], E
     raise AssertionError("unreachable")
+
+
+def bin_and_sort_async(cam, xy_depth, tiles_touched, buffers: BinBuffers, stream=None):
+    """gs_bin_and_sort_async: never waits. Returns (keys int64 [capacity], point_list int32
+    [capacity]); E lands in buffers.n_entries_dev (read it with buffers.entries())."""
+    c = _cam(cam)
+    n = int(tiles_touched.shape[0])
+    scratch = buffers.scratch_for(c, n)
+    nbytes = ctypes.c_size_t(scratch.numel())
+    _lib.check(_lib.load().gs_bin_and_sort_async(
+        ctypes.byref(c), n, _ptr(xy_depth, torch.float32, "xy_depth"),
+        _ptr(tiles_touched, torch.int32, "tiles_touched"), _ptr(buffers.keys), _ptr(buffers.point_list),
+        buffers.capacity, _ptr(scratch), ctypes.byref(nbytes), _ptr(buffers.n_entries_dev), _stream(stream)))
+    return buffers.keys, buffers.point_list
+
+
+def tile_ranges_async(cam, buffers: BinBuffers, out=None, stream=None):
+    """gs_tile_ranges_async over the last asynchronous binning into buffers."""
+    c = _cam(cam)
+    if out is None:
+        TX, TY = tiles_xy(dict(width=c.width, height=c.height))
+        out = torch.empty((TX * TY, 2), dtype=torch.int32, device=buffers.keys.device)
+    _lib.check(_lib.load().gs_tile_ranges_async(ctypes.byref(c), _ptr(buffers.keys), _ptr(buffers.n_entries_dev),
+                                                buffers.capacity, _ptr(out, torch.int32), _stream(stream)))
+    return out
 
 
 def tile_ranges(cam, keys, n_entries: int, out=None, stream=None):

@@ -21,6 +21,8 @@
  *  - Streams: `stream` is a hipStream_t passed as void* (NULL = the null
  *    stream). Work is enqueued asynchronously; the only call that blocks the
  *    host is gs_bin_and_sort, which waits once to read the entry count.
+ *    gs_bin_and_sort_async and gs_tile_ranges_async keep that count in
+ *    device memory instead, so a whole frame is enqueued without a wait.
  *  - Errors: every call returns a gs_status. Arguments are validated on the
  *    host before anything is launched; on GS_ERR_INVALID nothing was
  *    enqueued. gs_last_error() gives a message for the calling thread. HIP
@@ -130,10 +132,13 @@ gs_status gs_preprocess(const gs_camera* cam, int32_t n, const float* means, con
  * entry per tile of its span, ty outer and tx inner, with
  *     key   = (uint64)(ty * TX + tx) << 32 | float_bits(z_g)
  *     value = g.
- * The entries are then sorted by key with a stable LSD radix sort over the
- * key bits a tile id can occupy (32 + ceil(log2(TX*TY))), so equal keys keep
- * Gaussian-index order. The entry count E is copied to the host: this is
- * the call's one host synchronisation.
+ * The result is the entries in the order of one stable sort by key, so
+ * equal keys keep Gaussian-index order: (tile, depth bits, g). It is
+ * reached by a stable radix sort of the Gaussians by depth bits, emission
+ * in that order, and a stable radix sort of the entries on the
+ * ceil(log2(TX*TY)) tile-id bits. Everything is enqueued first; then the
+ * entry count E is copied to the host: this is the call's one host
+ * synchronisation.
  *
  *   cam, n         as gs_preprocess; n <= GS_MAX_GAUSSIANS
  *   xy_depth       [n][4] from gs_preprocess
@@ -144,15 +149,40 @@ gs_status gs_preprocess(const gs_camera* cam, int32_t n, const float* means, con
  *   scratch        device workspace of *scratch_bytes bytes (256-byte
  *                  aligned), or NULL to query the size
  *   scratch_bytes  (host) in: size of scratch; out: required size, which
- *                  depends on n, capacity and the camera's tile count
+ *                  depends on n and capacity
  *   n_entries      (host) out: E
- * Returns GS_ERR_CAPACITY (with *n_entries = E, keys/point_list
- * unspecified) when E > capacity, GS_ERR_OVERFLOW when E >= 2^32.
+ * Returns GS_ERR_CAPACITY (with *n_entries = E; keys/point_list are then
+ * not written) when E > capacity, GS_ERR_OVERFLOW when E >= 2^32, and
+ * GS_ERR_HIP if a radix pass's bounded wait for an earlier workgroup ever
+ * gave up (never expected; the outputs are then unspecified). Calls that
+ * share one scratch buffer must not overlap.
  * ------------------------------------------------------------------- */
 gs_status gs_bin_and_sort(const gs_camera* cam, int32_t n, const float* xy_depth,
                           const uint32_t* tiles_touched, uint64_t* keys, uint32_t* point_list,
                           int64_t capacity, void* scratch, size_t* scratch_bytes,
                           int64_t* n_entries, void* stream);
+
+/* Entry count stored by the asynchronous entry points when a radix pass
+ * gave up one of its bounded waits (never expected). */
+#define GS_ENTRIES_FAILED UINT64_MAX
+
+/* ---------------------------------------------------------------------
+ * gs_bin_and_sort_async - gs_bin_and_sort without the host wait.
+ *
+ * Same work, order and arguments as gs_bin_and_sort, except that E is
+ * written to device memory and the host never waits:
+ *   n_entries_dev  out, device uint64 (8-byte aligned): E, written on the
+ *                  stream; GS_ENTRIES_FAILED if a bounded wait gave up.
+ * When E > capacity (or on failure) keys and point_list are not written;
+ * gs_tile_ranges_async then marks every tile empty, so the frame renders the
+ * background and the caller, once it reads E, grows the buffers and renders
+ * the frame again. Host-side argument errors are returned as usual; calls
+ * that share one scratch buffer must not overlap.
+ * ------------------------------------------------------------------- */
+gs_status gs_bin_and_sort_async(const gs_camera* cam, int32_t n, const float* xy_depth,
+                                const uint32_t* tiles_touched, uint64_t* keys, uint32_t* point_list,
+                                int64_t capacity, void* scratch, size_t* scratch_bytes,
+                                uint64_t* n_entries_dev, void* stream);
 
 /* ---------------------------------------------------------------------
  * gs_tile_ranges - per-tile [start, end) of the sorted entries.
@@ -164,6 +194,18 @@ gs_status gs_bin_and_sort(const gs_camera* cam, int32_t n, const float* xy_depth
  * ------------------------------------------------------------------- */
 gs_status gs_tile_ranges(const gs_camera* cam, const uint64_t* keys, int64_t n_entries,
                          uint32_t* ranges, void* stream);
+
+/* ---------------------------------------------------------------------
+ * gs_tile_ranges_async - gs_tile_ranges with the entry count in device
+ * memory, as written by gs_bin_and_sort_async.
+ *
+ *   keys           [capacity] sorted keys
+ *   n_entries_dev  device uint64 (8-byte aligned): E
+ *   capacity       the capacity given to gs_bin_and_sort_async
+ *   ranges         out [TX*TY][2] uint32; every tile (0, 0) when E > capacity
+ * ------------------------------------------------------------------- */
+gs_status gs_tile_ranges_async(const gs_camera* cam, const uint64_t* keys, const uint64_t* n_entries_dev,
+                               int64_t capacity, uint32_t* ranges, void* stream);
 
 /* ---------------------------------------------------------------------
  * gs_composite_fwd - front-to-back alpha compositing per tile.

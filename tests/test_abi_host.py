@@ -122,3 +122,25 @@ def test_binding_refuses_host_tensors(gs):
     x = torch.zeros((3, 4))
     with pytest.raises(TypeError):
         pkg.preprocess(cam, x, x, torch.zeros((4, 4)), torch.zeros(4), rgb_in=x)
+
+
+def test_async_entry_points_validate(gs):
+    from gaussian_splatting_tile_amd import _lib
+    P = ctypes.c_void_p
+    c = _cam()
+    need = ctypes.c_size_t(0)
+    # the size query agrees with the blocking variant
+    assert gs.gs_bin_and_sort_async(ctypes.byref(c), 1000, None, None, None, None, 5000, None,
+                                    ctypes.byref(need), None, None) == _lib.GS_OK
+    q = ctypes.c_size_t(0)
+    assert gs.gs_bin_and_sort(ctypes.byref(c), 1000, None, None, None, None, 5000, None,
+                              ctypes.byref(q), None, None) == _lib.GS_OK
+    assert need.value == q.value
+    # a missing or misaligned device count is rejected before launch
+    nb = ctypes.c_size_t(need.value)
+    for bad in (None, P(260)):
+        assert gs.gs_bin_and_sort_async(ctypes.byref(c), 1000, P(256), P(256), P(256), P(256), 5000,
+                                        P(256), ctypes.byref(nb), bad, None) == _lib.GS_ERR_INVALID
+    assert gs.gs_tile_ranges_async(ctypes.byref(c), P(256), None, 10, P(256), None) == _lib.GS_ERR_INVALID
+    assert gs.gs_tile_ranges_async(ctypes.byref(c), P(256), P(260), 10, P(256), None) == _lib.GS_ERR_INVALID
+    assert gs.gs_tile_ranges_async(ctypes.byref(c), P(256), P(256), -1, P(256), None) == _lib.GS_ERR_INVALID

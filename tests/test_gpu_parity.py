@@ -190,3 +190,68 @@ def test_repeat_runs_are_bit_identical(orc):
     for k in ("xy_depth", "conic_op", "rgb", "tiles_touched", "keys", "point_list", "ranges",
               "image", "final_T", "n_contrib", "n_examined"):
         assert_bits_equal(a[k], b[k], k)
+
+
+def _async_forward(cam, scene, capacity, bg=(0.0, 0.0, 0.0)):
+    """Preprocess, asynchronous binning and ranges, forward compositing: no
+    host wait until the results are read."""
+    import gaussian_splatting_tile_amd as gs
+    import torch
+    from gpu_helpers import to_np
+    sc = gs.Scene.from_numpy(scene)
+    c = gs.camera(cam)
+    bins = gs.BinBuffers(torch.device("cuda"), capacity=capacity)
+    pre = gs.preprocess(c, sc.means, sc.scales, sc.quats, sc.opacity, sc.sh, sc.sh_degree, sc.rgb)
+    keys, pl = gs.bin_and_sort_async(c, pre["xy_depth"], pre["tiles_touched"], bins)
+    ranges = gs.tile_ranges_async(c, bins)
+    fwd = gs.composite_fwd(c, ranges, pl, pre["xy_depth"], pre["conic_op"], pre["rgb"], bg)
+    E = bins.entries()
+    res = {k: to_np(v) for k, v in fwd.items()}
+    res.update(n_entries=E, ranges=to_np(ranges).view(np.uint32),
+               keys=to_np(keys).view(np.uint64), point_list=to_np(pl).view(np.uint32))
+    return res
+
+
+@pytest.mark.parametrize("W,H,n,seed", [(257, 129, 2000, 11), (720, 720, 20000, 12)])
+def test_async_binning_matches_oracle(orc, W, H, n, seed):
+    say(f"[async {W}x{H} n={n}]")
+    cam, scene = _random_case(orc, W, H, n, seed=seed, sh_degree=1, spread=1.4)
+    ofwd = oracle_forward(orc, cam, scene)
+    E = int(ofwd["keys"].shape[0])
+    res = _async_forward(cam, scene, capacity=E + 4097)
+    assert res["n_entries"] == E
+    assert_bits_equal(res["keys"][:E], ofwd["keys"], "keys")
+    assert_bits_equal(res["point_list"][:E], ofwd["point_list"], "point_list")
+    assert_bits_equal(res["ranges"], ofwd["ranges"], "ranges")
+    assert (res["n_contrib"] == ofwd["n_contrib"]).mean() >= 0.999
+    np.testing.assert_allclose(res["image"], ofwd["image"], atol=1e-4, rtol=0)
+
+
+def test_async_overflow_renders_background(orc):
+    """E > capacity: nothing is binned, every tile is empty, the image is the
+    background and E is still reported."""
+    cam, scene = _random_case(orc, 257, 129, 2000, seed=11, sh_degree=1, spread=1.4)
+    ofwd = oracle_forward(orc, cam, scene)
+    E = int(ofwd["keys"].shape[0])
+    bg = (0.25, 0.5, 0.75)
+    res = _async_forward(cam, scene, capacity=E // 2, bg=bg)
+    assert res["n_entries"] == E
+    assert not res["ranges"].any()
+    assert (res["final_T"] == 1).all() and not res["n_contrib"].any()
+    for ch in range(3):
+        assert (res["image"][ch] == np.float32(bg[ch])).all()
+
+
+def test_async_empty_scene():
+    import gaussian_splatting_tile_amd as gs
+    import torch
+    cam = synth.look_at_camera((0, 0, -4), (0, 0, 0), 40, 24, 40.0, 40.0)
+    c = gs.camera(cam)
+    bins = gs.BinBuffers(torch.device("cuda"), capacity=1024)
+    bins.n_entries_dev.fill_(12345)
+    z = torch.zeros((0, 4), dtype=torch.float32, device="cuda")
+    t = torch.zeros((0,), dtype=torch.int32, device="cuda")
+    gs.bin_and_sort_async(c, z, t, bins)
+    ranges = gs.tile_ranges_async(c, bins)
+    assert bins.entries() == 0
+    assert not ranges.any()
