@@ -15,8 +15,6 @@ STATUS_NAMES = {0: "GS_OK", 1: "GS_ERR_INVALID", 2: "GS_ERR_CAPACITY", 3: "GS_ER
 EXPORTS = ("gs_constants", "gs_last_error", "gs_version", "gs_preprocess", "gs_bin_and_sort",
            "gs_bin_and_sort_async", "gs_tile_ranges", "gs_tile_ranges_async", "gs_composite_fwd",
            "gs_composite_bwd")
-# entry count stored by the asynchronous binning when a bounded wait gave up
-ENTRIES_FAILED = (1 << 64) - 1
 
 
 class GsCamera(ctypes.Structure):

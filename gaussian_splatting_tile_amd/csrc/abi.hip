@@ -141,14 +141,12 @@ gs_status gs_bin_and_sort(const gs_camera* cam, int32_t n, const float* xy_depth
                                                         point_list, (uint32_t)capacity, s, nullptr, st),
                                 "bin_and_sort launch"))
         return e;
-    // the error word and the entry count, in one copy, once everything is enqueued
-    uint32_t flags[3] = {0, 0, 0};
-    if (gs_status e = hip_check(hipMemcpyAsync(flags, s.err, sizeof(flags), hipMemcpyDeviceToHost, st),
+    // the entry count, once everything is enqueued
+    uint64_t total = 0;
+    if (gs_status e = hip_check(hipMemcpyAsync(&total, s.total, sizeof(total), hipMemcpyDeviceToHost, st),
                                 "entry count copy"))
         return e;
     if (gs_status e = hip_check(hipStreamSynchronize(st), "entry count sync")) return e;
-    if (flags[0] != 0) return fail(GS_ERR_HIP, "gs_bin_and_sort: a radix pass's bounded wait gave up");
-    const uint64_t total = (uint64_t)flags[1] | ((uint64_t)flags[2] << 32);
     *n_entries = (int64_t)total;
     if (total > (uint64_t)UINT32_MAX)
         return fail(GS_ERR_OVERFLOW, "%llu entries do not fit in 32 bits", (unsigned long long)total);

@@ -22,14 +22,17 @@
 //      1080p) then gives (tile, depth bits, index).
 //
 // MI355X design:
-//  * Each radix pass is one kernel, a chained scan with decoupled look-back:
-//    a workgroup takes a ticket from an atomic counter (so it only ever
-//    waits for workgroups that started before it and are running), ranks
-//    its 2048 keys, publishes its per-digit counts, looks back over
-//    predecessors' published counts for its exclusive prefix and scatters.
-//    Digit totals for every pass come from one histogram sweep. Every wait
-//    is bounded: past the limit the workgroup records an error and stops
-//    waiting, so no launch can hang.
+//  * Each radix pass is reduce-then-scan with no waits between workgroups:
+//    per-tile digit counts (LDS histograms, one column per tile), a small
+//    kernel that turns them into per-tile exclusive prefixes and digit
+//    totals (one wave per digit), and the pass itself, which ranks and
+//    scatters its tile independently. The first pass's counts come from the
+//    kernel that produces the keys; later passes count their input in a
+//    kernel of their own. Two alternatives were measured and dropped: a
+//    chained scan with decoupled look-back (its coherent polling across the
+//    eight L2s cost more than the passes) and counting the next pass's
+//    digits with global atomics while scattering (digits with few distinct
+//    values serialise on a handful of counters).
 //  * The in-workgroup rank uses 64-lane ballots: eight ballots, one per
 //    digit bit, give each lane the mask of lanes holding its digit (there is
 //    no match instruction on this architecture); popcount below the lane is
@@ -48,6 +51,10 @@
 namespace gs {
 namespace {
 
+constexpr int kDupThreads = 256;
+constexpr int kDupItems = 8;
+constexpr int kDupTile = kDupThreads * kDupItems;  // entries per duplication workgroup
+
 constexpr int kScanThreads = 256;
 constexpr int kScanItems = 8;
 constexpr int kScanTile = kScanThreads * kScanItems;  // splats per workgroup
@@ -61,13 +68,6 @@ constexpr int kGaussTile = kSortThreads * kGaussItems;  // splats per workgroup
 constexpr int kRadix = 256;
 constexpr int kGaussPasses = 4;                         // 32 depth bits
 constexpr int kMaxTilePasses = 3;                       // up to 24 tile-id bits
-constexpr int kTickets = 16;                            // tickets of every pass, error word last
-constexpr int kLookBack = 8;                            // predecessors read per round trip
-
-// look-back status words: (flag << 32) | count
-constexpr uint64_t kFlagAggregate = 1ull << 32;
-constexpr uint64_t kFlagPrefix = 2ull << 32;
-constexpr int kSpinLimit = 1 << 20;
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -152,13 +152,10 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_reduce(const uint32_t* __
 }
 
 // One workgroup of 1024 threads scans up to 8192 block sums (n <= 2^24).
-// The entry count goes to *total (and *n_dev if given); if an earlier
-// radix pass gave up a wait (*err), the count is replaced by kCountFailed so
-// that every later stage treats the frame as overflowed and writes nothing.
+// The entry count goes to *total (and *n_dev if given).
 __global__ __launch_bounds__(1024) void k_scan_block_sums(const uint32_t* __restrict__ block_sums,
                                                           int nb, uint64_t* __restrict__ block_offsets,
                                                           uint64_t* __restrict__ total,
-                                                          const uint32_t* __restrict__ err,
                                                           uint64_t* __restrict__ n_dev) {
     __shared__ uint64_t s[1024];
     constexpr int kPer = 8;
@@ -189,17 +186,20 @@ __global__ __launch_bounds__(1024) void k_scan_block_sums(const uint32_t* __rest
         run += local[i];
     }
     if (tid == 1023) {
-        const uint64_t t = *err ? kCountFailed : sum;
-        *total = t;
-        if (n_dev) *n_dev = t;
+        *total = sum;
+        if (n_dev) *n_dev = sum;
     }
 }
 
-// offsets[i]: first entry of the i-th splat of the depth order.
+// offsets[i]: first entry of the i-th splat of the depth order. Also
+// first_owner[B] = the i owning entry B * 2048 (the first entry of
+// duplication workgroup B), for B < n_dup_blocks.
 __global__ __launch_bounds__(kScanThreads) void k_scan_offsets(const uint32_t* __restrict__ counts,
                                                                const uint32_t* __restrict__ perm, int n,
                                                                const uint64_t* __restrict__ block_offsets,
-                                                               uint32_t* __restrict__ offsets) {
+                                                               uint32_t* __restrict__ offsets,
+                                                               uint32_t* __restrict__ first_owner,
+                                                               uint32_t n_dup_blocks) {
     __shared__ uint32_t s_c[kScanTile];
     __shared__ uint32_t s_tmp[kScanThreads];
     const int tid = threadIdx.x;
@@ -223,6 +223,13 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_offsets(const uint32_t* _
 #pragma unroll
     for (int i = 0; i < kScanItems; ++i) {
         s_c[tid * kScanItems + i] = run;
+        // duplication workgroups whose first entry this splat owns
+        if (c[i] != 0u) {
+            const uint64_t b0 = ((uint64_t)run + kDupTile - 1) / kDupTile;
+            const uint64_t b1 = ((uint64_t)run + c[i] - 1) / kDupTile;
+            for (uint64_t B = b0; B <= b1 && B < n_dup_blocks; ++B)
+                first_owner[B] = (uint32_t)(base + tid * kScanItems + i);
+        }
         run += c[i];
     }
     __syncthreads();
@@ -242,84 +249,81 @@ __device__ __forceinline__ uint32_t usable_entries(const uint64_t* __restrict__ 
     return e <= (uint64_t)capacity ? (uint32_t)e : 0u;
 }
 
-// Last index i in [lo, hi] with offsets[i] <= e (offsets is nondecreasing;
-// the answer owns entry e and never has a zero count).
-__device__ __forceinline__ int owner_search(const uint32_t* __restrict__ offsets, int lo, int hi, uint32_t e) {
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (offsets[mid] <= e) lo = mid; else hi = mid - 1;
-    }
-    return lo;
-}
-
-constexpr int kDupThreads = 256;
-constexpr int kDupItems = 8;
-constexpr int kDupTile = kDupThreads * kDupItems;
-constexpr int kDupWindow = 2048;  // staged offsets; longer owner ranges search global memory
 static_assert(kDupTile == kEntryTile, "a duplication workgroup fills exactly one sort tile");
 
-// Per-workgroup digit counts, written as counts[(p * 256 + d) * nblk + b],
-// and clearing of the look-back words of passes 1.. for this tile. `s_hist`
-// is [passes][256], filled by the caller.
-__device__ __forceinline__ void emit_counts(const uint32_t (*s_hist)[kRadix], int passes, int nblk,
-                                            uint32_t* __restrict__ counts, uint64_t* __restrict__ status) {
-    const int tid = threadIdx.x, b = blockIdx.x;
-    for (int p = 0; p < passes; ++p) {
-        counts[((size_t)p * kRadix + tid) * nblk + b] = s_hist[p][tid];
-        if (p > 0) status[((size_t)(p - 1) * nblk + b) * kRadix + tid] = 0ull;
-    }
+// This workgroup's column b of one pass's per-tile digit counts,
+// counts[d * nblk + b], from the LDS histogram `s_hist`.
+__device__ __forceinline__ void emit_counts(const uint32_t* s_hist, int nblk, uint32_t* __restrict__ counts) {
+    counts[(size_t)threadIdx.x * nblk + blockIdx.x] = s_hist[threadIdx.x];
 }
 
 // Entry e of the i-th splat g = perm[i] (its k-th tile, k = e - offsets[i])
 // is the tile (x0 + k % w, y0 + k / w) of g's span. Each workgroup covers
-// 2048 consecutive entries (one tile of the later sort); it finds the range
-// of splats owning them, stages their offsets in LDS and searches there. It
-// also counts the tile-id digits of its entries for every radix pass.
+// 2048 consecutive entries (one tile of the later sort). Owners without a
+// search: first_owner gives the owner i_lo of the first entry; every later
+// splat whose entries start inside the tile marks its first slot (LDS max,
+// so of several splats starting at one slot, the last, which is the one
+// with entries, wins), and an inclusive max-scan over the 2048 slots gives
+// every entry its owner. The workgroup also counts the first tile pass's
+// digits of its entries.
 __global__ __launch_bounds__(kDupThreads) void k_duplicate(
     const float4* __restrict__ xy_depth, const uint32_t* __restrict__ offsets,
-    const uint32_t* __restrict__ perm, int n, const uint64_t* __restrict__ total, uint32_t capacity, int TX,
-    int TY, int passes, uint64_t* __restrict__ keys, uint32_t* __restrict__ values,
-    uint32_t* __restrict__ counts, uint64_t* __restrict__ status) {
-    __shared__ uint32_t s_off[kDupWindow];
-    __shared__ uint32_t s_hist[kMaxTilePasses][kRadix];
-    __shared__ int s_range[2];
-    const int tid = threadIdx.x, lane = tid & 63;
+    const uint32_t* __restrict__ perm, const uint32_t* __restrict__ first_owner, int n,
+    const uint64_t* __restrict__ total, uint32_t capacity, int TX, int TY, int passes,
+    uint64_t* __restrict__ keys, uint32_t* __restrict__ values, uint32_t* __restrict__ counts) {
+    constexpr int kPer = kDupTile / kDupThreads;  // slots per thread in the scan
+    __shared__ uint32_t s_owner[kDupTile];
+    __shared__ uint32_t s_hist[kRadix];
+    __shared__ uint32_t s_wmax[kDupThreads / 64];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const uint32_t n_entries = usable_entries(total, capacity);
     const uint32_t e0 = blockIdx.x * kDupTile;
     if (e0 >= n_entries) return;  // the grid is sized for the capacity
     const uint32_t e1 = min(e0 + (uint32_t)kDupTile, n_entries);
+    const int i_lo = (int)first_owner[blockIdx.x];
+    s_hist[tid] = 0;
 #pragma unroll
-    for (int p = 0; p < kMaxTilePasses; ++p) s_hist[p][tid] = 0;
-    if (tid < 2) s_range[tid] = owner_search(offsets, 0, n - 1, tid == 0 ? e0 : e1 - 1);
+    for (int j = 0; j < kPer; ++j) s_owner[j * kDupThreads + tid] = 0u;
     __syncthreads();
-    const int i_lo = s_range[0], i_hi = s_range[1];
-    const int span = i_hi - i_lo + 1;
-    const bool staged = span <= kDupWindow;
-    if (staged)
-        for (int i = tid; i < span; i += kDupThreads) s_off[i] = offsets[i_lo + i];
+    // splats after i_lo start strictly inside the tile until the first one at or past e1
+    for (int i = i_lo + 1 + tid; i < n; i += kDupThreads) {
+        const uint32_t off = offsets[i];
+        if (off >= e1) break;
+        atomicMax(&s_owner[off - e0], (uint32_t)(i - i_lo));
+    }
+    __syncthreads();
+    // inclusive max-scan of s_owner: thread t holds slots [kPer t, kPer t + kPer)
+    uint32_t v[kPer];
+    uint32_t run = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        run = max(run, s_owner[tid * kPer + j]);
+        v[j] = run;
+    }
+    uint32_t incl = run;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = (uint32_t)__shfl_up((int)incl, off, 64);
+        if (lane >= off) incl = max(incl, y);
+    }
+    if (lane == 63) s_wmax[wave] = incl;
+    uint32_t excl = (uint32_t)__shfl_up((int)incl, 1, 64);
+    if (lane == 0) excl = 0;
+    __syncthreads();
+    for (int w = 0; w < wave; ++w) excl = max(excl, s_wmax[w]);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) s_owner[tid * kPer + j] = max(v[j], excl);
     __syncthreads();
 #pragma unroll 2
     for (int it = 0; it < kDupItems; ++it) {
-        const uint32_t e = e0 + it * kDupThreads + tid;
+        const uint32_t slot = it * kDupThreads + tid;
+        const uint32_t e = e0 + slot;
         const bool valid = e < e1;
         uint32_t t = 0;
         if (valid) {
-            int i;
-            uint32_t off;
-            if (staged) {
-                int lo = 0, hi = span - 1;
-                while (lo < hi) {
-                    const int mid = (lo + hi + 1) >> 1;
-                    if (s_off[mid] <= e) lo = mid; else hi = mid - 1;
-                }
-                i = i_lo + lo;
-                off = s_off[lo];
-            } else {
-                i = owner_search(offsets, i_lo, i_hi, e);
-                off = offsets[i];
-            }
+            const int i = i_lo + (int)s_owner[slot];
             const uint32_t g = perm[i];
-            const uint32_t k = e - off;
+            const uint32_t k = e - offsets[i];
             const float4 rec = xy_depth[g];
             const Span sp = tile_span(rec.x, rec.y, rec.w, TX, TY);
             const uint32_t w = (uint32_t)(sp.x1 - sp.x0);
@@ -334,34 +338,29 @@ __global__ __launch_bounds__(kDupThreads) void k_duplicate(
             keys[e] = ((uint64_t)t << 32) | (uint64_t)__float_as_uint(rec.z);
             values[e] = g;
         }
-        for (int p = 0; p < passes; ++p) {
-            const uint32_t d = (t >> (8 * p)) & (kRadix - 1);
+        if (passes > 0) {  // the first tile pass's digit: the low byte of the tile id
+            const uint32_t d = t & (kRadix - 1);
             const uint64_t peers = match_digit(d, valid);
             if (valid && lane == __ffsll((unsigned long long)peers) - 1)
-                atomicAdd(&s_hist[p][d], (uint32_t)__popcll(peers));
+                atomicAdd(&s_hist[d], (uint32_t)__popcll(peers));
         }
     }
     __syncthreads();
-    emit_counts(s_hist, passes, (int)gridDim.x, counts, status);
+    if (passes > 0) emit_counts(s_hist, (int)gridDim.x, counts);
 }
 
 // ---- radix sort ----
 
 // Depth keys of the splats (culled ones last), the identity permutation and
-// the per-tile digit counts of all four depth passes. Workgroup 0 also
-// clears the tickets and the error word of every pass of this call.
+// the per-tile counts of the first depth pass's digit.
 __global__ __launch_bounds__(kSortThreads) void k_depth_keys(const float4* __restrict__ xy_depth,
                                                              const uint32_t* __restrict__ tiles_touched,
                                                              int n, uint32_t* __restrict__ keys,
                                                              uint32_t* __restrict__ vals,
-                                                             uint32_t* __restrict__ counts,
-                                                             uint64_t* __restrict__ status,
-                                                             uint32_t* __restrict__ tickets) {
-    __shared__ uint32_t s_hist[kGaussPasses][kRadix];
+                                                             uint32_t* __restrict__ counts) {
+    __shared__ uint32_t s_hist[kRadix];
     const int tid = threadIdx.x, lane = tid & 63;
-    if (blockIdx.x == 0 && tid < kTickets) tickets[tid] = 0u;
-#pragma unroll
-    for (int p = 0; p < kGaussPasses; ++p) s_hist[p][tid] = 0;
+    s_hist[tid] = 0;
     __syncthreads();
     const int base = blockIdx.x * kGaussTile;
 #pragma unroll
@@ -374,28 +373,59 @@ __global__ __launch_bounds__(kSortThreads) void k_depth_keys(const float4* __res
             keys[g] = key;
             vals[g] = (uint32_t)g;
         }
-#pragma unroll
-        for (int p = 0; p < kGaussPasses; ++p) {
-            const uint32_t d = digit_of(key, 8 * p);
-            const uint64_t peers = match_digit(d, valid);
-            if (valid && lane == __ffsll((unsigned long long)peers) - 1)
-                atomicAdd(&s_hist[p][d], (uint32_t)__popcll(peers));
-        }
+        const uint32_t d = digit_of(key, 0);
+        const uint64_t peers = match_digit(d, valid);
+        if (valid && lane == __ffsll((unsigned long long)peers) - 1)
+            atomicAdd(&s_hist[d], (uint32_t)__popcll(peers));
     }
     __syncthreads();
-    emit_counts(s_hist, kGaussPasses, (int)gridDim.x, counts, status);
+    emit_counts(s_hist, (int)gridDim.x, counts);
 }
 
-// Rows r = p * 256 + d of counts (one per pass and digit, row stride
-// `stride`): hist[r] = the total of the row's first nblk tiles; rows of pass
-// 0 are replaced in place by their exclusive prefix over tiles. nblk covers
-// the usable entries (*total, capacity) when total is given. One wave per row.
+// Per-tile counts of digit (key >> shift) of the keys about to be sorted by
+// a later pass: one tile of 256 * ITEMS keys per workgroup, as in the pass.
+// The key count is n, or the usable entries (*total, capacity).
+template <typename K, int ITEMS>
+__global__ __launch_bounds__(kSortThreads) void k_count_digits(const K* __restrict__ keys, uint32_t n,
+                                                               const uint64_t* __restrict__ total,
+                                                               uint32_t capacity, int shift,
+                                                               uint32_t* __restrict__ counts) {
+    constexpr int kTileKeys = kSortThreads * ITEMS;
+    __shared__ uint32_t s_hist[kRadix];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (total) n = usable_entries(total, capacity);
+    const uint32_t base = blockIdx.x * kTileKeys;
+    if (base >= n) return;  // whole workgroup
+    s_hist[tid] = 0;
+    __syncthreads();
+    const uint32_t seg = base + wave * (64 * ITEMS);
+    K key[ITEMS];
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i) {
+        const uint32_t pos = seg + i * 64 + lane;
+        key[i] = pos < n ? keys[pos] : K(0);
+    }
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i) {
+        const bool valid = seg + i * 64 + lane < n;
+        const uint32_t d = digit_of(key[i], shift);
+        const uint64_t peers = match_digit(d, valid);
+        if (valid && lane == __ffsll((unsigned long long)peers) - 1)
+            atomicAdd(&s_hist[d], (uint32_t)__popcll(peers));
+    }
+    __syncthreads();
+    emit_counts(s_hist, (int)gridDim.x, counts);
+}
+
+// One pass's 256 rows of per-tile digit counts (row d at counts + d *
+// stride): hist[d] = the total of the row's first nblk tiles, and the row is
+// replaced in place by its exclusive prefix over tiles. nblk covers the
+// usable entries (*total, capacity) when total is given. One wave per row.
 __global__ __launch_bounds__(256) void k_count_scan(uint32_t* __restrict__ counts, int stride, int nblk,
                                                     const uint64_t* __restrict__ total, uint32_t capacity,
-                                                    int tile_keys, int rows, uint32_t* __restrict__ hist) {
+                                                    int tile_keys, uint32_t* __restrict__ hist) {
     const int lane = threadIdx.x & 63;
     const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (r >= rows) return;  // whole waves
     if (total) nblk = (int)((usable_entries(total, capacity) + (uint32_t)tile_keys - 1) / (uint32_t)tile_keys);
     uint32_t* row = counts + (size_t)r * stride;
     const int per = (nblk + 63) / 64;
@@ -408,55 +438,43 @@ __global__ __launch_bounds__(256) void k_count_scan(uint32_t* __restrict__ count
         const uint32_t y = (uint32_t)__shfl_up((int)incl, off, 64);
         if (lane >= off) incl += y;
     }
-    if (r < kRadix) {
-        uint32_t run = incl - sum;
-        for (int i = i0; i < i1; ++i) {
-            const uint32_t c = row[i];
-            row[i] = run;
-            run += c;
-        }
+    uint32_t run = incl - sum;
+    for (int i = i0; i < i1; ++i) {
+        const uint32_t c = row[i];
+        row[i] = run;
+        run += c;
     }
     const uint32_t row_total = (uint32_t)__shfl((int)incl, 63, 64);
     if (lane == 0) hist[r] = row_total;
 }
 
 // One stable radix pass over n (key, value) pairs on digit (key >> shift),
-// 256 * ITEMS keys per workgroup.
-//   hist     [256] digit totals of this pass
-//   prefix   if not NULL: [256][nblk] exclusive per-tile prefixes of each
-//            digit (known in advance for the first pass); else the prefixes
-//            come from a look-back over:
-//   status   [nblk][256] look-back words, zero on entry
-//   ticket   workgroup order counter, zero on entry
-//   err      set to 1 if a wait ever exceeded its bound; *fail_dev (if
-//            given) is then set to kCountFailed as well
+// 256 * ITEMS keys per workgroup (tile b = workgroup b).
+//   hist         [256] digit totals of this pass
+//   prefix       [256][nblk] per-tile exclusive prefix of each digit
 // The key count is n, or the usable entries (*total, capacity) when total
 // is given (the grid is then sized for the capacity; idle workgroups exit).
 template <typename K, int ITEMS>
-__global__ __launch_bounds__(kSortThreads) void k_onesweep(
+__global__ __launch_bounds__(kSortThreads) void k_radix_pass(
     const K* __restrict__ keys_in, const uint32_t* __restrict__ vals_in, uint32_t n,
     const uint64_t* __restrict__ total, uint32_t capacity, int shift, const uint32_t* __restrict__ hist,
-    const uint32_t* __restrict__ prefix, uint64_t* __restrict__ status, uint32_t* __restrict__ ticket,
-    uint32_t* __restrict__ err, uint64_t* __restrict__ fail_dev, K* __restrict__ keys_out,
-    uint32_t* __restrict__ vals_out) {
+    const uint32_t* __restrict__ prefix, K* __restrict__ keys_out, uint32_t* __restrict__ vals_out) {
     constexpr int kTileKeys = kSortThreads * ITEMS;
     __shared__ uint32_t s_wcount[kSortWaves][kRadix];  // per-wave digit counts, then prefixes
     __shared__ uint32_t s_local_start[kRadix];
     __shared__ uint32_t s_gbase[kRadix];
     __shared__ uint32_t s_wsum[2][4];
-    __shared__ uint32_t s_block;
     __shared__ K s_keys[kTileKeys];
     __shared__ uint32_t s_vals[kTileKeys];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    if (tid == 0) s_block = prefix ? blockIdx.x : atomicAdd(ticket, 1u);
-#pragma unroll
-    for (int w = 0; w < kSortWaves; ++w) s_wcount[w][tid] = 0;
-    __syncthreads();
-    const uint32_t b = s_block;
+    const uint32_t b = blockIdx.x;
     const uint32_t base = b * kTileKeys;
     if (total) n = usable_entries(total, capacity);
     if (base >= n) return;  // whole workgroup
+#pragma unroll
+    for (int w = 0; w < kSortWaves; ++w) s_wcount[w][tid] = 0;
+    __syncthreads();
 
     // stable rank of every key among equal digits of this workgroup's tile
     K key[ITEMS];
@@ -495,52 +513,7 @@ __global__ __launch_bounds__(kSortThreads) void k_onesweep(
     s_local_start[d] = block_exclusive_scan_fast(count, s_wsum[0]);
     const uint32_t dstart = block_exclusive_scan_fast(hist[d], s_wsum[1]);
 
-    uint32_t excl = 0;
-    if (prefix) {
-        excl = prefix[(size_t)d * gridDim.x + b];
-    } else {
-        // publish this tile's count, look back for the exclusive prefix,
-        // eight predecessors' words per round trip
-        uint64_t* mine = status + (size_t)b * kRadix + d;
-        if (b == 0) {
-            __hip_atomic_store(mine, kFlagPrefix | count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        } else {
-            __hip_atomic_store(mine, kFlagAggregate | count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            int j = (int)b - 1;
-            int spins = 0;
-            bool done = false;
-            while (!done) {
-                uint64_t w8[kLookBack];
-#pragma unroll
-                for (int k = 0; k < kLookBack; ++k)
-                    w8[k] = j - k >= 0 ? __hip_atomic_load(status + (size_t)(j - k) * kRadix + d, __ATOMIC_RELAXED,
-                                                           __HIP_MEMORY_SCOPE_AGENT)
-                                       : kFlagPrefix;
-#pragma unroll
-                for (int k = 0; k < kLookBack; ++k) {
-                    if (done) break;
-                    uint64_t v = w8[k];
-                    while ((v >> 32) == 0ull) {
-                        if (++spins > kSpinLimit) {  // never expected: give up rather than hang
-                            __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                            if (fail_dev)
-                                __hip_atomic_store(fail_dev, kCountFailed, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
-                            v = kFlagPrefix;
-                            break;
-                        }
-                        __builtin_amdgcn_s_sleep(1);
-                        v = __hip_atomic_load(status + (size_t)(j - k) * kRadix + d, __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT);
-                    }
-                    excl += (uint32_t)v;
-                    done = (v >> 32) == 2ull;
-                }
-                j -= kLookBack;
-            }
-            __hip_atomic_store(mine, kFlagPrefix | (excl + count), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
+    const uint32_t excl = prefix[(size_t)d * gridDim.x + b];
     s_gbase[d] = dstart + excl;
     __syncthreads();
 
@@ -599,20 +572,15 @@ size_t bin_scratch_layout(int n, int64_t capacity, BinScratch* out, void* base) 
         off += align256(bytes > 0 ? bytes : 1);
         return at;
     };
-    // tickets of every pass and the error word (word 15), cleared by the
-    // first kernel of every call, then the entry count, so the host reads
-    // the error word and the count with one copy
-    const size_t o_tick = take(kTickets * 4 + 8);
+    const size_t o_tot = take(8);
     const size_t o_ghist = take((size_t)kGaussPasses * kRadix * 4);
     const size_t o_ehist = take((size_t)kMaxTilePasses * kRadix * 4);
     const size_t o_gcnt = take(nb_gauss * kRadix * kGaussPasses * 4);
     const size_t o_ecnt = take(nb_entry * kRadix * kMaxTilePasses * 4);
-    // look-back words of passes 1.., cleared by the kernels that count
-    const size_t o_gstat = take(nb_gauss * kRadix * (kGaussPasses - 1) * 8);
-    const size_t o_estat = take(nb_entry * kRadix * (kMaxTilePasses - 1) * 8);
     const size_t o_bs = take(nb_scan * 4);
     const size_t o_bo = take(nb_scan * 8);
     const size_t o_off = take((size_t)n * 4);
+    const size_t o_fo = take(nb_entry * 4);
     const size_t o_gk0 = take((size_t)n * 4);
     const size_t o_gv0 = take((size_t)n * 4);
     const size_t o_gk1 = take((size_t)n * 4);
@@ -621,18 +589,15 @@ size_t bin_scratch_layout(int n, int64_t capacity, BinScratch* out, void* base) 
     const size_t o_vt = take((size_t)capacity * 4);
     if (out && base) {
         char* b = (char*)base;
-        out->tickets = (uint32_t*)(b + o_tick);
-        out->err = out->tickets + (kTickets - 1);
-        out->total = (uint64_t*)(b + o_tick + kTickets * 4);
+        out->total = (uint64_t*)(b + o_tot);
         out->gauss_hist = (uint32_t*)(b + o_ghist);
         out->entry_hist = (uint32_t*)(b + o_ehist);
         out->gauss_counts = (uint32_t*)(b + o_gcnt);
         out->entry_counts = (uint32_t*)(b + o_ecnt);
-        out->gauss_status = (uint64_t*)(b + o_gstat);
-        out->entry_status = (uint64_t*)(b + o_estat);
         out->block_sums = (uint32_t*)(b + o_bs);
         out->block_offsets = (uint64_t*)(b + o_bo);
         out->offsets = (uint32_t*)(b + o_off);
+        out->first_owner = (uint32_t*)(b + o_fo);
         out->gk[0] = (uint32_t*)(b + o_gk0);
         out->gv[0] = (uint32_t*)(b + o_gv0);
         out->gk[1] = (uint32_t*)(b + o_gk1);
@@ -649,17 +614,18 @@ hipError_t launch_bin_and_sort(const gs_camera& cam, int n, const float4* xy_dep
     // 1. stable depth order of the splats (culled last) into gv[0]
     const unsigned nbg = (unsigned)((n + kGaussTile - 1) / kGaussTile);
     hipLaunchKernelGGL(k_depth_keys, dim3(nbg), dim3(kSortThreads), 0, stream, xy_depth, tiles_touched, n,
-                       s.gk[0], s.gv[0], s.gauss_counts, s.gauss_status, s.tickets);
-    const int grows = kGaussPasses * kRadix;
-    hipLaunchKernelGGL(k_count_scan, dim3((grows + 3) / 4), dim3(256), 0, stream, s.gauss_counts, (int)nbg,
-                       (int)nbg, (const uint64_t*)nullptr, 0u, kGaussTile, grows, s.gauss_hist);
+                       s.gk[0], s.gv[0], s.gauss_counts);
     for (int p = 0; p < kGaussPasses; ++p) {
         const int src = p & 1, dst = src ^ 1;  // an even pass count leaves the order in gv[0]
-        hipLaunchKernelGGL((k_onesweep<uint32_t, kGaussItems>), dim3(nbg), dim3(kSortThreads), 0, stream,
+        uint32_t* cnt = s.gauss_counts + (size_t)p * kRadix * nbg;
+        if (p > 0)
+            hipLaunchKernelGGL((k_count_digits<uint32_t, kGaussItems>), dim3(nbg), dim3(kSortThreads), 0, stream,
+                               s.gk[src], (uint32_t)n, (const uint64_t*)nullptr, 0u, 8 * p, cnt);
+        hipLaunchKernelGGL(k_count_scan, dim3(kRadix / 4), dim3(256), 0, stream, cnt, (int)nbg, (int)nbg,
+                           (const uint64_t*)nullptr, 0u, kGaussTile, s.gauss_hist + p * kRadix);
+        hipLaunchKernelGGL((k_radix_pass<uint32_t, kGaussItems>), dim3(nbg), dim3(kSortThreads), 0, stream,
                            s.gk[src], s.gv[src], (uint32_t)n, (const uint64_t*)nullptr, 0u, 8 * p,
-                           s.gauss_hist + p * kRadix, p == 0 ? s.gauss_counts : nullptr,
-                           p == 0 ? nullptr : s.gauss_status + (size_t)(p - 1) * nbg * kRadix, s.tickets + p,
-                           s.err, n_dev, s.gk[dst], s.gv[dst]);
+                           s.gauss_hist + p * kRadix, cnt, s.gk[dst], s.gv[dst]);
     }
     // 2. exclusive scan of the tile counts in depth order; E -> s.total
     const int nbs = (n + kScanTile - 1) / kScanTile;
@@ -667,12 +633,12 @@ hipError_t launch_bin_and_sort(const gs_camera& cam, int n, const float4* xy_dep
     hipLaunchKernelGGL(k_scan_reduce, dim3(nbs), dim3(kScanThreads), 0, stream, tiles_touched, perm, n,
                        s.block_sums);
     hipLaunchKernelGGL(k_scan_block_sums, dim3(1), dim3(1024), 0, stream, s.block_sums, nbs, s.block_offsets,
-                       s.total, (const uint32_t*)s.err, n_dev);
+                       s.total, n_dev);
+    const unsigned nbe = (capacity + kEntryTile - 1) / kEntryTile;
     hipLaunchKernelGGL(k_scan_offsets, dim3(nbs), dim3(kScanThreads), 0, stream, tiles_touched, perm, n,
-                       s.block_offsets, s.offsets);
+                       s.block_offsets, s.offsets, s.first_owner, nbe);
     // 3. duplication and the stable sort on the tile-id bits. Grids cover the
     // capacity; the kernels read E and do nothing when it exceeds capacity.
-    const unsigned nbe = (capacity + kEntryTile - 1) / kEntryTile;
     if (nbe == 0) return hipGetLastError();
     int tile_bits = 0;
     while ((1 << tile_bits) < tiles_x(cam) * tiles_y(cam)) ++tile_bits;
@@ -683,19 +649,19 @@ hipError_t launch_bin_and_sort(const gs_camera& cam, int n, const float4* xy_dep
     uint32_t* vin = (passes & 1) ? s.vals_tmp : values;
     uint64_t* kout = (passes & 1) ? keys : s.keys_tmp;
     uint32_t* vout = (passes & 1) ? values : s.vals_tmp;
-    hipLaunchKernelGGL(k_duplicate, dim3(nbe), dim3(kDupThreads), 0, stream, xy_depth, s.offsets, s.gv[0], n,
-                       (const uint64_t*)s.total, capacity, tiles_x(cam), tiles_y(cam), passes, kin, vin,
-                       s.entry_counts, s.entry_status);
-    if (passes == 0) return hipGetLastError();
-    const int erows = passes * kRadix;
-    hipLaunchKernelGGL(k_count_scan, dim3((erows + 3) / 4), dim3(256), 0, stream, s.entry_counts, (int)nbe, 0,
-                       (const uint64_t*)s.total, capacity, kEntryTile, erows, s.entry_hist);
+    hipLaunchKernelGGL(k_duplicate, dim3(nbe), dim3(kDupThreads), 0, stream, xy_depth, s.offsets, s.gv[0],
+                       s.first_owner, n, (const uint64_t*)s.total, capacity, tiles_x(cam), tiles_y(cam), passes,
+                       kin, vin, s.entry_counts);
     for (int p = 0; p < passes; ++p) {
-        hipLaunchKernelGGL((k_onesweep<uint64_t, kEntryItems>), dim3(nbe), dim3(kSortThreads), 0, stream, kin,
-                           vin, 0u, (const uint64_t*)s.total, capacity, 32 + 8 * p, s.entry_hist + p * kRadix,
-                           p == 0 ? s.entry_counts : nullptr,
-                           p == 0 ? nullptr : s.entry_status + (size_t)(p - 1) * nbe * kRadix,
-                           s.tickets + kGaussPasses + p, s.err, n_dev, kout, vout);
+        uint32_t* cnt = s.entry_counts + (size_t)p * kRadix * nbe;
+        if (p > 0)
+            hipLaunchKernelGGL((k_count_digits<uint64_t, kEntryItems>), dim3(nbe), dim3(kSortThreads), 0, stream,
+                               kin, 0u, (const uint64_t*)s.total, capacity, 32 + 8 * p, cnt);
+        hipLaunchKernelGGL(k_count_scan, dim3(kRadix / 4), dim3(256), 0, stream, cnt, (int)nbe, 0,
+                           (const uint64_t*)s.total, capacity, kEntryTile, s.entry_hist + p * kRadix);
+        hipLaunchKernelGGL((k_radix_pass<uint64_t, kEntryItems>), dim3(nbe), dim3(kSortThreads), 0, stream, kin,
+                           vin, 0u, (const uint64_t*)s.total, capacity, 32 + 8 * p, s.entry_hist + p * kRadix, cnt,
+                           kout, vout);
         uint64_t* tk = kin; kin = kout; kout = tk;
         uint32_t* tv = vin; vin = vout; vout = tv;
     }

@@ -22,9 +22,6 @@ constexpr float kAlphaMin = 1.0f / 255.0f;
 constexpr float kAlphaMax = 0.99f;
 constexpr float kTStop = 1e-4f;
 
-// Entry count reported when a radix pass gave up one of its bounded waits.
-constexpr uint64_t kCountFailed = ~0ull;
-
 inline int tiles_x(const gs_camera& c) { return (c.width + kTile - 1) / kTile; }
 inline int tiles_y(const gs_camera& c) { return (c.height + kTile - 1) / kTile; }
 
@@ -58,23 +55,19 @@ hipError_t launch_preprocess(const gs_camera& cam, int n, const float* means, co
                              float4* conic_op, float4* rgb, uint32_t* tiles_touched,
                              hipStream_t stream);
 
-// Binning workspace, carved from the caller's scratch buffer. The first
-// kernel of every call clears the tickets and the error word, the counting
-// kernels clear the look-back words they will need; nothing else needs
-// initialisation.
+// Binning workspace, carved from the caller's scratch buffer. Nothing in it
+// needs initialisation: every word is written before it is read within one
+// call.
 struct BinScratch {
-    uint32_t* tickets;        // [16] workgroup tickets of each pass
-    uint32_t* err;            // = tickets + 15, set if a look-back wait gave up
-    uint64_t* total;          // [1] entry count, right after err
+    uint64_t* total;          // [1] entry count
     uint32_t* gauss_hist;     // [4][256] digit totals of the depth passes
     uint32_t* entry_hist;     // [3][256] digit totals of the tile-id passes
-    uint32_t* gauss_counts;   // [4][256][nb_gauss] per-tile digit counts
+    uint32_t* gauss_counts;   // [4][256][nb_gauss] per-tile digit counts, then prefixes
     uint32_t* entry_counts;   // [3][256][nb_entry]
-    uint64_t* gauss_status;   // [3][nb_gauss][256] look-back words of passes 1..3
-    uint64_t* entry_status;   // [2][nb_entry][256]
     uint32_t* block_sums;     // [nb_scan]
     uint64_t* block_offsets;  // [nb_scan]
     uint32_t* offsets;        // [n] first entry of the i-th splat in depth order
+    uint32_t* first_owner;    // [nb_entry] owner (depth-order index) of each 2048-entry tile's first entry
     uint32_t* gk[2];          // [n] depth keys, ping-pong
     uint32_t* gv[2];          // [n] splat ids, ping-pong; gv[0] ends as the depth order
     uint64_t* keys_tmp;       // [capacity]

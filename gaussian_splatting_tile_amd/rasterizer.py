@@ -122,13 +122,10 @@ class BinBuffers:
         return self.scratch
 
     def entries(self) -> int:
-        """E of the last asynchronous binning (waits for the stream). Raises
-        GsError if a bounded wait gave up; E > capacity means the frame
-        rendered nothing and must be redone after _ensure(E)."""
-        e = int(self.n_entries_dev.item()) & ((1 << 64) - 1)
-        if e == _lib.ENTRIES_FAILED:
-            raise _lib.GsError(_lib.GS_ERR_HIP, "a radix pass's bounded wait gave up")
-        return e
+        """E of the last asynchronous binning (waits for the stream). E >
+        capacity means the frame rendered nothing and must be redone after
+        _ensure(E)."""
+        return int(self.n_entries_dev.item())
 
 
 def bin_and_sort(cam, xy_depth, tiles_touched, buffers: BinBuffers | None = None, stream=None):

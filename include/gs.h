@@ -152,19 +152,13 @@ gs_status gs_preprocess(const gs_camera* cam, int32_t n, const float* means, con
  *                  depends on n and capacity
  *   n_entries      (host) out: E
  * Returns GS_ERR_CAPACITY (with *n_entries = E; keys/point_list are then
- * not written) when E > capacity, GS_ERR_OVERFLOW when E >= 2^32, and
- * GS_ERR_HIP if a radix pass's bounded wait for an earlier workgroup ever
- * gave up (never expected; the outputs are then unspecified). Calls that
- * share one scratch buffer must not overlap.
+ * not written) when E > capacity and GS_ERR_OVERFLOW when E >= 2^32.
+ * Calls that share one scratch buffer must not overlap.
  * ------------------------------------------------------------------- */
 gs_status gs_bin_and_sort(const gs_camera* cam, int32_t n, const float* xy_depth,
                           const uint32_t* tiles_touched, uint64_t* keys, uint32_t* point_list,
                           int64_t capacity, void* scratch, size_t* scratch_bytes,
                           int64_t* n_entries, void* stream);
-
-/* Entry count stored by the asynchronous entry points when a radix pass
- * gave up one of its bounded waits (never expected). */
-#define GS_ENTRIES_FAILED UINT64_MAX
 
 /* ---------------------------------------------------------------------
  * gs_bin_and_sort_async - gs_bin_and_sort without the host wait.
@@ -172,8 +166,8 @@ gs_status gs_bin_and_sort(const gs_camera* cam, int32_t n, const float* xy_depth
  * Same work, order and arguments as gs_bin_and_sort, except that E is
  * written to device memory and the host never waits:
  *   n_entries_dev  out, device uint64 (8-byte aligned): E, written on the
- *                  stream; GS_ENTRIES_FAILED if a bounded wait gave up.
- * When E > capacity (or on failure) keys and point_list are not written;
+ *                  stream.
+ * When E > capacity keys and point_list are not written;
  * gs_tile_ranges_async then marks every tile empty, so the frame renders the
  * background and the caller, once it reads E, grows the buffers and renders
  * the frame again. Host-side argument errors are returned as usual; calls
