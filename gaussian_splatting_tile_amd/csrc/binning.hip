@@ -4,7 +4,7 @@
 //
 // Follows "rigel" README "Binning" (count, a scan giving every Gaussian a
 // private slice, expansion, a sort restricted to the bits that can vary,
-// a range kernel); zenn 4.1 (hierarchical exclusive scan), 4.2 (duplicate
+// a range kernel); zenn 4.1 (exclusive scan of the tile counts), 4.2 (duplicate
 // into the slice), 4.3 (8-bit LSD radix passes: histogram, bin starts,
 // per-workgroup bin offsets, in-bin rank from the flag bits set before a
 // lane, ping-pong buffers), 4.4 (range boundaries, empty tiles cleared);
@@ -39,11 +39,16 @@
 //    its rank (the zenn flag-bit rank). Per-wave LDS counters carry the rank
 //    across rounds, so the order stays stable. Each workgroup stages its
 //    output in LDS and writes per-digit runs, so global writes coalesce.
-//  * The scan is reduce / scan-of-block-sums / rescan into per-splat
-//    offsets. The duplication is entry-parallel: each workgroup takes 2048
-//    consecutive entries, finds the splats that own them, stages their
-//    offsets in LDS and gives every lane one entry, so the work is balanced
-//    however many tiles a splat covers, and the stores coalesce.
+//  * The exclusive scan of tiles_touched in depth order rides on the last
+//    depth pass: its counting kernel also sums tiles_touched per (tile,
+//    digit), the prefix kernel scans those sums too, and the pass writes
+//    each splat's first entry where it writes the splat itself, plus the
+//    owner of every 2048-entry duplication tile's first entry and E.
+//  * The duplication is entry-parallel: each workgroup takes 2048
+//    consecutive entries (one tile of the later sort), derives the owner of
+//    each entry from the owners' start slots with a max-scan in LDS and
+//    gives every lane one entry, so the work is balanced however many tiles
+//    a splat covers, and the stores coalesce.
 #include <algorithm>
 
 #include "gs_internal.h"
@@ -54,10 +59,6 @@ namespace {
 constexpr int kDupThreads = 256;
 constexpr int kDupItems = 8;
 constexpr int kDupTile = kDupThreads * kDupItems;  // entries per duplication workgroup
-
-constexpr int kScanThreads = 256;
-constexpr int kScanItems = 8;
-constexpr int kScanTile = kScanThreads * kScanItems;  // splats per workgroup
 
 constexpr int kSortThreads = 256;
 constexpr int kSortWaves = kSortThreads / 64;
@@ -70,26 +71,6 @@ constexpr int kGaussPasses = 4;                         // 32 depth bits
 constexpr int kMaxTilePasses = 3;                       // up to 24 tile-id bits
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
-
-// Inclusive scan of one value per thread across a 256-thread workgroup
-// (Hillis-Steele in LDS). `tmp` holds 256 words. *total = the sum.
-template <typename T>
-__device__ T block_inclusive_scan_256(T x, T* tmp, T* total) {
-    const int tid = threadIdx.x;
-    tmp[tid] = x;
-    __syncthreads();
-#pragma unroll
-    for (int off = 1; off < 256; off <<= 1) {
-        T y = (tid >= off) ? tmp[tid - off] : T(0);
-        __syncthreads();
-        x += y;
-        tmp[tid] = x;
-        __syncthreads();
-    }
-    *total = tmp[255];
-    __syncthreads();
-    return x;
-}
 
 // Exclusive scan of one value per thread over a 256-thread workgroup: a
 // shuffle scan in each wave, then one barrier for the wave totals. `wsum`
@@ -105,6 +86,28 @@ __device__ __forceinline__ uint32_t block_exclusive_scan_fast(uint32_t x, uint32
     if (lane == 63) wsum[wave] = v;
     __syncthreads();
     uint32_t pre = 0;
+    for (int w = 0; w < wave; ++w) pre += wsum[w];
+    return pre + v - x;
+}
+
+__device__ __forceinline__ uint64_t shfl_up_u64(uint64_t v, int off) {
+    const uint32_t lo = (uint32_t)__shfl_up((int)(uint32_t)v, off, 64);
+    const uint32_t hi = (uint32_t)__shfl_up((int)(uint32_t)(v >> 32), off, 64);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// 64-bit version of block_exclusive_scan_fast; `wsum` holds 4 words.
+__device__ __forceinline__ uint64_t block_exclusive_scan_u64(uint64_t x, uint64_t* wsum) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint64_t v = x;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint64_t y = shfl_up_u64(v, off);
+        if (lane >= off) v += y;
+    }
+    if (lane == 63) wsum[wave] = v;
+    __syncthreads();
+    uint64_t pre = 0;
     for (int w = 0; w < wave; ++w) pre += wsum[w];
     return pre + v - x;
 }
@@ -125,119 +128,6 @@ __device__ __forceinline__ uint64_t match_digit(uint32_t d, bool valid) {
 template <typename K>
 __device__ __forceinline__ uint32_t digit_of(K key, int shift) {
     return (uint32_t)(key >> shift) & (kRadix - 1);
-}
-
-// ---- scan (in a given order of the splats) ----
-
-// counts are read as counts[perm[i]]: the i-th splat of the depth order.
-__global__ __launch_bounds__(kScanThreads) void k_scan_reduce(const uint32_t* __restrict__ counts,
-                                                              const uint32_t* __restrict__ perm, int n,
-                                                              uint32_t* __restrict__ block_sums) {
-    __shared__ uint32_t s_red[kScanThreads / 64];
-    const int base = blockIdx.x * kScanTile;
-    uint32_t sum = 0;
-#pragma unroll
-    for (int i = 0; i < kScanItems; ++i) {
-        const int idx = base + i * kScanThreads + threadIdx.x;
-        if (idx < n) sum += counts[perm[idx]];
-    }
-    for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
-    if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = sum;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t t = 0;
-        for (int w = 0; w < kScanThreads / 64; ++w) t += s_red[w];
-        block_sums[blockIdx.x] = t;
-    }
-}
-
-// One workgroup of 1024 threads scans up to 8192 block sums (n <= 2^24).
-// The entry count goes to *total (and *n_dev if given).
-__global__ __launch_bounds__(1024) void k_scan_block_sums(const uint32_t* __restrict__ block_sums,
-                                                          int nb, uint64_t* __restrict__ block_offsets,
-                                                          uint64_t* __restrict__ total,
-                                                          uint64_t* __restrict__ n_dev) {
-    __shared__ uint64_t s[1024];
-    constexpr int kPer = 8;
-    const int tid = threadIdx.x;
-    uint64_t local[kPer];
-    uint64_t mine = 0;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-        const int idx = tid * kPer + i;
-        local[i] = idx < nb ? (uint64_t)block_sums[idx] : 0;
-        mine += local[i];
-    }
-    uint64_t sum = mine;
-    s[tid] = sum;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-        uint64_t y = tid >= off ? s[tid - off] : 0;
-        __syncthreads();
-        sum += y;
-        s[tid] = sum;
-        __syncthreads();
-    }
-    uint64_t run = sum - mine;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-        const int idx = tid * kPer + i;
-        if (idx < nb) block_offsets[idx] = run;
-        run += local[i];
-    }
-    if (tid == 1023) {
-        *total = sum;
-        if (n_dev) *n_dev = sum;
-    }
-}
-
-// offsets[i]: first entry of the i-th splat of the depth order. Also
-// first_owner[B] = the i owning entry B * 2048 (the first entry of
-// duplication workgroup B), for B < n_dup_blocks.
-__global__ __launch_bounds__(kScanThreads) void k_scan_offsets(const uint32_t* __restrict__ counts,
-                                                               const uint32_t* __restrict__ perm, int n,
-                                                               const uint64_t* __restrict__ block_offsets,
-                                                               uint32_t* __restrict__ offsets,
-                                                               uint32_t* __restrict__ first_owner,
-                                                               uint32_t n_dup_blocks) {
-    __shared__ uint32_t s_c[kScanTile];
-    __shared__ uint32_t s_tmp[kScanThreads];
-    const int tid = threadIdx.x;
-    const int base = blockIdx.x * kScanTile;
-#pragma unroll
-    for (int i = 0; i < kScanItems; ++i) {
-        const int idx = i * kScanThreads + tid;
-        s_c[idx] = base + idx < n ? counts[perm[base + idx]] : 0u;
-    }
-    __syncthreads();
-    uint32_t c[kScanItems];
-    uint32_t sum = 0;
-#pragma unroll
-    for (int i = 0; i < kScanItems; ++i) {
-        c[i] = s_c[tid * kScanItems + i];
-        sum += c[i];
-    }
-    uint32_t total;
-    const uint32_t incl = block_inclusive_scan_256<uint32_t>(sum, s_tmp, &total);
-    uint32_t run = (uint32_t)block_offsets[blockIdx.x] + (incl - sum);
-#pragma unroll
-    for (int i = 0; i < kScanItems; ++i) {
-        s_c[tid * kScanItems + i] = run;
-        // duplication workgroups whose first entry this splat owns
-        if (c[i] != 0u) {
-            const uint64_t b0 = ((uint64_t)run + kDupTile - 1) / kDupTile;
-            const uint64_t b1 = ((uint64_t)run + c[i] - 1) / kDupTile;
-            for (uint64_t B = b0; B <= b1 && B < n_dup_blocks; ++B)
-                first_owner[B] = (uint32_t)(base + tid * kScanItems + i);
-        }
-        run += c[i];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < kScanItems; ++i) {
-        const int idx = i * kScanThreads + tid;
-        if (base + idx < n) offsets[base + idx] = s_c[idx];
-    }
 }
 
 // ---- duplication ----
@@ -384,26 +274,35 @@ __global__ __launch_bounds__(kSortThreads) void k_depth_keys(const float4* __res
 
 // Per-tile counts of digit (key >> shift) of the keys about to be sorted by
 // a later pass: one tile of 256 * ITEMS keys per workgroup, as in the pass.
-// The key count is n, or the usable entries (*total, capacity).
-template <typename K, int ITEMS>
+// The key count is n, or the usable entries (*total, capacity). With TT (the
+// last depth pass) it also sums, per tile and digit, tiles_touched of the
+// splats the keys belong to (vals), into tt_counts.
+template <typename K, int ITEMS, bool TT>
 __global__ __launch_bounds__(kSortThreads) void k_count_digits(const K* __restrict__ keys, uint32_t n,
                                                                const uint64_t* __restrict__ total,
                                                                uint32_t capacity, int shift,
-                                                               uint32_t* __restrict__ counts) {
+                                                               uint32_t* __restrict__ counts,
+                                                               const uint32_t* __restrict__ vals,
+                                                               const uint32_t* __restrict__ tiles_touched,
+                                                               uint32_t* __restrict__ tt_counts) {
     constexpr int kTileKeys = kSortThreads * ITEMS;
     __shared__ uint32_t s_hist[kRadix];
+    __shared__ uint32_t s_tt[TT ? kRadix : 1];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     if (total) n = usable_entries(total, capacity);
     const uint32_t base = blockIdx.x * kTileKeys;
     if (base >= n) return;  // whole workgroup
     s_hist[tid] = 0;
+    if (TT) s_tt[tid] = 0;
     __syncthreads();
     const uint32_t seg = base + wave * (64 * ITEMS);
     K key[ITEMS];
+    uint32_t tt[ITEMS];
 #pragma unroll
     for (int i = 0; i < ITEMS; ++i) {
         const uint32_t pos = seg + i * 64 + lane;
         key[i] = pos < n ? keys[pos] : K(0);
+        tt[i] = TT && pos < n ? tiles_touched[vals[pos]] : 0u;
     }
 #pragma unroll
     for (int i = 0; i < ITEMS; ++i) {
@@ -412,18 +311,25 @@ __global__ __launch_bounds__(kSortThreads) void k_count_digits(const K* __restri
         const uint64_t peers = match_digit(d, valid);
         if (valid && lane == __ffsll((unsigned long long)peers) - 1)
             atomicAdd(&s_hist[d], (uint32_t)__popcll(peers));
+        if (TT && valid && tt[i] != 0u) atomicAdd(&s_tt[d], tt[i]);
     }
     __syncthreads();
     emit_counts(s_hist, (int)gridDim.x, counts);
+    if (TT) emit_counts(s_tt, (int)gridDim.x, tt_counts);
 }
 
 // One pass's 256 rows of per-tile digit counts (row d at counts + d *
 // stride): hist[d] = the total of the row's first nblk tiles, and the row is
 // replaced in place by its exclusive prefix over tiles. nblk covers the
 // usable entries (*total, capacity) when total is given. One wave per row.
+// If tt_counts is given (the last depth pass), its rows are scanned the same
+// way in 64 bits into tt_prefix, with totals in tt_hist.
 __global__ __launch_bounds__(256) void k_count_scan(uint32_t* __restrict__ counts, int stride, int nblk,
                                                     const uint64_t* __restrict__ total, uint32_t capacity,
-                                                    int tile_keys, uint32_t* __restrict__ hist) {
+                                                    int tile_keys, uint32_t* __restrict__ hist,
+                                                    const uint32_t* __restrict__ tt_counts,
+                                                    uint64_t* __restrict__ tt_prefix,
+                                                    uint64_t* __restrict__ tt_hist) {
     const int lane = threadIdx.x & 63;
     const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (total) nblk = (int)((usable_entries(total, capacity) + (uint32_t)tile_keys - 1) / (uint32_t)tile_keys);
@@ -446,6 +352,24 @@ __global__ __launch_bounds__(256) void k_count_scan(uint32_t* __restrict__ count
     }
     const uint32_t row_total = (uint32_t)__shfl((int)incl, 63, 64);
     if (lane == 0) hist[r] = row_total;
+    if (tt_counts) {
+        const uint32_t* trow = tt_counts + (size_t)r * stride;
+        uint64_t* prow = tt_prefix + (size_t)r * stride;
+        uint64_t tsum = 0;
+        for (int i = i0; i < i1; ++i) tsum += trow[i];
+        uint64_t tincl = tsum;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const uint64_t y = shfl_up_u64(tincl, off);
+            if (lane >= off) tincl += y;
+        }
+        uint64_t trun = tincl - tsum;
+        for (int i = i0; i < i1; ++i) {
+            prow[i] = trun;
+            trun += trow[i];
+        }
+        if (lane == 63) tt_hist[r] = tincl;
+    }
 }
 
 // One stable radix pass over n (key, value) pairs on digit (key >> shift),
@@ -454,18 +378,43 @@ __global__ __launch_bounds__(256) void k_count_scan(uint32_t* __restrict__ count
 //   prefix       [256][nblk] per-tile exclusive prefix of each digit
 // The key count is n, or the usable entries (*total, capacity) when total
 // is given (the grid is then sized for the capacity; idle workgroups exit).
-template <typename K, int ITEMS>
+//
+// With TT (the last depth pass, whose output order is the depth order) the
+// pass also does the exclusive scan of tiles_touched in that order: the sum
+// over the splats before position `out` is the sum over all smaller digits
+// (exclusive scan of tt_hist), over this digit in earlier tiles (tt_prefix)
+// and over this digit earlier in this tile (a scan of the staged slots). It
+// writes offsets[out], first_owner[B] for every duplication workgroup B
+// whose first entry the splat owns, and the entry count E to *tt_total_out
+// (and *n_dev if given).
+struct DepthScanArgs {
+    const uint32_t* tiles_touched;
+    const uint64_t* tt_prefix;  // [256][nblk]
+    const uint64_t* tt_hist;    // [256]
+    uint32_t* offsets;
+    uint32_t* first_owner;
+    uint32_t n_dup_blocks;
+    uint64_t* tt_total_out;
+    uint64_t* n_dev;
+};
+
+template <typename K, int ITEMS, bool TT>
 __global__ __launch_bounds__(kSortThreads) void k_radix_pass(
     const K* __restrict__ keys_in, const uint32_t* __restrict__ vals_in, uint32_t n,
     const uint64_t* __restrict__ total, uint32_t capacity, int shift, const uint32_t* __restrict__ hist,
-    const uint32_t* __restrict__ prefix, K* __restrict__ keys_out, uint32_t* __restrict__ vals_out) {
+    const uint32_t* __restrict__ prefix, K* __restrict__ keys_out, uint32_t* __restrict__ vals_out,
+    DepthScanArgs ds) {
     constexpr int kTileKeys = kSortThreads * ITEMS;
     __shared__ uint32_t s_wcount[kSortWaves][kRadix];  // per-wave digit counts, then prefixes
     __shared__ uint32_t s_local_start[kRadix];
     __shared__ uint32_t s_gbase[kRadix];
-    __shared__ uint32_t s_wsum[2][4];
+    __shared__ uint32_t s_wsum[3][4];
     __shared__ K s_keys[kTileKeys];
     __shared__ uint32_t s_vals[kTileKeys];
+    __shared__ uint32_t s_tt[TT ? kTileKeys : 1];   // tiles_touched per staged slot
+    __shared__ uint32_t s_ttx[TT ? kTileKeys : 1];  // its exclusive scan over the slots
+    __shared__ uint64_t s_ttbase[TT ? kRadix : 1];
+    __shared__ uint64_t s_wsum64[4];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const uint32_t b = blockIdx.x;
@@ -515,6 +464,15 @@ __global__ __launch_bounds__(kSortThreads) void k_radix_pass(
 
     const uint32_t excl = prefix[(size_t)d * gridDim.x + b];
     s_gbase[d] = dstart + excl;
+    if (TT) {
+        const uint64_t th = ds.tt_hist[d];
+        const uint64_t tstart = block_exclusive_scan_u64(th, s_wsum64);
+        s_ttbase[d] = tstart + ds.tt_prefix[(size_t)d * gridDim.x + b];
+        if (b == 0 && d == kRadix - 1) {
+            *ds.tt_total_out = tstart + th;
+            if (ds.n_dev) *ds.n_dev = tstart + th;
+        }
+    }
     __syncthreads();
 
     // stage in digit order, write out per-digit runs
@@ -526,16 +484,44 @@ __global__ __launch_bounds__(kSortThreads) void k_radix_pass(
             const uint32_t slot = s_local_start[dd] + s_wcount[wave][dd] + rank[i];
             s_keys[slot] = key[i];
             s_vals[slot] = val[i];
+            if (TT) s_tt[slot] = ds.tiles_touched[val[i]];
         }
     }
     __syncthreads();
     const uint32_t valid_n = min(n - base, (uint32_t)kTileKeys);
+    if (TT) {  // exclusive scan of s_tt over the slots (thread t: slots [ITEMS t, ITEMS t + ITEMS))
+        uint32_t c[ITEMS];
+        uint32_t sum = 0;
+#pragma unroll
+        for (int j = 0; j < ITEMS; ++j) {
+            const uint32_t sl = tid * ITEMS + j;
+            c[j] = sl < valid_n ? s_tt[sl] : 0u;
+            sum += c[j];
+        }
+        uint32_t run = block_exclusive_scan_fast(sum, s_wsum[2]);
+#pragma unroll
+        for (int j = 0; j < ITEMS; ++j) {
+            s_ttx[tid * ITEMS + j] = run;
+            run += c[j];
+        }
+        __syncthreads();
+    }
     for (uint32_t s = tid; s < valid_n; s += kSortThreads) {
         const K k = s_keys[s];
         const uint32_t dd = digit_of(k, shift);
         const uint32_t out = s_gbase[dd] + (s - s_local_start[dd]);
         keys_out[out] = k;
         vals_out[out] = s_vals[s];
+        if (TT) {
+            const uint64_t off = s_ttbase[dd] + (s_ttx[s] - s_ttx[s_local_start[dd]]);
+            const uint32_t cnt = s_tt[s];
+            ds.offsets[out] = (uint32_t)off;
+            if (cnt != 0u) {  // duplication workgroups whose first entry this splat owns
+                const uint64_t b1 = (off + cnt - 1) / kDupTile;
+                for (uint64_t B = (off + kDupTile - 1) / kDupTile; B <= b1 && B < ds.n_dup_blocks; ++B)
+                    ds.first_owner[B] = out;
+            }
+        }
     }
 }
 
@@ -563,7 +549,6 @@ int tile_pass_count(int tile_bits) { return (tile_bits + 7) / 8; }
 }  // namespace
 
 size_t bin_scratch_layout(int n, int64_t capacity, BinScratch* out, void* base) {
-    const size_t nb_scan = (size_t)(n + kScanTile - 1) / kScanTile;
     const size_t nb_gauss = (size_t)(n + kGaussTile - 1) / kGaussTile;
     const size_t nb_entry = (size_t)((capacity + kEntryTile - 1) / kEntryTile);
     size_t off = 0;
@@ -577,8 +562,9 @@ size_t bin_scratch_layout(int n, int64_t capacity, BinScratch* out, void* base) 
     const size_t o_ehist = take((size_t)kMaxTilePasses * kRadix * 4);
     const size_t o_gcnt = take(nb_gauss * kRadix * kGaussPasses * 4);
     const size_t o_ecnt = take(nb_entry * kRadix * kMaxTilePasses * 4);
-    const size_t o_bs = take(nb_scan * 4);
-    const size_t o_bo = take(nb_scan * 8);
+    const size_t o_ttc = take(nb_gauss * kRadix * 4);
+    const size_t o_ttp = take(nb_gauss * kRadix * 8);
+    const size_t o_tth = take(kRadix * 8);
     const size_t o_off = take((size_t)n * 4);
     const size_t o_fo = take(nb_entry * 4);
     const size_t o_gk0 = take((size_t)n * 4);
@@ -594,8 +580,9 @@ size_t bin_scratch_layout(int n, int64_t capacity, BinScratch* out, void* base) 
         out->entry_hist = (uint32_t*)(b + o_ehist);
         out->gauss_counts = (uint32_t*)(b + o_gcnt);
         out->entry_counts = (uint32_t*)(b + o_ecnt);
-        out->block_sums = (uint32_t*)(b + o_bs);
-        out->block_offsets = (uint64_t*)(b + o_bo);
+        out->tt_counts = (uint32_t*)(b + o_ttc);
+        out->tt_prefix = (uint64_t*)(b + o_ttp);
+        out->tt_hist = (uint64_t*)(b + o_tth);
         out->offsets = (uint32_t*)(b + o_off);
         out->first_owner = (uint32_t*)(b + o_fo);
         out->gk[0] = (uint32_t*)(b + o_gk0);
@@ -611,33 +598,40 @@ size_t bin_scratch_layout(int n, int64_t capacity, BinScratch* out, void* base) 
 hipError_t launch_bin_and_sort(const gs_camera& cam, int n, const float4* xy_depth,
                                const uint32_t* tiles_touched, uint64_t* keys, uint32_t* values,
                                uint32_t capacity, const BinScratch& s, uint64_t* n_dev, hipStream_t stream) {
-    // 1. stable depth order of the splats (culled last) into gv[0]
+    // 1. stable depth order of the splats (culled last) into gv[0]; the last
+    // pass also scans tiles_touched in that order: offsets, first_owner, E
     const unsigned nbg = (unsigned)((n + kGaussTile - 1) / kGaussTile);
+    const unsigned nbe = (capacity + kEntryTile - 1) / kEntryTile;
     hipLaunchKernelGGL(k_depth_keys, dim3(nbg), dim3(kSortThreads), 0, stream, xy_depth, tiles_touched, n,
                        s.gk[0], s.gv[0], s.gauss_counts);
+    const DepthScanArgs none{};
+    const DepthScanArgs scan{tiles_touched, s.tt_prefix, s.tt_hist, s.offsets, s.first_owner, nbe, s.total, n_dev};
     for (int p = 0; p < kGaussPasses; ++p) {
         const int src = p & 1, dst = src ^ 1;  // an even pass count leaves the order in gv[0]
+        const bool last = p == kGaussPasses - 1;
         uint32_t* cnt = s.gauss_counts + (size_t)p * kRadix * nbg;
-        if (p > 0)
-            hipLaunchKernelGGL((k_count_digits<uint32_t, kGaussItems>), dim3(nbg), dim3(kSortThreads), 0, stream,
-                               s.gk[src], (uint32_t)n, (const uint64_t*)nullptr, 0u, 8 * p, cnt);
+        if (last)
+            hipLaunchKernelGGL((k_count_digits<uint32_t, kGaussItems, true>), dim3(nbg), dim3(kSortThreads), 0,
+                               stream, s.gk[src], (uint32_t)n, (const uint64_t*)nullptr, 0u, 8 * p, cnt,
+                               (const uint32_t*)s.gv[src], tiles_touched, s.tt_counts);
+        else if (p > 0)
+            hipLaunchKernelGGL((k_count_digits<uint32_t, kGaussItems, false>), dim3(nbg), dim3(kSortThreads), 0,
+                               stream, s.gk[src], (uint32_t)n, (const uint64_t*)nullptr, 0u, 8 * p, cnt,
+                               (const uint32_t*)nullptr, (const uint32_t*)nullptr, (uint32_t*)nullptr);
         hipLaunchKernelGGL(k_count_scan, dim3(kRadix / 4), dim3(256), 0, stream, cnt, (int)nbg, (int)nbg,
-                           (const uint64_t*)nullptr, 0u, kGaussTile, s.gauss_hist + p * kRadix);
-        hipLaunchKernelGGL((k_radix_pass<uint32_t, kGaussItems>), dim3(nbg), dim3(kSortThreads), 0, stream,
-                           s.gk[src], s.gv[src], (uint32_t)n, (const uint64_t*)nullptr, 0u, 8 * p,
-                           s.gauss_hist + p * kRadix, cnt, s.gk[dst], s.gv[dst]);
+                           (const uint64_t*)nullptr, 0u, kGaussTile, s.gauss_hist + p * kRadix,
+                           last ? (const uint32_t*)s.tt_counts : nullptr, last ? s.tt_prefix : nullptr,
+                           last ? s.tt_hist : nullptr);
+        if (last)
+            hipLaunchKernelGGL((k_radix_pass<uint32_t, kGaussItems, true>), dim3(nbg), dim3(kSortThreads), 0,
+                               stream, s.gk[src], s.gv[src], (uint32_t)n, (const uint64_t*)nullptr, 0u, 8 * p,
+                               s.gauss_hist + p * kRadix, cnt, s.gk[dst], s.gv[dst], scan);
+        else
+            hipLaunchKernelGGL((k_radix_pass<uint32_t, kGaussItems, false>), dim3(nbg), dim3(kSortThreads), 0,
+                               stream, s.gk[src], s.gv[src], (uint32_t)n, (const uint64_t*)nullptr, 0u, 8 * p,
+                               s.gauss_hist + p * kRadix, cnt, s.gk[dst], s.gv[dst], none);
     }
-    // 2. exclusive scan of the tile counts in depth order; E -> s.total
-    const int nbs = (n + kScanTile - 1) / kScanTile;
-    const uint32_t* perm = s.gv[0];
-    hipLaunchKernelGGL(k_scan_reduce, dim3(nbs), dim3(kScanThreads), 0, stream, tiles_touched, perm, n,
-                       s.block_sums);
-    hipLaunchKernelGGL(k_scan_block_sums, dim3(1), dim3(1024), 0, stream, s.block_sums, nbs, s.block_offsets,
-                       s.total, n_dev);
-    const unsigned nbe = (capacity + kEntryTile - 1) / kEntryTile;
-    hipLaunchKernelGGL(k_scan_offsets, dim3(nbs), dim3(kScanThreads), 0, stream, tiles_touched, perm, n,
-                       s.block_offsets, s.offsets, s.first_owner, nbe);
-    // 3. duplication and the stable sort on the tile-id bits. Grids cover the
+    // 2. duplication and the stable sort on the tile-id bits. Grids cover the
     // capacity; the kernels read E and do nothing when it exceeds capacity.
     if (nbe == 0) return hipGetLastError();
     int tile_bits = 0;
@@ -655,13 +649,15 @@ hipError_t launch_bin_and_sort(const gs_camera& cam, int n, const float4* xy_dep
     for (int p = 0; p < passes; ++p) {
         uint32_t* cnt = s.entry_counts + (size_t)p * kRadix * nbe;
         if (p > 0)
-            hipLaunchKernelGGL((k_count_digits<uint64_t, kEntryItems>), dim3(nbe), dim3(kSortThreads), 0, stream,
-                               kin, 0u, (const uint64_t*)s.total, capacity, 32 + 8 * p, cnt);
+            hipLaunchKernelGGL((k_count_digits<uint64_t, kEntryItems, false>), dim3(nbe), dim3(kSortThreads), 0,
+                               stream, kin, 0u, (const uint64_t*)s.total, capacity, 32 + 8 * p, cnt,
+                               (const uint32_t*)nullptr, (const uint32_t*)nullptr, (uint32_t*)nullptr);
         hipLaunchKernelGGL(k_count_scan, dim3(kRadix / 4), dim3(256), 0, stream, cnt, (int)nbe, 0,
-                           (const uint64_t*)s.total, capacity, kEntryTile, s.entry_hist + p * kRadix);
-        hipLaunchKernelGGL((k_radix_pass<uint64_t, kEntryItems>), dim3(nbe), dim3(kSortThreads), 0, stream, kin,
-                           vin, 0u, (const uint64_t*)s.total, capacity, 32 + 8 * p, s.entry_hist + p * kRadix, cnt,
-                           kout, vout);
+                           (const uint64_t*)s.total, capacity, kEntryTile, s.entry_hist + p * kRadix,
+                           (const uint32_t*)nullptr, (uint64_t*)nullptr, (uint64_t*)nullptr);
+        hipLaunchKernelGGL((k_radix_pass<uint64_t, kEntryItems, false>), dim3(nbe), dim3(kSortThreads), 0, stream,
+                           kin, vin, 0u, (const uint64_t*)s.total, capacity, 32 + 8 * p, s.entry_hist + p * kRadix,
+                           cnt, kout, vout, DepthScanArgs{});
         uint64_t* tk = kin; kin = kout; kout = tk;
         uint32_t* tv = vin; vin = vout; vout = tv;
     }

@@ -64,8 +64,9 @@ struct BinScratch {
     uint32_t* entry_hist;     // [3][256] digit totals of the tile-id passes
     uint32_t* gauss_counts;   // [4][256][nb_gauss] per-tile digit counts, then prefixes
     uint32_t* entry_counts;   // [3][256][nb_entry]
-    uint32_t* block_sums;     // [nb_scan]
-    uint64_t* block_offsets;  // [nb_scan]
+    uint32_t* tt_counts;      // [256][nb_gauss] per-tile sums of tiles_touched, last depth pass
+    uint64_t* tt_prefix;      // [256][nb_gauss] their exclusive prefix over tiles
+    uint64_t* tt_hist;        // [256] their totals
     uint32_t* offsets;        // [n] first entry of the i-th splat in depth order
     uint32_t* first_owner;    // [nb_entry] owner (depth-order index) of each 2048-entry tile's first entry
     uint32_t* gk[2];          // [n] depth keys, ping-pong
@@ -75,8 +76,8 @@ struct BinScratch {
 };
 size_t bin_scratch_layout(int n, int64_t capacity, BinScratch* out, void* base);
 
-// The whole binning: stable depth order of the splats, scan of their tile
-// counts in that order (E -> *s.total, and *n_dev if given), duplication,
+// The whole binning: stable depth order of the splats with the scan of
+// their tile counts in that order (E -> *s.total, and *n_dev if given), duplication,
 // stable sort on the tile-id bits into (keys, values). Never waits on the
 // host. When E > capacity nothing is written to keys/values.
 hipError_t launch_bin_and_sort(const gs_camera& cam, int n, const float4* xy_depth,
