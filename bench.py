@@ -75,6 +75,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="cfg2", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--tile-order", choices=("heavy-first", "index"), default="index",
+                    help="tile schedule of the compositing kernels (results are identical)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -112,6 +114,7 @@ def main():
                tiles_touched=torch.empty((n,), dtype=i32, device=dev))
     bins = gs.BinBuffers(dev, capacity=1 << 16)
     ranges = torch.empty((TX * TY, 2), dtype=i32, device=dev)
+    order = torch.empty((TX * TY,), dtype=i32, device=dev) if args.tile_order == "heavy-first" else None
     fwd = dict(image=torch.empty((3, H, W), dtype=f32, device=dev),
                final_T=torch.empty((H, W), dtype=f32, device=dev),
                n_contrib=torch.empty((H, W), dtype=i32, device=dev))
@@ -148,12 +151,12 @@ def main():
         mark(False)
         k, p = gs.bin_and_sort_async(c, pre["xy_depth"], pre["tiles_touched"], bins)
         mark(False)
-        gs.tile_ranges_async(c, bins, out=ranges)
+        gs.tile_ranges_async(c, bins, out=ranges, order=order)
         mark(True)
-        gs.composite_fwd(c, ranges, p, pre["xy_depth"], pre["conic_op"], pre["rgb"], out=fwd)
+        gs.composite_fwd(c, ranges, p, pre["xy_depth"], pre["conic_op"], pre["rgb"], out=fwd, order=order)
         mark(True)
         gs.composite_bwd(c, n, ranges, p, pre["xy_depth"], pre["conic_op"], pre["rgb"],
-                         fwd["final_T"], fwd["n_contrib"], dLdI, out=grads)
+                         fwd["final_T"], fwd["n_contrib"], dLdI, out=grads, order=order)
         mark(True)
 
     for _ in range(args.warmup):
@@ -209,7 +212,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": f"{args.workload}: {WORKLOADS[args.workload]}",
+        "config": {"workload": f"{args.workload}: {WORKLOADS[args.workload]}", "tile_order": args.tile_order,
                    "n_gaussians": n, "width": W, "height": H, "n_entries": E,
                    "evals_fwd": evals_fwd, "evals_bwd": evals_bwd},
         "pixel_splat_evals_per_s": round((evals_fwd + evals_bwd) * fps, 1),

@@ -59,13 +59,13 @@ def load() -> ctypes.CDLL:
     lib.gs_bin_and_sort_async.restype = ctypes.c_int
     lib.gs_bin_and_sort_async.argtypes = [CAM, I32, P, P, P, P, I64, P, ctypes.POINTER(ctypes.c_size_t), P, P]
     lib.gs_tile_ranges.restype = ctypes.c_int
-    lib.gs_tile_ranges.argtypes = [CAM, P, I64, P, P]
+    lib.gs_tile_ranges.argtypes = [CAM, P, I64, P, P, P]
     lib.gs_tile_ranges_async.restype = ctypes.c_int
-    lib.gs_tile_ranges_async.argtypes = [CAM, P, P, I64, P, P]
+    lib.gs_tile_ranges_async.argtypes = [CAM, P, P, I64, P, P, P]
     lib.gs_composite_fwd.restype = ctypes.c_int
-    lib.gs_composite_fwd.argtypes = [CAM, P, P, P, P, P, P, P, P, P, P, P]
+    lib.gs_composite_fwd.argtypes = [CAM, P, P, P, P, P, P, P, P, P, P, P, P]
     lib.gs_composite_bwd.restype = ctypes.c_int
-    lib.gs_composite_bwd.argtypes = [CAM, I32, P, P, P, P, P, P, P, P, P, P, P, P, P]
+    lib.gs_composite_bwd.argtypes = [CAM, I32, P, P, P, P, P, P, P, P, P, P, P, P, P, P]
     _lib = lib
     return lib
 

@@ -178,20 +178,20 @@ gs_status gs_bin_and_sort_async(const gs_camera* cam, int32_t n, const float* xy
 }
 
 gs_status gs_tile_ranges(const gs_camera* cam, const uint64_t* keys, int64_t n_entries,
-                         uint32_t* ranges, void* stream) {
+                         uint32_t* ranges, uint32_t* tile_order, void* stream) {
     g_last_error.clear();
     if (gs_status s = check_camera(cam)) return s;
     if (n_entries < 0 || n_entries > (int64_t)UINT32_MAX)
         return fail(GS_ERR_INVALID, "n_entries %lld outside [0, 2^32 - 1]", (long long)n_entries);
     if (!ranges || (n_entries > 0 && !keys)) return fail(GS_ERR_INVALID, "gs_tile_ranges: NULL pointer");
     const int n_tiles = gs::tiles_x(*cam) * gs::tiles_y(*cam);
-    return hip_check(gs::launch_tile_ranges(keys, (uint32_t)n_entries, nullptr, 0u, n_tiles, ranges,
+    return hip_check(gs::launch_tile_ranges(keys, (uint32_t)n_entries, nullptr, 0u, n_tiles, ranges, tile_order,
                                             (hipStream_t)stream),
                      "tile ranges launch");
 }
 
 gs_status gs_tile_ranges_async(const gs_camera* cam, const uint64_t* keys, const uint64_t* n_entries_dev,
-                               int64_t capacity, uint32_t* ranges, void* stream) {
+                               int64_t capacity, uint32_t* ranges, uint32_t* tile_order, void* stream) {
     g_last_error.clear();
     if (gs_status s = check_camera(cam)) return s;
     if (capacity < 0 || capacity > (int64_t)UINT32_MAX)
@@ -200,14 +200,14 @@ gs_status gs_tile_ranges_async(const gs_camera* cam, const uint64_t* keys, const
         return fail(GS_ERR_INVALID, "gs_tile_ranges_async: NULL or misaligned pointer");
     const int n_tiles = gs::tiles_x(*cam) * gs::tiles_y(*cam);
     return hip_check(gs::launch_tile_ranges(keys, 0u, n_entries_dev, (uint32_t)capacity, n_tiles, ranges,
-                                            (hipStream_t)stream),
+                                            tile_order, (hipStream_t)stream),
                      "tile ranges launch");
 }
 
 gs_status gs_composite_fwd(const gs_camera* cam, const uint32_t* ranges, const uint32_t* point_list,
                            const float* xy_depth, const float* conic_op, const float* rgb,
                            const float bg[3], float* image, float* final_T, uint32_t* n_contrib,
-                           uint32_t* n_examined, void* stream) {
+                           uint32_t* n_examined, const uint32_t* tile_order, void* stream) {
     g_last_error.clear();
     if (gs_status s = check_camera(cam)) return s;
     if (!ranges || !bg || !image || !final_T || !n_contrib)
@@ -217,7 +217,7 @@ gs_status gs_composite_fwd(const gs_camera* cam, const uint32_t* ranges, const u
     const float3 b = make_float3(bg[0], bg[1], bg[2]);
     return hip_check(gs::launch_composite_fwd(*cam, ranges, point_list, (const float4*)xy_depth,
                                               (const float4*)conic_op, (const float4*)rgb, b, image,
-                                              final_T, n_contrib, n_examined, (hipStream_t)stream),
+                                              final_T, n_contrib, n_examined, tile_order, (hipStream_t)stream),
                      "composite fwd launch");
 }
 
@@ -226,7 +226,7 @@ gs_status gs_composite_bwd(const gs_camera* cam, int32_t n, const uint32_t* rang
                            const float* conic_op, const float* rgb, const float bg[3],
                            const float* final_T, const uint32_t* n_contrib,
                            const float* dL_dimage, float* grad_mean2d, float* grad_conic_op,
-                           float* grad_rgb, void* stream) {
+                           float* grad_rgb, const uint32_t* tile_order, void* stream) {
     g_last_error.clear();
     if (gs_status s = check_camera(cam)) return s;
     if (n < 0 || n > GS_MAX_GAUSSIANS) return fail(GS_ERR_INVALID, "n = %d outside [0, %d]", n, GS_MAX_GAUSSIANS);
@@ -241,7 +241,7 @@ gs_status gs_composite_bwd(const gs_camera* cam, int32_t n, const uint32_t* rang
     return hip_check(gs::launch_composite_bwd(*cam, n, ranges, point_list, (const float4*)xy_depth,
                                               (const float4*)conic_op, (const float4*)rgb, b, final_T,
                                               n_contrib, dL_dimage, (float2*)grad_mean2d,
-                                              (float4*)grad_conic_op, (float4*)grad_rgb,
+                                              (float4*)grad_conic_op, (float4*)grad_rgb, tile_order,
                                               (hipStream_t)stream),
                      "composite bwd launch");
 }

@@ -544,6 +544,52 @@ __global__ void k_ranges(const uint64_t* __restrict__ keys, uint32_t n, const ui
     if (i == n - 1 || (uint32_t)(keys[i + 1] >> 32) != t) ranges[2 * (size_t)t + 1] = i + 1;
 }
 
+// Sort class of a tile for heaviest-first scheduling: 255 - (1 + 16 log2
+// of its list length, 16 linear steps per octave), clamped; empty tiles last.
+__device__ __forceinline__ uint32_t heavy_first_key(uint32_t len) {
+    if (len == 0u) return 255u;
+    const int msb = 31 - __clz((int)len);
+    const uint32_t frac = ((len << (31 - msb)) >> 27) & 15u;  // the 4 bits below the leading one
+    return 255u - min(255u, 1u + 16u * (uint32_t)msb + frac);
+}
+
+// order = the tiles in descending order of list length (by class; the
+// order within a class is unspecified). One workgroup of 1024 threads:
+// class histogram, exclusive scan, scatter through per-class cursors.
+__global__ __launch_bounds__(1024) void k_tile_order(const uint32_t* __restrict__ ranges, int n_tiles,
+                                                     uint32_t* __restrict__ order) {
+    __shared__ uint32_t s_hist[kRadix];
+    __shared__ uint32_t s_wsum[kRadix / 64];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (tid < kRadix) s_hist[tid] = 0u;
+    __syncthreads();
+    for (int t = tid; t < n_tiles; t += 1024)
+        atomicAdd(&s_hist[heavy_first_key(ranges[2 * t + 1] - ranges[2 * t])], 1u);
+    __syncthreads();
+    uint32_t h = 0, incl = 0;
+    if (tid < kRadix) {  // waves 0..3: exclusive scan of the 256 class counts
+        h = s_hist[tid];
+        incl = h;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t y = (uint32_t)__shfl_up((int)incl, off, 64);
+            if (lane >= off) incl += y;
+        }
+        if (lane == 63) s_wsum[wave] = incl;
+    }
+    __syncthreads();
+    if (tid < kRadix) {
+        uint32_t pre = 0;
+        for (int w = 0; w < wave; ++w) pre += s_wsum[w];
+        s_hist[tid] = pre + incl - h;  // now the class cursors
+    }
+    __syncthreads();
+    for (int t = tid; t < n_tiles; t += 1024) {
+        const uint32_t c = heavy_first_key(ranges[2 * t + 1] - ranges[2 * t]);
+        order[atomicAdd(&s_hist[c], 1u)] = (uint32_t)t;
+    }
+}
+
 int tile_pass_count(int tile_bits) { return (tile_bits + 7) / 8; }
 
 }  // namespace
@@ -671,7 +717,7 @@ hipError_t launch_fill_u32(uint32_t* p, size_t words, uint32_t v, hipStream_t st
 }
 
 hipError_t launch_tile_ranges(const uint64_t* keys, uint32_t n_entries, const uint64_t* n_dev, uint32_t capacity,
-                              int n_tiles, uint32_t* ranges, hipStream_t stream) {
+                              int n_tiles, uint32_t* ranges, uint32_t* tile_order, hipStream_t stream) {
     // clear every tile (empty tiles keep (0, 0)), then mark the run boundaries
     const size_t words = 2 * (size_t)n_tiles;
     hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, stream,
@@ -680,6 +726,8 @@ hipError_t launch_tile_ranges(const uint64_t* keys, uint32_t n_entries, const ui
     if (grid_n > 0)
         hipLaunchKernelGGL(k_ranges, dim3((grid_n + 255) / 256), dim3(256), 0, stream, keys, n_entries, n_dev,
                            capacity, ranges);
+    if (tile_order)
+        hipLaunchKernelGGL(k_tile_order, dim3(1), dim3(1024), 0, stream, (const uint32_t*)ranges, n_tiles, tile_order);
     return hipGetLastError();
 }
 

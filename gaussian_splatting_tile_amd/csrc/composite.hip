@@ -22,10 +22,13 @@
 //    (in double), so the skip decision is the exactly defined one.
 //  * Both kernels call the same alpha routine, so the backward re-derives
 //    exactly the alphas, skips and clamps the forward saw.
-//  * Tiles are taken in workgroup-id order, which the dispatcher deals out
-//    round-robin over the 8 XCDs, so the dense middle rows of the image are
-//    spread over all of them (contiguous bands per XCD left some XCDs with
-//    most of the work).
+//  * Tiles are taken in the order given by tile_order (heaviest list first,
+//    from the ranges call), else in workgroup-id order. A launch's length is
+//    set by its heaviest tile, which is several times an average slot's
+//    share of the work; starting it first lets it overlap everything else.
+//    Consecutive workgroup ids go round-robin to the 8 XCDs, so the heavy
+//    tiles are spread over all of them (contiguous bands per XCD left some
+//    XCDs with most of the work).
 //  * Backward: per splat, each wave sums nine per-pixel terms over its 16-lane
 //    rows with DPP adds (skipped when no lane contributed) into LDS; the
 //    terms are the colour gradient, dL/do, and the moments of dL/dpower
@@ -118,13 +121,13 @@ __global__ __launch_bounds__(256) void k_composite_fwd(
     const uint32_t* __restrict__ point_list, const float4* __restrict__ xy_depth,
     const float4* __restrict__ conic_op, const float4* __restrict__ rgb, const float3 bg,
     float* __restrict__ image, float* __restrict__ final_T, uint32_t* __restrict__ n_contrib,
-    uint32_t* __restrict__ n_examined) {
+    uint32_t* __restrict__ n_examined, const uint32_t* __restrict__ tile_order) {
     __shared__ float4 s_conic[kBatch];  // A, B, C, opacity
     __shared__ float4 s_xyc[kBatch];    // u, v, r, g
     __shared__ float s_blue[kBatch];
     __shared__ uint32_t s_live[kBatch];
 
-    const int tile = blockIdx.x;
+    const int tile = tile_order ? (int)tile_order[blockIdx.x] : (int)blockIdx.x;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -217,7 +220,29 @@ __device__ __forceinline__ float dpp_row_sum(float x) {
     return x;
 }
 
-// Sum of the 16 row partials of one term.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, true));
+}
+
+// Transpose-reduce of four per-lane values over each 16-lane row: returns,
+// in lane i, the row sum of value (i & 3). Two butterfly steps over lane
+// bits 0 and 1 halve the number of live values each time (a lane keeps the
+// value its bit selects and adds its partner's copy of the same value), so
+// every lane of a quad ends with a different value's quad sum; rotating the
+// row by 4 and by 8 then adds the four quads. 11 instructions for four
+// values, against 16 for four separate row sums. b0, b1: lane bits 0 and 1.
+__device__ __forceinline__ float quad_transpose_row_sum(float a0, float a1, float a2, float a3, bool b0,
+                                                        bool b1) {
+    const float p01 = (b0 ? a1 : a0) + dpp_mov<0xB1>(b0 ? a0 : a1);  // quad_perm [1,0,3,2]
+    const float p23 = (b0 ? a3 : a2) + dpp_mov<0xB1>(b0 ? a2 : a3);
+    float q = (b1 ? p23 : p01) + dpp_mov<0x4E>(b1 ? p01 : p23);      // quad_perm [2,3,0,1]
+    q = dpp_add<0x124>(q);                                           // row_ror:4
+    q = dpp_add<0x128>(q);                                           // row_ror:8
+    return q;
+}
+
+// Sum of the 16 row partials of one term (16-byte aligned).
 __device__ __forceinline__ float part_sum(const float* p) {
     const float4* pv = reinterpret_cast<const float4*>(p);
     const float4 a = pv[0], b = pv[1], c = pv[2], d = pv[3];
@@ -250,19 +275,20 @@ __global__ __launch_bounds__(256) void k_composite_bwd(
     const float4* __restrict__ conic_op, const float4* __restrict__ rgb, const float3 bg,
     const float* __restrict__ final_T, const uint32_t* __restrict__ n_contrib,
     const float* __restrict__ dL_dimage, float* __restrict__ grad_mean2d,
-    float* __restrict__ grad_conic_op, float* __restrict__ grad_rgb) {
+    float* __restrict__ grad_conic_op, float* __restrict__ grad_rgb, const uint32_t* __restrict__ tile_order) {
     __shared__ float4 s_conic[kBwdBatch];  // A, B, C, opacity
     __shared__ float4 s_xyc[kBwdBatch];    // u, v, r, g
     __shared__ float s_blue[kBwdBatch];
     __shared__ uint32_t s_gid[kBwdBatch];
     __shared__ uint32_t s_live[kBwdBatch];
-    __shared__ float s_part[kBwdBatch][9][kParts];  // per-row partial sums
+    __shared__ __align__(16) float s_part[kBwdBatch][9][kParts];  // per-row partial sums
     __shared__ uint32_t s_maxnc[4];
 
-    const int tile = blockIdx.x;
+    const int tile = tile_order ? (int)tile_order[blockIdx.x] : (int)blockIdx.x;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
+    const bool lane_b0 = (lane & 1) != 0, lane_b1 = (lane & 2) != 0;
     const int tx = tile % TX, ty = tile / TX;
     const int px = tx * kTile + (tid & 15);
     const int py = ty * kTile + (tid >> 4);
@@ -342,15 +368,19 @@ __global__ __launch_bounds__(256) void k_composite_bwd(
             const float d2 = dx * d0, d3 = dy * d0, d4 = dy * d1;  // dx^2 dp, dx dy dp, dy^2 dp
             const bool any = use;
             if (__ballot(any) != 0ull) {
-                const float r0 = dpp_row_sum(d0), r1 = dpp_row_sum(d1), r2 = dpp_row_sum(d2);
-                const float r3 = dpp_row_sum(d3), r4 = dpp_row_sum(d4), r5 = dpp_row_sum(d5);
-                const float r6 = dpp_row_sum(d6), r7 = dpp_row_sum(d7), r8 = dpp_row_sum(d8);
-                if ((lane & 15) == 0) {
-                    const int slot = wave * 4 + (lane >> 4);
-                    s_part[k][0][slot] = r0; s_part[k][1][slot] = r1; s_part[k][2][slot] = r2;
-                    s_part[k][3][slot] = r3; s_part[k][4][slot] = r4; s_part[k][5][slot] = r5;
-                    s_part[k][6][slot] = r6; s_part[k][7][slot] = r7; s_part[k][8][slot] = r8;
+                const float qa = quad_transpose_row_sum(d0, d1, d2, d3, lane_b0, lane_b1);
+                const float qb = quad_transpose_row_sum(d4, d5, d6, d7, lane_b0, lane_b1);
+                const float r8 = dpp_row_sum(d8);
+                const int slot = wave * 4 + (lane >> 4);
+                const int j = lane & 15;
+                if (j < 4) {  // lane j of each row holds terms j and 4 + j
+                    // terms 2, 3 (and 6, 7) lie 32 floats after 0, 1: swap slot
+                    // halves for them so the 16 stores hit 16 different banks
+                    const int sl = slot ^ ((j & 2) << 1);
+                    s_part[k][j][sl] = qa;
+                    s_part[k][4 + j][sl] = qb;
                 }
+                if (j == 0) s_part[k][8][slot] = r8;
             }
         }
         __syncthreads();
@@ -383,11 +413,11 @@ hipError_t launch_composite_fwd(const gs_camera& cam, const uint32_t* ranges,
                                 const uint32_t* point_list, const float4* xy_depth,
                                 const float4* conic_op, const float4* rgb, float3 bg,
                                 float* image, float* final_T, uint32_t* n_contrib,
-                                uint32_t* n_examined, hipStream_t stream) {
+                                uint32_t* n_examined, const uint32_t* tile_order, hipStream_t stream) {
     const int TX = tiles_x(cam), TY = tiles_y(cam);
     hipLaunchKernelGGL(k_composite_fwd, dim3(TX * TY), dim3(256), 0, stream, cam.width, cam.height,
                        TX, ranges, point_list, xy_depth, conic_op, rgb, bg, image, final_T,
-                       n_contrib, n_examined);
+                       n_contrib, n_examined, tile_order);
     return hipGetLastError();
 }
 
@@ -396,14 +426,15 @@ hipError_t launch_composite_bwd(const gs_camera& cam, int n, const uint32_t* ran
                                 const float4* conic_op, const float4* rgb, float3 bg,
                                 const float* final_T, const uint32_t* n_contrib,
                                 const float* dL_dimage, float2* grad_mean2d,
-                                float4* grad_conic_op, float4* grad_rgb, hipStream_t stream) {
+                                float4* grad_conic_op, float4* grad_rgb, const uint32_t* tile_order,
+                                hipStream_t stream) {
     if (n > 0)
         hipLaunchKernelGGL(k_zero_grads, dim3((n + 255) / 256), dim3(256), 0, stream, grad_mean2d,
                            grad_conic_op, grad_rgb, n);
     const int TX = tiles_x(cam), TY = tiles_y(cam);
     hipLaunchKernelGGL(k_composite_bwd, dim3(TX * TY), dim3(256), 0, stream, cam.width, cam.height,
                        TX, ranges, point_list, xy_depth, conic_op, rgb, bg, final_T, n_contrib,
-                       dL_dimage, (float*)grad_mean2d, (float*)grad_conic_op, (float*)grad_rgb);
+                       dL_dimage, (float*)grad_mean2d, (float*)grad_conic_op, (float*)grad_rgb, tile_order);
     return hipGetLastError();
 }
 

@@ -87,21 +87,23 @@ hipError_t launch_bin_and_sort(const gs_camera& cam, int n, const float4* xy_dep
 hipError_t launch_fill_u32(uint32_t* p, size_t words, uint32_t v, hipStream_t stream);
 
 // Per-tile ranges. The entry count is n_entries, or, when n_dev is given,
-// *n_dev if it does not exceed capacity and 0 otherwise.
+// *n_dev if it does not exceed capacity and 0 otherwise. If tile_order is
+// given it receives the tiles, heaviest list first.
 hipError_t launch_tile_ranges(const uint64_t* keys, uint32_t n_entries, const uint64_t* n_dev, uint32_t capacity,
-                              int n_tiles, uint32_t* ranges, hipStream_t stream);
+                              int n_tiles, uint32_t* ranges, uint32_t* tile_order, hipStream_t stream);
 
 hipError_t launch_composite_fwd(const gs_camera& cam, const uint32_t* ranges,
                                 const uint32_t* point_list, const float4* xy_depth,
                                 const float4* conic_op, const float4* rgb, float3 bg,
                                 float* image, float* final_T, uint32_t* n_contrib,
-                                uint32_t* n_examined, hipStream_t stream);
+                                uint32_t* n_examined, const uint32_t* tile_order, hipStream_t stream);
 
 hipError_t launch_composite_bwd(const gs_camera& cam, int n, const uint32_t* ranges,
                                 const uint32_t* point_list, const float4* xy_depth,
                                 const float4* conic_op, const float4* rgb, float3 bg,
                                 const float* final_T, const uint32_t* n_contrib,
                                 const float* dL_dimage, float2* grad_mean2d,
-                                float4* grad_conic_op, float4* grad_rgb, hipStream_t stream);
+                                float4* grad_conic_op, float4* grad_rgb, const uint32_t* tile_order,
+                                hipStream_t stream);
 
 }  // namespace gs

@@ -170,31 +170,35 @@ def bin_and_sort_async(cam, xy_depth, tiles_touched, buffers: BinBuffers, stream
     return buffers.keys, buffers.point_list
 
 
-def tile_ranges_async(cam, buffers: BinBuffers, out=None, stream=None):
-    """gs_tile_ranges_async over the last asynchronous binning into buffers."""
+def tile_ranges_async(cam, buffers: BinBuffers, out=None, order=None, stream=None):
+    """gs_tile_ranges_async over the last asynchronous binning into buffers.
+    `order` (int32 [TX*TY]) receives the heaviest-first tile schedule if given."""
     c = _cam(cam)
     if out is None:
         TX, TY = tiles_xy(dict(width=c.width, height=c.height))
         out = torch.empty((TX * TY, 2), dtype=torch.int32, device=buffers.keys.device)
     _lib.check(_lib.load().gs_tile_ranges_async(ctypes.byref(c), _ptr(buffers.keys), _ptr(buffers.n_entries_dev),
-                                                buffers.capacity, _ptr(out, torch.int32), _stream(stream)))
+                                                buffers.capacity, _ptr(out, torch.int32),
+                                                _ptr(order, torch.int32, "order"), _stream(stream)))
     return out
 
 
-def tile_ranges(cam, keys, n_entries: int, out=None, stream=None):
-    """gs_tile_ranges. Returns ranges int32 [TX*TY, 2] (uint32 values)."""
+def tile_ranges(cam, keys, n_entries: int, out=None, order=None, stream=None):
+    """gs_tile_ranges. Returns ranges int32 [TX*TY, 2] (uint32 values); `order`
+    (int32 [TX*TY]) receives the heaviest-first tile schedule if given."""
     TX, TY = tiles_xy(cam if isinstance(cam, dict) else
                       dict(width=cam.width, height=cam.height))
     if out is None:
         out = torch.empty((TX * TY, 2), dtype=torch.int32, device=keys.device)
     c = _cam(cam)
     _lib.check(_lib.load().gs_tile_ranges(ctypes.byref(c), _ptr(keys, torch.int64, "keys"),
-                                          int(n_entries), _ptr(out, torch.int32), _stream(stream)))
+                                          int(n_entries), _ptr(out, torch.int32),
+                                          _ptr(order, torch.int32, "order"), _stream(stream)))
     return out
 
 
 def composite_fwd(cam, ranges, point_list, xy_depth, conic_op, rgb, bg=(0.0, 0.0, 0.0),
-                  with_examined=False, out=None, stream=None):
+                  with_examined=False, out=None, order=None, stream=None):
     """gs_composite_fwd. Returns dict image [3,H,W], final_T [H,W], n_contrib [H,W] (int32),
     and n_examined [H,W] when requested."""
     W, H = (cam["width"], cam["height"]) if isinstance(cam, dict) else (cam.width, cam.height)
@@ -211,12 +215,13 @@ def composite_fwd(cam, ranges, point_list, xy_depth, conic_op, rgb, bg=(0.0, 0.0
         ctypes.byref(c), _ptr(ranges, torch.int32, "ranges"), _ptr(point_list, torch.int32, "point_list"),
         _ptr(xy_depth, torch.float32), _ptr(conic_op, torch.float32), _ptr(rgb, torch.float32),
         ctypes.cast(bgc, ctypes.c_void_p), _ptr(out["image"]), _ptr(out["final_T"]),
-        _ptr(out["n_contrib"]), _ptr(out.get("n_examined")), _stream(stream)))
+        _ptr(out["n_contrib"]), _ptr(out.get("n_examined")), _ptr(order, torch.int32, "order"),
+        _stream(stream)))
     return out
 
 
 def composite_bwd(cam, n, ranges, point_list, xy_depth, conic_op, rgb, final_T, n_contrib,
-                  dL_dimage, bg=(0.0, 0.0, 0.0), out=None, stream=None):
+                  dL_dimage, bg=(0.0, 0.0, 0.0), out=None, order=None, stream=None):
     """gs_composite_bwd. Returns dict grad_mean2d [n,2], grad_conic_op [n,4], grad_rgb [n,4]."""
     dev = xy_depth.device
     if out is None:
@@ -231,7 +236,8 @@ def composite_bwd(cam, n, ranges, point_list, xy_depth, conic_op, rgb, final_T, 
         _ptr(conic_op, torch.float32), _ptr(rgb, torch.float32), ctypes.cast(bgc, ctypes.c_void_p),
         _ptr(final_T, torch.float32, "final_T"), _ptr(n_contrib, torch.int32, "n_contrib"),
         _ptr(dL_dimage, torch.float32, "dL_dimage"), _ptr(out["grad_mean2d"]),
-        _ptr(out["grad_conic_op"]), _ptr(out["grad_rgb"]), _stream(stream)))
+        _ptr(out["grad_conic_op"]), _ptr(out["grad_rgb"]), _ptr(order, torch.int32, "order"),
+        _stream(stream)))
     return out
 
 
@@ -269,13 +275,16 @@ class Rasterizer:
         pre = preprocess(c, scene.means, scene.scales, scene.quats, scene.opacity, scene.sh,
                          scene.sh_degree, scene.rgb)
         keys, point_list, E = bin_and_sort(c, pre["xy_depth"], pre["tiles_touched"], self.bins)
-        ranges = tile_ranges(cam, keys, E)
+        TX, TY = tiles_xy(cam)
+        order = torch.empty((TX * TY,), dtype=torch.int32, device=self.device)
+        ranges = tile_ranges(cam, keys, E, order=order)
         fwd = composite_fwd(cam, ranges, point_list, pre["xy_depth"], pre["conic_op"], pre["rgb"], bg,
-                            with_examined=with_examined)
+                            with_examined=with_examined, order=order)
         out = dict(pre)
-        out.update(keys=keys, point_list=point_list, n_entries=E, ranges=ranges, **fwd)
+        out.update(keys=keys, point_list=point_list, n_entries=E, ranges=ranges, tile_order=order, **fwd)
         return out
 
     def backward(self, cam: dict, scene: Scene, fwd: dict, dL_dimage, bg=(0.0, 0.0, 0.0)):
         return composite_bwd(cam, scene.n, fwd["ranges"], fwd["point_list"], fwd["xy_depth"],
-                             fwd["conic_op"], fwd["rgb"], fwd["final_T"], fwd["n_contrib"], dL_dimage, bg)
+                             fwd["conic_op"], fwd["rgb"], fwd["final_T"], fwd["n_contrib"], dL_dimage, bg,
+                             order=fwd.get("tile_order"))

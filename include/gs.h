@@ -182,12 +182,18 @@ gs_status gs_bin_and_sort_async(const gs_camera* cam, int32_t n, const float* xy
  * gs_tile_ranges - per-tile [start, end) of the sorted entries.
  * (zenn 4.4.1-4.4.2; "rigel" README "Binning": the range kernel.)
  *
- *   keys       [n_entries] sorted keys from gs_bin_and_sort
- *   n_entries  E
- *   ranges     out [TX*TY][2] uint32: (start, end); (0, 0) for an empty tile
+ *   keys        [n_entries] sorted keys from gs_bin_and_sort
+ *   n_entries   E
+ *   ranges      out [TX*TY][2] uint32: (start, end); (0, 0) for an empty tile
+ *   tile_order  out [TX*TY] uint32, or NULL: a schedule for the compositing
+ *               calls, every tile once, in descending order of list length
+ *               (by classes of 1/16 octave; order within a class
+ *               unspecified). It changes no result, only the order in which
+ *               tiles are processed: a compositing launch lasts at least as
+ *               long as its heaviest tile, so that tile is started first.
  * ------------------------------------------------------------------- */
 gs_status gs_tile_ranges(const gs_camera* cam, const uint64_t* keys, int64_t n_entries,
-                         uint32_t* ranges, void* stream);
+                         uint32_t* ranges, uint32_t* tile_order, void* stream);
 
 /* ---------------------------------------------------------------------
  * gs_tile_ranges_async - gs_tile_ranges with the entry count in device
@@ -197,9 +203,10 @@ gs_status gs_tile_ranges(const gs_camera* cam, const uint64_t* keys, int64_t n_e
  *   n_entries_dev  device uint64 (8-byte aligned): E
  *   capacity       the capacity given to gs_bin_and_sort_async
  *   ranges         out [TX*TY][2] uint32; every tile (0, 0) when E > capacity
+ *   tile_order     out [TX*TY] uint32, or NULL: as gs_tile_ranges
  * ------------------------------------------------------------------- */
 gs_status gs_tile_ranges_async(const gs_camera* cam, const uint64_t* keys, const uint64_t* n_entries_dev,
-                               int64_t capacity, uint32_t* ranges, void* stream);
+                               int64_t capacity, uint32_t* ranges, uint32_t* tile_order, void* stream);
 
 /* ---------------------------------------------------------------------
  * gs_composite_fwd - front-to-back alpha compositing per tile.
@@ -221,11 +228,14 @@ gs_status gs_tile_ranges_async(const gs_camera* cam, const uint64_t* keys, const
  *               the last contributing splat, 0 if none
  *   n_examined  out [H][W] uint32, or NULL: splats evaluated before the
  *               pixel stopped (diagnostic; pixel-splat evaluations)
+ *   tile_order  [TX*TY] uint32 from gs_tile_ranges, or NULL (tile-id order):
+ *               the order tiles are processed in; any permutation of the
+ *               tiles gives the same results
  * ------------------------------------------------------------------- */
 gs_status gs_composite_fwd(const gs_camera* cam, const uint32_t* ranges, const uint32_t* point_list,
                            const float* xy_depth, const float* conic_op, const float* rgb,
                            const float bg[3], float* image, float* final_T, uint32_t* n_contrib,
-                           uint32_t* n_examined, void* stream);
+                           uint32_t* n_examined, const uint32_t* tile_order, void* stream);
 
 /* ---------------------------------------------------------------------
  * gs_composite_bwd - reverse walk of the compositing, per tile.
@@ -251,13 +261,14 @@ gs_status gs_composite_fwd(const gs_camera* cam, const uint32_t* ranges, const u
  *   grad_mean2d       out [n][2]: (du, dv)
  *   grad_conic_op     out [n][4]: (dA, dB, dC, dopacity)
  *   grad_rgb          out [n][4]: (dr, dg, db, 0)
+ *   tile_order        as gs_composite_fwd, or NULL
  * ------------------------------------------------------------------- */
 gs_status gs_composite_bwd(const gs_camera* cam, int32_t n, const uint32_t* ranges,
                            const uint32_t* point_list, const float* xy_depth,
                            const float* conic_op, const float* rgb, const float bg[3],
                            const float* final_T, const uint32_t* n_contrib,
                            const float* dL_dimage, float* grad_mean2d, float* grad_conic_op,
-                           float* grad_rgb, void* stream);
+                           float* grad_rgb, const uint32_t* tile_order, void* stream);
 
 #ifdef __cplusplus
 }

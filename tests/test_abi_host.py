@@ -83,13 +83,13 @@ def test_invalid_arguments_rejected_before_launch(gs):
     # bad image sizes / focal lengths
     for bad in (_cam(width=0), _cam(height=-3), _cam(width=20000), _cam(fx=0.0),
                 _cam(fy=float("nan")), _cam(cx=float("inf"))):
-        assert gs.gs_tile_ranges(ctypes.byref(bad), None, 0, dummy, None) == _lib.GS_ERR_INVALID
+        assert gs.gs_tile_ranges(ctypes.byref(bad), None, 0, dummy, None, None) == _lib.GS_ERR_INVALID
     # n == 0 is a valid no-op
     assert gs.gs_preprocess(ctypes.byref(c), 0, None, None, None, None, None, 0, None, None, None,
                             None, None, None) == _lib.GS_OK
     # misaligned float4 buffer
     assert gs.gs_composite_fwd(ctypes.byref(c), dummy, dummy, P(260), dummy, dummy,
-                               (ctypes.c_float * 3)(), dummy, dummy, dummy, None, None) == _lib.GS_ERR_INVALID
+                               (ctypes.c_float * 3)(), dummy, dummy, dummy, None, None, None) == _lib.GS_ERR_INVALID
 
 
 def test_bin_scratch_size_query(gs):
@@ -141,6 +141,6 @@ def test_async_entry_points_validate(gs):
     for bad in (None, P(260)):
         assert gs.gs_bin_and_sort_async(ctypes.byref(c), 1000, P(256), P(256), P(256), P(256), 5000,
                                         P(256), ctypes.byref(nb), bad, None) == _lib.GS_ERR_INVALID
-    assert gs.gs_tile_ranges_async(ctypes.byref(c), P(256), None, 10, P(256), None) == _lib.GS_ERR_INVALID
-    assert gs.gs_tile_ranges_async(ctypes.byref(c), P(256), P(260), 10, P(256), None) == _lib.GS_ERR_INVALID
-    assert gs.gs_tile_ranges_async(ctypes.byref(c), P(256), P(256), -1, P(256), None) == _lib.GS_ERR_INVALID
+    assert gs.gs_tile_ranges_async(ctypes.byref(c), P(256), None, 10, P(256), None, None) == _lib.GS_ERR_INVALID
+    assert gs.gs_tile_ranges_async(ctypes.byref(c), P(256), P(260), 10, P(256), None, None) == _lib.GS_ERR_INVALID
+    assert gs.gs_tile_ranges_async(ctypes.byref(c), P(256), P(256), -1, P(256), None, None) == _lib.GS_ERR_INVALID

@@ -255,3 +255,38 @@ def test_async_empty_scene():
     ranges = gs.tile_ranges_async(c, bins)
     assert bins.entries() == 0
     assert not ranges.any()
+
+
+def test_tile_order_is_a_heaviest_first_schedule(orc):
+    """The schedule from the ranges call is a permutation of the tiles in
+    non-increasing length class, and rendering in it gives bit-identical
+    forward results and equal gradients to tile-id order."""
+    import gaussian_splatting_tile_amd as gs
+    import torch
+    from gpu_helpers import to_np
+    scene, cam, dLdI, ofwd, obwd = workload(orc, "cfg2")
+    g, out, sc, r = gpu_forward(cam, scene, capacity=1 << 22)
+    order = to_np(out["tile_order"]).view(np.uint32).astype(np.int64)
+    n_tiles = g["ranges"].shape[0]
+    assert np.array_equal(np.sort(order), np.arange(n_tiles))
+    L = (g["ranges"][:, 1].astype(np.int64) - g["ranges"][:, 0])[order]
+    # length classes: 16 linear steps per octave (the 4 bits below the
+    # leading one), empty tiles lowest; they never increase along the schedule
+    msb = np.floor(np.log2(np.maximum(L, 1))).astype(np.int64)
+    frac = ((L << (31 - msb)) >> 27) & 15
+    cls = np.where(L == 0, -1, np.minimum(255, 1 + 16 * msb + frac))
+    assert (np.diff(cls) <= 0).all()
+    assert L[0] >= L.max() // 2
+    c = gs.camera(cam)
+    plain = gs.composite_fwd(c, out["ranges"], out["point_list"], out["xy_depth"], out["conic_op"], out["rgb"])
+    torch.cuda.synchronize()
+    for k in ("image", "final_T", "n_contrib"):
+        assert_bits_equal(to_np(plain[k]), g[k], k)
+    grads = gpu_backward(cam, sc, out, dLdI)
+    ordered = gs.composite_bwd(c, sc.n, out["ranges"], out["point_list"], out["xy_depth"], out["conic_op"],
+                               out["rgb"], out["final_T"], out["n_contrib"],
+                               torch.from_numpy(np.ascontiguousarray(dLdI, np.float32)).cuda(),
+                               order=out["tile_order"])
+    torch.cuda.synchronize()
+    compare_gradients({k: to_np(v).astype(np.float64) for k, v in ordered.items()}, obwd)
+    compare_gradients(grads, obwd)
