@@ -21,6 +21,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -50,22 +51,66 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(name: str):
-    """Time the oracle (single thread, as it stands) on one full frame of the
-    same workload, forward and backward."""
-    import numpy as np
+def cpu_baseline(name: str, min_seconds: float = 10.0, max_frames: int = 8):
+    """Time the oracle (single thread, as it stands) on whole frames of the
+    same workload, forward and backward, repeating the frame until about
+    min_seconds of CPU work have been timed."""
     import oracle
     import synth
     scene, cam, dLdI = synth.config_scene(name)
-    t0 = time.perf_counter()
-    fwd = oracle.render_fwd(cam, scene)
-    oracle.composite_bwd(cam, scene["n"], fwd["ranges"], fwd["point_list"], fwd["xy_depth"],
-                         fwd["conic_op"], fwd["rgb"], fwd["final_T"], fwd["n_contrib"], dLdI)
-    dt = time.perf_counter() - t0
-    return {"value": round(1.0 / dt, 4), "unit": "frames/s", "cores": 1, "kind": "oracle",
-            "sample": f"one full {name} frame (preprocess, bin, sort, ranges, forward and backward "
-                      f"compositing), single-threaded, {dt:.2f} s",
-            "seconds": round(dt, 3)}
+    frames, total = 0, 0.0
+    while frames < max_frames and (frames == 0 or total < min_seconds):
+        t0 = time.perf_counter()
+        fwd = oracle.render_fwd(cam, scene)
+        oracle.composite_bwd(cam, scene["n"], fwd["ranges"], fwd["point_list"], fwd["xy_depth"],
+                             fwd["conic_op"], fwd["rgb"], fwd["final_T"], fwd["n_contrib"], dLdI)
+        total += time.perf_counter() - t0
+        frames += 1
+    return {"value": round(frames / total, 4), "unit": "frames/s", "cores": 1, "kind": "oracle",
+            "sample": f"{frames} full {name} frame(s) (preprocess, bin, sort, ranges, forward and "
+                      f"backward compositing), single-threaded, {total:.2f} s in total",
+            "seconds": round(total, 3)}
+
+
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "k_composite_bwd_cfg2_hbm_traffic.md")
+KERNEL_SOURCE = os.path.join(ROOT, "gaussian_splatting_tile_amd", "csrc", "composite.hip")
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the backward compositing kernel, from the
+    committed rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE, each
+    scaled by what the counter reads for a copy of known size). None when
+    the summary is missing, covers another workload, or was taken on a
+    different version of the kernel source."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_SUMMARY).read()
+        src = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    fields = dict(re.findall(r"^- (\w+): `([^`]*)`", text, flags=re.M))
+    if fields.get("workload") != workload or fields.get("source_sha256") != src:
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(mib: int, repeats: int = 3):
+    """Device-to-device copies of a known size, so that a counter run over
+    this process also records what FETCH_SIZE and WRITE_SIZE read for a
+    plain copy kernel (mib MiB read and mib MiB written per launch)."""
+    import torch
+    n = (mib << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(repeats):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] copy calibration: {repeats} copies of {mib} MiB ({n * 4} bytes read and written each)")
+    del src, dst
 
 
 def main():
@@ -77,6 +122,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tile-order", choices=("heavy-first", "index"), default="index",
                     help="tile schedule of the compositing kernels (results are identical)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="first run device copies of this many MiB (for HBM counter scaling)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -94,6 +141,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
+    if args.copy_calibration_mib > 0:
+        copy_calibration(args.copy_calibration_mib)
 
     log(f"[bench] generating {args.workload}")
     scene_np, cam, dLdI_np = synth.config_scene(args.workload)
@@ -222,7 +271,7 @@ def main():
         "roofline": {"bound": "alu", "kernel": "k_composite_bwd",
                      "achieved": round(achieved / 1e12, 4), "peak": PEAK_FP32_VECTOR / 1e12,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_VECTOR, 5),
-                     "traffic": None,
+                     "traffic": measured_traffic(args.workload),
                      "per_unit": f"{FLOPS_PER_BWD_EVAL:.0f} flop per backward pixel-splat eval "
                                  f"x {evals_bwd} evals per launch"},
         "secondary": {
