@@ -89,6 +89,11 @@ def lib():
         _lib.orc_duplicate.argtypes = [ctypes.POINTER(Camera), ctypes.c_int32, P, P, P, P, P]
         _lib.orc_sort_pairs.restype = None
         _lib.orc_sort_pairs.argtypes = [P, P, ctypes.c_int64]
+        _lib.orc_preprocess_bwd.restype = ctypes.c_int
+        _lib.orc_preprocess_bwd.argtypes = [ctypes.POINTER(Camera), ctypes.c_int32, P, P, P, P, P,
+                                            ctypes.c_int32, P, P, P, P, P, P, P, P, P, P]
+        _lib.orc_project_f64.restype = ctypes.c_int
+        _lib.orc_project_f64.argtypes = [ctypes.POINTER(Camera), P, P, P, P, ctypes.c_int32, P, P]
     return _lib
 
 
@@ -172,6 +177,54 @@ def preprocess(cam: dict, scene: dict):
     if rc != 0:
         raise ValueError("orc_preprocess rejected its arguments")
     return out
+
+
+def preprocess_bwd(cam: dict, scene: dict, grad_mean2d, grad_conic_op, grad_rgb):
+    """Backward of preprocess. Upstream gradients [n,2], [n,4], [n,4] (any
+    float type, used as float64). Returns float64 dict grad_means [3,n],
+    grad_scales [3,n], grad_quats [4,n], grad_opacity [n], and grad_sh
+    [(d+1)^2*3, n] (coefficient-major, as the sh input) or grad_rgb_in [3,n]."""
+    n = int(scene["n"])
+    means = _c(scene["means"], np.float32)
+    scales = _c(scene["scales"], np.float32)
+    quats = _c(scene["quats"], np.float32)
+    opacity = _c(scene["opacity"], np.float32)
+    sh = scene.get("sh")
+    sh = None if sh is None else _c(sh, np.float32)
+    rgb_in = scene.get("rgb")
+    rgb_in = None if rgb_in is None else _c(rgb_in, np.float32)
+    deg = int(scene.get("sh_degree", 0))
+    gm, gc, gr = (_c(a, np.float64) for a in (grad_mean2d, grad_conic_op, grad_rgb))
+    out = dict(grad_means=np.zeros((3, n)), grad_scales=np.zeros((3, n)), grad_quats=np.zeros((4, n)),
+               grad_opacity=np.zeros(n))
+    if sh is not None:
+        out["grad_sh"] = np.zeros((3 * (deg + 1) ** 2, n))
+    else:
+        out["grad_rgb_in"] = np.zeros((3, n))
+    c = make_camera(cam)
+    rc = lib().orc_preprocess_bwd(ctypes.byref(c), n, _p(means), _p(scales), _p(quats), _p(opacity),
+                                  _p(sh), deg, _p(rgb_in), _p(gm), _p(gc), _p(gr), _p(out["grad_means"]),
+                                  _p(out["grad_scales"]), _p(out["grad_quats"]), _p(out["grad_opacity"]),
+                                  _p(out.get("grad_sh")), _p(out.get("grad_rgb_in")))
+    if rc != 0:
+        raise ValueError("orc_preprocess_bwd rejected its arguments")
+    return out
+
+
+def project_f64(cam: dict, mean, scale, quat, sh_coef=None, rgb=None):
+    """The projection of one Gaussian in float64. sh_coef: [n_coef, 3] or
+    None (then rgb [3]). Returns None when culled, else dict u, v, conic
+    (A, B, C), rgb [3], clamp (x, y)."""
+    m, s, q = (_c(a, np.float64) for a in (mean, scale, quat))
+    shc = None if sh_coef is None else _c(sh_coef, np.float64)
+    n_coef = 0 if shc is None else shc.shape[0]
+    rgbc = None if rgb is None else _c(rgb, np.float64)
+    out = np.zeros(10)
+    c = make_camera(cam)
+    if not lib().orc_project_f64(ctypes.byref(c), _p(m), _p(s), _p(q), _p(shc), n_coef, _p(rgbc), _p(out)):
+        return None
+    return dict(u=out[0], v=out[1], conic=out[2:5].copy(), rgb=out[5:8].copy(),
+                clamp=(bool(out[8]), bool(out[9])))
 
 
 def bin_and_sort(cam: dict, xy_depth, tiles_touched):

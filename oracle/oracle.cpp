@@ -93,24 +93,29 @@ struct ShConstants {
 };
 const ShConstants SH;
 
-void sh_basis(float x, float y, float z, float Y[16]) {
-    const float xx = x * x, yy = y * y, zz = z * z;
-    Y[0]  = SH.k[0];
-    Y[1]  = SH.k[1] * y;
-    Y[2]  = SH.k[2] * z;
-    Y[3]  = SH.k[3] * x;
-    Y[4]  = SH.k[4] * (x * y);
-    Y[5]  = SH.k[5] * (y * z);
-    Y[6]  = SH.k[6] * ((2.0f * zz - xx) - yy);
-    Y[7]  = SH.k[7] * (z * x);
-    Y[8]  = SH.k[8] * (xx - yy);
-    Y[9]  = SH.k[9] * ((3.0f * xx - yy) * y);
-    Y[10] = SH.k[10] * ((x * y) * z);
-    Y[11] = SH.k[11] * (((4.0f * zz - xx) - yy) * y);
-    Y[12] = SH.k[12] * (z * ((2.0f * zz - 3.0f * xx) - 3.0f * yy));
-    Y[13] = SH.k[13] * (x * ((4.0f * zz - xx) - yy));
-    Y[14] = SH.k[14] * ((xx - yy) * z);
-    Y[15] = SH.k[15] * (x * (xx - 3.0f * yy));
+template <typename F>
+void sh_basis(F x, F y, F z, F Y[16]) {
+    const F xx = x * x, yy = y * y, zz = z * z;
+    const F* k = nullptr;
+    F kk[16];
+    for (int i = 0; i < 16; ++i) kk[i] = (F)SH.k[i];
+    k = kk;
+    Y[0]  = k[0];
+    Y[1]  = k[1] * y;
+    Y[2]  = k[2] * z;
+    Y[3]  = k[3] * x;
+    Y[4]  = k[4] * (x * y);
+    Y[5]  = k[5] * (y * z);
+    Y[6]  = k[6] * (((F)2 * zz - xx) - yy);
+    Y[7]  = k[7] * (z * x);
+    Y[8]  = k[8] * (xx - yy);
+    Y[9]  = k[9] * (((F)3 * xx - yy) * y);
+    Y[10] = k[10] * ((x * y) * z);
+    Y[11] = k[11] * ((((F)4 * zz - xx) - yy) * y);
+    Y[12] = k[12] * (z * (((F)2 * zz - (F)3 * xx) - (F)3 * yy));
+    Y[13] = k[13] * (x * (((F)4 * zz - xx) - yy));
+    Y[14] = k[14] * ((xx - yy) * z);
+    Y[15] = k[15] * (x * (xx - (F)3 * yy));
 }
 
 // Tile span of a splat: the tiles its 2r square touches. [learn-gs]
@@ -137,6 +142,330 @@ inline uint32_t float_bits(float f) {
     return b;
 }
 
+// Projection of one Gaussian: every continuous quantity of the preprocess,
+// in the real type F with the operation order below. F = float is the
+// preprocess itself (bit-exact reference for the kernels); F = double is the
+// same function widened, used only as the function that finite differences
+// of the projection backward are taken of.
+//   [rigel] "Projection": camera transform, explicit pinhole, EWA
+//     Sigma_2d = J W Sigma W^T J^T + 0.3 I with x/z, y/z clamped to 1.3x the
+//     half-width before J is built; conic; 3-sigma radius; radius 0 for
+//     anything behind the near plane, degenerate or off-screen.
+//   [zenn] 2.1.1: Sigma = R S S^T R^T; 2.1.2: J; 2.3.1: conic;
+//     2.3.3: lambda_max with the 0.1 discriminant floor; 2.2.3: SH colour.
+//   [learn-gs] prep_splats: z > Z_NEAR cull, u = fx x/z + cx, det > 0.
+// sh_g: this Gaussian's coefficients [k][channel] (n_coef of them), or
+// NULL, then rgb_g holds its colour. Returns false when the Gaussian is
+// culled before the tile span is known (near plane, non-finite, zero
+// quaternion, det <= 0); the span cull is the caller's.
+template <typename F>
+struct Projected {
+    F u, v, z, r;
+    F a, b, c;     // Sigma_2d with the dilation
+    F A, B, C;     // conic
+    F col[3];
+    bool clamp_x, clamp_y;  // was x/z (y/z) clamped when J was built
+};
+
+template <typename F>
+bool project_gaussian(const orc_camera* cam, const F m[3], const F s3[3], const F q[4],
+                      const F* sh_g, int n_coef, const F* rgb_g, Projected<F>* out) {
+    const F W[9] = {(F)cam->R[0], (F)cam->R[1], (F)cam->R[2], (F)cam->R[3], (F)cam->R[4],
+                    (F)cam->R[5], (F)cam->R[6], (F)cam->R[7], (F)cam->R[8]};
+    const F fx = (F)cam->fx, fy = (F)cam->fy;
+    const F mx = m[0], my = m[1], mz = m[2];
+
+    // Camera space.
+    const F px = ((W[0] * mx + W[1] * my) + W[2] * mz) + (F)cam->t[0];
+    const F py = ((W[3] * mx + W[4] * my) + W[5] * mz) + (F)cam->t[1];
+    const F pz = ((W[6] * mx + W[7] * my) + W[8] * mz) + (F)cam->t[2];
+    if (!(pz > (F)Z_NEAR)) return false;  // also rejects NaN
+
+    // Pinhole projection of the centre.
+    const F u = (fx * px) / pz + (F)cam->cx;
+    const F v = (fy * py) / pz + (F)cam->cy;
+    if (!std::isfinite(u) || !std::isfinite(v)) return false;
+
+    // Jacobian of the pinhole at the centre, x/z and y/z clamped.
+    const F limx = (F)FRUSTUM_CLAMP * (((F)0.5 * (F)cam->width) / fx);
+    const F limy = (F)FRUSTUM_CLAMP * (((F)0.5 * (F)cam->height) / fy);
+    const F tx = px / pz, ty = py / pz;
+    const F xj = std::min(limx, std::max(-limx, tx)) * pz;
+    const F yj = std::min(limy, std::max(-limy, ty)) * pz;
+    const F zz = pz * pz;
+    const F J00 = fx / pz;
+    const F J02 = -(fx * xj) / zz;
+    const F J11 = fy / pz;
+    const F J12 = -(fy * yj) / zz;
+
+    // Rotation from the quaternion, normalised here.
+    F qw = q[0], qx = q[1], qy = q[2], qz = q[3];
+    const F qn = std::sqrt(((qw * qw + qx * qx) + qy * qy) + qz * qz);
+    if (!(qn > (F)0)) return false;
+    qw = qw / qn; qx = qx / qn; qy = qy / qn; qz = qz / qn;
+    F Rq[3][3];
+    Rq[0][0] = (F)1 - (F)2 * (qy * qy + qz * qz);
+    Rq[0][1] = (F)2 * (qx * qy - qw * qz);
+    Rq[0][2] = (F)2 * (qx * qz + qw * qy);
+    Rq[1][0] = (F)2 * (qx * qy + qw * qz);
+    Rq[1][1] = (F)1 - (F)2 * (qx * qx + qz * qz);
+    Rq[1][2] = (F)2 * (qy * qz - qw * qx);
+    Rq[2][0] = (F)2 * (qx * qz - qw * qy);
+    Rq[2][1] = (F)2 * (qy * qz + qw * qx);
+    Rq[2][2] = (F)1 - (F)2 * (qx * qx + qy * qy);
+
+    // Sigma = (R S)(R S)^T.
+    F M[3][3];
+    for (int i = 0; i < 3; ++i)
+        for (int j = 0; j < 3; ++j) M[i][j] = Rq[i][j] * s3[j];
+    F Sig[3][3];
+    for (int i = 0; i < 3; ++i)
+        for (int j = 0; j < 3; ++j)
+            Sig[i][j] = (M[i][0] * M[j][0] + M[i][1] * M[j][1]) + M[i][2] * M[j][2];
+
+    // T = J W (J's structural zeros skipped), U = T Sigma, Sigma_2d = U T^T.
+    F T[2][3];
+    for (int j = 0; j < 3; ++j) {
+        T[0][j] = J00 * W[0 * 3 + j] + J02 * W[2 * 3 + j];
+        T[1][j] = J11 * W[1 * 3 + j] + J12 * W[2 * 3 + j];
+    }
+    F U[2][3];
+    for (int i = 0; i < 2; ++i)
+        for (int j = 0; j < 3; ++j)
+            U[i][j] = (T[i][0] * Sig[0][j] + T[i][1] * Sig[1][j]) + T[i][2] * Sig[2][j];
+    const F a = ((U[0][0] * T[0][0] + U[0][1] * T[0][1]) + U[0][2] * T[0][2]) + (F)DILATION;
+    const F b = (U[0][0] * T[1][0] + U[0][1] * T[1][1]) + U[0][2] * T[1][2];
+    const F c = ((U[1][0] * T[1][0] + U[1][1] * T[1][1]) + U[1][2] * T[1][2]) + (F)DILATION;
+
+    // Conic and degenerate cull (non-finite covariances are culled too).
+    if (!std::isfinite(a) || !std::isfinite(b) || !std::isfinite(c)) return false;
+    const F det = a * c - b * b;
+    if (!(det > (F)0) || !std::isfinite(det)) return false;
+
+    // Bounding radius: 3 sqrt(lambda_max), discriminant floored at 0.1.
+    const F mid = (F)0.5 * (a + c);
+    const F lam = mid + std::sqrt(std::max(mid * mid - det, (F)DISC_FLOOR));
+    const F r = std::ceil((F)SIGMA * std::sqrt(lam));
+    if (!std::isfinite(r)) return false;
+
+    // Colour: SH evaluated at the unit direction from the camera centre.
+    if (sh_g) {
+        F dx = mx - (F)cam->campos[0], dy = my - (F)cam->campos[1], dz = mz - (F)cam->campos[2];
+        const F dn = std::sqrt((dx * dx + dy * dy) + dz * dz);
+        dx = dx / dn; dy = dy / dn; dz = dz / dn;
+        F Y[16];
+        sh_basis(dx, dy, dz, Y);
+        for (int ch = 0; ch < 3; ++ch) {
+            F acc = sh_g[0 * 3 + ch] * Y[0];
+            for (int k = 1; k < n_coef; ++k) acc = acc + sh_g[k * 3 + ch] * Y[k];
+            out->col[ch] = acc;
+        }
+    } else {
+        for (int ch = 0; ch < 3; ++ch) out->col[ch] = rgb_g[ch];
+    }
+    out->u = u; out->v = v; out->z = pz; out->r = r;
+    out->a = a; out->b = b; out->c = c;
+    out->A = c / det; out->B = -b / det; out->C = a / det;
+    out->clamp_x = !(tx >= -limx && tx <= limx);
+    out->clamp_y = !(ty >= -limy && ty <= limy);
+    return true;
+}
+
+// Gathers Gaussian g's inputs from the structure-of-arrays layout.
+template <typename F, typename In>
+void gather_gaussian(int32_t n, int g, const In* means, const In* scales, const In* quats,
+                     const In* sh, int n_coef, const In* rgb_in, F m[3], F s3[3], F q[4],
+                     F sh_g[48], F rgb_g[3]) {
+    for (int i = 0; i < 3; ++i) {
+        m[i] = (F)means[(size_t)i * n + g];
+        s3[i] = (F)scales[(size_t)i * n + g];
+    }
+    for (int i = 0; i < 4; ++i) q[i] = (F)quats[(size_t)i * n + g];
+    for (int k = 0; k < n_coef; ++k)
+        for (int ch = 0; ch < 3; ++ch) sh_g[k * 3 + ch] = (F)sh[(size_t)(k * 3 + ch) * n + g];
+    if (rgb_in)
+        for (int ch = 0; ch < 3; ++ch) rgb_g[ch] = (F)rgb_in[(size_t)ch * n + g];
+}
+
+// Gradient of the SH basis polynomials with respect to the direction
+// components (x, y, z), differentiated term by term from the forms in
+// sh_basis ([zenn] 2.2.3). dY[k][0..2] = dY_k/dx, dY_k/dy, dY_k/dz.
+void sh_basis_grad(double x, double y, double z, double dY[16][3]) {
+    double k[16];
+    for (int i = 0; i < 16; ++i) k[i] = (double)SH.k[i];
+    const double xx = x * x, yy = y * y, zz = z * z;
+    const double g[16][3] = {
+        {0, 0, 0},
+        {0, k[1], 0},
+        {0, 0, k[2]},
+        {k[3], 0, 0},
+        {k[4] * y, k[4] * x, 0},
+        {0, k[5] * z, k[5] * y},
+        {-2 * k[6] * x, -2 * k[6] * y, 4 * k[6] * z},
+        {k[7] * z, 0, k[7] * x},
+        {2 * k[8] * x, -2 * k[8] * y, 0},
+        {6 * k[9] * x * y, k[9] * (3 * xx - 3 * yy), 0},
+        {k[10] * y * z, k[10] * x * z, k[10] * x * y},
+        {-2 * k[11] * x * y, k[11] * (4 * zz - xx - 3 * yy), 8 * k[11] * y * z},
+        {-6 * k[12] * x * z, -6 * k[12] * y * z, k[12] * (6 * zz - 3 * xx - 3 * yy)},
+        {k[13] * (4 * zz - 3 * xx - yy), -2 * k[13] * x * y, 8 * k[13] * x * z},
+        {2 * k[14] * x * z, -2 * k[14] * y * z, k[14] * (xx - yy)},
+        {k[15] * (3 * xx - 3 * yy), -6 * k[15] * x * y, 0},
+    };
+    for (int i = 0; i < 16; ++i)
+        for (int j = 0; j < 3; ++j) dY[i][j] = g[i][j];
+}
+
+// Backward of project_gaussian for one Gaussian, in double, by the chain
+// rule the "rigel" README "Backward" section lays out for its projection
+// backward: from dL/d(u, v) and dL/d(A, B, C) through the 2x2 inverse, through
+// Sigma_2d = T Sigma T^T with T = J W, through J's dependence on the camera-
+// space centre (a clamped x/z or y/z sends its gradient to z only), through
+// the pinhole and the camera transform to the mean; through Sigma = M M^T,
+// M = R(q) S to the scales and the normalised quaternion, and through the
+// normalisation to the raw quaternion ("Deliberate differences": the
+// quaternion normalisation is part of the backward). The colour gradient
+// reaches the SH coefficients and, through the view direction
+// normalize(mean - campos), the mean ([zenn] 2.2.3 basis).
+// clamp_x / clamp_y: which branch the forward took (decided in fp32).
+struct Grad3d {
+    double mean[3], scale[3], quat[4], sh[48], rgb[3];
+};
+
+void project_bwd(const orc_camera* cam, const double m[3], const double s3[3], const double q[4],
+                 const double* sh_g, int n_coef, bool clamp_x, bool clamp_y, const double dL_duv[2],
+                 const double dL_dconic[3], const double dL_dcol[3], Grad3d* out) {
+    double W[9];
+    for (int i = 0; i < 9; ++i) W[i] = (double)cam->R[i];
+    const double fx = cam->fx, fy = cam->fy;
+    // forward quantities
+    double p[3];
+    for (int i = 0; i < 3; ++i)
+        p[i] = W[3 * i + 0] * m[0] + W[3 * i + 1] * m[1] + W[3 * i + 2] * m[2] + (double)cam->t[i];
+    const double px = p[0], py = p[1], pz = p[2];
+    const double limx = (double)FRUSTUM_CLAMP * ((0.5 * cam->width) / fx);
+    const double limy = (double)FRUSTUM_CLAMP * ((0.5 * cam->height) / fy);
+    const double Lx = px / pz > 0 ? limx : -limx, Ly = py / pz > 0 ? limy : -limy;
+    const double xj = clamp_x ? Lx * pz : px, yj = clamp_y ? Ly * pz : py;
+    const double J00 = fx / pz, J02 = -fx * xj / (pz * pz);
+    const double J11 = fy / pz, J12 = -fy * yj / (pz * pz);
+    const double qn = std::sqrt(q[0] * q[0] + q[1] * q[1] + q[2] * q[2] + q[3] * q[3]);
+    const double w = q[0] / qn, x = q[1] / qn, y = q[2] / qn, z = q[3] / qn;
+    const double R[3][3] = {
+        {1 - 2 * (y * y + z * z), 2 * (x * y - w * z), 2 * (x * z + w * y)},
+        {2 * (x * y + w * z), 1 - 2 * (x * x + z * z), 2 * (y * z - w * x)},
+        {2 * (x * z - w * y), 2 * (y * z + w * x), 1 - 2 * (x * x + y * y)}};
+    double M[3][3], Sig[3][3];
+    for (int i = 0; i < 3; ++i)
+        for (int j = 0; j < 3; ++j) M[i][j] = R[i][j] * s3[j];
+    for (int i = 0; i < 3; ++i)
+        for (int j = 0; j < 3; ++j) Sig[i][j] = M[i][0] * M[j][0] + M[i][1] * M[j][1] + M[i][2] * M[j][2];
+    double T[2][3];
+    for (int j = 0; j < 3; ++j) {
+        T[0][j] = J00 * W[j] + J02 * W[6 + j];
+        T[1][j] = J11 * W[3 + j] + J12 * W[6 + j];
+    }
+    double ST[2][3];  // (Sigma T_r^T) for rows r = 0, 1
+    for (int r = 0; r < 2; ++r)
+        for (int i = 0; i < 3; ++i) ST[r][i] = Sig[i][0] * T[r][0] + Sig[i][1] * T[r][1] + Sig[i][2] * T[r][2];
+    const double a = T[0][0] * ST[0][0] + T[0][1] * ST[0][1] + T[0][2] * ST[0][2] + (double)DILATION;
+    const double b = T[0][0] * ST[1][0] + T[0][1] * ST[1][1] + T[0][2] * ST[1][2];
+    const double c = T[1][0] * ST[1][0] + T[1][1] * ST[1][1] + T[1][2] * ST[1][2] + (double)DILATION;
+    const double det = a * c - b * b, det2 = det * det;
+
+    // conic (A, B, C) = (c, -b, a) / det  ->  Sigma_2d entries
+    const double gA = dL_dconic[0], gB = dL_dconic[1], gC = dL_dconic[2];
+    const double ga = (-c * c * gA + b * c * gB - b * b * gC) / det2;
+    const double gb = (2 * b * c * gA - (a * c + b * b) * gB + 2 * a * b * gC) / det2;
+    const double gc = (-b * b * gA + a * b * gB - a * a * gC) / det2;
+
+    // Sigma_2d = T Sigma T^T  ->  T and Sigma
+    double gT[2][3];
+    for (int j = 0; j < 3; ++j) {
+        gT[0][j] = 2 * ga * ST[0][j] + gb * ST[1][j];
+        gT[1][j] = gb * ST[0][j] + 2 * gc * ST[1][j];
+    }
+    double gSig[3][3];  // symmetric part of dL/dSigma
+    for (int i = 0; i < 3; ++i)
+        for (int j = 0; j < 3; ++j)
+            gSig[i][j] = ga * T[0][i] * T[0][j] + 0.5 * gb * (T[0][i] * T[1][j] + T[1][i] * T[0][j]) +
+                         gc * T[1][i] * T[1][j];
+
+    // T = J W  ->  J
+    double gJ00 = 0, gJ02 = 0, gJ11 = 0, gJ12 = 0;
+    for (int j = 0; j < 3; ++j) {
+        gJ00 += gT[0][j] * W[j];
+        gJ02 += gT[0][j] * W[6 + j];
+        gJ11 += gT[1][j] * W[3 + j];
+        gJ12 += gT[1][j] * W[6 + j];
+    }
+    // J and the pinhole  ->  camera-space centre
+    double gp[3] = {0, 0, 0};
+    gp[0] += dL_duv[0] * fx / pz;
+    gp[1] += dL_duv[1] * fy / pz;
+    gp[2] += -dL_duv[0] * fx * px / (pz * pz) - dL_duv[1] * fy * py / (pz * pz);
+    gp[2] += -gJ00 * fx / (pz * pz) - gJ11 * fy / (pz * pz);
+    if (clamp_x) {
+        gp[2] += gJ02 * fx * Lx / (pz * pz);
+    } else {
+        gp[0] += -gJ02 * fx / (pz * pz);
+        gp[2] += gJ02 * 2 * fx * px / (pz * pz * pz);
+    }
+    if (clamp_y) {
+        gp[2] += gJ12 * fy * Ly / (pz * pz);
+    } else {
+        gp[1] += -gJ12 * fy / (pz * pz);
+        gp[2] += gJ12 * 2 * fy * py / (pz * pz * pz);
+    }
+    // camera transform p = W m + t  ->  mean
+    for (int i = 0; i < 3; ++i) out->mean[i] = W[i] * gp[0] + W[3 + i] * gp[1] + W[6 + i] * gp[2];
+
+    // Sigma = M M^T  ->  M;  M = R S  ->  R and S
+    double gM[3][3];
+    for (int i = 0; i < 3; ++i)
+        for (int j = 0; j < 3; ++j)
+            gM[i][j] = 2 * (gSig[i][0] * M[0][j] + gSig[i][1] * M[1][j] + gSig[i][2] * M[2][j]);
+    double gR[3][3];
+    for (int j = 0; j < 3; ++j) {
+        out->scale[j] = gM[0][j] * R[0][j] + gM[1][j] * R[1][j] + gM[2][j] * R[2][j];
+        for (int i = 0; i < 3; ++i) gR[i][j] = gM[i][j] * s3[j];
+    }
+    // R(q) of the normalised quaternion  ->  (w, x, y, z)
+    const double gw = 2 * (-z * gR[0][1] + y * gR[0][2] + z * gR[1][0] - x * gR[1][2] - y * gR[2][0] + x * gR[2][1]);
+    const double gx = 2 * (y * gR[0][1] + z * gR[0][2] + y * gR[1][0] - 2 * x * gR[1][1] - w * gR[1][2] +
+                           z * gR[2][0] + w * gR[2][1] - 2 * x * gR[2][2]);
+    const double gy = 2 * (-2 * y * gR[0][0] + x * gR[0][1] + w * gR[0][2] + x * gR[1][0] + z * gR[1][2] -
+                           w * gR[2][0] + z * gR[2][1] - 2 * y * gR[2][2]);
+    const double gz = 2 * (-2 * z * gR[0][0] - w * gR[0][1] + x * gR[0][2] + w * gR[1][0] - 2 * z * gR[1][1] +
+                           y * gR[1][2] + x * gR[2][0] + y * gR[2][1]);
+    // normalisation q_hat = q / |q|: remove the radial part, divide by |q|
+    const double dot = w * gw + x * gx + y * gy + z * gz;
+    out->quat[0] = (gw - w * dot) / qn;
+    out->quat[1] = (gx - x * dot) / qn;
+    out->quat[2] = (gy - y * dot) / qn;
+    out->quat[3] = (gz - z * dot) / qn;
+
+    // colour
+    if (sh_g) {
+        const double v0 = m[0] - cam->campos[0], v1 = m[1] - cam->campos[1], v2 = m[2] - cam->campos[2];
+        const double vn = std::sqrt(v0 * v0 + v1 * v1 + v2 * v2);
+        const double d[3] = {v0 / vn, v1 / vn, v2 / vn};
+        double Y[16], dY[16][3];
+        sh_basis<double>(d[0], d[1], d[2], Y);
+        sh_basis_grad(d[0], d[1], d[2], dY);
+        double gd[3] = {0, 0, 0};
+        for (int k = 0; k < n_coef; ++k)
+            for (int ch = 0; ch < 3; ++ch) {
+                out->sh[k * 3 + ch] = dL_dcol[ch] * Y[k];
+                for (int j = 0; j < 3; ++j) gd[j] += dL_dcol[ch] * sh_g[k * 3 + ch] * dY[k][j];
+            }
+        const double dd = d[0] * gd[0] + d[1] * gd[1] + d[2] * gd[2];
+        for (int j = 0; j < 3; ++j) out->mean[j] += (gd[j] - d[j] * dd) / vn;
+    } else {
+        for (int ch = 0; ch < 3; ++ch) out->rgb[ch] = dL_dcol[ch];
+    }
+}
+
 }  // namespace
 
 extern "C" {
@@ -152,18 +481,12 @@ void orc_constants(float out[9]) {
 // The 16 SH basis values for a unit direction (exposed for the pins).
 void orc_sh_basis(float x, float y, float z, float* out16) { sh_basis(x, y, z, out16); }
 
-// Preprocess, one Gaussian at a time.
-//   [rigel] "Projection": camera transform, explicit pinhole, EWA
-//     Sigma_2d = J W Sigma W^T J^T + 0.3 I with x/z, y/z clamped to 1.3x the
-//     half-width before J is built; conic; 3-sigma radius; radius 0 for
-//     anything behind the near plane, degenerate or off-screen.
-//   [zenn] 2.1.1: Sigma = R S S^T R^T; 2.1.2: J; 2.3.1: conic;
-//     2.3.3: lambda_max with the 0.1 discriminant floor; 2.2.3: SH colour.
-//   [learn-gs] prep_splats: z > Z_NEAR cull, u = fx x/z + cx, det > 0.
-// Layouts: means/scales [3][n], quats [4][n] (w,x,y,z), opacity [n],
-// sh [(d+1)^2][3][n] or NULL (then rgb_in [3][n]). Outputs per Gaussian:
-// xy_depth (u, v, z, radius), conic_op (A, B, C, opacity), rgb (r, g, b, 0),
-// tiles_touched. A culled Gaussian gets all-zero outputs.
+// Preprocess, one Gaussian at a time (project_gaussian in fp32, then the
+// tile span). Layouts: means/scales [3][n], quats [4][n] (w,x,y,z), opacity
+// [n], sh [(d+1)^2][3][n] or NULL (then rgb_in [3][n]). Outputs per
+// Gaussian: xy_depth (u, v, z, radius), conic_op (A, B, C, opacity), rgb
+// (r, g, b, 0), tiles_touched. A culled Gaussian gets all-zero outputs; a
+// Gaussian whose opacity or colour is not finite is culled as well.
 // Returns 0, or -1 on an invalid argument.
 int orc_preprocess(const orc_camera* cam, int32_t n, const float* means,
                    const float* scales, const float* quats, const float* opacity,
@@ -173,7 +496,6 @@ int orc_preprocess(const orc_camera* cam, int32_t n, const float* means,
     if (!cam || n < 0) return -1;
     if (sh && (sh_degree < 0 || sh_degree > 3)) return -1;
     const int TX = tiles_x(cam), TY = tiles_y(cam);
-    const float* W = cam->R;  // the view rotation
     const int n_coef = sh ? (sh_degree + 1) * (sh_degree + 1) : 0;
 
     for (int g = 0; g < n; ++g) {
@@ -183,113 +505,101 @@ int orc_preprocess(const orc_camera* cam, int32_t n, const float* means,
         for (int k = 0; k < 4; ++k) { o_xy[k] = 0.0f; o_co[k] = 0.0f; o_rgb[k] = 0.0f; }
         tiles_touched[g] = 0;
 
-        const float mx = means[g], my = means[n + g], mz = means[2 * n + g];
-
-        // Camera space.
-        const float px = ((W[0] * mx + W[1] * my) + W[2] * mz) + cam->t[0];
-        const float py = ((W[3] * mx + W[4] * my) + W[5] * mz) + cam->t[1];
-        const float pz = ((W[6] * mx + W[7] * my) + W[8] * mz) + cam->t[2];
-        if (!(pz > Z_NEAR)) continue;  // also rejects NaN
-
-        // Pinhole projection of the centre.
-        const float u = (cam->fx * px) / pz + cam->cx;
-        const float v = (cam->fy * py) / pz + cam->cy;
-        if (!std::isfinite(u) || !std::isfinite(v)) continue;
-
-        // Jacobian of the pinhole at the centre, x/z and y/z clamped.
-        const float limx = FRUSTUM_CLAMP * ((0.5f * (float)cam->width) / cam->fx);
-        const float limy = FRUSTUM_CLAMP * ((0.5f * (float)cam->height) / cam->fy);
-        const float xj = std::min(limx, std::max(-limx, px / pz)) * pz;
-        const float yj = std::min(limy, std::max(-limy, py / pz)) * pz;
-        const float zz = pz * pz;
-        const float J00 = cam->fx / pz;
-        const float J02 = -(cam->fx * xj) / zz;
-        const float J11 = cam->fy / pz;
-        const float J12 = -(cam->fy * yj) / zz;
-
-        // Rotation from the quaternion, normalised here.
-        float qw = quats[g], qx = quats[n + g], qy = quats[2 * n + g], qz = quats[3 * n + g];
-        const float qn = std::sqrt(((qw * qw + qx * qx) + qy * qy) + qz * qz);
-        if (!(qn > 0.0f)) continue;
-        qw = qw / qn; qx = qx / qn; qy = qy / qn; qz = qz / qn;
-        float Rq[3][3];
-        Rq[0][0] = 1.0f - 2.0f * (qy * qy + qz * qz);
-        Rq[0][1] = 2.0f * (qx * qy - qw * qz);
-        Rq[0][2] = 2.0f * (qx * qz + qw * qy);
-        Rq[1][0] = 2.0f * (qx * qy + qw * qz);
-        Rq[1][1] = 1.0f - 2.0f * (qx * qx + qz * qz);
-        Rq[1][2] = 2.0f * (qy * qz - qw * qx);
-        Rq[2][0] = 2.0f * (qx * qz - qw * qy);
-        Rq[2][1] = 2.0f * (qy * qz + qw * qx);
-        Rq[2][2] = 1.0f - 2.0f * (qx * qx + qy * qy);
-
-        // Sigma = (R S)(R S)^T.
-        const float s[3] = {scales[g], scales[n + g], scales[2 * n + g]};
-        float M[3][3];
-        for (int i = 0; i < 3; ++i)
-            for (int j = 0; j < 3; ++j) M[i][j] = Rq[i][j] * s[j];
-        float Sig[3][3];
-        for (int i = 0; i < 3; ++i)
-            for (int j = 0; j < 3; ++j)
-                Sig[i][j] = (M[i][0] * M[j][0] + M[i][1] * M[j][1]) + M[i][2] * M[j][2];
-
-        // T = J W (J's structural zeros skipped), U = T Sigma, Sigma_2d = U T^T.
-        float T[2][3];
-        for (int j = 0; j < 3; ++j) {
-            T[0][j] = J00 * W[0 * 3 + j] + J02 * W[2 * 3 + j];
-            T[1][j] = J11 * W[1 * 3 + j] + J12 * W[2 * 3 + j];
-        }
-        float U[2][3];
-        for (int i = 0; i < 2; ++i)
-            for (int j = 0; j < 3; ++j)
-                U[i][j] = (T[i][0] * Sig[0][j] + T[i][1] * Sig[1][j]) + T[i][2] * Sig[2][j];
-        const float a = ((U[0][0] * T[0][0] + U[0][1] * T[0][1]) + U[0][2] * T[0][2]) + DILATION;
-        const float b = (U[0][0] * T[1][0] + U[0][1] * T[1][1]) + U[0][2] * T[1][2];
-        const float c = ((U[1][0] * T[1][0] + U[1][1] * T[1][1]) + U[1][2] * T[1][2]) + DILATION;
-
-        // Conic and degenerate cull (non-finite covariances are culled too).
-        if (!std::isfinite(a) || !std::isfinite(b) || !std::isfinite(c)) continue;
-        const float det = a * c - b * b;
-        if (!(det > 0.0f) || !std::isfinite(det)) continue;
-        const float cA = c / det, cB = -b / det, cC = a / det;
-
-        // Bounding radius: 3 sqrt(lambda_max), discriminant floored at 0.1.
-        const float mid = 0.5f * (a + c);
-        const float lam = mid + std::sqrt(std::max(mid * mid - det, DISC_FLOOR));
-        const float r = std::ceil(SIGMA * std::sqrt(lam));
-        if (!std::isfinite(r)) continue;
+        float m[3], s3[3], q[4], sh_g[48], rgb_g[3];
+        gather_gaussian<float, float>(n, g, means, scales, quats, sh, n_coef, sh ? nullptr : rgb_in,
+                                      m, s3, q, sh_g, rgb_g);
+        Projected<float> P;
+        if (!project_gaussian<float>(cam, m, s3, q, sh ? sh_g : nullptr, n_coef, rgb_g, &P)) continue;
 
         // Tile span; nothing on screen means culled.
-        const Span sp = tile_span(u, v, r, TX, TY);
+        const Span sp = tile_span(P.u, P.v, P.r, TX, TY);
         const int count = (sp.x1 - sp.x0) * (sp.y1 - sp.y0);
         if (count <= 0) continue;
+        if (!std::isfinite(opacity[g]) || !std::isfinite(P.col[0]) || !std::isfinite(P.col[1]) ||
+            !std::isfinite(P.col[2])) continue;
 
-        // Colour: SH evaluated at the unit direction from the camera centre.
-        float col[3];
-        if (sh) {
-            float dx = mx - cam->campos[0], dy = my - cam->campos[1], dz = mz - cam->campos[2];
-            const float dn = std::sqrt((dx * dx + dy * dy) + dz * dz);
-            dx = dx / dn; dy = dy / dn; dz = dz / dn;
-            float Y[16];
-            sh_basis(dx, dy, dz, Y);
-            for (int ch = 0; ch < 3; ++ch) {
-                float acc = sh[(size_t)(0 * 3 + ch) * n + g] * Y[0];
-                for (int k = 1; k < n_coef; ++k) acc = acc + sh[(size_t)(k * 3 + ch) * n + g] * Y[k];
-                col[ch] = acc;
-            }
-        } else {
-            for (int ch = 0; ch < 3; ++ch) col[ch] = rgb_in[(size_t)ch * n + g];
-        }
-        // A Gaussian whose opacity or colour is not finite is culled as well.
-        if (!std::isfinite(opacity[g]) || !std::isfinite(col[0]) || !std::isfinite(col[1]) ||
-            !std::isfinite(col[2])) continue;
-
-        o_xy[0] = u; o_xy[1] = v; o_xy[2] = pz; o_xy[3] = r;
-        o_co[0] = cA; o_co[1] = cB; o_co[2] = cC; o_co[3] = opacity[g];
-        o_rgb[0] = col[0]; o_rgb[1] = col[1]; o_rgb[2] = col[2];
+        o_xy[0] = P.u; o_xy[1] = P.v; o_xy[2] = P.z; o_xy[3] = P.r;
+        o_co[0] = P.A; o_co[1] = P.B; o_co[2] = P.C; o_co[3] = opacity[g];
+        o_rgb[0] = P.col[0]; o_rgb[1] = P.col[1]; o_rgb[2] = P.col[2];
         tiles_touched[g] = (uint32_t)count;
     }
     return 0;
+}
+
+// Backward of orc_preprocess (the projection backward of the "rigel" README
+// "Backward" section, plus the SH colour). The cull and the clamp branches
+// are decided by the fp32 preprocess exactly as orc_preprocess decides
+// them; the derivatives are evaluated in double at the fp32 inputs. A
+// culled Gaussian gets zero gradients.
+// In:  grad_mean2d [n][2] (du, dv), grad_conic_op [n][4] (dA, dB, dC,
+//      dopacity), grad_rgb [n][4] (dr, dg, db, -), all double.
+// Out: grad_means [3][n], grad_scales [3][n], grad_quats [4][n],
+//      grad_opacity [n], and grad_sh [(d+1)^2][3][n] when sh != NULL, else
+//      grad_rgb_in [3][n]. Everything is overwritten. Returns 0, or -1 on an
+//      invalid argument.
+int orc_preprocess_bwd(const orc_camera* cam, int32_t n, const float* means, const float* scales,
+                       const float* quats, const float* opacity, const float* sh, int32_t sh_degree,
+                       const float* rgb_in, const double* grad_mean2d, const double* grad_conic_op,
+                       const double* grad_rgb, double* grad_means, double* grad_scales,
+                       double* grad_quats, double* grad_opacity, double* grad_sh,
+                       double* grad_rgb_in) {
+    if (!cam || n < 0) return -1;
+    if (sh && (sh_degree < 0 || sh_degree > 3)) return -1;
+    const int TX = tiles_x(cam), TY = tiles_y(cam);
+    const int n_coef = sh ? (sh_degree + 1) * (sh_degree + 1) : 0;
+    for (int g = 0; g < n; ++g) {
+        for (int i = 0; i < 3; ++i) { grad_means[(size_t)i * n + g] = 0; grad_scales[(size_t)i * n + g] = 0; }
+        for (int i = 0; i < 4; ++i) grad_quats[(size_t)i * n + g] = 0;
+        grad_opacity[g] = 0;
+        if (sh) {
+            for (int k = 0; k < 3 * n_coef; ++k) grad_sh[(size_t)k * n + g] = 0;
+        } else {
+            for (int ch = 0; ch < 3; ++ch) grad_rgb_in[(size_t)ch * n + g] = 0;
+        }
+        // the forward's decisions, in fp32
+        float m[3], s3[3], q[4], sh_g[48], rgb_g[3];
+        gather_gaussian<float, float>(n, g, means, scales, quats, sh, n_coef, sh ? nullptr : rgb_in,
+                                      m, s3, q, sh_g, rgb_g);
+        Projected<float> P;
+        if (!project_gaussian<float>(cam, m, s3, q, sh ? sh_g : nullptr, n_coef, rgb_g, &P)) continue;
+        const Span sp = tile_span(P.u, P.v, P.r, TX, TY);
+        if ((sp.x1 - sp.x0) * (sp.y1 - sp.y0) <= 0) continue;
+        if (!std::isfinite(opacity[g]) || !std::isfinite(P.col[0]) || !std::isfinite(P.col[1]) ||
+            !std::isfinite(P.col[2])) continue;
+        // the derivatives, in double
+        double md[3], sd[3], qd[4], shd[48], rgbd[3];
+        gather_gaussian<double, float>(n, g, means, scales, quats, sh, n_coef, sh ? nullptr : rgb_in,
+                                       md, sd, qd, shd, rgbd);
+        const double duv[2] = {grad_mean2d[2 * (size_t)g], grad_mean2d[2 * (size_t)g + 1]};
+        const double dcon[3] = {grad_conic_op[4 * (size_t)g], grad_conic_op[4 * (size_t)g + 1],
+                                grad_conic_op[4 * (size_t)g + 2]};
+        const double dcol[3] = {grad_rgb[4 * (size_t)g], grad_rgb[4 * (size_t)g + 1], grad_rgb[4 * (size_t)g + 2]};
+        Grad3d G;
+        project_bwd(cam, md, sd, qd, sh ? shd : nullptr, n_coef, P.clamp_x, P.clamp_y, duv, dcon, dcol, &G);
+        for (int i = 0; i < 3; ++i) { grad_means[(size_t)i * n + g] = G.mean[i]; grad_scales[(size_t)i * n + g] = G.scale[i]; }
+        for (int i = 0; i < 4; ++i) grad_quats[(size_t)i * n + g] = G.quat[i];
+        grad_opacity[g] = grad_conic_op[4 * (size_t)g + 3];
+        if (sh) {
+            for (int k = 0; k < 3 * n_coef; ++k) grad_sh[(size_t)k * n + g] = G.sh[k];
+        } else {
+            for (int ch = 0; ch < 3; ++ch) grad_rgb_in[(size_t)ch * n + g] = G.rgb[ch];
+        }
+    }
+    return 0;
+}
+
+// project_gaussian in double for one Gaussian (the function whose finite
+// differences pin orc_preprocess_bwd). Inputs in double: m[3], s[3], q[4],
+// sh_g [n_coef][3] (or NULL with rgb_g[3]). out[0..9] = u, v, A, B, C,
+// r, g, b, clamp_x, clamp_y. Returns 1, or 0 when culled.
+int orc_project_f64(const orc_camera* cam, const double* m, const double* s3, const double* q,
+                    const double* sh_g, int32_t n_coef, const double* rgb_g, double* out) {
+    Projected<double> P;
+    if (!project_gaussian<double>(cam, m, s3, q, sh_g, n_coef, rgb_g, &P)) return 0;
+    out[0] = P.u; out[1] = P.v; out[2] = P.A; out[3] = P.B; out[4] = P.C;
+    out[5] = P.col[0]; out[6] = P.col[1]; out[7] = P.col[2];
+    out[8] = P.clamp_x ? 1.0 : 0.0; out[9] = P.clamp_y ? 1.0 : 0.0;
+    return 1;
 }
 
 // Tile span of one splat (exposed for the pins): out = x0, x1, y0, y1.
