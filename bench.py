@@ -239,6 +239,28 @@ def main():
     for i, s in enumerate(STAGES):
         vals = [m[i].elapsed_time(m[i + 1]) for m in staged]
         stage_ms[s] = float(np.median(vals)), float(np.mean(vals))
+    # The projection backward (gs_preprocess_bwd) is the step after this
+    # path: timed on its own, over the same frame's splat gradients.
+    pgrads = gs.preprocess_bwd(c, scene.means, scene.scales, scene.quats, scene.sh, scene.sh_degree,
+                               pre["tiles_touched"], grads["grad_mean2d"], grads["grad_conic_op"],
+                               grads["grad_rgb"])
+    pb = []
+    for _ in range(args.steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        gs.preprocess_bwd(c, scene.means, scene.scales, scene.quats, scene.sh, scene.sh_degree,
+                          pre["tiles_touched"], grads["grad_mean2d"], grads["grad_conic_op"],
+                          grads["grad_rgb"], out=pgrads)
+        e1.record(stream)
+        pb.append((e0, e1))
+    torch.cuda.synchronize()
+    pbwd_s = float(np.mean([a.elapsed_time(b) for a, b in pb])) * 1e-3
+    n_coef = (scene.sh_degree + 1) ** 2 if scene.sh is not None else 1
+    # per Gaussian: means, scales, quats, tiles_touched, the three upstream
+    # records (8 + 16 + 16 B) and the SH (or RGB) read; eleven gradient
+    # floats and the SH (or RGB) gradient written
+    pbwd_bytes = n * (44 + 40 + 12 * n_coef + 44 + 12 * n_coef)
+
     ms_per_step = 1e3 * elapsed / args.steps
     fps = args.steps / elapsed
 
@@ -278,6 +300,8 @@ def main():
             "composite_fwd_tflops": round(evals_fwd * FLOPS_PER_FWD_EVAL / fwd_s / 1e12, 4),
             "composite_fwd_frac": round(evals_fwd * FLOPS_PER_FWD_EVAL / fwd_s / PEAK_FP32_VECTOR, 5),
             "entries_per_s": round(E / sort_s, 1),
+            "preprocess_bwd_ms": round(pbwd_s * 1e3, 4),
+            "preprocess_bwd_hbm_frac": round(pbwd_bytes / pbwd_s / PEAK_HBM, 4),
         },
         "baseline_context": {"value": 25.8, "unit": "frames/s", "hardware": "Tesla T4",
                              "note": "derived 1000/(4.60 ms fwd + 34.12 ms bwd) for the pages' "

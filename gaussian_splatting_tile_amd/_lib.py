@@ -12,7 +12,8 @@ STATUS_NAMES = {0: "GS_OK", 1: "GS_ERR_INVALID", 2: "GS_ERR_CAPACITY", 3: "GS_ER
                 4: "GS_ERR_HIP"}
 
 # Every symbol include/gs.h declares.
-EXPORTS = ("gs_constants", "gs_last_error", "gs_version", "gs_preprocess", "gs_bin_and_sort",
+EXPORTS = ("gs_constants", "gs_last_error", "gs_version", "gs_preprocess", "gs_preprocess_bwd",
+           "gs_bin_and_sort",
            "gs_bin_and_sort_async", "gs_tile_ranges", "gs_tile_ranges_async", "gs_composite_fwd",
            "gs_composite_bwd")
 
@@ -53,6 +54,8 @@ def load() -> ctypes.CDLL:
     lib.gs_version.argtypes = [P]
     lib.gs_preprocess.restype = ctypes.c_int
     lib.gs_preprocess.argtypes = [CAM, I32, P, P, P, P, P, I32, P, P, P, P, P, P]
+    lib.gs_preprocess_bwd.restype = ctypes.c_int
+    lib.gs_preprocess_bwd.argtypes = [CAM, I32, P, P, P, P, I32, P, P, P, P, P, P, P, P, P, P, P]
     lib.gs_bin_and_sort.restype = ctypes.c_int
     lib.gs_bin_and_sort.argtypes = [CAM, I32, P, P, P, P, I64, P, ctypes.POINTER(ctypes.c_size_t),
                                     ctypes.POINTER(ctypes.c_int64), P]

@@ -91,6 +91,37 @@ gs_status gs_preprocess(const gs_camera* cam, int32_t n, const float* means, con
                      "gs_preprocess launch");
 }
 
+gs_status gs_preprocess_bwd(const gs_camera* cam, int32_t n, const float* means, const float* scales,
+                            const float* quats, const float* sh, int32_t sh_degree,
+                            const uint32_t* tiles_touched, const float* grad_mean2d,
+                            const float* grad_conic_op, const float* grad_rgb, float* grad_means,
+                            float* grad_scales, float* grad_quats, float* grad_opacity, float* grad_sh,
+                            float* grad_rgb_in, void* stream) {
+    g_last_error.clear();
+    if (gs_status s = check_camera(cam)) return s;
+    if (n < 0 || n > GS_MAX_GAUSSIANS) return fail(GS_ERR_INVALID, "n = %d outside [0, %d]", n, GS_MAX_GAUSSIANS);
+    if (n == 0) return GS_OK;
+    if (!means || !scales || !quats || !tiles_touched || !grad_mean2d || !grad_conic_op || !grad_rgb ||
+        !grad_means || !grad_scales || !grad_quats || !grad_opacity)
+        return fail(GS_ERR_INVALID, "gs_preprocess_bwd: a required pointer is NULL");
+    if (sh) {
+        if (sh_degree < 0 || sh_degree > 3) return fail(GS_ERR_INVALID, "sh_degree %d outside 0..3", sh_degree);
+        if (!grad_sh) return fail(GS_ERR_INVALID, "gs_preprocess_bwd: grad_sh is required when sh is given");
+    } else if (!grad_rgb_in) {
+        return fail(GS_ERR_INVALID, "gs_preprocess_bwd: grad_rgb_in is required when sh is NULL");
+    }
+    if (((uintptr_t)grad_conic_op | (uintptr_t)grad_rgb) & 15)
+        return fail(GS_ERR_INVALID, "gs_preprocess_bwd: float4 gradients must be 16-byte aligned");
+    if ((uintptr_t)grad_mean2d & 7)
+        return fail(GS_ERR_INVALID, "gs_preprocess_bwd: grad_mean2d must be 8-byte aligned");
+    return hip_check(gs::launch_preprocess_bwd(*cam, n, means, scales, quats, sh, sh_degree, tiles_touched,
+                                               (const float2*)grad_mean2d, (const float4*)grad_conic_op,
+                                               (const float4*)grad_rgb, grad_means, grad_scales, grad_quats,
+                                               grad_opacity, sh ? grad_sh : nullptr, sh ? nullptr : grad_rgb_in,
+                                               (hipStream_t)stream),
+                     "gs_preprocess_bwd launch");
+}
+
 namespace {
 
 // Checks shared by the blocking and the asynchronous binning entry points;

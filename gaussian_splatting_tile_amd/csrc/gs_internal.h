@@ -55,6 +55,13 @@ hipError_t launch_preprocess(const gs_camera& cam, int n, const float* means, co
                              float4* conic_op, float4* rgb, uint32_t* tiles_touched,
                              hipStream_t stream);
 
+hipError_t launch_preprocess_bwd(const gs_camera& cam, int n, const float* means, const float* scales,
+                                 const float* quats, const float* sh, int sh_degree,
+                                 const uint32_t* tiles_touched, const float2* grad_mean2d,
+                                 const float4* grad_conic_op, const float4* grad_rgb, float* grad_means,
+                                 float* grad_scales, float* grad_quats, float* grad_opacity,
+                                 float* grad_sh, float* grad_rgb_in, hipStream_t stream);
+
 // Binning workspace, carved from the caller's scratch buffer. Nothing in it
 // needs initialisation: every word is written before it is read within one
 // call.

@@ -89,6 +89,34 @@ def preprocess(cam, means, scales, quats, opacity, sh=None, sh_degree=0, rgb_in=
     return out
 
 
+def preprocess_bwd(cam, means, scales=None, quats=None, sh=None, sh_degree=0, tiles_touched=None,
+                   grad_mean2d=None, grad_conic_op=None, grad_rgb=None, out=None, stream=None):
+    """gs_preprocess_bwd. Returns dict grad_means [3,n], grad_scales [3,n], grad_quats [4,n],
+    grad_opacity [n], and grad_sh [(d+1)^2,3,n] (when sh is given) or grad_rgb_in [3,n]."""
+    n = int(means.shape[1])
+    dev = means.device
+    f32, i32 = torch.float32, torch.int32
+    if out is None:
+        out = dict(grad_means=torch.empty((3, n), dtype=f32, device=dev),
+                   grad_scales=torch.empty((3, n), dtype=f32, device=dev),
+                   grad_quats=torch.empty((4, n), dtype=f32, device=dev),
+                   grad_opacity=torch.empty((n,), dtype=f32, device=dev))
+        if sh is not None:
+            out["grad_sh"] = torch.empty(((sh_degree + 1) ** 2, 3, n), dtype=f32, device=dev)
+        else:
+            out["grad_rgb_in"] = torch.empty((3, n), dtype=f32, device=dev)
+    c = _cam(cam)
+    _lib.check(_lib.load().gs_preprocess_bwd(
+        ctypes.byref(c), n, _ptr(means, f32, "means"), _ptr(scales, f32, "scales"),
+        _ptr(quats, f32, "quats"), _ptr(sh, f32, "sh"), int(sh_degree),
+        _ptr(tiles_touched, i32, "tiles_touched"), _ptr(grad_mean2d, f32, "grad_mean2d"),
+        _ptr(grad_conic_op, f32, "grad_conic_op"), _ptr(grad_rgb, f32, "grad_rgb"),
+        _ptr(out["grad_means"], f32), _ptr(out["grad_scales"], f32), _ptr(out["grad_quats"], f32),
+        _ptr(out["grad_opacity"], f32), _ptr(out.get("grad_sh"), f32), _ptr(out.get("grad_rgb_in"), f32),
+        _stream(stream)))
+    return out
+
+
 class BinBuffers:
     """Entry buffers (keys, point_list, scratch, the device entry count)
     reused across frames; grown on demand when a frame needs more entries
@@ -284,7 +312,14 @@ class Rasterizer:
         out.update(keys=keys, point_list=point_list, n_entries=E, ranges=ranges, tile_order=order, **fwd)
         return out
 
-    def backward(self, cam: dict, scene: Scene, fwd: dict, dL_dimage, bg=(0.0, 0.0, 0.0)):
-        return composite_bwd(cam, scene.n, fwd["ranges"], fwd["point_list"], fwd["xy_depth"],
-                             fwd["conic_op"], fwd["rgb"], fwd["final_T"], fwd["n_contrib"], dL_dimage, bg,
-                             order=fwd.get("tile_order"))
+    def backward(self, cam: dict, scene: Scene, fwd: dict, dL_dimage, bg=(0.0, 0.0, 0.0),
+                 to_parameters=False):
+        """Gradients of the splat records (grad_mean2d, grad_conic_op, grad_rgb); with
+        to_parameters, also those of the Gaussians' parameters (gs_preprocess_bwd)."""
+        g = composite_bwd(cam, scene.n, fwd["ranges"], fwd["point_list"], fwd["xy_depth"],
+                          fwd["conic_op"], fwd["rgb"], fwd["final_T"], fwd["n_contrib"], dL_dimage, bg,
+                          order=fwd.get("tile_order"))
+        if to_parameters:
+            g.update(preprocess_bwd(cam, scene.means, scene.scales, scene.quats, scene.sh, scene.sh_degree,
+                                    fwd["tiles_touched"], g["grad_mean2d"], g["grad_conic_op"], g["grad_rgb"]))
+        return g

@@ -124,6 +124,45 @@ gs_status gs_preprocess(const gs_camera* cam, int32_t n, const float* means, con
                         float* rgb, uint32_t* tiles_touched, void* stream);
 
 /* ---------------------------------------------------------------------
+ * gs_preprocess_bwd - gradients of gs_preprocess's outputs with respect to
+ * the Gaussians' parameters (the projection backward).
+ * ("rigel" README "Backward", its last paragraph, and "Deliberate
+ * differences" (quaternion normalisation in the backward); zenn 2.2.3 for
+ * the SH basis.)
+ *
+ * Chains dL/d(u, v), dL/d(A, B, C) and dL/d(colour) through the 2x2
+ * inverse, Sigma_2d = T Sigma T^T with T = J W, the Jacobian's dependence on
+ * the camera-space centre (when x/z or y/z was clamped, that entry of J sends
+ * its gradient to z only), the pinhole, the camera transform, and
+ * Sigma = M M^T, M = R(q) S, down to the scales and the raw quaternion
+ * (through its normalisation). The colour gradient reaches the SH
+ * coefficients and, through the view direction normalize(mean - campos),
+ * the mean. dL/dopacity is passed through from grad_conic_op. A Gaussian
+ * with tiles_touched == 0 (culled by the forward) gets zero gradients.
+ * Computed in float32; each Gaussian's gradients are formed by one thread
+ * (no atomics, deterministic).
+ *
+ *   cam, n, means, scales, quats, sh, sh_degree: as given to gs_preprocess
+ *   tiles_touched   [n] from gs_preprocess
+ *   grad_mean2d     [n][2] dL/d(u, v) (from gs_composite_bwd)
+ *   grad_conic_op   [n][4] dL/d(A, B, C, opacity)
+ *   grad_rgb        [n][4] dL/d(r, g, b, -)
+ *   grad_means      out [3][n]
+ *   grad_scales     out [3][n]
+ *   grad_quats      out [4][n] (w, x, y, z); orthogonal to the quaternion
+ *   grad_opacity    out [n]
+ *   grad_sh         out [(sh_degree+1)^2][3][n]; required iff sh != NULL
+ *   grad_rgb_in     out [3][n]; required iff sh == NULL (dL/d rgb_in)
+ * Every output is overwritten.
+ * ------------------------------------------------------------------- */
+gs_status gs_preprocess_bwd(const gs_camera* cam, int32_t n, const float* means, const float* scales,
+                            const float* quats, const float* sh, int32_t sh_degree,
+                            const uint32_t* tiles_touched, const float* grad_mean2d,
+                            const float* grad_conic_op, const float* grad_rgb, float* grad_means,
+                            float* grad_scales, float* grad_quats, float* grad_opacity, float* grad_sh,
+                            float* grad_rgb_in, void* stream);
+
+/* ---------------------------------------------------------------------
  * gs_bin_and_sort - duplicate splats into tile entries and sort them.
  * ("rigel" README "Binning"; zenn 4.1-4.3; learn-gs build_tile_lists.)
  *

@@ -92,6 +92,27 @@ def test_invalid_arguments_rejected_before_launch(gs):
                                (ctypes.c_float * 3)(), dummy, dummy, dummy, None, None, None) == _lib.GS_ERR_INVALID
 
 
+def test_preprocess_bwd_validates_before_launch(gs):
+    from gaussian_splatting_tile_amd import _lib
+    P = ctypes.c_void_p
+    d = P(256)  # never dereferenced: validation fails first
+    c = _cam()
+    args = lambda **kw: [kw.get(k, d) for k in ("means", "scales", "quats")] + [kw.get("sh", None), kw.get("deg", 0)] + \
+        [kw.get(k, d) for k in ("tt", "gm", "gc", "gr", "om", "os", "oq", "oo")] + [kw.get("osh", None), kw.get("orgb", d), None]
+    ok = gs.gs_preprocess_bwd(ctypes.byref(c), 0, *args())
+    assert ok == _lib.GS_OK  # n == 0: nothing to do
+    assert gs.gs_preprocess_bwd(None, 4, *args()) == _lib.GS_ERR_INVALID
+    assert gs.gs_preprocess_bwd(ctypes.byref(c), -2, *args()) == _lib.GS_ERR_INVALID
+    assert gs.gs_preprocess_bwd(ctypes.byref(c), 4, *args(orgb=None)) == _lib.GS_ERR_INVALID
+    assert b"grad_rgb_in" in gs.gs_last_error()
+    assert gs.gs_preprocess_bwd(ctypes.byref(c), 4, *args(sh=d, deg=2)) == _lib.GS_ERR_INVALID
+    assert b"grad_sh" in gs.gs_last_error()
+    assert gs.gs_preprocess_bwd(ctypes.byref(c), 4, *args(sh=d, deg=5, osh=d)) == _lib.GS_ERR_INVALID
+    assert gs.gs_preprocess_bwd(ctypes.byref(c), 4, *args(tt=None)) == _lib.GS_ERR_INVALID
+    assert gs.gs_preprocess_bwd(ctypes.byref(c), 4, *args(gc=P(260))) == _lib.GS_ERR_INVALID
+    assert b"aligned" in gs.gs_last_error()
+
+
 def test_bin_scratch_size_query(gs):
     from gaussian_splatting_tile_amd import _lib
     c = _cam()
