@@ -120,7 +120,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="cfg2", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--tile-order", choices=("heavy-first", "index"), default="index",
+    ap.add_argument("--tile-order", choices=("heavy-first", "index"), default="heavy-first",
                     help="tile schedule of the compositing kernels (results are identical)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run device copies of this many MiB (for HBM counter scaling)")
