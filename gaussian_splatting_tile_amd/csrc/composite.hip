@@ -36,8 +36,13 @@
 //    rows with DPP adds (skipped when no lane contributed) into LDS; the
 //    terms are the colour gradient, dL/do, and the moments of dL/dpower
 //    (dx, dy, dx^2, dx dy, dy^2 times it), from which the conic and mean
-//    gradients follow once per (splat, tile). One global atomic per value
-//    per tile entry lands in the per-Gaussian gradient.
+//    gradients follow once per (splat, tile). After each 32-splat batch all
+//    256 threads finish it (one output per thread), summing only the
+//    partials of waves that wrote them (a per-wave batch stamp replaces
+//    clearing the partials); one global atomic per value per tile entry
+//    lands in the per-Gaussian gradient.
+//  * Culling is per 4 x 4 pixel block (see block_mask), exact up to a
+//    rounding bound, so a skipped (splat, block) pair changes no result.
 #include "gs_internal.h"
 
 namespace gs {
@@ -73,54 +78,66 @@ __device__ __forceinline__ void splat_alpha(float hA, float B, float hC, float o
     }
 }
 
-// ---- which waves can a splat reach? ----
+// ---- which pixels can a splat reach? ----
 //
-// A workgroup's four waves each own an 8 x 8 quadrant of the tile (wave w:
-// columns 8 (w & 1) .. +7, rows 8 (w >> 1) .. +7). A splat can only change a pixel if alpha >= 1/255, i.e. if
-// Q(d) = A dx^2 + 2B dx dy + C dy^2 <= 2 ln(255 o). live_mask() computes the
-// minimum of Q over each strip's pixel rectangle (Q is convex along every
-// edge, so off the centre the minimum lies on an edge) and keeps the strip
-// unless that minimum exceeds the threshold by more than a bound on the
-// rounding of Q (in the kernels' fp32 evaluation and in this one) and of
-// the exponential. A culled (splat, strip) pair therefore has
-// alpha < 1/255 at every pixel of the strip: skipping it changes no result.
-__device__ __forceinline__ float edge_min_q(float A, float B, float C, float fixed, float lo, float hi,
-                                            bool fixed_is_x) {
-    // minimise Q along the segment where one offset is `fixed`
-    if (fixed_is_x) {
-        const float t = fminf(fmaxf(-B * fixed * __builtin_amdgcn_rcpf(C), lo), hi);
-        return (A * fixed + 2.0f * B * t) * fixed + C * t * t;
-    }
-    const float t = fminf(fmaxf(-B * fixed * __builtin_amdgcn_rcpf(A), lo), hi);
-    return A * t * t + (2.0f * B * t + C * fixed) * fixed;
-}
+// A splat can only change a pixel if alpha >= 1/255, i.e. if
+// Q(d) = A dx^2 + 2B dx dy + C dy^2 <= 2 ln(255 o): the pixel lies in an
+// ellipse. block_mask() marks which of the tile's sixteen 4 x 4 pixel blocks
+// that ellipse reaches. For each row of blocks it takes the ellipse's slice
+// over the row's y-range: the slice's x-extent is [L, R] with
+//   x(dy) = (-B dy -+ sqrt(thr A - det dy^2)) / A,   det = AC - B^2,
+// whose right edge is concave and left edge convex in dy, so R (L) is the
+// edge at the dy of the ellipse's rightmost (leftmost) point, -+B hx / C,
+// clamped into the row's y-range; the blocks of the row whose x-range meets
+// [L, R] are kept. The threshold is raised by a bound on the rounding of Q
+// in the kernels' fp32 evaluation and of the exponential, and every edge is
+// widened by a slack far above this function's own rounding, so a culled
+// (splat, block) pair has alpha < 1/255 at every pixel of the block: skipping
+// it changes no result. Anything not finite keeps every block.
+// Bit 4 by + bx is block (bx, by): pixels x0 + 4 bx .. +3, y0 + 4 by .. +3.
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float fast_sqrt(float x) { return __builtin_amdgcn_sqrtf(x); }
+__device__ __forceinline__ float fast_log(float x) { return __logf(x); }
 
-__device__ __forceinline__ uint32_t live_mask(float4 co, float u, float v, int x0, int y0) {
+__device__ __forceinline__ uint32_t block_mask(float4 co, float u, float v, int x0, int y0) {
     const float A = co.x, B = co.y, C = co.z, o = co.w;
     if (!(o > 0.0f)) return 0u;  // alpha = o G <= 0 never reaches the floor
-    const float thr = 2.0f * __logf(255.0f * o) * (1.0f + 1e-5f) + 1e-3f;
-    // 64 ulp of |A| dx^2 + |C| dy^2 + 2|B dx dy| covers both evaluations
+    const float rx0 = (float)x0 - u, ry0 = (float)y0 - v;  // tile corner relative to the centre
+    const float dxm = fmaxf(fabsf(rx0), fabsf(rx0 + 15.0f)), dym = fmaxf(fabsf(ry0), fabsf(ry0 + 15.0f));
+    // 64 ulp of |A| dx^2 + |C| dy^2 + 2|B dx dy| covers the kernels' evaluation of Q
     const float bound = 64.0f * 5.96e-8f * (fabsf(A) + fabsf(C) + 2.0f * fabsf(B));
-    uint32_t mask = 0;
-#pragma unroll 1
-    for (int w = 0; w < 4; ++w) {
-        const int qx = x0 + 8 * (w & 1), qy = y0 + 8 * (w >> 1);
-        const float dx0 = (float)qx - u, dx1 = (float)(qx + 7) - u;
-        const float dy0 = (float)qy - v, dy1 = (float)(qy + 7) - v;
-        bool live;
-        if (dx0 <= 0.0f && dx1 >= 0.0f && dy0 <= 0.0f && dy1 >= 0.0f) {
-            live = true;
-        } else {
-            float q = edge_min_q(A, B, C, dx0, dy0, dy1, true);
-            q = fminf(q, edge_min_q(A, B, C, dx1, dy0, dy1, true));
-            q = fminf(q, edge_min_q(A, B, C, dy0, dx0, dx1, false));
-            q = fminf(q, edge_min_q(A, B, C, dy1, dx0, dx1, false));
-            const float dmax2 = fmaxf(dx0 * dx0, dx1 * dx1) + fmaxf(dy0 * dy0, dy1 * dy1);
-            live = !(q - bound * dmax2 > thr);  // a NaN anywhere keeps the strip
-        }
-        mask |= (live ? 1u : 0u) << w;
+    const float thr = 2.0f * fast_log(255.0f * o) * (1.0f + 1e-5f) + 1e-3f + bound * (dxm * dxm + dym * dym);
+    if (thr <= 0.0f) return 0u;  // Q >= 0 > thr everywhere
+    const float det = A * C - B * B;
+    if (!(det > 0.0f && A > 0.0f && C > 0.0f && thr < 3.0e38f)) return 0xFFFFu;
+    const float idet = fast_rcp(det), iA = fast_rcp(A);
+    const float hy = fast_sqrt(thr * A * idet);  // half-extents of the ellipse
+    const float hx = fast_sqrt(thr * C * idet);
+    const float ydr = -B * hx * fast_rcp(C);     // dy of the rightmost point; the leftmost is at -ydr
+    const float slack = 1e-2f + 1e-4f * (hx + hy);
+    const float thrA = thr * A;
+    uint32_t mask = 0u;
+#pragma unroll
+    for (int by = 0; by < 4; ++by) {
+        const float y0r = ry0 + (float)(4 * by);
+        const float lo = fmaxf(y0r, -hy), hi = fminf(y0r + 3.0f, hy);
+        if (lo > hi + slack) continue;  // the row's y-range misses the ellipse (false on NaN)
+        const float yr = fminf(fmaxf(ydr, lo), hi);
+        const float yl = fminf(fmaxf(-ydr, lo), hi);
+        const float R = (-B * yr + fast_sqrt(fmaxf(0.0f, thrA - det * yr * yr))) * iA + slack;
+        const float L = (-B * yl - fast_sqrt(fmaxf(0.0f, thrA - det * yl * yl))) * iA - slack;
+        // block bx spans [rx0 + 4 bx, rx0 + 4 bx + 3]; keep bx in [ceil((L - rx0 - 3) / 4), floor((R - rx0) / 4)]
+        const float flo = fmaxf(ceilf((L - rx0 - 3.0f) * 0.25f), 0.0f);   // NaN -> 0
+        const float fhi = fminf(floorf((R - rx0) * 0.25f), 3.0f);         // NaN -> 3
+        if (flo <= fhi) mask |= ((2u << (int)fhi) - (1u << (int)flo)) << (4 * by);
     }
     return mask;
+}
+
+// The blocks of each wave's 8 x 8 quadrant (wave w: blocks 2 (w & 1) .. +1,
+// rows 2 (w >> 1) .. +1).
+__device__ __forceinline__ uint32_t quadrant_blocks(int w) {
+    return 0x33u << (2 * (w & 1) + 8 * (w >> 1));
 }
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) void k_composite_fwd(
@@ -141,6 +158,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
     const int tx = tile % TX, ty = tile / TX;
     const int px = tx * kTile + 8 * (wave & 1) + (lane & 7);
     const int py = ty * kTile + 8 * (wave >> 1) + (lane >> 3);
+    const uint32_t qblocks = quadrant_blocks(wave);
     const bool inside = px < W && py < H;
     const float fx = (float)px, fy = (float)py;
     const uint32_t start = ranges[2 * tile], end = ranges[2 * tile + 1];
@@ -162,7 +180,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
             s_conic[tid] = make_float4(-0.5f * co.x, co.y, -0.5f * co.z, co.w);
             s_xyc[tid] = make_float4(xy.x, xy.y, c.x, c.y);
             s_blue[tid] = c.z;
-            s_live[tid] = live_mask(co, xy.x, xy.y, tx * kTile, ty * kTile);
+            s_live[tid] = block_mask(co, xy.x, xy.y, tx * kTile, ty * kTile);
         }
         __syncthreads();
         const int cnt = (int)min((uint32_t)kBatch, end - base);
@@ -172,7 +190,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int k = q * 64 + lane;
-            m[q] = __ballot(k < cnt && ((s_live[k] >> wave) & 1u));
+            m[q] = __ballot(k < cnt && (s_live[k] & qblocks) != 0u);
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -249,14 +267,6 @@ __device__ __forceinline__ float quad_transpose_row_sum(float a0, float a1, floa
     return q;
 }
 
-// Sum of the 16 row partials of one term (16-byte aligned).
-__device__ __forceinline__ float part_sum(const float* p) {
-    const float4* pv = reinterpret_cast<const float4*>(p);
-    const float4 a = pv[0], b = pv[1], c = pv[2], d = pv[3];
-    return (((a.x + a.y) + (a.z + a.w)) + ((b.x + b.y) + (b.z + b.w))) +
-           (((c.x + c.y) + (c.z + c.w)) + ((d.x + d.y) + (d.z + d.w)));
-}
-
 __device__ __forceinline__ void atomic_add_nz(float* p, float v) {
     if (v != 0.0f) unsafeAtomicAdd(p, v);
 }
@@ -289,6 +299,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
     __shared__ uint32_t s_gid[kBwdBatch];
     __shared__ uint32_t s_live[kBwdBatch];
     __shared__ __align__(16) float s_part[kBwdBatch][9][kParts];  // per-row partial sums
+    __shared__ int s_epoch[4][kBwdBatch];  // batch whose partials of slot k wave w wrote last
     __shared__ uint32_t s_maxnc[4];
 
     const int tile = tile_order ? (int)tile_order[blockIdx.x] : (int)blockIdx.x;
@@ -299,6 +310,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
     const int tx = tile % TX, ty = tile / TX;
     const int px = tx * kTile + 8 * (wave & 1) + (lane & 7);
     const int py = ty * kTile + 8 * (wave >> 1) + (lane >> 3);
+    const uint32_t qblocks = quadrant_blocks(wave);
     const bool inside = px < W && py < H;
     const float fx = (float)px, fy = (float)py;
     const uint32_t start = ranges[2 * tile], len = ranges[2 * tile + 1] - start;
@@ -315,6 +327,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
         g2 = dL_dimage[2 * plane + p];
     }
     float B0 = bg.x, B1 = bg.y, B2 = bg.z;
+    if (tid < 4 * kBwdBatch) (&s_epoch[0][0])[tid] = -1;
 
     // per-wave and per-tile maximum of n_contrib
     uint32_t wmax = nc;
@@ -325,11 +338,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
     const int maxnc = (int)max(max(s_maxnc[0], s_maxnc[1]), max(s_maxnc[2], s_maxnc[3]));
     const int wave_maxnc = (int)wmax;
 
-    for (int bend = maxnc; bend > 0; bend -= kBwdBatch) {
+    int batch = 0;
+    for (int bend = maxnc; bend > 0; bend -= kBwdBatch, ++batch) {
         const int bstart = bend > kBwdBatch ? bend - kBwdBatch : 0;
         const int cnt = bend - bstart;
         __syncthreads();  // the previous batch is fully consumed
-        for (int i = tid; i < kBwdBatch * 9 * kParts; i += 256) (&s_part[0][0][0])[i] = 0.0f;
         if (tid < cnt) {
             const uint32_t g = point_list[start + bstart + tid];
             const float4 xy = xy_depth[g];
@@ -339,13 +352,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
             s_xyc[tid] = make_float4(xy.x, xy.y, c.x, c.y);
             s_blue[tid] = c.z;
             s_gid[tid] = g;
-            s_live[tid] = live_mask(co, xy.x, xy.y, tx * kTile, ty * kTile);
+            s_live[tid] = block_mask(co, xy.x, xy.y, tx * kTile, ty * kTile);
         }
+        // fetch the next batch's list entries now, so their latency overlaps this batch
+
         __syncthreads();
 
         // live splats of this wave below its largest n_contrib, walked back to front
         static_assert(kBwdBatch <= 64, "one 64-bit live mask");
-        uint64_t mk = __ballot(lane < cnt && bstart + lane < wave_maxnc && ((s_live[lane] >> wave) & 1u));
+        uint64_t mk = __ballot(lane < cnt && bstart + lane < wave_maxnc && (s_live[lane] & qblocks) != 0u);
         while (mk != 0ull) {
             const int k = 63 - __clzll((long long)mk);
             mk &= ~(1ull << k);
@@ -374,8 +389,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
             // moments of dL/dpower; the conic is applied once per splat afterwards
             const float d0 = dx * dp, d1 = dy * dp;         // sum dx dp, sum dy dp
             const float d2 = dx * d0, d3 = dy * d0, d4 = dy * d1;  // dx^2 dp, dx dy dp, dy^2 dp
-            const bool any = use;
-            if (__ballot(any) != 0ull) {
+            if (__ballot(use) != 0ull) {
                 const float qa = quad_transpose_row_sum(d0, d1, d2, d3, lane_b0, lane_b1);
                 const float qb = quad_transpose_row_sum(d4, d5, d6, d7, lane_b0, lane_b1);
                 const float r8 = dpp_row_sum(d8);
@@ -389,29 +403,49 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
                     s_part[k][4 + j][sl] = qb;
                 }
                 if (j == 0) s_part[k][8][slot] = r8;
+                if (lane == 0) s_epoch[wave][k] = batch;
             }
         }
         __syncthreads();
-        // one thread per splat: sum the 16 row partials of each term, turn
-        // the moments into gradients, one atomic per output
+        // all 256 threads: splat slot k = tid % 32, one output group per
+        // thread (tid / 32): the mean pair, dA, dB, dC, dopacity, r, g, b.
+        // Only the partials of waves that wrote slot k in this batch count.
         //   d(u, v) = (A Sx + B Sy, B Sx + C Sy); dA = -Sxx / 2; dB = -Sxy; dC = -Syy / 2
-        if (tid < cnt) {
-            const float4 co = s_conic[tid];
-            const uint32_t g = s_gid[tid];
-            float* gm = grad_mean2d + 2 * (size_t)g;
-            float* gc = grad_conic_op + 4 * (size_t)g;
-            float* gr = grad_rgb + 4 * (size_t)g;
-            const float Sx = part_sum(s_part[tid][0]), Sy = part_sum(s_part[tid][1]);
-            const float A = -2.0f * co.x, C = -2.0f * co.z;  // exact
-            atomic_add_nz(gm + 0, A * Sx + co.y * Sy);
-            atomic_add_nz(gm + 1, co.y * Sx + C * Sy);
-            atomic_add_nz(gc + 0, -0.5f * part_sum(s_part[tid][2]));
-            atomic_add_nz(gc + 1, -part_sum(s_part[tid][3]));
-            atomic_add_nz(gc + 2, -0.5f * part_sum(s_part[tid][4]));
-            atomic_add_nz(gc + 3, part_sum(s_part[tid][5]));
-            atomic_add_nz(gr + 0, part_sum(s_part[tid][6]));
-            atomic_add_nz(gr + 1, part_sum(s_part[tid][7]));
-            atomic_add_nz(gr + 2, part_sum(s_part[tid][8]));
+        {
+            const int k = tid & (kBwdBatch - 1), grp = tid >> 5;
+            if (k < cnt) {
+                uint32_t wm = 0u;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) wm |= (s_epoch[w][k] == batch ? 1u : 0u) << w;
+                if (wm != 0u) {
+                    const uint32_t g = s_gid[k];
+                    // term t of wave w sits in slots 4 w' .. 4 w' + 3 with w' = w ^ 1 for t = 2, 3, 6, 7
+                    auto term_sum = [&](int t) {
+                        const int flip = (t & 2) ? 1 : 0;
+                        float sum = 0.0f;
+#pragma unroll
+                        for (int w = 0; w < 4; ++w) {
+                            if ((wm >> w) & 1u) {
+                                const float4 q = reinterpret_cast<const float4*>(&s_part[k][t][0])[w ^ flip];
+                                sum += (q.x + q.y) + (q.z + q.w);
+                            }
+                        }
+                        return sum;
+                    };
+                    if (grp == 0) {
+                        const float4 co = s_conic[k];
+                        const float Sx = term_sum(0), Sy = term_sum(1);
+                        const float A = -2.0f * co.x, C = -2.0f * co.z;  // exact
+                        atomic_add_nz(grad_mean2d + 2 * (size_t)g, A * Sx + co.y * Sy);
+                        atomic_add_nz(grad_mean2d + 2 * (size_t)g + 1, co.y * Sx + C * Sy);
+                    } else if (grp <= 4) {
+                        const float scale = grp == 2 ? -1.0f : (grp == 4 ? 1.0f : -0.5f);
+                        atomic_add_nz(grad_conic_op + 4 * (size_t)g + (grp - 1), scale * term_sum(grp + 1));
+                    } else {
+                        atomic_add_nz(grad_rgb + 4 * (size_t)g + (grp - 5), term_sum(grp + 1));
+                    }
+                }
+            }
         }
     }
 }
