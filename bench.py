@@ -36,6 +36,9 @@ WORKLOADS = {
     "cfg3": "1,000,000-Gaussian dense-overdraw scene (80% thick shell, 20% cube), SH degree 3, "
             "1920x1080, forward + backward with dL/dI ~ N(0,1)",
     "cfg1": "160,000-Gaussian procedural scene, SH degree 3, 720x720, forward + backward",
+    "cfg4": "training-step shape: 300,000-Gaussian dense scene, 16 views at 400x400 per step, forward + "
+            "backward with dL/dI = sign(I - I_ref) against a second scene's render; the 16 views are "
+            "recorded once as a HIP graph and replayed",
 }
 # Algorithmic work per unit: a forward pixel-splat evaluation
 # is ~25 fp32 flop-equivalents; a backward one ~45 plus its share of the
@@ -113,6 +116,74 @@ def copy_calibration(mib: int, repeats: int = 3):
     del src, dst
 
 
+def bench_views(args):
+    """The training-step shape: one step renders 16 views of a 300k-Gaussian
+    scene forward and backward (dL/dI = sign(I - I_ref), I_ref rendered once
+    from a second scene), enqueued without host waits and replayed as one HIP
+    graph. frames/s counts views."""
+    import numpy as np
+    import torch
+
+    import synth
+    import gaussian_splatting_tile_amd as gs
+
+    dev = torch.device("cuda:0")
+    n_views = 16
+    scene_np, _, _ = synth.config_scene("cfg4")
+    ref_np, _, _ = synth.config_scene("cfg4_ref")
+    cams = [synth.config_scene("cfg4", view=v)[1] for v in range(n_views)]
+    sc, ref_sc = gs.Scene.from_numpy(scene_np, device=dev), gs.Scene.from_numpy(ref_np, device=dev)
+    rast = gs.Rasterizer(device=dev, capacity=1 << 21)
+    refs, E_max = [], 0
+    for cam in cams:
+        out = rast.forward(cam, ref_sc)
+        refs.append(out["image"].clone())
+        E_max = max(E_max, rast.forward(cam, sc)["n_entries"])
+    torch.cuda.synchronize()
+
+    def loss_grad(i, image, out):
+        out.copy_(image).sub_(refs[i]).sign_()
+
+    batch = gs.ViewBatch(cams, sc, capacity=int(E_max * 1.25) + 1024, device=dev, streams=args.streams)
+    batch.enqueue(loss_grad)
+    E = batch.check()
+    st = torch.cuda.current_stream()
+    # eager: every call launched from the host each step
+    for _ in range(args.warmup):
+        batch.enqueue(loss_grad)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        batch.enqueue(loss_grad)
+    torch.cuda.synchronize()
+    eager_s = (time.perf_counter() - t0) / args.steps
+    # graph: the whole step recorded once
+    batch.capture(loss_grad)
+    for _ in range(args.warmup):
+        batch.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(st)
+    for _ in range(args.steps):
+        batch.replay()
+    e1.record(st)
+    torch.cuda.synchronize()
+    graph_s = (time.perf_counter() - t0) / args.steps
+    if batch.check() != E:
+        raise SystemExit("entry counts changed between runs")
+    return {
+        "metric": METRIC, "value": round(n_views / graph_s, 3), "unit": "frames/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(1e3 * graph_s, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"cfg4: {WORKLOADS['cfg4']}", "n_gaussians": sc.n, "views_per_step": n_views,
+                   "streams": args.streams,
+                   "width": 400, "height": 400, "entries_per_view": E},
+        "secondary": {"eager_frames_per_s": round(n_views / eager_s, 3),
+                      "graph_event_ms_per_step": round(e0.elapsed_time(e1) / args.steps, 4)},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -122,6 +193,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tile-order", choices=("heavy-first", "index"), default="heavy-first",
                     help="tile schedule of the compositing kernels (results are identical)")
+    ap.add_argument("--streams", type=int, default=4,
+                    help="cfg4: streams the 16 views are spread over (fork/join inside the graph)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run device copies of this many MiB (for HBM counter scaling)")
     args = ap.parse_args()
@@ -141,6 +214,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
+    if args.workload == "cfg4":
+        print(json.dumps(bench_views(args)), flush=True)
+        return
     if args.copy_calibration_mib > 0:
         copy_calibration(args.copy_calibration_mib)
 

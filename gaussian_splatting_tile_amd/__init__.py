@@ -8,9 +8,9 @@ on first use; every entry point raises ImportError if it has not been built
 from ._lib import EXPORTS, GsError, LIB_PATH
 from .rasterizer import (BinBuffers, Rasterizer, Scene, bin_and_sort, bin_and_sort_async, camera,
                          composite_bwd, composite_fwd, constants, preprocess, preprocess_bwd, tile_ranges,
-                         tile_ranges_async, tiles_xy, version)
+                         tile_ranges_async, tiles_xy, version, ViewBatch)
 
 __all__ = ["EXPORTS", "GsError", "LIB_PATH", "BinBuffers", "Rasterizer", "Scene", "bin_and_sort",
            "bin_and_sort_async", "camera", "composite_bwd", "composite_fwd", "constants", "preprocess",
            "preprocess_bwd",
-           "tile_ranges", "tile_ranges_async", "tiles_xy", "version"]
+           "tile_ranges", "tile_ranges_async", "tiles_xy", "version", "ViewBatch"]

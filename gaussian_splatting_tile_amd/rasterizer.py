@@ -14,6 +14,7 @@ import numpy as np
 import torch
 
 from . import _lib
+from ._lib import GsError
 
 TILE = 16
 
@@ -323,3 +324,121 @@ class Rasterizer:
             g.update(preprocess_bwd(cam, scene.means, scene.scales, scene.quats, scene.sh, scene.sh_degree,
                                     fwd["tiles_touched"], g["grad_mean2d"], g["grad_conic_op"], g["grad_rgb"]))
         return g
+
+
+class ViewBatch:
+    """Forward and backward of one scene seen from a fixed list of cameras,
+    enqueued with no host synchronisation (asynchronous binning keeps each
+    view's entry count on the device), so the whole batch can be recorded
+    once as a HIP graph and replayed.
+
+    Each view owns its buffers, sized for `capacity` entries. A view whose
+    entry count exceeds the capacity renders the background; `entries()`
+    reads every view's count after a run (one wait per batch, not per frame)
+    and `check()` raises if any view overflowed.
+
+    loss_grad(view, image, out): writes dL/dI of that view into `out`
+    ([3, H, W] float32) from its rendered image; it is enqueued on the same
+    stream between the forward and the backward, so it must not allocate or
+    synchronise if the batch is to be captured.
+    """
+
+    def __init__(self, cams, scene: "Scene", capacity: int, device="cuda", bg=(0.0, 0.0, 0.0),
+                 tile_order=True, streams: int = 1):
+        self.device = torch.device(device)
+        self.scene = scene
+        self.bg = bg
+        self.views = []
+        # views are spread round-robin over `streams` streams (default
+        # priority), so small frames that cannot fill the GPU alone overlap
+        self.streams = [torch.cuda.Stream(device=self.device) for _ in range(streams)] if streams > 1 else []
+        n = scene.n
+        f32, i32 = torch.float32, torch.int32
+        for cam in cams:
+            c = camera(cam)
+            W, H = int(cam["width"]), int(cam["height"])
+            TX, TY = tiles_xy(cam)
+            bins = BinBuffers(self.device, capacity)
+            bins.scratch_for(c, n)
+            v = dict(
+                cam=cam, c=c, bins=bins,
+                pre=dict(xy_depth=torch.empty((n, 4), dtype=f32, device=self.device),
+                         conic_op=torch.empty((n, 4), dtype=f32, device=self.device),
+                         rgb=torch.empty((n, 4), dtype=f32, device=self.device),
+                         tiles_touched=torch.empty((n,), dtype=i32, device=self.device)),
+                ranges=torch.empty((TX * TY, 2), dtype=i32, device=self.device),
+                order=torch.empty((TX * TY,), dtype=i32, device=self.device) if tile_order else None,
+                fwd=dict(image=torch.empty((3, H, W), dtype=f32, device=self.device),
+                         final_T=torch.empty((H, W), dtype=f32, device=self.device),
+                         n_contrib=torch.empty((H, W), dtype=i32, device=self.device)),
+                dL_dimage=torch.zeros((3, H, W), dtype=f32, device=self.device),
+                grads=dict(grad_mean2d=torch.empty((n, 2), dtype=f32, device=self.device),
+                           grad_conic_op=torch.empty((n, 4), dtype=f32, device=self.device),
+                           grad_rgb=torch.empty((n, 4), dtype=f32, device=self.device)))
+            self.views.append(v)
+        self.graph = None
+
+    def enqueue(self, loss_grad=None):
+        """Enqueue every view on the current stream (forked over the batch's
+        streams and joined back when it has several): preprocess, binning,
+        ranges, forward, loss_grad (if given), backward. Nothing waits on the
+        host."""
+        main = torch.cuda.current_stream(self.device)
+        if self.streams:
+            fork = torch.cuda.Event()
+            fork.record(main)
+            for s in self.streams:
+                s.wait_event(fork)
+        for i, v in enumerate(self.views):
+            s = self.streams[i % len(self.streams)] if self.streams else main
+            with torch.cuda.stream(s):
+                self._enqueue_view(i, v, loss_grad)
+        for s in self.streams:
+            join = torch.cuda.Event()
+            join.record(s)
+            main.wait_event(join)
+
+    def _enqueue_view(self, i, v, loss_grad):
+        sc = self.scene
+        c, pre, bins = v["c"], v["pre"], v["bins"]
+        preprocess(c, sc.means, sc.scales, sc.quats, sc.opacity, sc.sh, sc.sh_degree, sc.rgb, out=pre)
+        keys, pl = bin_and_sort_async(c, pre["xy_depth"], pre["tiles_touched"], bins)
+        tile_ranges_async(c, bins, out=v["ranges"], order=v["order"])
+        composite_fwd(c, v["ranges"], pl, pre["xy_depth"], pre["conic_op"], pre["rgb"], self.bg,
+                      out=v["fwd"], order=v["order"])
+        if loss_grad is not None:
+            loss_grad(i, v["fwd"]["image"], v["dL_dimage"])
+        composite_bwd(c, sc.n, v["ranges"], pl, pre["xy_depth"], pre["conic_op"], pre["rgb"],
+                      v["fwd"]["final_T"], v["fwd"]["n_contrib"], v["dL_dimage"], self.bg,
+                      out=v["grads"], order=v["order"])
+
+    def capture(self, loss_grad=None, warmup: int = 1):
+        """Record enqueue(loss_grad) as one HIP graph (after `warmup` eager runs
+        on a side stream, as graph capture requires)."""
+        s = torch.cuda.Stream(device=self.device)
+        s.wait_stream(torch.cuda.current_stream(self.device))
+        with torch.cuda.stream(s):
+            for _ in range(warmup):
+                self.enqueue(loss_grad)
+        torch.cuda.current_stream(self.device).wait_stream(s)
+        torch.cuda.synchronize(self.device)
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self.enqueue(loss_grad)
+        return self.graph
+
+    def replay(self):
+        if self.graph is None:
+            raise RuntimeError("ViewBatch.replay: capture() first")
+        self.graph.replay()
+
+    def entries(self):
+        """Entry count of every view after the last run (waits for the stream)."""
+        return [v["bins"].entries() for v in self.views]
+
+    def check(self):
+        E = self.entries()
+        over = [(i, e) for i, e in enumerate(E) if e > self.views[i]["bins"].capacity]
+        if over:
+            raise GsError(_lib.GS_ERR_CAPACITY, f"views over capacity (view, entries): {over}")
+        return E
