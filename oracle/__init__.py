@@ -66,6 +66,14 @@ def lib():
         _lib.orc_preprocess.restype = ctypes.c_int
         _lib.orc_preprocess.argtypes = [ctypes.POINTER(Camera), ctypes.c_int32, P, P, P, P, P,
                                         ctypes.c_int32, P, P, P, P, P]
+        _lib.orc_preprocess_ex.restype = ctypes.c_int
+        _lib.orc_preprocess_ex.argtypes = [ctypes.POINTER(Camera), ctypes.c_int32, P, P, P, P, P,
+                                           ctypes.c_int32, P, P, P, P, P, ctypes.c_int32]
+        _lib.orc_bin_ex.restype = ctypes.c_int64
+        _lib.orc_bin_ex.argtypes = [ctypes.POINTER(Camera), ctypes.c_int32, P, P, P, P, P, ctypes.c_int64,
+                                    ctypes.c_int32]
+        _lib.orc_ellipse_row_range.restype = None
+        _lib.orc_ellipse_row_range.argtypes = [ctypes.c_float] * 6 + [ctypes.c_int32] * 3 + [P]
         _lib.orc_bin.restype = ctypes.c_int64
         _lib.orc_bin.argtypes = [ctypes.POINTER(Camera), ctypes.c_int32, P, P, P, P, ctypes.c_int64]
         _lib.orc_tile_ranges.restype = None
@@ -156,8 +164,9 @@ def sort_pairs(keys, values):
     return keys, values
 
 
-def preprocess(cam: dict, scene: dict):
-    """Returns dict of xy_depth [n,4], conic_op [n,4], rgb [n,4], tiles_touched [n]."""
+def preprocess(cam: dict, scene: dict, tile_test: int = 0):
+    """Returns dict of xy_depth [n,4], conic_op [n,4], rgb [n,4], tiles_touched [n].
+    tile_test: 0 = every tile of the span rectangle, 1 = the ellipse test."""
     n = int(scene["n"])
     means = _c(scene["means"], np.float32)
     scales = _c(scene["scales"], np.float32)
@@ -171,9 +180,9 @@ def preprocess(cam: dict, scene: dict):
     out = dict(xy_depth=np.zeros((n, 4), np.float32), conic_op=np.zeros((n, 4), np.float32),
                rgb=np.zeros((n, 4), np.float32), tiles_touched=np.zeros(n, np.uint32))
     c = make_camera(cam)
-    rc = lib().orc_preprocess(ctypes.byref(c), n, _p(means), _p(scales), _p(quats), _p(opacity),
-                              _p(sh), deg, _p(rgb_in), _p(out["xy_depth"]), _p(out["conic_op"]),
-                              _p(out["rgb"]), _p(out["tiles_touched"]))
+    rc = lib().orc_preprocess_ex(ctypes.byref(c), n, _p(means), _p(scales), _p(quats), _p(opacity),
+                                 _p(sh), deg, _p(rgb_in), _p(out["xy_depth"]), _p(out["conic_op"]),
+                                 _p(out["rgb"]), _p(out["tiles_touched"]), int(tile_test))
     if rc != 0:
         raise ValueError("orc_preprocess rejected its arguments")
     return out
@@ -227,18 +236,22 @@ def project_f64(cam: dict, mean, scale, quat, sh_coef=None, rgb=None):
                 clamp=(bool(out[8]), bool(out[9])))
 
 
-def bin_and_sort(cam: dict, xy_depth, tiles_touched):
-    """Returns (keys u64 [E], point_list u32 [E])."""
+def bin_and_sort(cam: dict, xy_depth, tiles_touched, conic_op=None, tile_test: int = 0):
+    """Returns (keys u64 [E], point_list u32 [E]). tile_test 1 (the ellipse
+    test) needs conic_op."""
     xy_depth = _c(xy_depth, np.float32)
     tiles_touched = _c(tiles_touched, np.uint32)
+    conic_op = None if conic_op is None else _c(conic_op, np.float32)
     n = tiles_touched.shape[0]
     c = make_camera(cam)
-    E = lib().orc_bin(ctypes.byref(c), n, _p(xy_depth), _p(tiles_touched), None, None, 0)
+    E = lib().orc_bin_ex(ctypes.byref(c), n, _p(xy_depth), _p(conic_op), _p(tiles_touched), None, None, 0,
+                         int(tile_test))
     if E < 0:
         raise ValueError("orc_bin rejected its arguments")
     keys = np.zeros(max(E, 1), np.uint64)
     vals = np.zeros(max(E, 1), np.uint32)
-    E2 = lib().orc_bin(ctypes.byref(c), n, _p(xy_depth), _p(tiles_touched), _p(keys), _p(vals), E)
+    E2 = lib().orc_bin_ex(ctypes.byref(c), n, _p(xy_depth), _p(conic_op), _p(tiles_touched), _p(keys),
+                          _p(vals), E, int(tile_test))
     assert E2 == E
     return keys[:E], vals[:E]
 
@@ -288,10 +301,19 @@ def composite_bwd(cam: dict, n: int, ranges, point_list, xy_depth, conic_op, rgb
     return out
 
 
-def render_fwd(cam: dict, scene: dict, bg=(0.0, 0.0, 0.0)):
+def ellipse_row_range(u, v, r, conic, TX, TY, ty):
+    """Kept tiles [lo, hi) of row ty under the ellipse test."""
+    out = np.zeros(2, np.int32)
+    f = lambda x: float(np.float32(x))
+    lib().orc_ellipse_row_range(f(u), f(v), f(r), f(conic[0]), f(conic[1]), f(conic[2]), int(TX), int(TY),
+                                int(ty), _p(out))
+    return int(out[0]), int(out[1])
+
+
+def render_fwd(cam: dict, scene: dict, bg=(0.0, 0.0, 0.0), tile_test: int = 0):
     """All forward stages; returns a dict with every intermediate."""
-    pre = preprocess(cam, scene)
-    keys, point_list = bin_and_sort(cam, pre["xy_depth"], pre["tiles_touched"])
+    pre = preprocess(cam, scene, tile_test)
+    keys, point_list = bin_and_sort(cam, pre["xy_depth"], pre["tiles_touched"], pre["conic_op"], tile_test)
     ranges = tile_ranges(cam, keys)
     fwd = composite_fwd(cam, ranges, point_list, pre["xy_depth"], pre["conic_op"], pre["rgb"], bg)
     out = dict(pre)

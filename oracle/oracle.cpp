@@ -136,6 +136,65 @@ Span tile_span(float u, float v, float r, int TX, int TY) {
     return Span{(int)x0, (int)x1, (int)y0, (int)y1};
 }
 
+// Ellipse tile test ([zenn] 2.3.4: of the tiles in the span rectangle, keep
+// those the splat's ellipse may overlap). The page does not give the test;
+// the reading taken: the ellipse is the region where the splat can reach
+// alpha >= 1/255, Q(d) = A dx^2 + 2B dx dy + C dy^2 <= 2 ln(255 o) <= 2 ln 255,
+// taken with the opacity-independent threshold 11.1 (> 2 ln 255 = 11.0825)
+// raised by a bound on the compositing's fp32 rounding of Q, so a dropped
+// tile holds no pixel the splat changes and the image is unchanged. Per
+// row of tiles, the kept tiles are those whose pixel centres meet the
+// x-extent [L, R] of the ellipse's slice over the row's pixel-centre
+// y-range; L and R are the slice edges at the dy of the ellipse's leftmost
+// and rightmost points, clamped into the row (the edges are convex and
+// concave in dy), widened by a slack. Every step is + - * / sqrt floor ceil
+// fminf fmaxf in float32 in the order written, so the kernels can take the
+// identical decision. A conic that is not positive definite, or anything
+// not finite, keeps the whole span.
+struct EllipseRows {
+    bool full;  // keep every tile of the span
+    float u, v, A, B, C, det, hx, hy, ydr, slack, thr;
+};
+
+EllipseRows ellipse_rows(float u, float v, float A, float B, float C, const Span& sp) {
+    EllipseRows e;
+    e.u = u; e.v = v; e.A = A; e.B = B; e.C = C;
+    e.det = A * C - B * B;
+    e.full = !(e.det > 0.0f && A > 0.0f && C > 0.0f);
+    // farthest pixel centre of the span from the centre, per axis
+    const float ex = fmaxf(fabsf(16.0f * (float)sp.x0 - u), fabsf(16.0f * (float)sp.x1 - 1.0f - u));
+    const float ey = fmaxf(fabsf(16.0f * (float)sp.y0 - v), fabsf(16.0f * (float)sp.y1 - 1.0f - v));
+    const float bound = 64.0f * 5.96e-8f * ((fabsf(A) + fabsf(C)) + 2.0f * fabsf(B)) * (ex * ex + ey * ey);
+    e.thr = 11.1f + bound;
+    if (e.full) return e;
+    e.hy = std::sqrt((e.thr * A) / e.det);
+    e.hx = std::sqrt((e.thr * C) / e.det);
+    e.ydr = -(B * e.hx) / C;
+    e.slack = 0.01f + 1e-4f * (e.hx + e.hy);
+    if (!std::isfinite(e.hx) || !std::isfinite(e.hy) || !std::isfinite(e.ydr) || !std::isfinite(e.slack))
+        e.full = true;
+    return e;
+}
+
+// Kept tiles [lo, hi) of row ty (within the span's [x0, x1)); lo >= hi: none.
+void ellipse_row_range(const EllipseRows& e, const Span& sp, int ty, int* lo_out, int* hi_out) {
+    if (e.full) { *lo_out = sp.x0; *hi_out = sp.x1; return; }
+    const float ylo = 16.0f * (float)ty - e.v;
+    const float lo = fmaxf(ylo, -e.hy), hi = fminf(ylo + 15.0f, e.hy);
+    if (lo > hi + e.slack) { *lo_out = sp.x0; *hi_out = sp.x0; return; }
+    const float yr = fminf(fmaxf(e.ydr, lo), hi);
+    const float yl = fminf(fmaxf(-e.ydr, lo), hi);
+    const float thrA = e.thr * e.A;
+    const float R = (-(e.B * yr) + std::sqrt(fmaxf(0.0f, thrA - (e.det * yr) * yr))) / e.A + e.slack;
+    const float L = (-(e.B * yl) - std::sqrt(fmaxf(0.0f, thrA - (e.det * yl) * yl))) / e.A - e.slack;
+    // tile tx has pixel centres [16 tx - u, 16 tx + 15 - u]
+    const float tlo = fmaxf(std::ceil(((L + e.u) - 15.0f) / 16.0f), (float)sp.x0);
+    const float thi = fminf(std::floor((R + e.u) / 16.0f) + 1.0f, (float)sp.x1);
+    if (!(tlo < thi)) { *lo_out = sp.x0; *hi_out = sp.x0; return; }
+    *lo_out = (int)tlo;
+    *hi_out = (int)thi;
+}
+
 inline uint32_t float_bits(float f) {
     uint32_t b;
     std::memcpy(&b, &f, 4);
@@ -488,12 +547,12 @@ void orc_sh_basis(float x, float y, float z, float* out16) { sh_basis(x, y, z, o
 // (r, g, b, 0), tiles_touched. A culled Gaussian gets all-zero outputs; a
 // Gaussian whose opacity or colour is not finite is culled as well.
 // Returns 0, or -1 on an invalid argument.
-int orc_preprocess(const orc_camera* cam, int32_t n, const float* means,
-                   const float* scales, const float* quats, const float* opacity,
-                   const float* sh, int32_t sh_degree, const float* rgb_in,
-                   float* xy_depth, float* conic_op, float* rgb,
-                   uint32_t* tiles_touched) {
-    if (!cam || n < 0) return -1;
+int orc_preprocess_ex(const orc_camera* cam, int32_t n, const float* means,
+                      const float* scales, const float* quats, const float* opacity,
+                      const float* sh, int32_t sh_degree, const float* rgb_in,
+                      float* xy_depth, float* conic_op, float* rgb,
+                      uint32_t* tiles_touched, int32_t tile_test) {
+    if (!cam || n < 0 || tile_test < 0 || tile_test > 1) return -1;
     if (sh && (sh_degree < 0 || sh_degree > 3)) return -1;
     const int TX = tiles_x(cam), TY = tiles_y(cam);
     const int n_coef = sh ? (sh_degree + 1) * (sh_degree + 1) : 0;
@@ -511,9 +570,19 @@ int orc_preprocess(const orc_camera* cam, int32_t n, const float* means,
         Projected<float> P;
         if (!project_gaussian<float>(cam, m, s3, q, sh ? sh_g : nullptr, n_coef, rgb_g, &P)) continue;
 
-        // Tile span; nothing on screen means culled.
+        // Tile span; nothing on screen means culled. With the ellipse test,
+        // only the tiles it keeps are counted (none kept: culled).
         const Span sp = tile_span(P.u, P.v, P.r, TX, TY);
-        const int count = (sp.x1 - sp.x0) * (sp.y1 - sp.y0);
+        int count = (sp.x1 - sp.x0) * (sp.y1 - sp.y0);
+        if (count > 0 && tile_test == 1) {
+            const EllipseRows er = ellipse_rows(P.u, P.v, P.A, P.B, P.C, sp);
+            count = 0;
+            for (int ty = sp.y0; ty < sp.y1; ++ty) {
+                int lo, hi;
+                ellipse_row_range(er, sp, ty, &lo, &hi);
+                count += hi > lo ? hi - lo : 0;
+            }
+        }
         if (count <= 0) continue;
         if (!std::isfinite(opacity[g]) || !std::isfinite(P.col[0]) || !std::isfinite(P.col[1]) ||
             !std::isfinite(P.col[2])) continue;
@@ -602,6 +671,26 @@ int orc_project_f64(const orc_camera* cam, const double* m, const double* s3, co
     return 1;
 }
 
+int orc_preprocess(const orc_camera* cam, int32_t n, const float* means,
+                   const float* scales, const float* quats, const float* opacity,
+                   const float* sh, int32_t sh_degree, const float* rgb_in,
+                   float* xy_depth, float* conic_op, float* rgb,
+                   uint32_t* tiles_touched) {
+    return orc_preprocess_ex(cam, n, means, scales, quats, opacity, sh, sh_degree, rgb_in, xy_depth,
+                             conic_op, rgb, tiles_touched, 0);
+}
+
+// Kept tile range [lo, hi) of row ty for one splat under the ellipse test
+// (exposed for the pins): out = lo, hi.
+void orc_ellipse_row_range(float u, float v, float r, float A, float B, float C, int32_t TX,
+                           int32_t TY, int32_t ty, int32_t* out) {
+    const Span sp = tile_span(u, v, r, TX, TY);
+    const EllipseRows er = ellipse_rows(u, v, A, B, C, sp);
+    int lo, hi;
+    ellipse_row_range(er, sp, ty, &lo, &hi);
+    out[0] = lo; out[1] = hi;
+}
+
 // Tile span of one splat (exposed for the pins): out = x0, x1, y0, y1.
 void orc_tile_span(float u, float v, float r, int32_t TX, int32_t TY, int32_t* out) {
     const Span sp = tile_span(u, v, r, TX, TY);
@@ -624,25 +713,50 @@ uint64_t orc_exclusive_scan(const uint32_t* counts, int64_t n, uint64_t* offsets
 //   [rigel] "Binning" (the key), [zenn] 4.2 (pair_key / pair_value, written
 //   at offsets), [learn-gs] build_tile_lists (tile_id = ty*TX + tx).
 // Returns 0, or -2 if a Gaussian's span disagrees with its count.
-int orc_duplicate(const orc_camera* cam, int32_t n, const float* xy_depth,
-                  const uint32_t* tiles_touched, const uint64_t* offsets,
-                  uint64_t* keys, uint32_t* values) {
+// With tile_test == 1 (conic_op given) only the tiles the ellipse test
+// keeps are written, in the same order.
+int orc_duplicate_ex(const orc_camera* cam, int32_t n, const float* xy_depth, const float* conic_op,
+                     const uint32_t* tiles_touched, const uint64_t* offsets,
+                     uint64_t* keys, uint32_t* values, int32_t tile_test) {
     const int TX = tiles_x(cam), TY = tiles_y(cam);
     for (int g = 0; g < n; ++g) {
         if (tiles_touched[g] == 0) continue;
         const float* rec = xy_depth + 4 * (size_t)g;
         const Span sp = tile_span(rec[0], rec[1], rec[3], TX, TY);
-        if ((uint32_t)((sp.x1 - sp.x0) * (sp.y1 - sp.y0)) != tiles_touched[g]) return -2;
         const uint64_t depth_bits = float_bits(rec[2]);
-        uint64_t k = offsets[g];
-        for (int ty = sp.y0; ty < sp.y1; ++ty)
-            for (int tx = sp.x0; tx < sp.x1; ++tx) {
-                keys[k] = ((uint64_t)(ty * TX + tx) << 32) | depth_bits;
-                values[k] = (uint32_t)g;
-                ++k;
+        const uint64_t k0 = offsets[g];
+        uint64_t k = k0;
+        if (tile_test == 1) {
+            const float* co = conic_op + 4 * (size_t)g;
+            const EllipseRows er = ellipse_rows(rec[0], rec[1], co[0], co[1], co[2], sp);
+            for (int ty = sp.y0; ty < sp.y1; ++ty) {
+                int lo, hi;
+                ellipse_row_range(er, sp, ty, &lo, &hi);
+                for (int tx = lo; tx < hi; ++tx) {
+                    if (k - k0 >= tiles_touched[g]) return -2;
+                    keys[k] = ((uint64_t)(ty * TX + tx) << 32) | depth_bits;
+                    values[k] = (uint32_t)g;
+                    ++k;
+                }
             }
+        } else {
+            if ((uint32_t)((sp.x1 - sp.x0) * (sp.y1 - sp.y0)) != tiles_touched[g]) return -2;
+            for (int ty = sp.y0; ty < sp.y1; ++ty)
+                for (int tx = sp.x0; tx < sp.x1; ++tx) {
+                    keys[k] = ((uint64_t)(ty * TX + tx) << 32) | depth_bits;
+                    values[k] = (uint32_t)g;
+                    ++k;
+                }
+        }
+        if (k - k0 != tiles_touched[g]) return -2;
     }
     return 0;
+}
+
+int orc_duplicate(const orc_camera* cam, int32_t n, const float* xy_depth,
+                  const uint32_t* tiles_touched, const uint64_t* offsets,
+                  uint64_t* keys, uint32_t* values) {
+    return orc_duplicate_ex(cam, n, xy_depth, nullptr, tiles_touched, offsets, keys, values, 0);
 }
 
 // One stable sort of the pairs by key, ascending: ties keep their input
@@ -660,16 +774,24 @@ void orc_sort_pairs(uint64_t* keys, uint32_t* values, int64_t n) {
 // Binning end to end: scan, duplicate, sort. Returns the entry count E (also
 // when capacity < E, in which case nothing is written), -1 on an invalid
 // argument, -2 if a count disagrees with its span.
-int64_t orc_bin(const orc_camera* cam, int32_t n, const float* xy_depth,
-                const uint32_t* tiles_touched, uint64_t* keys, uint32_t* point_list,
-                int64_t capacity) {
-    if (!cam || n < 0) return -1;
+int64_t orc_bin_ex(const orc_camera* cam, int32_t n, const float* xy_depth, const float* conic_op,
+                   const uint32_t* tiles_touched, uint64_t* keys, uint32_t* point_list,
+                   int64_t capacity, int32_t tile_test) {
+    if (!cam || n < 0 || tile_test < 0 || tile_test > 1 || (tile_test == 1 && !conic_op)) return -1;
     std::vector<uint64_t> offsets((size_t)n);
     const uint64_t total = orc_exclusive_scan(tiles_touched, n, offsets.data());
     if ((int64_t)total > capacity) return (int64_t)total;
-    if (orc_duplicate(cam, n, xy_depth, tiles_touched, offsets.data(), keys, point_list) != 0) return -2;
+    if (orc_duplicate_ex(cam, n, xy_depth, conic_op, tiles_touched, offsets.data(), keys, point_list,
+                         tile_test) != 0)
+        return -2;
     orc_sort_pairs(keys, point_list, (int64_t)total);
     return (int64_t)total;
+}
+
+int64_t orc_bin(const orc_camera* cam, int32_t n, const float* xy_depth,
+                const uint32_t* tiles_touched, uint64_t* keys, uint32_t* point_list,
+                int64_t capacity) {
+    return orc_bin_ex(cam, n, xy_depth, nullptr, tiles_touched, keys, point_list, capacity, 0);
 }
 
 // Tile ranges over the sorted keys: ranges[t] = [start, end) of tile t's
