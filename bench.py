@@ -261,7 +261,7 @@ def main():
     del probe
     log(f"[bench] n={n} E={E} evals fwd={evals_fwd} bwd={evals_bwd}")
 
-    def step(marks=None, stage_marks=False):
+    def step(marks=None, stage_marks=False, tile_test=0):
         """One frame. `marks` (a list) receives HIP events recorded on the
         kernels' stream: around the two compositing kernels, or at every
         stage boundary when stage_marks is set."""
@@ -272,9 +272,10 @@ def main():
                 marks.append(e)
         mark(False)
         gs.preprocess(c, scene.means, scene.scales, scene.quats, scene.opacity, scene.sh,
-                      scene.sh_degree, scene.rgb, out=pre)
+                      scene.sh_degree, scene.rgb, out=pre, tile_test=tile_test)
         mark(False)
-        k, p = gs.bin_and_sort_async(c, pre["xy_depth"], pre["tiles_touched"], bins)
+        k, p = gs.bin_and_sort_async(c, pre["xy_depth"], pre["tiles_touched"], bins, conic_op=pre["conic_op"],
+                                     tile_test=tile_test)
         mark(False)
         gs.tile_ranges_async(c, bins, out=ranges, order=order)
         mark(True)
@@ -315,6 +316,20 @@ def main():
     for i, s in enumerate(STAGES):
         vals = [m[i].elapsed_time(m[i + 1]) for m in staged]
         stage_ms[s] = float(np.median(vals)), float(np.mean(vals))
+    # The same frames with the ellipse tile test (identical image, shorter
+    # lists): timed the same way, reported as a secondary figure.
+    for _ in range(args.warmup):
+        step(tile_test=1)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(tile_test=1)
+    torch.cuda.synchronize()
+    ellipse_fps = args.steps / (time.perf_counter() - t0)
+    E_ellipse = bins.entries()
+    step()  # back to the square spans for what follows
+    torch.cuda.synchronize()
+
     # The projection backward (gs_preprocess_bwd) is the step after this
     # path: timed on its own, over the same frame's splat gradients.
     pgrads = gs.preprocess_bwd(c, scene.means, scene.scales, scene.quats, scene.sh, scene.sh_degree,
@@ -376,6 +391,8 @@ def main():
             "composite_fwd_tflops": round(evals_fwd * FLOPS_PER_FWD_EVAL / fwd_s / 1e12, 4),
             "composite_fwd_frac": round(evals_fwd * FLOPS_PER_FWD_EVAL / fwd_s / PEAK_FP32_VECTOR, 5),
             "entries_per_s": round(E / sort_s, 1),
+            "ellipse_tile_test_frames_per_s": round(ellipse_fps, 3),
+            "ellipse_tile_test_n_entries": E_ellipse,
             "preprocess_bwd_ms": round(pbwd_s * 1e3, 4),
             "preprocess_bwd_hbm_frac": round(pbwd_bytes / pbwd_s / PEAK_HBM, 4),
         },

@@ -8,12 +8,13 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgs.so")
 
 GS_OK, GS_ERR_INVALID, GS_ERR_CAPACITY, GS_ERR_OVERFLOW, GS_ERR_HIP = range(5)
+GS_TILES_SQUARE, GS_TILES_ELLIPSE = 0, 1
 STATUS_NAMES = {0: "GS_OK", 1: "GS_ERR_INVALID", 2: "GS_ERR_CAPACITY", 3: "GS_ERR_OVERFLOW",
                 4: "GS_ERR_HIP"}
 
 # Every symbol include/gs.h declares.
-EXPORTS = ("gs_constants", "gs_last_error", "gs_version", "gs_preprocess", "gs_preprocess_bwd",
-           "gs_bin_and_sort",
+EXPORTS = ("gs_constants", "gs_last_error", "gs_version", "gs_preprocess", "gs_preprocess_ex",
+           "gs_preprocess_bwd", "gs_bin_and_sort", "gs_bin_and_sort_ex", "gs_bin_and_sort_async_ex",
            "gs_bin_and_sort_async", "gs_tile_ranges", "gs_tile_ranges_async", "gs_composite_fwd",
            "gs_composite_bwd")
 
@@ -44,7 +45,7 @@ def load() -> ctypes.CDLL:
                           "`python -m gaussian_splatting_tile_amd.build` (or __graft_entry__.build())")
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.c_void_p
-    I32, I64 = ctypes.c_int32, ctypes.c_int64
+    I32, I64, U32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32
     CAM = ctypes.POINTER(GsCamera)
     lib.gs_constants.restype = None
     lib.gs_constants.argtypes = [P]
@@ -54,6 +55,14 @@ def load() -> ctypes.CDLL:
     lib.gs_version.argtypes = [P]
     lib.gs_preprocess.restype = ctypes.c_int
     lib.gs_preprocess.argtypes = [CAM, I32, P, P, P, P, P, I32, P, P, P, P, P, P]
+    lib.gs_preprocess_ex.restype = ctypes.c_int
+    lib.gs_preprocess_ex.argtypes = [CAM, I32, P, P, P, P, P, I32, P, P, P, P, P, U32, P]
+    lib.gs_bin_and_sort_ex.restype = ctypes.c_int
+    lib.gs_bin_and_sort_ex.argtypes = [CAM, I32, P, P, P, P, P, I64, P, ctypes.POINTER(ctypes.c_size_t),
+                                       ctypes.POINTER(ctypes.c_int64), U32, P]
+    lib.gs_bin_and_sort_async_ex.restype = ctypes.c_int
+    lib.gs_bin_and_sort_async_ex.argtypes = [CAM, I32, P, P, P, P, P, I64, P, ctypes.POINTER(ctypes.c_size_t),
+                                             P, U32, P]
     lib.gs_preprocess_bwd.restype = ctypes.c_int
     lib.gs_preprocess_bwd.argtypes = [CAM, I32, P, P, P, P, I32, P, P, P, P, P, P, P, P, P, P, P]
     lib.gs_bin_and_sort.restype = ctypes.c_int

@@ -68,12 +68,13 @@ void gs_version(int32_t out[3]) {
     out[2] = 0;
 }
 
-gs_status gs_preprocess(const gs_camera* cam, int32_t n, const float* means, const float* scales,
-                        const float* quats, const float* opacity, const float* sh,
-                        int32_t sh_degree, const float* rgb_in, float* xy_depth, float* conic_op,
-                        float* rgb, uint32_t* tiles_touched, void* stream) {
+gs_status gs_preprocess_ex(const gs_camera* cam, int32_t n, const float* means, const float* scales,
+                           const float* quats, const float* opacity, const float* sh,
+                           int32_t sh_degree, const float* rgb_in, float* xy_depth, float* conic_op,
+                           float* rgb, uint32_t* tiles_touched, uint32_t flags, void* stream) {
     g_last_error.clear();
     if (gs_status s = check_camera(cam)) return s;
+    if (flags & ~(uint32_t)GS_TILES_ELLIPSE) return fail(GS_ERR_INVALID, "unknown flags 0x%x", flags);
     if (n < 0 || n > GS_MAX_GAUSSIANS) return fail(GS_ERR_INVALID, "n = %d outside [0, %d]", n, GS_MAX_GAUSSIANS);
     if (n == 0) return GS_OK;
     if (!means || !scales || !quats || !opacity || !xy_depth || !conic_op || !rgb || !tiles_touched)
@@ -87,8 +88,16 @@ gs_status gs_preprocess(const gs_camera* cam, int32_t n, const float* means, con
         return fail(GS_ERR_INVALID, "gs_preprocess: float4 outputs must be 16-byte aligned");
     return hip_check(gs::launch_preprocess(*cam, n, means, scales, quats, opacity, sh, sh_degree,
                                            rgb_in, (float4*)xy_depth, (float4*)conic_op,
-                                           (float4*)rgb, tiles_touched, (hipStream_t)stream),
+                                           (float4*)rgb, tiles_touched, flags, (hipStream_t)stream),
                      "gs_preprocess launch");
+}
+
+gs_status gs_preprocess(const gs_camera* cam, int32_t n, const float* means, const float* scales,
+                        const float* quats, const float* opacity, const float* sh,
+                        int32_t sh_degree, const float* rgb_in, float* xy_depth, float* conic_op,
+                        float* rgb, uint32_t* tiles_touched, void* stream) {
+    return gs_preprocess_ex(cam, n, means, scales, quats, opacity, sh, sh_degree, rgb_in, xy_depth, conic_op,
+                            rgb, tiles_touched, GS_TILES_SQUARE, stream);
 }
 
 gs_status gs_preprocess_bwd(const gs_camera* cam, int32_t n, const float* means, const float* scales,
@@ -151,12 +160,21 @@ gs_status bin_args(const char* fn, const gs_camera* cam, int32_t n, const float*
     return GS_OK;
 }
 
+// The tile-test flags of the binning entry points: the ellipse test reads
+// the conic of every splat.
+gs_status tile_test_args(const char* fn, int32_t n, const float* conic_op, uint32_t flags) {
+    if (flags & ~(uint32_t)GS_TILES_ELLIPSE) return fail(GS_ERR_INVALID, "%s: unknown flags 0x%x", fn, flags);
+    if ((flags & GS_TILES_ELLIPSE) && n > 0 && (!conic_op || ((uintptr_t)conic_op & 15)))
+        return fail(GS_ERR_INVALID, "%s: the ellipse test needs a 16-byte aligned conic_op", fn);
+    return GS_OK;
+}
+
 }  // namespace
 
-gs_status gs_bin_and_sort(const gs_camera* cam, int32_t n, const float* xy_depth,
-                          const uint32_t* tiles_touched, uint64_t* keys, uint32_t* point_list,
-                          int64_t capacity, void* scratch, size_t* scratch_bytes,
-                          int64_t* n_entries, void* stream) {
+gs_status gs_bin_and_sort_ex(const gs_camera* cam, int32_t n, const float* xy_depth, const float* conic_op,
+                             const uint32_t* tiles_touched, uint64_t* keys, uint32_t* point_list,
+                             int64_t capacity, void* scratch, size_t* scratch_bytes, int64_t* n_entries,
+                             uint32_t flags, void* stream) {
     g_last_error.clear();
     gs::BinScratch s{};
     bool query = false;
@@ -164,12 +182,14 @@ gs_status gs_bin_and_sort(const gs_camera* cam, int32_t n, const float* xy_depth
                                scratch, scratch_bytes, &query, &s))
         return e;
     if (query) return GS_OK;
+    if (gs_status e = tile_test_args("gs_bin_and_sort", n, conic_op, flags)) return e;
     if (!n_entries) return fail(GS_ERR_INVALID, "gs_bin_and_sort: n_entries is NULL");
     *n_entries = 0;
     if (n == 0) return GS_OK;
     hipStream_t st = (hipStream_t)stream;
-    if (gs_status e = hip_check(gs::launch_bin_and_sort(*cam, n, (const float4*)xy_depth, tiles_touched, keys,
-                                                        point_list, (uint32_t)capacity, s, nullptr, st),
+    if (gs_status e = hip_check(gs::launch_bin_and_sort(*cam, n, (const float4*)xy_depth, (const float4*)conic_op,
+                                                        tiles_touched, keys, point_list, (uint32_t)capacity, s,
+                                                        nullptr, flags, st),
                                 "bin_and_sort launch"))
         return e;
     // the entry count, once everything is enqueued
@@ -187,10 +207,18 @@ gs_status gs_bin_and_sort(const gs_camera* cam, int32_t n, const float* xy_depth
     return GS_OK;
 }
 
-gs_status gs_bin_and_sort_async(const gs_camera* cam, int32_t n, const float* xy_depth,
-                                const uint32_t* tiles_touched, uint64_t* keys, uint32_t* point_list,
-                                int64_t capacity, void* scratch, size_t* scratch_bytes,
-                                uint64_t* n_entries_dev, void* stream) {
+gs_status gs_bin_and_sort(const gs_camera* cam, int32_t n, const float* xy_depth,
+                          const uint32_t* tiles_touched, uint64_t* keys, uint32_t* point_list,
+                          int64_t capacity, void* scratch, size_t* scratch_bytes,
+                          int64_t* n_entries, void* stream) {
+    return gs_bin_and_sort_ex(cam, n, xy_depth, nullptr, tiles_touched, keys, point_list, capacity, scratch,
+                              scratch_bytes, n_entries, GS_TILES_SQUARE, stream);
+}
+
+gs_status gs_bin_and_sort_async_ex(const gs_camera* cam, int32_t n, const float* xy_depth, const float* conic_op,
+                                   const uint32_t* tiles_touched, uint64_t* keys, uint32_t* point_list,
+                                   int64_t capacity, void* scratch, size_t* scratch_bytes,
+                                   uint64_t* n_entries_dev, uint32_t flags, void* stream) {
     g_last_error.clear();
     gs::BinScratch s{};
     bool query = false;
@@ -198,14 +226,24 @@ gs_status gs_bin_and_sort_async(const gs_camera* cam, int32_t n, const float* xy
                                capacity, scratch, scratch_bytes, &query, &s))
         return e;
     if (query) return GS_OK;
+    if (gs_status e = tile_test_args("gs_bin_and_sort_async", n, conic_op, flags)) return e;
     if (!n_entries_dev || ((uintptr_t)n_entries_dev & 7))
         return fail(GS_ERR_INVALID, "gs_bin_and_sort_async: n_entries_dev must be an 8-byte aligned device pointer");
     hipStream_t st = (hipStream_t)stream;
     if (n == 0)
         return hip_check(gs::launch_fill_u32((uint32_t*)n_entries_dev, 2, 0u, st), "entry count clear");
-    return hip_check(gs::launch_bin_and_sort(*cam, n, (const float4*)xy_depth, tiles_touched, keys, point_list,
-                                             (uint32_t)capacity, s, n_entries_dev, st),
+    return hip_check(gs::launch_bin_and_sort(*cam, n, (const float4*)xy_depth, (const float4*)conic_op,
+                                             tiles_touched, keys, point_list, (uint32_t)capacity, s, n_entries_dev,
+                                             flags, st),
                      "bin_and_sort launch");
+}
+
+gs_status gs_bin_and_sort_async(const gs_camera* cam, int32_t n, const float* xy_depth,
+                                const uint32_t* tiles_touched, uint64_t* keys, uint32_t* point_list,
+                                int64_t capacity, void* scratch, size_t* scratch_bytes,
+                                uint64_t* n_entries_dev, void* stream) {
+    return gs_bin_and_sort_async_ex(cam, n, xy_depth, nullptr, tiles_touched, keys, point_list, capacity,
+                                    scratch, scratch_bytes, n_entries_dev, GS_TILES_SQUARE, stream);
 }
 
 gs_status gs_tile_ranges(const gs_camera* cam, const uint64_t* keys, int64_t n_entries,

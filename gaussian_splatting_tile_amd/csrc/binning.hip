@@ -156,8 +156,9 @@ __device__ __forceinline__ void emit_counts(const uint32_t* s_hist, int nblk, ui
 // with entries, wins), and an inclusive max-scan over the 2048 slots gives
 // every entry its owner. The workgroup also counts the first tile pass's
 // digits of its entries.
+template <bool ELLIPSE>
 __global__ __launch_bounds__(kDupThreads) void k_duplicate(
-    const float4* __restrict__ xy_depth, const uint32_t* __restrict__ offsets,
+    const float4* __restrict__ xy_depth, const float4* __restrict__ conic_op, const uint32_t* __restrict__ offsets,
     const uint32_t* __restrict__ perm, const uint32_t* __restrict__ first_owner, int n,
     const uint64_t* __restrict__ total, uint32_t capacity, int TX, int TY, int passes,
     uint64_t* __restrict__ keys, uint32_t* __restrict__ values, uint32_t* __restrict__ counts) {
@@ -216,14 +217,32 @@ __global__ __launch_bounds__(kDupThreads) void k_duplicate(
             const uint32_t k = e - offsets[i];
             const float4 rec = xy_depth[g];
             const Span sp = tile_span(rec.x, rec.y, rec.w, TX, TY);
-            const uint32_t w = (uint32_t)(sp.x1 - sp.x0);
-            // k / w and k % w: float quotient (k < 2^21) fixed up by one step
-            uint32_t q = (uint32_t)((float)k * __builtin_amdgcn_rcpf((float)w));
-            int r = (int)k - (int)(q * w);
-            if (r < 0) { --q; r += (int)w; }
-            if (r >= (int)w) { ++q; r -= (int)w; }
-            const uint32_t tx = (uint32_t)sp.x0 + (uint32_t)r;
-            const uint32_t ty = (uint32_t)sp.y0 + q;
+            uint32_t tx, ty;
+            if (ELLIPSE) {
+                // the k-th kept tile, rows of kept runs in span order
+                const float4 co = conic_op[g];
+                const EllipseRows er = ellipse_rows(rec.x, rec.y, co.x, co.y, co.z, sp);
+                int kk = (int)k, row = sp.y0, lo = sp.x0, hi = sp.x0;
+                for (; row < sp.y1; ++row) {
+                    ellipse_row_range(er, sp, row, lo, hi);
+                    const int cnt = hi > lo ? hi - lo : 0;
+                    if (kk < cnt) break;
+                    kk -= cnt;
+                }
+                // row < sp.y1 always: k < tiles_touched, the count of the same runs;
+                // the clamps keep any tile id inside the grid regardless
+                tx = (uint32_t)max(sp.x0, min(lo + kk, sp.x1 - 1));
+                ty = (uint32_t)min(row, sp.y1 - 1);
+            } else {
+                const uint32_t w = (uint32_t)(sp.x1 - sp.x0);
+                // k / w and k % w: float quotient (k < 2^21) fixed up by one step
+                uint32_t q = (uint32_t)((float)k * __builtin_amdgcn_rcpf((float)w));
+                int r = (int)k - (int)(q * w);
+                if (r < 0) { --q; r += (int)w; }
+                if (r >= (int)w) { ++q; r -= (int)w; }
+                tx = (uint32_t)sp.x0 + (uint32_t)r;
+                ty = (uint32_t)sp.y0 + q;
+            }
             t = ty * (uint32_t)TX + tx;
             keys[e] = ((uint64_t)t << 32) | (uint64_t)__float_as_uint(rec.z);
             values[e] = g;
@@ -642,8 +661,9 @@ size_t bin_scratch_layout(int n, int64_t capacity, BinScratch* out, void* base) 
 }
 
 hipError_t launch_bin_and_sort(const gs_camera& cam, int n, const float4* xy_depth,
-                               const uint32_t* tiles_touched, uint64_t* keys, uint32_t* values,
-                               uint32_t capacity, const BinScratch& s, uint64_t* n_dev, hipStream_t stream) {
+                               const float4* conic_op, const uint32_t* tiles_touched, uint64_t* keys,
+                               uint32_t* values, uint32_t capacity, const BinScratch& s, uint64_t* n_dev,
+                               uint32_t flags, hipStream_t stream) {
     // 1. stable depth order of the splats (culled last) into gv[0]; the last
     // pass also scans tiles_touched in that order: offsets, first_owner, E
     const unsigned nbg = (unsigned)((n + kGaussTile - 1) / kGaussTile);
@@ -689,9 +709,14 @@ hipError_t launch_bin_and_sort(const gs_camera& cam, int n, const float4* xy_dep
     uint32_t* vin = (passes & 1) ? s.vals_tmp : values;
     uint64_t* kout = (passes & 1) ? keys : s.keys_tmp;
     uint32_t* vout = (passes & 1) ? values : s.vals_tmp;
-    hipLaunchKernelGGL(k_duplicate, dim3(nbe), dim3(kDupThreads), 0, stream, xy_depth, s.offsets, s.gv[0],
-                       s.first_owner, n, (const uint64_t*)s.total, capacity, tiles_x(cam), tiles_y(cam), passes,
-                       kin, vin, s.entry_counts);
+    if (flags & kTilesEllipse)
+        hipLaunchKernelGGL(k_duplicate<true>, dim3(nbe), dim3(kDupThreads), 0, stream, xy_depth, conic_op,
+                           s.offsets, s.gv[0], s.first_owner, n, (const uint64_t*)s.total, capacity, tiles_x(cam),
+                           tiles_y(cam), passes, kin, vin, s.entry_counts);
+    else
+        hipLaunchKernelGGL(k_duplicate<false>, dim3(nbe), dim3(kDupThreads), 0, stream, xy_depth, conic_op,
+                           s.offsets, s.gv[0], s.first_owner, n, (const uint64_t*)s.total, capacity, tiles_x(cam),
+                           tiles_y(cam), passes, kin, vin, s.entry_counts);
     for (int p = 0; p < passes; ++p) {
         uint32_t* cnt = s.entry_counts + (size_t)p * kRadix * nbe;
         if (p > 0)

@@ -47,13 +47,76 @@ __device__ __forceinline__ Span tile_span(float u, float v, float r, int TX, int
     return Span{(int)x0, (int)x1, (int)y0, (int)y1};
 }
 
+// Ellipse tile test (zenn 2.3.4: of the span's tiles keep those the splat's
+// ellipse may overlap). The ellipse taken is the region where the splat can
+// reach alpha >= 1/255: Q(d) = A dx^2 + 2B dx dy + C dy^2 <= 2 ln(255 o), with
+// the opacity-independent bound 2 ln 255 = 11.0825 < 11.1, raised by 64 ulp
+// of |A| dx^2 + |C| dy^2 + 2|B dx dy| at the span's farthest pixel centre (the
+// compositing's rounding of Q). A dropped tile therefore holds no pixel the
+// splat changes: results are those of the full span; only the lists shrink.
+// Per row of tiles the kept tiles are a run: those whose pixel centres meet
+// the x-extent [L, R] of the ellipse's slice over the row's pixel-centre
+// y-range, L and R taken at the dy of the leftmost / rightmost point clamped
+// into the row, widened by a slack. Float32, + - * / sqrt (correctly rounded)
+// floor ceil fminf fmaxf only, in a fixed order: preprocess (counting) and
+// duplication (enumerating) take the identical decision, and so does any
+// host evaluation of the same steps. A conic that is not positive definite,
+// or a non-finite extent, keeps the whole span.
+struct EllipseRows {
+    bool full;
+    float u, v, A, B, C, det, hx, hy, ydr, slack, thr;
+};
+
+__device__ __forceinline__ EllipseRows ellipse_rows(float u, float v, float A, float B, float C, const Span& sp) {
+    EllipseRows e;
+    e.u = u; e.v = v; e.A = A; e.B = B; e.C = C;
+    e.det = A * C - B * B;
+    e.full = !(e.det > 0.0f && A > 0.0f && C > 0.0f);
+    const float ex = fmaxf(fabsf(16.0f * (float)sp.x0 - u), fabsf(16.0f * (float)sp.x1 - 1.0f - u));
+    const float ey = fmaxf(fabsf(16.0f * (float)sp.y0 - v), fabsf(16.0f * (float)sp.y1 - 1.0f - v));
+    const float bound = 64.0f * 5.96e-8f * ((fabsf(A) + fabsf(C)) + 2.0f * fabsf(B)) * (ex * ex + ey * ey);
+    e.thr = 11.1f + bound;
+    e.hx = e.hy = e.ydr = e.slack = 0.0f;
+    if (e.full) return e;
+    e.hy = sqrtf((e.thr * A) / e.det);
+    e.hx = sqrtf((e.thr * C) / e.det);
+    e.ydr = -(B * e.hx) / C;
+    e.slack = 0.01f + 1e-4f * (e.hx + e.hy);
+    if (!isfinite(e.hx) || !isfinite(e.hy) || !isfinite(e.ydr) || !isfinite(e.slack)) e.full = true;
+    return e;
+}
+
+// Kept tiles [lo, hi) of row ty; hi <= lo means none.
+__device__ __forceinline__ void ellipse_row_range(const EllipseRows& e, const Span& sp, int ty, int& lo_out,
+                                                  int& hi_out) {
+    lo_out = sp.x0;
+    hi_out = sp.x0;
+    if (e.full) { hi_out = sp.x1; return; }
+    const float ylo = 16.0f * (float)ty - e.v;
+    const float lo = fmaxf(ylo, -e.hy), hi = fminf(ylo + 15.0f, e.hy);
+    if (lo > hi + e.slack) return;
+    const float yr = fminf(fmaxf(e.ydr, lo), hi);
+    const float yl = fminf(fmaxf(-e.ydr, lo), hi);
+    const float thrA = e.thr * e.A;
+    const float R = (-(e.B * yr) + sqrtf(fmaxf(0.0f, thrA - (e.det * yr) * yr))) / e.A + e.slack;
+    const float L = (-(e.B * yl) - sqrtf(fmaxf(0.0f, thrA - (e.det * yl) * yl))) / e.A - e.slack;
+    const float tlo = fmaxf(ceilf(((L + e.u) - 15.0f) / 16.0f), (float)sp.x0);
+    const float thi = fminf(floorf((R + e.u) / 16.0f) + 1.0f, (float)sp.x1);
+    if (!(tlo < thi)) return;
+    lo_out = (int)tlo;
+    hi_out = (int)thi;
+}
+
+// Tile-test modes (the flags argument of the _ex entry points).
+constexpr uint32_t kTilesEllipse = 1u;
+
 // ---- launchers (each returns the launch's hipError_t) ----
 
 hipError_t launch_preprocess(const gs_camera& cam, int n, const float* means, const float* scales,
                              const float* quats, const float* opacity, const float* sh,
                              int sh_degree, const float* rgb_in, float4* xy_depth,
                              float4* conic_op, float4* rgb, uint32_t* tiles_touched,
-                             hipStream_t stream);
+                             uint32_t flags, hipStream_t stream);
 
 hipError_t launch_preprocess_bwd(const gs_camera& cam, int n, const float* means, const float* scales,
                                  const float* quats, const float* sh, int sh_degree,
@@ -88,8 +151,9 @@ size_t bin_scratch_layout(int n, int64_t capacity, BinScratch* out, void* base);
 // stable sort on the tile-id bits into (keys, values). Never waits on the
 // host. When E > capacity nothing is written to keys/values.
 hipError_t launch_bin_and_sort(const gs_camera& cam, int n, const float4* xy_depth,
-                               const uint32_t* tiles_touched, uint64_t* keys, uint32_t* values,
-                               uint32_t capacity, const BinScratch& s, uint64_t* n_dev, hipStream_t stream);
+                               const float4* conic_op, const uint32_t* tiles_touched, uint64_t* keys,
+                               uint32_t* values, uint32_t capacity, const BinScratch& s, uint64_t* n_dev,
+                               uint32_t flags, hipStream_t stream);
 
 hipError_t launch_fill_u32(uint32_t* p, size_t words, uint32_t v, hipStream_t stream);
 

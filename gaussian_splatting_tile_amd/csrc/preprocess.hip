@@ -35,7 +35,7 @@ __global__ __launch_bounds__(256) void k_preprocess(
     const float* __restrict__ scales, const float* __restrict__ quats,
     const float* __restrict__ opacity, const float* __restrict__ sh, const int n_coef,
     const float* __restrict__ rgb_in, float4* __restrict__ xy_depth, float4* __restrict__ conic_op,
-    float4* __restrict__ rgb_out, uint32_t* __restrict__ tiles_touched) {
+    float4* __restrict__ rgb_out, uint32_t* __restrict__ tiles_touched, const uint32_t flags) {
     const int g = blockIdx.x * blockDim.x + threadIdx.x;
     if (g >= n) return;
     const int TX = (cam.width + kTile - 1) / kTile;
@@ -131,7 +131,16 @@ __global__ __launch_bounds__(256) void k_preprocess(
         if (!isfinite(r)) break;
 
         const Span sp = tile_span(u, v, r, TX, TY);
-        const int cnt = (sp.x1 - sp.x0) * (sp.y1 - sp.y0);
+        int cnt = (sp.x1 - sp.x0) * (sp.y1 - sp.y0);
+        if (cnt > 0 && (flags & kTilesEllipse)) {  // count only the tiles the ellipse test keeps
+            const EllipseRows er = ellipse_rows(u, v, cA, cB, cC, sp);
+            cnt = 0;
+            for (int ty = sp.y0; ty < sp.y1; ++ty) {
+                int lo, hi;
+                ellipse_row_range(er, sp, ty, lo, hi);
+                cnt += hi > lo ? hi - lo : 0;
+            }
+        }
         if (cnt <= 0) break;
 
         // Colour.
@@ -196,12 +205,12 @@ hipError_t launch_preprocess(const gs_camera& cam, int n, const float* means, co
                              const float* quats, const float* opacity, const float* sh,
                              int sh_degree, const float* rgb_in, float4* xy_depth,
                              float4* conic_op, float4* rgb, uint32_t* tiles_touched,
-                             hipStream_t stream) {
+                             uint32_t flags, hipStream_t stream) {
     if (n <= 0) return hipSuccess;
     const int n_coef = sh ? (sh_degree + 1) * (sh_degree + 1) : 0;
     const int blocks = (n + 255) / 256;
     hipLaunchKernelGGL(k_preprocess, dim3(blocks), dim3(256), 0, stream, cam, n, means, scales,
-                       quats, opacity, sh, n_coef, rgb_in, xy_depth, conic_op, rgb, tiles_touched);
+                       quats, opacity, sh, n_coef, rgb_in, xy_depth, conic_op, rgb, tiles_touched, flags);
     return hipGetLastError();
 }
 

@@ -70,8 +70,9 @@ def version():
 
 
 def preprocess(cam, means, scales, quats, opacity, sh=None, sh_degree=0, rgb_in=None, out=None,
-               stream=None):
-    """gs_preprocess. Returns dict xy_depth [n,4], conic_op [n,4], rgb [n,4], tiles_touched [n]."""
+               stream=None, tile_test=0):
+    """gs_preprocess_ex. Returns dict xy_depth [n,4], conic_op [n,4], rgb [n,4], tiles_touched [n].
+    tile_test: _lib.GS_TILES_SQUARE (0) or _lib.GS_TILES_ELLIPSE (1)."""
     n = int(opacity.shape[0])
     dev = opacity.device
     if out is None:
@@ -81,12 +82,12 @@ def preprocess(cam, means, scales, quats, opacity, sh=None, sh_degree=0, rgb_in=
                    tiles_touched=torch.empty((n,), dtype=torch.int32, device=dev))
     f32, i32 = torch.float32, torch.int32
     c = _cam(cam)
-    _lib.check(_lib.load().gs_preprocess(
+    _lib.check(_lib.load().gs_preprocess_ex(
         ctypes.byref(c), n, _ptr(means, f32, "means"), _ptr(scales, f32, "scales"),
         _ptr(quats, f32, "quats"), _ptr(opacity, f32, "opacity"), _ptr(sh, f32, "sh"),
         int(sh_degree), _ptr(rgb_in, f32, "rgb_in"), _ptr(out["xy_depth"], f32),
         _ptr(out["conic_op"], f32), _ptr(out["rgb"], f32), _ptr(out["tiles_touched"], i32),
-        _stream(stream)))
+        int(tile_test), _stream(stream)))
     return out
 
 
@@ -157,8 +158,10 @@ class BinBuffers:
         return int(self.n_entries_dev.item())
 
 
-def bin_and_sort(cam, xy_depth, tiles_touched, buffers: BinBuffers | None = None, stream=None):
-    """gs_bin_and_sort. Returns (keys int64 [E] (uint64 bits), point_list int32 [E], E).
+def bin_and_sort(cam, xy_depth, tiles_touched, buffers: BinBuffers | None = None, stream=None,
+                 conic_op=None, tile_test=0):
+    """gs_bin_and_sort_ex. Returns (keys int64 [E] (uint64 bits), point_list int32 [E], E).
+    The ellipse tile test (tile_test=1) needs conic_op.
 
     Grows the buffers and retries once if the entry count exceeds capacity.
     """
@@ -171,11 +174,12 @@ def bin_and_sort(cam, xy_depth, tiles_touched, buffers: BinBuffers | None = None
         scratch = buffers.scratch_for(c, n)
         nbytes = ctypes.c_size_t(scratch.numel())
         n_entries = ctypes.c_int64(0)
-        st = lib.gs_bin_and_sort(ctypes.byref(c), n, _ptr(xy_depth, torch.float32, "xy_depth"),
-                                 _ptr(tiles_touched, torch.int32, "tiles_touched"),
-                                 _ptr(buffers.keys), _ptr(buffers.point_list), buffers.capacity,
-                                 _ptr(scratch), ctypes.byref(nbytes), ctypes.byref(n_entries),
-                                 _stream(stream))
+        st = lib.gs_bin_and_sort_ex(ctypes.byref(c), n, _ptr(xy_depth, torch.float32, "xy_depth"),
+                                    _ptr(conic_op, torch.float32, "conic_op"),
+                                    _ptr(tiles_touched, torch.int32, "tiles_touched"),
+                                    _ptr(buffers.keys), _ptr(buffers.point_list), buffers.capacity,
+                                    _ptr(scratch), ctypes.byref(nbytes), ctypes.byref(n_entries),
+                                    int(tile_test), _stream(stream))
         if st == _lib.GS_ERR_CAPACITY and attempt == 0:
             buffers._ensure(int(n_entries.value * 5 // 4 + 1024))
             continue
@@ -185,17 +189,19 @@ def bin_and_sort(cam, xy_depth, tiles_touched, buffers: BinBuffers | None = None
     raise AssertionError("unreachable")
 
 
-def bin_and_sort_async(cam, xy_depth, tiles_touched, buffers: BinBuffers, stream=None):
-    """gs_bin_and_sort_async: never waits. Returns (keys int64 [capacity], point_list int32
+def bin_and_sort_async(cam, xy_depth, tiles_touched, buffers: BinBuffers, stream=None, conic_op=None,
+                       tile_test=0):
+    """gs_bin_and_sort_async_ex: never waits. Returns (keys int64 [capacity], point_list int32
     [capacity]); E lands in buffers.n_entries_dev (read it with buffers.entries())."""
     c = _cam(cam)
     n = int(tiles_touched.shape[0])
     scratch = buffers.scratch_for(c, n)
     nbytes = ctypes.c_size_t(scratch.numel())
-    _lib.check(_lib.load().gs_bin_and_sort_async(
-        ctypes.byref(c), n, _ptr(xy_depth, torch.float32, "xy_depth"),
+    _lib.check(_lib.load().gs_bin_and_sort_async_ex(
+        ctypes.byref(c), n, _ptr(xy_depth, torch.float32, "xy_depth"), _ptr(conic_op, torch.float32, "conic_op"),
         _ptr(tiles_touched, torch.int32, "tiles_touched"), _ptr(buffers.keys), _ptr(buffers.point_list),
-        buffers.capacity, _ptr(scratch), ctypes.byref(nbytes), _ptr(buffers.n_entries_dev), _stream(stream)))
+        buffers.capacity, _ptr(scratch), ctypes.byref(nbytes), _ptr(buffers.n_entries_dev), int(tile_test),
+        _stream(stream)))
     return buffers.keys, buffers.point_list
 
 
@@ -295,15 +301,17 @@ class Scene:
 class Rasterizer:
     """Runs the whole path for one camera at a time, reusing its buffers."""
 
-    def __init__(self, device="cuda", capacity: int = 1 << 20):
+    def __init__(self, device="cuda", capacity: int = 1 << 20, tile_test: int = 0):
         self.device = torch.device(device)
         self.bins = BinBuffers(self.device, capacity)
+        self.tile_test = int(tile_test)
 
     def forward(self, cam: dict, scene: Scene, bg=(0.0, 0.0, 0.0), with_examined=False):
         c = camera(cam)
         pre = preprocess(c, scene.means, scene.scales, scene.quats, scene.opacity, scene.sh,
-                         scene.sh_degree, scene.rgb)
-        keys, point_list, E = bin_and_sort(c, pre["xy_depth"], pre["tiles_touched"], self.bins)
+                         scene.sh_degree, scene.rgb, tile_test=self.tile_test)
+        keys, point_list, E = bin_and_sort(c, pre["xy_depth"], pre["tiles_touched"], self.bins,
+                                           conic_op=pre["conic_op"], tile_test=self.tile_test)
         TX, TY = tiles_xy(cam)
         order = torch.empty((TX * TY,), dtype=torch.int32, device=self.device)
         ranges = tile_ranges(cam, keys, E, order=order)
@@ -344,10 +352,11 @@ class ViewBatch:
     """
 
     def __init__(self, cams, scene: "Scene", capacity: int, device="cuda", bg=(0.0, 0.0, 0.0),
-                 tile_order=True, streams: int = 1):
+                 tile_order=True, streams: int = 1, tile_test: int = 0):
         self.device = torch.device(device)
         self.scene = scene
         self.bg = bg
+        self.tile_test = int(tile_test)
         self.views = []
         # views are spread round-robin over `streams` streams (default
         # priority), so small frames that cannot fill the GPU alone overlap
@@ -401,8 +410,10 @@ class ViewBatch:
     def _enqueue_view(self, i, v, loss_grad):
         sc = self.scene
         c, pre, bins = v["c"], v["pre"], v["bins"]
-        preprocess(c, sc.means, sc.scales, sc.quats, sc.opacity, sc.sh, sc.sh_degree, sc.rgb, out=pre)
-        keys, pl = bin_and_sort_async(c, pre["xy_depth"], pre["tiles_touched"], bins)
+        preprocess(c, sc.means, sc.scales, sc.quats, sc.opacity, sc.sh, sc.sh_degree, sc.rgb, out=pre,
+                   tile_test=self.tile_test)
+        keys, pl = bin_and_sort_async(c, pre["xy_depth"], pre["tiles_touched"], bins, conic_op=pre["conic_op"],
+                                      tile_test=self.tile_test)
         tile_ranges_async(c, bins, out=v["ranges"], order=v["order"])
         composite_fwd(c, v["ranges"], pl, pre["xy_depth"], pre["conic_op"], pre["rgb"], self.bg,
                       out=v["fwd"], order=v["order"])

@@ -113,6 +113,31 @@ def test_preprocess_bwd_validates_before_launch(gs):
     assert b"aligned" in gs.gs_last_error()
 
 
+def test_tile_test_flags_validated(gs):
+    from gaussian_splatting_tile_amd import _lib
+    P = ctypes.c_void_p
+    d = P(256)
+    c = _cam()
+    # unknown flag bits
+    assert gs.gs_preprocess_ex(ctypes.byref(c), 4, d, d, d, d, None, 0, d, d, d, d, d, 2, None) == _lib.GS_ERR_INVALID
+    assert b"flags" in gs.gs_last_error()
+    need = ctypes.c_size_t(0)
+    assert gs.gs_bin_and_sort_ex(ctypes.byref(c), 10, None, None, None, None, None, 100, None,
+                                 ctypes.byref(need), None, 0, None) == _lib.GS_OK and need.value > 0
+    buf = ctypes.c_size_t(need.value)
+    n_e = ctypes.c_int64(0)
+    scratch = P(4096)  # 256-aligned, never dereferenced: validation fails first
+    # the ellipse test without a conic
+    assert gs.gs_bin_and_sort_ex(ctypes.byref(c), 10, d, None, d, d, d, 100, scratch, ctypes.byref(buf),
+                                 ctypes.byref(n_e), _lib.GS_TILES_ELLIPSE, None) == _lib.GS_ERR_INVALID
+    assert b"conic" in gs.gs_last_error()
+    # a misaligned conic
+    assert gs.gs_bin_and_sort_async_ex(ctypes.byref(c), 10, d, P(264), d, d, d, 100, scratch, ctypes.byref(buf),
+                                       P(512), _lib.GS_TILES_ELLIPSE, None) == _lib.GS_ERR_INVALID
+    assert gs.gs_bin_and_sort_async_ex(ctypes.byref(c), 10, d, d, d, d, d, 100, scratch, ctypes.byref(buf),
+                                       P(512), 4, None) == _lib.GS_ERR_INVALID
+
+
 def test_bin_scratch_size_query(gs):
     from gaussian_splatting_tile_amd import _lib
     c = _cam()
