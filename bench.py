@@ -352,6 +352,27 @@ def main():
     # floats and the SH (or RGB) gradient written
     pbwd_bytes = n * (44 + 40 + 12 * n_coef + 44 + 12 * n_coef)
 
+    # The appearance MLP (8 latents, 32 hidden units) over the same
+    # Gaussians, forward and backward: the alternative colour source.
+    gen = torch.Generator(device=dev).manual_seed(5)
+    app_L, app_H = 8, 32
+    latent = torch.randn((app_L, n), device=dev, generator=gen)
+    app_w = 0.3 * torch.randn((gs.appearance_params(app_L, app_H),), device=dev, generator=gen)
+    app_rgb = gs.appearance_fwd(c, scene.means, latent, app_w, app_H)
+    app_g = gs.appearance_bwd(c, scene.means, latent, app_w, app_H, app_rgb)
+    ev = []
+    for _ in range(args.steps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record(stream)
+        gs.appearance_fwd(c, scene.means, latent, app_w, app_H, out=app_rgb)
+        e[1].record(stream)
+        gs.appearance_bwd(c, scene.means, latent, app_w, app_H, app_rgb, out=app_g)
+        e[2].record(stream)
+        ev.append(e)
+    torch.cuda.synchronize()
+    app_fwd_ms = float(np.mean([x[0].elapsed_time(x[1]) for x in ev]))
+    app_bwd_ms = float(np.mean([x[1].elapsed_time(x[2]) for x in ev]))
+
     ms_per_step = 1e3 * elapsed / args.steps
     fps = args.steps / elapsed
 
@@ -394,6 +415,8 @@ def main():
             "ellipse_tile_test_frames_per_s": round(ellipse_fps, 3),
             "ellipse_tile_test_n_entries": E_ellipse,
             "preprocess_bwd_ms": round(pbwd_s * 1e3, 4),
+            "appearance_mlp_8x32_fwd_ms": round(app_fwd_ms, 4),
+            "appearance_mlp_8x32_bwd_ms": round(app_bwd_ms, 4),
             "preprocess_bwd_hbm_frac": round(pbwd_bytes / pbwd_s / PEAK_HBM, 4),
         },
         "baseline_context": {"value": 25.8, "unit": "frames/s", "hardware": "Tesla T4",

@@ -16,7 +16,7 @@ STATUS_NAMES = {0: "GS_OK", 1: "GS_ERR_INVALID", 2: "GS_ERR_CAPACITY", 3: "GS_ER
 EXPORTS = ("gs_constants", "gs_last_error", "gs_version", "gs_preprocess", "gs_preprocess_ex",
            "gs_preprocess_bwd", "gs_bin_and_sort", "gs_bin_and_sort_ex", "gs_bin_and_sort_async_ex",
            "gs_bin_and_sort_async", "gs_tile_ranges", "gs_tile_ranges_async", "gs_composite_fwd",
-           "gs_composite_bwd")
+           "gs_composite_bwd", "gs_appearance_fwd", "gs_appearance_bwd")
 
 
 class GsCamera(ctypes.Structure):
@@ -78,6 +78,10 @@ def load() -> ctypes.CDLL:
     lib.gs_composite_fwd.argtypes = [CAM, P, P, P, P, P, P, P, P, P, P, P, P]
     lib.gs_composite_bwd.restype = ctypes.c_int
     lib.gs_composite_bwd.argtypes = [CAM, I32, P, P, P, P, P, P, P, P, P, P, P, P, P, P]
+    lib.gs_appearance_fwd.restype = ctypes.c_int
+    lib.gs_appearance_fwd.argtypes = [CAM, I32, P, P, I32, I32, P, P, P]
+    lib.gs_appearance_bwd.restype = ctypes.c_int
+    lib.gs_appearance_bwd.argtypes = [CAM, I32, P, P, I32, I32, P, P, P, P, P, ctypes.POINTER(ctypes.c_size_t), P]
     _lib = lib
     return lib
 

@@ -246,6 +246,52 @@ gs_status gs_bin_and_sort_async(const gs_camera* cam, int32_t n, const float* xy
                                     scratch, scratch_bytes, n_entries_dev, GS_TILES_SQUARE, stream);
 }
 
+namespace {
+
+gs_status appearance_args(const char* fn, const gs_camera* cam, int32_t n, int32_t L, int32_t H) {
+    if (gs_status s = check_camera(cam)) return s;
+    if (n < 0 || n > GS_MAX_GAUSSIANS) return fail(GS_ERR_INVALID, "%s: n = %d outside [0, %d]", fn, n, GS_MAX_GAUSSIANS);
+    if (L < 1 || L > GS_APP_MAX_LATENT) return fail(GS_ERR_INVALID, "%s: n_latent %d outside [1, %d]", fn, L, GS_APP_MAX_LATENT);
+    if (H < 1 || H > GS_APP_MAX_HIDDEN) return fail(GS_ERR_INVALID, "%s: n_hidden %d outside [1, %d]", fn, H, GS_APP_MAX_HIDDEN);
+    return GS_OK;
+}
+
+}  // namespace
+
+gs_status gs_appearance_fwd(const gs_camera* cam, int32_t n, const float* means, const float* latent,
+                            int32_t n_latent, int32_t n_hidden, const float* weights, float* rgb, void* stream) {
+    g_last_error.clear();
+    if (gs_status s = appearance_args("gs_appearance_fwd", cam, n, n_latent, n_hidden)) return s;
+    if (n == 0) return GS_OK;
+    if (!means || !latent || !weights || !rgb) return fail(GS_ERR_INVALID, "gs_appearance_fwd: a required pointer is NULL");
+    return hip_check(gs::launch_appearance_fwd(*cam, n, means, latent, n_latent, n_hidden, weights, rgb,
+                                               (hipStream_t)stream),
+                     "gs_appearance_fwd launch");
+}
+
+gs_status gs_appearance_bwd(const gs_camera* cam, int32_t n, const float* means, const float* latent,
+                            int32_t n_latent, int32_t n_hidden, const float* weights, const float* grad_rgb,
+                            float* grad_latent, float* grad_weights, void* scratch, size_t* scratch_bytes,
+                            void* stream) {
+    g_last_error.clear();
+    if (gs_status s = appearance_args("gs_appearance_bwd", cam, n, n_latent, n_hidden)) return s;
+    if (!scratch_bytes) return fail(GS_ERR_INVALID, "gs_appearance_bwd: scratch_bytes is NULL");
+    const size_t need = gs::appearance_bwd_scratch(n, n_latent, n_hidden);
+    if (!scratch) {
+        *scratch_bytes = need;
+        return GS_OK;
+    }
+    if (*scratch_bytes < need)
+        return fail(GS_ERR_INVALID, "gs_appearance_bwd: scratch of %zu bytes is smaller than the %zu required",
+                    *scratch_bytes, need);
+    if ((uintptr_t)scratch & 3) return fail(GS_ERR_INVALID, "gs_appearance_bwd: scratch must be 4-byte aligned");
+    if (!grad_weights || (n > 0 && (!means || !latent || !weights || !grad_rgb || !grad_latent)))
+        return fail(GS_ERR_INVALID, "gs_appearance_bwd: a required pointer is NULL");
+    return hip_check(gs::launch_appearance_bwd(*cam, n, means, latent, n_latent, n_hidden, weights, grad_rgb,
+                                               grad_latent, grad_weights, (float*)scratch, (hipStream_t)stream),
+                     "gs_appearance_bwd launch");
+}
+
 gs_status gs_tile_ranges(const gs_camera* cam, const uint64_t* keys, int64_t n_entries,
                          uint32_t* ranges, uint32_t* tile_order, void* stream) {
     g_last_error.clear();

@@ -177,4 +177,14 @@ hipError_t launch_composite_bwd(const gs_camera& cam, int n, const uint32_t* ran
                                 float4* grad_conic_op, float4* grad_rgb, const uint32_t* tile_order,
                                 hipStream_t stream);
 
+// Appearance MLP: parameter count, backward scratch (per-workgroup partial
+// weight gradients) and launchers.
+int appearance_params(int L, int H);
+size_t appearance_bwd_scratch(int n, int L, int H);
+hipError_t launch_appearance_fwd(const gs_camera& cam, int n, const float* means, const float* latent, int L,
+                                 int H, const float* weights, float* rgb, hipStream_t stream);
+hipError_t launch_appearance_bwd(const gs_camera& cam, int n, const float* means, const float* latent, int L,
+                                 int H, const float* weights, const float* grad_rgb, float* grad_latent,
+                                 float* grad_weights, float* partials, hipStream_t stream);
+
 }  // namespace gs

@@ -119,6 +119,49 @@ def preprocess_bwd(cam, means, scales=None, quats=None, sh=None, sh_degree=0, ti
     return out
 
 
+def appearance_params(n_latent: int, n_hidden: int) -> int:
+    """Floats in the packed appearance weights: W1 [H][L+3], b1 [H], W2 [3][H], b2 [3]."""
+    return n_hidden * (n_latent + 3) + 4 * n_hidden + 3
+
+
+def appearance_fwd(cam, means, latent, weights, n_hidden, out=None, stream=None):
+    """gs_appearance_fwd. latent [L, n]; returns rgb [3, n] (feed it to preprocess as rgb_in)."""
+    L, n = int(latent.shape[0]), int(latent.shape[1])
+    f32 = torch.float32
+    if weights.numel() != appearance_params(L, n_hidden):
+        raise ValueError("weights do not match n_latent / n_hidden")
+    if out is None:
+        out = torch.empty((3, n), dtype=f32, device=latent.device)
+    c = _cam(cam)
+    _lib.check(_lib.load().gs_appearance_fwd(ctypes.byref(c), n, _ptr(means, f32, "means"),
+                                             _ptr(latent, f32, "latent"), L, int(n_hidden),
+                                             _ptr(weights, f32, "weights"), _ptr(out, f32), _stream(stream)))
+    return out
+
+
+def appearance_bwd(cam, means, latent, weights, n_hidden, grad_rgb, out=None, scratch=None, stream=None):
+    """gs_appearance_bwd. Returns dict grad_latent [L, n], grad_weights (packed as weights)."""
+    L, n = int(latent.shape[0]), int(latent.shape[1])
+    f32 = torch.float32
+    dev = latent.device
+    if out is None:
+        out = dict(grad_latent=torch.empty((L, n), dtype=f32, device=dev),
+                   grad_weights=torch.empty_like(weights))
+    c = _cam(cam)
+    lib = _lib.load()
+    need = ctypes.c_size_t(0)
+    _lib.check(lib.gs_appearance_bwd(ctypes.byref(c), n, None, None, L, int(n_hidden), None, None, None, None,
+                                     None, ctypes.byref(need), None))
+    if scratch is None or scratch.numel() < need.value:
+        scratch = torch.empty((max(int(need.value), 4),), dtype=torch.uint8, device=dev)
+    have = ctypes.c_size_t(scratch.numel())
+    _lib.check(lib.gs_appearance_bwd(ctypes.byref(c), n, _ptr(means, f32, "means"), _ptr(latent, f32, "latent"), L,
+                                     int(n_hidden), _ptr(weights, f32, "weights"), _ptr(grad_rgb, f32, "grad_rgb"),
+                                     _ptr(out["grad_latent"], f32), _ptr(out["grad_weights"], f32),
+                                     _ptr(scratch), ctypes.byref(have), _stream(stream)))
+    return out
+
+
 class BinBuffers:
     """Entry buffers (keys, point_list, scratch, the device entry count)
     reused across frames; grown on demand when a frame needs more entries

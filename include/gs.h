@@ -68,6 +68,11 @@ extern "C" {
 #define GS_TILES_SQUARE 0u
 #define GS_TILES_ELLIPSE 1u
 
+/* Appearance MLP limits ("rigel" README, "Appearance MLP": sized for up to
+ * 29 latent dims and 64 hidden units). */
+#define GS_APP_MAX_LATENT 29
+#define GS_APP_MAX_HIDDEN 64
+
 typedef enum {
     GS_OK = 0,
     GS_ERR_INVALID = 1,  /* bad argument; nothing enqueued */
@@ -352,6 +357,55 @@ gs_status gs_composite_bwd(const gs_camera* cam, int32_t n, const uint32_t* rang
                            const float* final_T, const uint32_t* n_contrib,
                            const float* dL_dimage, float* grad_mean2d, float* grad_conic_op,
                            float* grad_rgb, const uint32_t* tile_order, void* stream);
+
+/* ---------------------------------------------------------------------
+ * gs_appearance_fwd - colour of every Gaussian from a latent code and the
+ * view direction through a small MLP ("rigel" README, "Appearance MLP": an
+ * L-float latent concatenated with the unit view direction, an H-wide ReLU
+ * layer, a 3-wide sigmoid layer). The result feeds gs_preprocess as rgb_in
+ * (the rasterizer never sees how colour was produced).
+ *
+ *   cam        (host) camera; only campos is used: dir = normalize(mean - campos),
+ *              computed as gs_preprocess computes the SH direction
+ *   n          number of Gaussians
+ *   means      [3][n]
+ *   latent     [n_latent][n]
+ *   n_latent   L, 1..GS_APP_MAX_LATENT
+ *   n_hidden   H, 1..GS_APP_MAX_HIDDEN
+ *   weights    packed float32: W1 [H][L+3] (row i = hidden unit i; columns
+ *              the latent, then dir x, y, z), b1 [H], W2 [3][H], b2 [3];
+ *              H (L+3) + 4H + 3 floats
+ *   rgb        out [3][n]: sigmoid(b2 + W2 max(0, b1 + W1 [latent; dir]))
+ * z = b1 + W1 x is summed in float32 in input order without fused
+ * multiply-add, so which units are active is decided reproducibly.
+ * ------------------------------------------------------------------- */
+gs_status gs_appearance_fwd(const gs_camera* cam, int32_t n, const float* means, const float* latent,
+                            int32_t n_latent, int32_t n_hidden, const float* weights, float* rgb, void* stream);
+
+/* ---------------------------------------------------------------------
+ * gs_appearance_bwd - gradients of gs_appearance_fwd ("rigel" README,
+ * "Appearance MLP": latents get their gradient directly, view directions
+ * are constants). With g = dL/drgb:
+ *   dy = g s (1 - s);  dz = (W2^T dy) on the active units (z > 0), else 0;
+ *   dL/dlatent = W1[:, :L]^T dz;  dW2 = sum dy h^T;  db2 = sum dy;
+ *   dW1 = sum dz x^T;  db1 = sum dz  (sums over all n Gaussians).
+ * The weight sums are formed per workgroup of 128 Gaussians as dot
+ * products and then summed over workgroups in a fixed order: the result is
+ * deterministic.
+ *
+ *   cam, n, means, latent, n_latent, n_hidden, weights: as gs_appearance_fwd
+ *   grad_rgb       [3][n] dL/drgb (e.g. grad_rgb_in from gs_preprocess_bwd)
+ *   grad_latent    out [n_latent][n]
+ *   grad_weights   out, packed as weights (overwritten)
+ *   scratch        device workspace of *scratch_bytes bytes (4-byte aligned),
+ *                  or NULL to query the size (ceil(n / 128) * (H (L+3) + 4H + 3)
+ *                  floats)
+ *   scratch_bytes  (host) in: size of scratch; out: required size
+ * ------------------------------------------------------------------- */
+gs_status gs_appearance_bwd(const gs_camera* cam, int32_t n, const float* means, const float* latent,
+                            int32_t n_latent, int32_t n_hidden, const float* weights, const float* grad_rgb,
+                            float* grad_latent, float* grad_weights, void* scratch, size_t* scratch_bytes,
+                            void* stream);
 
 #ifdef __cplusplus
 }

@@ -138,6 +138,27 @@ def test_tile_test_flags_validated(gs):
                                        P(512), 4, None) == _lib.GS_ERR_INVALID
 
 
+def test_appearance_validates_before_launch(gs):
+    from gaussian_splatting_tile_amd import _lib
+    P = ctypes.c_void_p
+    d = P(256)
+    c = _cam()
+    assert gs.gs_appearance_fwd(ctypes.byref(c), 10, d, d, 0, 32, d, d, None) == _lib.GS_ERR_INVALID
+    assert b"n_latent" in gs.gs_last_error()
+    assert gs.gs_appearance_fwd(ctypes.byref(c), 10, d, d, 30, 32, d, d, None) == _lib.GS_ERR_INVALID
+    assert gs.gs_appearance_fwd(ctypes.byref(c), 10, d, d, 8, 65, d, d, None) == _lib.GS_ERR_INVALID
+    assert b"n_hidden" in gs.gs_last_error()
+    assert gs.gs_appearance_fwd(ctypes.byref(c), 10, d, None, 8, 32, d, d, None) == _lib.GS_ERR_INVALID
+    need = ctypes.c_size_t(0)
+    assert gs.gs_appearance_bwd(ctypes.byref(c), 1000, None, None, 8, 32, None, None, None, None, None,
+                                ctypes.byref(need), None) == _lib.GS_OK
+    assert need.value == 8 * 483 * 4  # ceil(1000 / 128) workgroups x 483 weights
+    small = ctypes.c_size_t(need.value - 4)
+    assert gs.gs_appearance_bwd(ctypes.byref(c), 1000, d, d, 8, 32, d, d, d, d, P(4096), ctypes.byref(small),
+                                None) == _lib.GS_ERR_INVALID
+    assert b"smaller" in gs.gs_last_error()
+
+
 def test_bin_scratch_size_query(gs):
     from gaussian_splatting_tile_amd import _lib
     c = _cam()
