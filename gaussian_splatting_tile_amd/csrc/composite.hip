@@ -165,12 +165,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
 
     // A pixel has stopped exactly when its transmittance is below the stop
     // threshold (T only decreases, and compositing ends at the first splat
-    // that takes it there), so no separate flag is carried.
-    float T = 1.0f, C0 = 0.0f, C1 = 0.0f, C2 = 0.0f;
+    // that takes it there), so no separate flag is carried. A lane outside
+    // the image starts stopped (T = 0; it writes nothing).
+    float T = inside ? 1.0f : 0.0f, C0 = 0.0f, C1 = 0.0f, C2 = 0.0f;
     uint32_t last = 0;
 
     for (uint32_t base = start; base < end; base += kBatch) {
-        if (__syncthreads_count(!inside || T < kTStop) == 256) break;
+        if (__syncthreads_count(T < kTStop) == 256) break;
         const uint32_t j = base + tid;
         if (j < end) {
             const uint32_t g = point_list[j];
@@ -196,7 +197,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
         for (int q = 0; q < 4; ++q) {
             uint64_t mq = m[q];
             while (mq != 0ull) {
-                if (__ballot(inside && T >= kTStop) == 0ull) { mq = 0ull; break; }
+                if (__ballot(T >= kTStop) == 0ull) { mq = 0ull; break; }
                 const int k = q * 64 + (__ffsll((unsigned long long)mq) - 1);
                 mq &= mq - 1ull;
                 const float4 co = s_conic[k];
@@ -205,7 +206,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
                 float G, alpha;
                 splat_alpha(co.x, co.y, co.z, co.w, fx - xc.x, fy - xc.y, G, alpha);
                 // branch-free update; stopped lanes and alphas below the floor change nothing
-                const bool use = inside && T >= kTStop && alpha >= kAlphaMin;
+                const bool use = T >= kTStop && alpha >= kAlphaMin;
                 const float w = use ? alpha * T : 0.0f;
                 C0 = __builtin_fmaf(xc.z, w, C0);
                 C1 = __builtin_fmaf(xc.w, w, C1);
