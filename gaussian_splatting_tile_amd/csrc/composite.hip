@@ -65,15 +65,17 @@ __device__ __noinline__ float exp_rn(float x) { return (float)exp((double)x); }
 // Must be called with the whole wave active (the rare exact path is behind
 // a wave-uniform test).
 __device__ __forceinline__ void splat_alpha(float hA, float B, float hC, float o, float dx, float dy,
-                                            float& G, float& alpha) {
+                                            float& G, float& oG, float& alpha) {
     const float power = ((hA * dx) * dx + (hC * dy) * dy) - (B * dx) * dy;
     G = __builtin_amdgcn_exp2f(power * kLog2e);
-    alpha = fminf(kAlphaMax, o * G);
+    oG = o * G;
+    alpha = fminf(kAlphaMax, oG);
     const bool near = fabsf(alpha - kAlphaMin) <= kAlphaMin * 4e-6f;
     if (__builtin_expect(__ballot(near) != 0ull, 0)) {
         if (near) {
             G = exp_rn(power);
-            alpha = fminf(kAlphaMax, o * G);
+            oG = o * G;
+            alpha = fminf(kAlphaMax, oG);
         }
     }
 }
@@ -203,8 +205,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
                 const float4 co = s_conic[k];
                 const float4 xc = s_xyc[k];
                 const float cb = s_blue[k];
-                float G, alpha;
-                splat_alpha(co.x, co.y, co.z, co.w, fx - xc.x, fy - xc.y, G, alpha);
+                float G, oG, alpha;
+                splat_alpha(co.x, co.y, co.z, co.w, fx - xc.x, fy - xc.y, G, oG, alpha);
                 // branch-free update; stopped lanes and alphas below the floor change nothing
                 const bool use = T >= kTStop && alpha >= kAlphaMin;
                 const float w = use ? alpha * T : 0.0f;
@@ -231,19 +233,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
     }
 }
 
-// Sum over the 16 lanes of each row of the wave with DPP lane permutes
-// (quad swaps, then half-row and row mirrors); every lane of a row ends
-// with the row's sum. Must be called with all 64 lanes active.
+// x plus the value of x that DPP control kCtrl moves into this lane (lane
+// permutes within a row of 16). Must be called with all 64 lanes active.
 template <int kCtrl>
 __device__ __forceinline__ float dpp_add(float x) {
     return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, true));
-}
-__device__ __forceinline__ float dpp_row_sum(float x) {
-    x = dpp_add<0xB1>(x);   // quad_perm [1,0,3,2]
-    x = dpp_add<0x4E>(x);   // quad_perm [2,3,0,1]
-    x = dpp_add<0x141>(x);  // row_half_mirror
-    x = dpp_add<0x140>(x);  // row_mirror
-    return x;
 }
 
 template <int kCtrl>
@@ -251,21 +245,30 @@ __device__ __forceinline__ float dpp_mov(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, true));
 }
 
-// Transpose-reduce of four per-lane values over each 16-lane row: returns,
-// in lane i, the row sum of value (i & 3). Two butterfly steps over lane
-// bits 0 and 1 halve the number of live values each time (a lane keeps the
-// value its bit selects and adds its partner's copy of the same value), so
-// every lane of a quad ends with a different value's quad sum; rotating the
-// row by 4 and by 8 then adds the four quads. 11 instructions for four
-// values, against 16 for four separate row sums. b0, b1: lane bits 0 and 1.
-__device__ __forceinline__ float quad_transpose_row_sum(float a0, float a1, float a2, float a3, bool b0,
-                                                        bool b1) {
+// Transpose-reduce of nine per-lane values over each 16-lane row into one
+// register: lane j of a row ends with the row sum of value j for j < 8, and
+// lanes 8..15 with that of value 8. Each merge step pairs every lane with a
+// partner whose lane bit b differs (quad_perm for bits 0 and 1, a rotation of
+// the row by 4 and by 8 for bits 2 and 3: both flip the bit); a lane keeps
+// the half of its values that its bit selects and adds its partner's copy of
+// the same values, so the live values halve while the lanes summed double.
+// Value 8 is summed over half rows first and enters at the last step. 27
+// instructions, against 26 for two four-value transposes and a row sum into
+// three registers. b0..b3: lane bits 0..3. All 64 lanes must be active.
+__device__ __forceinline__ float transpose_row_sum9(float a0, float a1, float a2, float a3, float a4, float a5,
+                                                   float a6, float a7, float a8, bool b0, bool b1, bool b2,
+                                                   bool b3) {
     const float p01 = (b0 ? a1 : a0) + dpp_mov<0xB1>(b0 ? a0 : a1);  // quad_perm [1,0,3,2]
     const float p23 = (b0 ? a3 : a2) + dpp_mov<0xB1>(b0 ? a2 : a3);
-    float q = (b1 ? p23 : p01) + dpp_mov<0x4E>(b1 ? p01 : p23);      // quad_perm [2,3,0,1]
-    q = dpp_add<0x124>(q);                                           // row_ror:4
-    q = dpp_add<0x128>(q);                                           // row_ror:8
-    return q;
+    const float p45 = (b0 ? a5 : a4) + dpp_mov<0xB1>(b0 ? a4 : a5);
+    const float p67 = (b0 ? a7 : a6) + dpp_mov<0xB1>(b0 ? a6 : a7);
+    const float qa = (b1 ? p23 : p01) + dpp_mov<0x4E>(b1 ? p01 : p23);  // quad_perm [2,3,0,1]
+    const float qb = (b1 ? p67 : p45) + dpp_mov<0x4E>(b1 ? p45 : p67);
+    const float r = (b2 ? qb : qa) + dpp_mov<0x124>(b2 ? qa : qb);      // row_ror:4
+    float h8 = dpp_add<0xB1>(a8);
+    h8 = dpp_add<0x4E>(h8);
+    h8 = dpp_add<0x141>(h8);                                             // row_half_mirror
+    return (b3 ? h8 : r) + dpp_mov<0x128>(b3 ? r : h8);                  // row_ror:8
 }
 
 __device__ __forceinline__ void atomic_add_nz(float* p, float v) {
@@ -284,8 +287,11 @@ __global__ void k_zero_grads(float2* __restrict__ gm, float4* __restrict__ gc, f
 
 // Per (splat, wave) the nine terms are summed over each 16-lane row with
 // DPP; the four row sums of each wave go to LDS (16 partials per splat).
+// Term t of row slot s is stored at slot s ^ part_swizzle(t), so terms 0..7
+// of one wave's four rows fall in 32 different banks.
 constexpr int kBwdBatch = 32;
 constexpr int kParts = 16;  // 4 waves x 4 rows
+__host__ __device__ constexpr int part_swizzle(int t) { return t < 8 ? ((t & 2) << 1) | ((t & 4) << 1) : 0; }
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) void k_composite_bwd(
     const int W, const int H, const int TX, const uint32_t* __restrict__ ranges,
@@ -296,22 +302,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
     float* __restrict__ grad_conic_op, float* __restrict__ grad_rgb, const uint32_t* __restrict__ tile_order) {
     __shared__ float4 s_conic[kBwdBatch];  // -A/2, B, -C/2, opacity
     __shared__ float4 s_xyc[kBwdBatch];    // u, v, r, g
-    __shared__ float s_blue[kBwdBatch];
-    __shared__ uint32_t s_gid[kBwdBatch];
+    __shared__ float2 s_aux[kBwdBatch];    // b, Gaussian id
     __shared__ uint32_t s_live[kBwdBatch];
     __shared__ __align__(16) float s_part[kBwdBatch][9][kParts];  // per-row partial sums
-    __shared__ int s_epoch[4][kBwdBatch];  // batch whose partials of slot k wave w wrote last
+    __shared__ float s_epoch[4][kBwdBatch];  // batch (as int bits) whose partials of slot k wave w wrote last
     __shared__ uint32_t s_maxnc[4];
 
     const int tile = tile_order ? (int)tile_order[blockIdx.x] : (int)blockIdx.x;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const bool lane_b0 = (lane & 1) != 0, lane_b1 = (lane & 2) != 0;
+    const bool lane_b0 = (lane & 1) != 0, lane_b1 = (lane & 2) != 0, lane_b2 = (lane & 4) != 0,
+               lane_b3 = (lane & 8) != 0;
     const int tx = tile % TX, ty = tile / TX;
     const int px = tx * kTile + 8 * (wave & 1) + (lane & 7);
     const int py = ty * kTile + 8 * (wave >> 1) + (lane >> 3);
     const uint32_t qblocks = quadrant_blocks(wave);
+    // the one LDS store per (splat, wave): lane j <= 8 of each row writes its
+    // row's sum of term j, lane 9 of row 0 the wave's batch stamp
+    const int j16 = lane & 15;
+    const bool store_lane = j16 <= 8 || lane == 9;
+    float* const store_base = lane == 9 ? &s_epoch[wave][0]
+                                        : &s_part[0][min(j16, 8)][(wave * 4 + (lane >> 4)) ^ part_swizzle(j16)];
+    const int store_stride = lane == 9 ? 1 : 9 * kParts;
     const bool inside = px < W && py < H;
     const float fx = (float)px, fy = (float)py;
     const uint32_t start = ranges[2 * tile], len = ranges[2 * tile + 1] - start;
@@ -328,7 +341,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
         g2 = dL_dimage[2 * plane + p];
     }
     float B0 = bg.x, B1 = bg.y, B2 = bg.z;
-    if (tid < 4 * kBwdBatch) (&s_epoch[0][0])[tid] = -1;
+    if (tid < 4 * kBwdBatch) (&s_epoch[0][0])[tid] = __int_as_float(-1);
 
     // per-wave and per-tile maximum of n_contrib
     uint32_t wmax = nc;
@@ -351,28 +364,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
             const float4 c = rgb[g];
             s_conic[tid] = make_float4(-0.5f * co.x, co.y, -0.5f * co.z, co.w);
             s_xyc[tid] = make_float4(xy.x, xy.y, c.x, c.y);
-            s_blue[tid] = c.z;
-            s_gid[tid] = g;
+            s_aux[tid] = make_float2(c.z, __uint_as_float(g));
             s_live[tid] = block_mask(co, xy.x, xy.y, tx * kTile, ty * kTile);
         }
-        // fetch the next batch's list entries now, so their latency overlaps this batch
-
         __syncthreads();
 
         // live splats of this wave below its largest n_contrib, walked back to front
         static_assert(kBwdBatch <= 64, "one 64-bit live mask");
         uint64_t mk = __ballot(lane < cnt && bstart + lane < wave_maxnc && (s_live[lane] & qblocks) != 0u);
+        const int ncb = (int)nc - bstart;  // this lane uses slot k only if k < ncb
         while (mk != 0ull) {
             const int k = 63 - __clzll((long long)mk);
             mk &= ~(1ull << k);
             const float4 co = s_conic[k];
             const float4 xc = s_xyc[k];
-            const float cb = s_blue[k];
+            const float cb = s_aux[k].x;
             const float dx = fx - xc.x, dy = fy - xc.y;
-            float G, alpha;
-            splat_alpha(co.x, co.y, co.z, co.w, dx, dy, G, alpha);
+            float G, oG, alpha;
+            splat_alpha(co.x, co.y, co.z, co.w, dx, dy, G, oG, alpha);
             // branch-free: lanes past their n_contrib or below the floor add nothing
-            const bool use = bstart + k < (int)nc && alpha >= kAlphaMin;
+            const bool use = k < ncb && alpha >= kAlphaMin;
             const float Tj = T * __builtin_amdgcn_rcpf(1.0f - alpha);  // transmittance in front of k
             const float a = use ? alpha : 0.0f;  // a lane that does not use k adds nothing below
             const float w = a * Tj;
@@ -384,27 +395,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
             B2 = __builtin_fmaf(a, e2, B2);
             T = use ? Tj : T;
             // unsaturated alpha = o G: dL/do = G dL/da, dL/dpower = o G dL/da
-            const bool geo = use && co.w * G <= kAlphaMax;
+            const bool geo = use && oG <= kAlphaMax;
             const float d5 = geo ? G * dL_da : 0.0f;
             const float dp = co.w * d5;
             // moments of dL/dpower; the conic is applied once per splat afterwards
             const float d0 = dx * dp, d1 = dy * dp;         // sum dx dp, sum dy dp
             const float d2 = dx * d0, d3 = dy * d0, d4 = dy * d1;  // dx^2 dp, dx dy dp, dy^2 dp
             if (__ballot(use) != 0ull) {
-                const float qa = quad_transpose_row_sum(d0, d1, d2, d3, lane_b0, lane_b1);
-                const float qb = quad_transpose_row_sum(d4, d5, d6, d7, lane_b0, lane_b1);
-                const float r8 = dpp_row_sum(d8);
-                const int slot = wave * 4 + (lane >> 4);
-                const int j = lane & 15;
-                if (j < 4) {  // lane j of each row holds terms j and 4 + j
-                    // terms 2, 3 (and 6, 7) lie 32 floats after 0, 1: swap slot
-                    // halves for them so the 16 stores hit 16 different banks
-                    const int sl = slot ^ ((j & 2) << 1);
-                    s_part[k][j][sl] = qa;
-                    s_part[k][4 + j][sl] = qb;
-                }
-                if (j == 0) s_part[k][8][slot] = r8;
-                if (lane == 0) s_epoch[wave][k] = batch;
+                const float r = transpose_row_sum9(d0, d1, d2, d3, d4, d5, d6, d7, d8, lane_b0, lane_b1, lane_b2,
+                                                   lane_b3);
+                const float v = lane == 9 ? __int_as_float(batch) : r;
+                if (store_lane) store_base[k * store_stride] = v;
             }
         }
         __syncthreads();
@@ -417,12 +418,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
             if (k < cnt) {
                 uint32_t wm = 0u;
 #pragma unroll
-                for (int w = 0; w < 4; ++w) wm |= (s_epoch[w][k] == batch ? 1u : 0u) << w;
+                for (int w = 0; w < 4; ++w) wm |= (__float_as_int(s_epoch[w][k]) == batch ? 1u : 0u) << w;
                 if (wm != 0u) {
-                    const uint32_t g = s_gid[k];
-                    // term t of wave w sits in slots 4 w' .. 4 w' + 3 with w' = w ^ 1 for t = 2, 3, 6, 7
+                    const uint32_t g = __float_as_uint(s_aux[k].y);
+                    // term t of wave w sits in slots 4 w' .. 4 w' + 3, w' = w ^ part_swizzle(t) / 4
                     auto term_sum = [&](int t) {
-                        const int flip = (t & 2) ? 1 : 0;
+                        const int flip = part_swizzle(t) >> 2;
                         float sum = 0.0f;
 #pragma unroll
                         for (int w = 0; w < 4; ++w) {
