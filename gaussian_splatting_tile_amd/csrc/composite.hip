@@ -150,8 +150,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
     uint32_t* __restrict__ n_examined, const uint32_t* __restrict__ tile_order) {
     __shared__ float4 s_conic[kBatch];  // -A/2, B, -C/2, opacity
     __shared__ float4 s_xyc[kBatch];    // u, v, r, g
-    __shared__ float s_blue[kBatch];
-    __shared__ uint32_t s_live[kBatch];
+    __shared__ float4 s_bl[kBatch];     // b, live blocks (as bits), -, -: one address with the two above
 
     const int tile = tile_order ? (int)tile_order[blockIdx.x] : (int)blockIdx.x;
     const int tid = threadIdx.x;
@@ -182,8 +181,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
             const float4 c = rgb[g];
             s_conic[tid] = make_float4(-0.5f * co.x, co.y, -0.5f * co.z, co.w);
             s_xyc[tid] = make_float4(xy.x, xy.y, c.x, c.y);
-            s_blue[tid] = c.z;
-            s_live[tid] = block_mask(co, xy.x, xy.y, tx * kTile, ty * kTile);
+            s_bl[tid] = make_float4(c.z, __uint_as_float(block_mask(co, xy.x, xy.y, tx * kTile, ty * kTile)),
+                                    0.0f, 0.0f);
         }
         __syncthreads();
         const int cnt = (int)min((uint32_t)kBatch, end - base);
@@ -193,7 +192,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int k = q * 64 + lane;
-            m[q] = __ballot(k < cnt && (s_live[k] & qblocks) != 0u);
+            m[q] = __ballot(k < cnt && (__float_as_uint(s_bl[k].y) & qblocks) != 0u);
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -204,7 +203,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
                 mq &= mq - 1ull;
                 const float4 co = s_conic[k];
                 const float4 xc = s_xyc[k];
-                const float cb = s_blue[k];
+                const float cb = s_bl[k].x;
                 float G, oG, alpha;
                 splat_alpha(co.x, co.y, co.z, co.w, fx - xc.x, fy - xc.y, G, oG, alpha);
                 // branch-free update; stopped lanes and alphas below the floor change nothing
