@@ -333,6 +333,11 @@ __global__ void k_zero_grads(float2* __restrict__ gm, float4* __restrict__ gc, f
 // Term t of row slot s is stored at slot s ^ part_swizzle(t), so terms 0..7
 // of one wave's four rows fall in 32 different banks.
 constexpr int kBwdBatch = 32;
+// Splats staged per round, walked in batches of kBwdBatch: the gathers of a
+// round (list entry, then the splat's records) are two dependent memory
+// round trips, paid once per round. The heaviest tile bounds the launch and
+// its workgroup runs nearly alone, so that latency is on its critical path.
+constexpr int kBwdStage = 128;
 constexpr int kParts = 16;  // 4 waves x 4 rows
 __host__ __device__ constexpr int part_swizzle(int t) { return t < 8 ? ((t & 2) << 1) | ((t & 4) << 1) : 0; }
 
@@ -343,10 +348,10 @@ __global__ __launch_bounds__(256) void k_composite_bwd(
     const float* __restrict__ final_T, const uint32_t* __restrict__ n_contrib,
     const float* __restrict__ dL_dimage, float* __restrict__ grad_mean2d,
     float* __restrict__ grad_conic_op, float* __restrict__ grad_rgb, const uint32_t* __restrict__ tile_order) {
-    __shared__ float4 s_conic[kBwdBatch];  // -A/2, B, -C/2, opacity
-    __shared__ float4 s_xyc[kBwdBatch];    // u, v, r, g
-    __shared__ float2 s_aux[kBwdBatch];    // b, Gaussian id
-    __shared__ uint32_t s_live[kBwdBatch];
+    __shared__ float4 s_conic[kBwdStage];  // -A/2, B, -C/2, opacity
+    __shared__ float4 s_xyc[kBwdStage];    // u, v, r, g
+    __shared__ float2 s_aux[kBwdStage];    // b, Gaussian id
+    __shared__ uint32_t s_live[kBwdStage];
     __shared__ __align__(16) float s_part[kBwdBatch][9][kParts];  // per-row partial sums
     __shared__ float s_epoch[4][kBwdBatch];  // batch (as int bits) whose partials of slot k wave w wrote last
     __shared__ uint32_t s_maxnc[4];
@@ -396,12 +401,11 @@ __global__ __launch_bounds__(256) void k_composite_bwd(
     const int wave_maxnc = (int)wmax;
 
     int batch = 0;
-    for (int bend = maxnc; bend > 0; bend -= kBwdBatch, ++batch) {
-        const int bstart = bend > kBwdBatch ? bend - kBwdBatch : 0;
-        const int cnt = bend - bstart;
-        __syncthreads();  // the previous batch is fully consumed
-        if (tid < cnt) {
-            const uint32_t g = point_list[start + bstart + tid];
+    for (int send = maxnc; send > 0; send -= kBwdStage) {  // rounds, back to front
+        const int sstart = send > kBwdStage ? send - kBwdStage : 0;
+        __syncthreads();  // the previous round is fully consumed
+        if (tid < send - sstart) {
+            const uint32_t g = point_list[start + sstart + tid];
             const float4 xy = xy_depth[g];
             const float4 co = conic_op[g];
             const float4 c = rgb[g];
@@ -410,115 +414,120 @@ __global__ __launch_bounds__(256) void k_composite_bwd(
             s_aux[tid] = make_float2(c.z, __uint_as_float(g));
             s_live[tid] = block_mask(co, xy.x, xy.y, tx * kTile, ty * kTile);
         }
-        __syncthreads();
+        for (int bend = send; bend > sstart; bend -= kBwdBatch, ++batch) {  // batches of the round
+            const int bstart = bend - kBwdBatch > sstart ? bend - kBwdBatch : sstart;
+            const int cnt = bend - bstart;
+            const int off = bstart - sstart;  // staging slot of this batch's slot 0
+            __syncthreads();  // staged, and the previous batch's partials are consumed
 
-        // live splats of this wave below its largest n_contrib, walked back to front
-        static_assert(kBwdBatch <= 64, "one 64-bit live mask");
-        uint64_t mk = __ballot(lane < cnt && bstart + lane < wave_maxnc && (s_live[lane] & qblocks) != 0u);
-        const int ncb = (int)nc - bstart;  // this lane uses slot k only if k < ncb
-        // Two splats per step: their alphas are independent, so the second's
-        // exponential and reciprocal overlap the first's updates, and the two
-        // reductions interleave. A launch lasts as long as its heaviest tiles,
-        // which end up running nearly alone on their compute units, where a
-        // single splat per step leaves the wave waiting on its own latency.
-        while (mk != 0ull) {
-            const int k1 = 63 - __clzll((long long)mk);
-            mk &= ~(1ull << k1);
-            const bool two = mk != 0ull;
-            const int k2 = two ? 63 - __clzll((long long)mk) : k1;
-            mk &= ~(1ull << k2);
-            const float4 co1 = s_conic[k1], xc1 = s_xyc[k1];
-            const float4 co2 = s_conic[k2], xc2 = s_xyc[k2];
-            const float cb1 = s_aux[k1].x, cb2 = s_aux[k2].x;
-            const float dx1 = fx - xc1.x, dy1 = fy - xc1.y;
-            const float dx2 = fx - xc2.x, dy2 = fy - xc2.y;
-            float G1, oG1, alpha1, G2, oG2, alpha2;
-            splat_alpha(co1.x, co1.y, co1.z, co1.w, dx1, dy1, G1, oG1, alpha1);
-            splat_alpha(co2.x, co2.y, co2.z, co2.w, dx2, dy2, G2, oG2, alpha2);
-            const float rinv1 = __builtin_amdgcn_rcpf(1.0f - alpha1);
-            const float rinv2 = __builtin_amdgcn_rcpf(1.0f - alpha2);
-            float t1[9], t2[9];
-            bool use1, use2;
-            auto step = [&](int k, const float4& co, const float4& xc, float cb, float dx, float dy, float G, float oG,
-                            float alpha, float rinv, bool valid, float* d, bool& use) {
-                // branch-free: lanes past their n_contrib or below the floor add nothing
-                use = valid && k < ncb && alpha >= kAlphaMin;
-                const float Tj = T * rinv;  // transmittance in front of k
-                const float a = use ? alpha : 0.0f;
-                const float w = a * Tj;
-                d[6] = w * g0;
-                d[7] = w * g1;
-                d[8] = w * g2;
-                const float e0 = xc.z - B0, e1 = xc.w - B1, e2 = cb - B2;  // colour minus colour behind
-                const float dL_da = __builtin_fmaf(g2, e2, __builtin_fmaf(g1, e1, g0 * e0)) * Tj;
-                B0 = __builtin_fmaf(a, e0, B0);  // B + a (c - B); exact no-op at a = 0
-                B1 = __builtin_fmaf(a, e1, B1);
-                B2 = __builtin_fmaf(a, e2, B2);
-                T = use ? Tj : T;
-                // unsaturated alpha = o G: dL/do = G dL/da, dL/dpower = o G dL/da
-                const bool geo = use && oG <= kAlphaMax;
-                d[5] = geo ? G * dL_da : 0.0f;
-                const float dp = co.w * d[5];
-                // moments of dL/dpower; the conic is applied once per splat afterwards
-                d[0] = dx * dp;        // dx dp
-                d[1] = dy * dp;        // dy dp
-                d[2] = dx * d[0];      // dx^2 dp
-                d[3] = dy * d[0];      // dx dy dp
-                d[4] = dy * d[1];      // dy^2 dp
-            };
-            step(k1, co1, xc1, cb1, dx1, dy1, G1, oG1, alpha1, rinv1, true, t1, use1);
-            step(k2, co2, xc2, cb2, dx2, dy2, G2, oG2, alpha2, rinv2, two, t2, use2);
-            const uint64_t u1 = __ballot(use1), u2 = __ballot(use2);
-            if ((u1 | u2) != 0ull) {
-                const float r1 = transpose_row_sum9(t1[0], t1[1], t1[2], t1[3], t1[4], t1[5], t1[6], t1[7], t1[8],
-                                                    lane_b0, lane_b1, lane_b2, lane_b3);
-                const float r2 = transpose_row_sum9(t2[0], t2[1], t2[2], t2[3], t2[4], t2[5], t2[6], t2[7], t2[8],
-                                                    lane_b0, lane_b1, lane_b2, lane_b3);
-                const float v1 = lane == 9 ? __int_as_float(batch) : r1;
-                const float v2 = lane == 9 ? __int_as_float(batch) : r2;
-                if (store_lane) {
-                    if (u1 != 0ull) store_base[k1 * store_stride] = v1;
-                    if (u2 != 0ull) store_base[k2 * store_stride] = v2;
+            // live splats of this wave below its largest n_contrib, walked back to front
+            static_assert(kBwdBatch <= 64, "one 64-bit live mask");
+            uint64_t mk = __ballot(lane < cnt && bstart + lane < wave_maxnc && (s_live[off + lane] & qblocks) != 0u);
+            const int ncb = (int)nc - bstart;  // this lane uses slot k only if k < ncb
+            // Two splats per step: their alphas are independent, so the second's
+            // exponential and reciprocal overlap the first's updates, and the two
+            // reductions interleave. A launch lasts as long as its heaviest tiles,
+            // which end up running nearly alone on their compute units, where a
+            // single splat per step leaves the wave waiting on its own latency.
+            while (mk != 0ull) {
+                const int k1 = 63 - __clzll((long long)mk);
+                mk &= ~(1ull << k1);
+                const bool two = mk != 0ull;
+                const int k2 = two ? 63 - __clzll((long long)mk) : k1;
+                mk &= ~(1ull << k2);
+                const float4 co1 = s_conic[off + k1], xc1 = s_xyc[off + k1];
+                const float4 co2 = s_conic[off + k2], xc2 = s_xyc[off + k2];
+                const float cb1 = s_aux[off + k1].x, cb2 = s_aux[off + k2].x;
+                const float dx1 = fx - xc1.x, dy1 = fy - xc1.y;
+                const float dx2 = fx - xc2.x, dy2 = fy - xc2.y;
+                float G1, oG1, alpha1, G2, oG2, alpha2;
+                splat_alpha(co1.x, co1.y, co1.z, co1.w, dx1, dy1, G1, oG1, alpha1);
+                splat_alpha(co2.x, co2.y, co2.z, co2.w, dx2, dy2, G2, oG2, alpha2);
+                const float rinv1 = __builtin_amdgcn_rcpf(1.0f - alpha1);
+                const float rinv2 = __builtin_amdgcn_rcpf(1.0f - alpha2);
+                float t1[9], t2[9];
+                bool use1, use2;
+                auto step = [&](int k, const float4& co, const float4& xc, float cb, float dx, float dy, float G, float oG,
+                                float alpha, float rinv, bool valid, float* d, bool& use) {
+                    // branch-free: lanes past their n_contrib or below the floor add nothing
+                    use = valid && k < ncb && alpha >= kAlphaMin;
+                    const float Tj = T * rinv;  // transmittance in front of k
+                    const float a = use ? alpha : 0.0f;
+                    const float w = a * Tj;
+                    d[6] = w * g0;
+                    d[7] = w * g1;
+                    d[8] = w * g2;
+                    const float e0 = xc.z - B0, e1 = xc.w - B1, e2 = cb - B2;  // colour minus colour behind
+                    const float dL_da = __builtin_fmaf(g2, e2, __builtin_fmaf(g1, e1, g0 * e0)) * Tj;
+                    B0 = __builtin_fmaf(a, e0, B0);  // B + a (c - B); exact no-op at a = 0
+                    B1 = __builtin_fmaf(a, e1, B1);
+                    B2 = __builtin_fmaf(a, e2, B2);
+                    T = use ? Tj : T;
+                    // unsaturated alpha = o G: dL/do = G dL/da, dL/dpower = o G dL/da
+                    const bool geo = use && oG <= kAlphaMax;
+                    d[5] = geo ? G * dL_da : 0.0f;
+                    const float dp = co.w * d[5];
+                    // moments of dL/dpower; the conic is applied once per splat afterwards
+                    d[0] = dx * dp;        // dx dp
+                    d[1] = dy * dp;        // dy dp
+                    d[2] = dx * d[0];      // dx^2 dp
+                    d[3] = dy * d[0];      // dx dy dp
+                    d[4] = dy * d[1];      // dy^2 dp
+                };
+                step(k1, co1, xc1, cb1, dx1, dy1, G1, oG1, alpha1, rinv1, true, t1, use1);
+                step(k2, co2, xc2, cb2, dx2, dy2, G2, oG2, alpha2, rinv2, two, t2, use2);
+                const uint64_t u1 = __ballot(use1), u2 = __ballot(use2);
+                if ((u1 | u2) != 0ull) {
+                    const float r1 = transpose_row_sum9(t1[0], t1[1], t1[2], t1[3], t1[4], t1[5], t1[6], t1[7], t1[8],
+                                                        lane_b0, lane_b1, lane_b2, lane_b3);
+                    const float r2 = transpose_row_sum9(t2[0], t2[1], t2[2], t2[3], t2[4], t2[5], t2[6], t2[7], t2[8],
+                                                        lane_b0, lane_b1, lane_b2, lane_b3);
+                    const float v1 = lane == 9 ? __int_as_float(batch) : r1;
+                    const float v2 = lane == 9 ? __int_as_float(batch) : r2;
+                    if (store_lane) {
+                        if (u1 != 0ull) store_base[k1 * store_stride] = v1;
+                        if (u2 != 0ull) store_base[k2 * store_stride] = v2;
+                    }
                 }
             }
-        }
-        __syncthreads();
-        // all 256 threads: splat slot k = tid % 32, one output group per
-        // thread (tid / 32): the mean pair, dA, dB, dC, dopacity, r, g, b.
-        // Only the partials of waves that wrote slot k in this batch count.
-        //   d(u, v) = (A Sx + B Sy, B Sx + C Sy); dA = -Sxx / 2; dB = -Sxy; dC = -Syy / 2
-        {
-            const int k = tid & (kBwdBatch - 1), grp = tid >> 5;
-            if (k < cnt) {
-                uint32_t wm = 0u;
-#pragma unroll
-                for (int w = 0; w < 4; ++w) wm |= (__float_as_int(s_epoch[w][k]) == batch ? 1u : 0u) << w;
-                if (wm != 0u) {
-                    const uint32_t g = __float_as_uint(s_aux[k].y);
-                    // term t of wave w sits in slots 4 w' .. 4 w' + 3, w' = w ^ part_swizzle(t) / 4
-                    auto term_sum = [&](int t) {
-                        const int flip = part_swizzle(t) >> 2;
-                        float sum = 0.0f;
-#pragma unroll
-                        for (int w = 0; w < 4; ++w) {
-                            if ((wm >> w) & 1u) {
-                                const float4 q = reinterpret_cast<const float4*>(&s_part[k][t][0])[w ^ flip];
-                                sum += (q.x + q.y) + (q.z + q.w);
+            __syncthreads();
+            // all 256 threads: splat slot k = tid % 32, one output group per
+            // thread (tid / 32): the mean pair, dA, dB, dC, dopacity, r, g, b.
+            // Only the partials of waves that wrote slot k in this batch count.
+            //   d(u, v) = (A Sx + B Sy, B Sx + C Sy); dA = -Sxx / 2; dB = -Sxy; dC = -Syy / 2
+            {
+                const int k = tid & (kBwdBatch - 1), grp = tid >> 5;
+                if (k < cnt) {
+                    uint32_t wm = 0u;
+    #pragma unroll
+                    for (int w = 0; w < 4; ++w) wm |= (__float_as_int(s_epoch[w][k]) == batch ? 1u : 0u) << w;
+                    if (wm != 0u) {
+                        const uint32_t g = __float_as_uint(s_aux[off + k].y);
+                        // term t of wave w sits in slots 4 w' .. 4 w' + 3, w' = w ^ part_swizzle(t) / 4
+                        auto term_sum = [&](int t) {
+                            const int flip = part_swizzle(t) >> 2;
+                            float sum = 0.0f;
+    #pragma unroll
+                            for (int w = 0; w < 4; ++w) {
+                                if ((wm >> w) & 1u) {
+                                    const float4 q = reinterpret_cast<const float4*>(&s_part[k][t][0])[w ^ flip];
+                                    sum += (q.x + q.y) + (q.z + q.w);
+                                }
                             }
+                            return sum;
+                        };
+                        if (grp == 0) {
+                            const float4 co = s_conic[off + k];
+                            const float Sx = term_sum(0), Sy = term_sum(1);
+                            const float A = -2.0f * co.x, C = -2.0f * co.z;  // exact
+                            atomic_add_nz(grad_mean2d + 2 * (size_t)g, A * Sx + co.y * Sy);
+                            atomic_add_nz(grad_mean2d + 2 * (size_t)g + 1, co.y * Sx + C * Sy);
+                        } else if (grp <= 4) {
+                            const float scale = grp == 2 ? -1.0f : (grp == 4 ? 1.0f : -0.5f);
+                            atomic_add_nz(grad_conic_op + 4 * (size_t)g + (grp - 1), scale * term_sum(grp + 1));
+                        } else {
+                            atomic_add_nz(grad_rgb + 4 * (size_t)g + (grp - 5), term_sum(grp + 1));
                         }
-                        return sum;
-                    };
-                    if (grp == 0) {
-                        const float4 co = s_conic[k];
-                        const float Sx = term_sum(0), Sy = term_sum(1);
-                        const float A = -2.0f * co.x, C = -2.0f * co.z;  // exact
-                        atomic_add_nz(grad_mean2d + 2 * (size_t)g, A * Sx + co.y * Sy);
-                        atomic_add_nz(grad_mean2d + 2 * (size_t)g + 1, co.y * Sx + C * Sy);
-                    } else if (grp <= 4) {
-                        const float scale = grp == 2 ? -1.0f : (grp == 4 ? 1.0f : -0.5f);
-                        atomic_add_nz(grad_conic_op + 4 * (size_t)g + (grp - 1), scale * term_sum(grp + 1));
-                    } else {
-                        atomic_add_nz(grad_rgb + 4 * (size_t)g + (grp - 5), term_sum(grp + 1));
                     }
                 }
             }
