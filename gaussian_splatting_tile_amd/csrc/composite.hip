@@ -350,7 +350,7 @@ __global__ __launch_bounds__(256) void k_composite_bwd(
     float* __restrict__ grad_conic_op, float* __restrict__ grad_rgb, const uint32_t* __restrict__ tile_order) {
     __shared__ float4 s_conic[kBwdStage];  // -A/2, B, -C/2, opacity
     __shared__ float4 s_xyc[kBwdStage];    // u, v, r, g
-    __shared__ float2 s_aux[kBwdStage];    // b, Gaussian id
+    __shared__ float4 s_aux[kBwdStage];    // b, Gaussian id, -, -: one address with the two above
     __shared__ uint32_t s_live[kBwdStage];
     __shared__ __align__(16) float s_part[kBwdBatch][9][kParts];  // per-row partial sums
     __shared__ float s_epoch[4][kBwdBatch];  // batch (as int bits) whose partials of slot k wave w wrote last
@@ -388,7 +388,11 @@ __global__ __launch_bounds__(256) void k_composite_bwd(
         g1 = dL_dimage[plane + p];
         g2 = dL_dimage[2 * plane + p];
     }
-    float B0 = bg.x, B1 = bg.y, B2 = bg.z;
+    // g.R: the upstream gradient dotted with the radiance from behind the
+    // splats walked so far (their c alpha T, plus the background's T_final
+    // bg). With it dL/dalpha_j = T_j (g.c_j) - (g.R_j) / (1 - alpha_j): the
+    // colour behind splat j is R_j / T_(j+1), and T_(j+1) = T_j (1 - alpha_j).
+    float gR = T * __builtin_fmaf(g2, bg.z, __builtin_fmaf(g1, bg.y, g0 * bg.x));
     if (tid < 4 * kBwdBatch) (&s_epoch[0][0])[tid] = __int_as_float(-1);
 
     // per-wave and per-tile maximum of n_contrib
@@ -411,7 +415,7 @@ __global__ __launch_bounds__(256) void k_composite_bwd(
             const float4 c = rgb[g];
             s_conic[tid] = make_float4(-0.5f * co.x, co.y, -0.5f * co.z, co.w);
             s_xyc[tid] = make_float4(xy.x, xy.y, c.x, c.y);
-            s_aux[tid] = make_float2(c.z, __uint_as_float(g));
+            s_aux[tid] = make_float4(c.z, __uint_as_float(g), 0.0f, 0.0f);
             s_live[tid] = block_mask(co, xy.x, xy.y, tx * kTile, ty * kTile);
         }
         for (int bend = send; bend > sstart; bend -= kBwdBatch, ++batch) {  // batches of the round
@@ -446,22 +450,22 @@ __global__ __launch_bounds__(256) void k_composite_bwd(
                 const float rinv1 = __builtin_amdgcn_rcpf(1.0f - alpha1);
                 const float rinv2 = __builtin_amdgcn_rcpf(1.0f - alpha2);
                 float t1[9], t2[9];
-                bool use1, use2;
-                auto step = [&](int k, const float4& co, const float4& xc, float cb, float dx, float dy, float G, float oG,
-                                float alpha, float rinv, bool valid, float* d, bool& use) {
-                    // branch-free: lanes past their n_contrib or below the floor add nothing
-                    use = valid && k < ncb && alpha >= kAlphaMin;
-                    const float Tj = T * rinv;  // transmittance in front of k
+                // branch-free: lanes past their n_contrib or below the floor add nothing
+                const bool use1 = k1 < ncb && alpha1 >= kAlphaMin;
+                const bool use2 = two && k2 < ncb && alpha2 >= kAlphaMin;
+                const uint64_t u1 = __ballot(k1 < ncb && alpha1 >= kAlphaMin);
+                const uint64_t u2 = two ? __ballot(k2 < ncb && alpha2 >= kAlphaMin) : 0ull;
+                auto step = [&](const float4& co, const float4& xc, float cb, float dx, float dy, float G, float oG,
+                                float alpha, float rinv, bool use, float* d) {
+                    const float Tj = T * rinv;  // transmittance in front of the splat
                     const float a = use ? alpha : 0.0f;
                     const float w = a * Tj;
                     d[6] = w * g0;
                     d[7] = w * g1;
                     d[8] = w * g2;
-                    const float e0 = xc.z - B0, e1 = xc.w - B1, e2 = cb - B2;  // colour minus colour behind
-                    const float dL_da = __builtin_fmaf(g2, e2, __builtin_fmaf(g1, e1, g0 * e0)) * Tj;
-                    B0 = __builtin_fmaf(a, e0, B0);  // B + a (c - B); exact no-op at a = 0
-                    B1 = __builtin_fmaf(a, e1, B1);
-                    B2 = __builtin_fmaf(a, e2, B2);
+                    const float gc = __builtin_fmaf(g2, cb, __builtin_fmaf(g1, xc.w, g0 * xc.z));  // g.c
+                    const float dL_da = __builtin_fmaf(-rinv, gR, Tj * gc);
+                    gR = __builtin_fmaf(w, gc, gR);  // exact no-op at w = 0
                     T = use ? Tj : T;
                     // unsaturated alpha = o G: dL/do = G dL/da, dL/dpower = o G dL/da
                     const bool geo = use && oG <= kAlphaMax;
@@ -474,9 +478,8 @@ __global__ __launch_bounds__(256) void k_composite_bwd(
                     d[3] = dy * d[0];      // dx dy dp
                     d[4] = dy * d[1];      // dy^2 dp
                 };
-                step(k1, co1, xc1, cb1, dx1, dy1, G1, oG1, alpha1, rinv1, true, t1, use1);
-                step(k2, co2, xc2, cb2, dx2, dy2, G2, oG2, alpha2, rinv2, two, t2, use2);
-                const uint64_t u1 = __ballot(use1), u2 = __ballot(use2);
+                step(co1, xc1, cb1, dx1, dy1, G1, oG1, alpha1, rinv1, use1, t1);
+                step(co2, xc2, cb2, dx2, dy2, G2, oG2, alpha2, rinv2, use2, t2);
                 if ((u1 | u2) != 0ull) {
                     const float r1 = transpose_row_sum9(t1[0], t1[1], t1[2], t1[3], t1[4], t1[5], t1[6], t1[7], t1[8],
                                                         lane_b0, lane_b1, lane_b2, lane_b3);
