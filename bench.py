@@ -40,9 +40,10 @@ WORKLOADS = {
             "backward with dL/dI = sign(I - I_ref) against a second scene's render; the 16 views are "
             "recorded once as a HIP graph and replayed",
 }
-# Algorithmic work per unit: a forward pixel-splat evaluation
-# is ~25 fp32 flop-equivalents; a backward one ~45 plus its share of the
-# per-splat reduction.
+# Algorithmic work per unit: a forward pixel-splat evaluation is ~25 fp32
+# flop-equivalents (the quadratic form, one exponential counted as 8, the
+# clamp, the colour and transmittance updates); a backward one ~45 plus its
+# share of the per-splat reduction.
 FLOPS_PER_FWD_EVAL = 25.0
 FLOPS_PER_BWD_EVAL = 45.0
 PEAK_FP32_VECTOR = 157.3e12   # MI355X fp32 vector (packed) FLOP/s
@@ -200,8 +201,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(see DESIGN.md for how the path would shard). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path. Run with --gpus 1.",
+              file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
