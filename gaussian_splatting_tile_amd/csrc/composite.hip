@@ -8,8 +8,10 @@
 // test the stop threshold); learn-gs "The kernel" (lanes retire by flag and
 // keep fetching for the others; the vote is __syncthreads_count).
 // Backward: "rigel" README "Backward" (walk back to front from final_T and
-// n_contrib with the colour behind carried along, T_i = T_{i+1}/(1-a_i))
-// and "Deliberate differences" (no gradient through a saturated alpha).
+// n_contrib, T_i = T_{i+1}/(1-a_i), with what lies behind carried along:
+// here as g.R, the upstream gradient dotted with the radiance from behind,
+// instead of the colour behind; the two give the same dL/dalpha) and
+// "Deliberate differences" (no gradient through a saturated alpha).
 //
 // MI355X design:
 //  * The exponent -0.5 (A dx^2 + C dy^2) - B dx dy is evaluated in fp32 in
@@ -36,7 +38,8 @@
 //    rows with DPP adds (skipped when no lane contributed) into LDS; the
 //    terms are the colour gradient, dL/do, and the moments of dL/dpower
 //    (dx, dy, dx^2, dx dy, dy^2 times it), from which the conic and mean
-//    gradients follow once per (splat, tile). After each 32-splat batch all
+//    gradients follow once per (splat, tile). Splats are staged 128 at a time
+//    and walked in 32-splat batches; after each batch all
 //    256 threads finish it (one output per thread), summing only the
 //    partials of waves that wrote them (a per-wave batch stamp replaces
 //    clearing the partials); one global atomic per value per tile entry
@@ -49,9 +52,9 @@
 //    updates, and the backward's two reductions interleave. A launch lasts as
 //    long as its heaviest tiles (lists of 1,000-1,500 splats at 1080p),
 //    which end up running almost alone on their compute units; with one
-//    splat per step their waves mostly wait on their own latency. Measured
-//    per workgroup, the backward's last 70 of 245 us ran under 5% of the
-//    workgroup slots before this change.
+//    splat per step their waves mostly wait on their own latency (measured
+//    per workgroup at 1080p: the backward's last 70 of 245 us then ran on
+//    under 5% of the workgroup slots).
 #include "gs_internal.h"
 
 namespace gs {
@@ -68,14 +71,15 @@ __device__ __noinline__ float exp_rn(float x) { return (float)exp((double)x); }
 // Gaussian weight and alpha of a splat with conic (A, B, C) and opacity o at
 // offset (dx, dy) from its centre:
 //   power = -0.5 (A dx^2 + C dy^2) - B dx dy,  G = exp(power),
-//   alpha = min(0.99, o G).
+//   alpha = min(0.99, o G),  and oG = o G (unclamped).
 // Takes hA = -A/2 and hC = -C/2 (staged once per splat): scaling by a power
 // of two commutes with rounding, so (hA dx) dx + (hC dy) dy - (B dx) dy is
 // bit-identical to the written order and saves a multiply per pixel.
-// Must be called with the whole wave active (the rare exact path is behind
-// a wave-uniform test).
-// splat_alpha in two parts, so that several splats' fast parts can be
-// issued back to back with one wave-uniform test for the rare exact path.
+// In two parts, so that several splats' fast parts can be issued back to
+// back behind one wave-uniform test for the rare exact path:
+// splat_alpha_fast returns whether alpha lies near the 1/255 floor, and
+// splat_alpha_exact recomputes those lanes. splat_alpha does both for one
+// splat; it must be called with the whole wave active.
 __device__ __forceinline__ bool splat_alpha_fast(float hA, float B, float hC, float o, float dx, float dy,
                                                  float& power, float& G, float& oG, float& alpha) {
     power = ((hA * dx) * dx + (hC * dy) * dy) - (B * dx) * dy;
