@@ -145,7 +145,8 @@ def bench_views(args):
     def loss_grad(i, image, out):
         out.copy_(image).sub_(refs[i]).sign_()
 
-    batch = gs.ViewBatch(cams, sc, capacity=int(E_max * 1.25) + 1024, device=dev, streams=args.streams)
+    batch = gs.ViewBatch(cams, sc, capacity=int(E_max * 1.25) + 1024, device=dev, streams=args.streams,
+                         chunked=args.backward == "chunked")
     batch.enqueue(loss_grad)
     E = batch.check()
     st = torch.cuda.current_stream()
@@ -178,7 +179,7 @@ def bench_views(args):
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(1e3 * graph_s, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"cfg4: {WORKLOADS['cfg4']}", "n_gaussians": sc.n, "views_per_step": n_views,
-                   "streams": args.streams,
+                   "streams": args.streams, "backward": args.backward,
                    "width": 400, "height": 400, "entries_per_view": E},
         "secondary": {"eager_frames_per_s": round(n_views / eager_s, 3),
                       "graph_event_ms_per_step": round(e0.elapsed_time(e1) / args.steps, 4)},
@@ -194,6 +195,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tile-order", choices=("heavy-first", "index"), default="heavy-first",
                     help="tile schedule of the compositing kernels (results are identical)")
+    ap.add_argument("--backward", choices=("chunked", "whole"), default="chunked",
+                    help="backward compositing over 256-entry chunks of each list (from the forward's "
+                         "checkpoints) or over whole lists (results agree to float32 rounding)")
     ap.add_argument("--streams", type=int, default=4,
                     help="cfg4: streams the 16 views are spread over (fork/join inside the graph)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -253,6 +257,9 @@ def main():
                   scene.rgb, out=pre)
     keys, pl, E = gs.bin_and_sort(c, pre["xy_depth"], pre["tiles_touched"], bins)
     bins._ensure(int(E * 1.1) + 1024)  # headroom so timed frames never regrow
+    chunked = args.backward == "chunked"
+    ckpt = torch.empty((gs.ckpt_rows(bins.capacity), 4), dtype=f32, device=dev) if chunked else None
+    chunks = torch.empty((gs.chunk_words(cam, bins.capacity),), dtype=i32, device=dev) if chunked else None
     gs.tile_ranges(cam, keys, E, out=ranges)
     probe = gs.composite_fwd(cam, ranges, pl, pre["xy_depth"], pre["conic_op"], pre["rgb"],
                              with_examined=True)
@@ -278,12 +285,14 @@ def main():
         k, p = gs.bin_and_sort_async(c, pre["xy_depth"], pre["tiles_touched"], bins, conic_op=pre["conic_op"],
                                      tile_test=tile_test)
         mark(False)
-        gs.tile_ranges_async(c, bins, out=ranges, order=order)
+        gs.tile_ranges_async(c, bins, out=ranges, order=order, chunks=chunks)
         mark(True)
-        gs.composite_fwd(c, ranges, p, pre["xy_depth"], pre["conic_op"], pre["rgb"], out=fwd, order=order)
+        gs.composite_fwd(c, ranges, p, pre["xy_depth"], pre["conic_op"], pre["rgb"], out=fwd, order=order,
+                         ckpt=ckpt, capacity=bins.capacity)
         mark(True)
         gs.composite_bwd(c, n, ranges, p, pre["xy_depth"], pre["conic_op"], pre["rgb"],
-                         fwd["final_T"], fwd["n_contrib"], dLdI, out=grads, order=order)
+                         fwd["final_T"], fwd["n_contrib"], dLdI, out=grads, order=order, chunks=chunks,
+                         image=fwd["image"] if chunked else None, ckpt=ckpt, capacity=bins.capacity)
         mark(True)
 
     for _ in range(args.warmup):
@@ -397,6 +406,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: {WORKLOADS[args.workload]}", "tile_order": args.tile_order,
+                   "backward": args.backward,
                    "n_gaussians": n, "width": W, "height": H, "n_entries": E,
                    "evals_fwd": evals_fwd, "evals_bwd": evals_bwd},
         "pixel_splat_evals_per_s": round((evals_fwd + evals_bwd) * fps, 1),

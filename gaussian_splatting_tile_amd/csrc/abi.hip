@@ -301,7 +301,7 @@ gs_status gs_tile_ranges(const gs_camera* cam, const uint64_t* keys, int64_t n_e
     if (!ranges || (n_entries > 0 && !keys)) return fail(GS_ERR_INVALID, "gs_tile_ranges: NULL pointer");
     const int n_tiles = gs::tiles_x(*cam) * gs::tiles_y(*cam);
     return hip_check(gs::launch_tile_ranges(keys, (uint32_t)n_entries, nullptr, 0u, n_tiles, ranges, tile_order,
-                                            (hipStream_t)stream),
+                                            nullptr, (hipStream_t)stream),
                      "tile ranges launch");
 }
 
@@ -315,7 +315,26 @@ gs_status gs_tile_ranges_async(const gs_camera* cam, const uint64_t* keys, const
         return fail(GS_ERR_INVALID, "gs_tile_ranges_async: NULL or misaligned pointer");
     const int n_tiles = gs::tiles_x(*cam) * gs::tiles_y(*cam);
     return hip_check(gs::launch_tile_ranges(keys, 0u, n_entries_dev, (uint32_t)capacity, n_tiles, ranges,
-                                            tile_order, (hipStream_t)stream),
+                                            tile_order, nullptr, (hipStream_t)stream),
+                     "tile ranges launch");
+}
+
+gs_status gs_tile_ranges_ex(const gs_camera* cam, const uint64_t* keys, int64_t n_entries,
+                            const uint64_t* n_entries_dev, int64_t capacity, uint32_t* ranges,
+                            uint32_t* tile_order, uint32_t* chunks, void* stream) {
+    g_last_error.clear();
+    if (gs_status s = check_camera(cam)) return s;
+    if (capacity < 0 || capacity > (int64_t)UINT32_MAX)
+        return fail(GS_ERR_INVALID, "capacity %lld outside [0, 2^32 - 1]", (long long)capacity);
+    if (!n_entries_dev && (n_entries < 0 || n_entries > capacity))
+        return fail(GS_ERR_INVALID, "n_entries %lld outside [0, capacity %lld]", (long long)n_entries,
+                    (long long)capacity);
+    if (!ranges || (capacity > 0 && !keys) || ((uintptr_t)n_entries_dev & 7) || ((uintptr_t)chunks & 15))
+        return fail(GS_ERR_INVALID, "gs_tile_ranges_ex: NULL or misaligned pointer");
+    const int n_tiles = gs::tiles_x(*cam) * gs::tiles_y(*cam);
+    return hip_check(gs::launch_tile_ranges(keys, n_entries_dev ? 0u : (uint32_t)n_entries, n_entries_dev,
+                                            (uint32_t)capacity, n_tiles, ranges, tile_order, chunks,
+                                            (hipStream_t)stream),
                      "tile ranges launch");
 }
 
@@ -332,7 +351,32 @@ gs_status gs_composite_fwd(const gs_camera* cam, const uint32_t* ranges, const u
     const float3 b = make_float3(bg[0], bg[1], bg[2]);
     return hip_check(gs::launch_composite_fwd(*cam, ranges, point_list, (const float4*)xy_depth,
                                               (const float4*)conic_op, (const float4*)rgb, b, image,
-                                              final_T, n_contrib, n_examined, tile_order, (hipStream_t)stream),
+                                              final_T, n_contrib, n_examined, tile_order, nullptr, 0u,
+                                              (hipStream_t)stream),
+                     "composite fwd launch");
+}
+
+gs_status gs_composite_fwd_ex(const gs_camera* cam, const uint32_t* ranges, const uint32_t* point_list,
+                              const float* xy_depth, const float* conic_op, const float* rgb,
+                              const float bg[3], float* image, float* final_T, uint32_t* n_contrib,
+                              uint32_t* n_examined, const uint32_t* tile_order, int64_t capacity,
+                              float* ckpt, void* stream) {
+    g_last_error.clear();
+    if (!ckpt)
+        return gs_composite_fwd(cam, ranges, point_list, xy_depth, conic_op, rgb, bg, image, final_T, n_contrib,
+                                n_examined, tile_order, stream);
+    if (gs_status s = check_camera(cam)) return s;
+    if (capacity < 0 || capacity > (int64_t)UINT32_MAX)
+        return fail(GS_ERR_INVALID, "gs_composite_fwd_ex: capacity %lld outside [0, 2^32 - 1]", (long long)capacity);
+    if (!ranges || !bg || !image || !final_T || !n_contrib)
+        return fail(GS_ERR_INVALID, "gs_composite_fwd_ex: a required pointer is NULL");
+    if (((uintptr_t)xy_depth | (uintptr_t)conic_op | (uintptr_t)rgb | (uintptr_t)ckpt) & 15)
+        return fail(GS_ERR_INVALID, "gs_composite_fwd_ex: float4 buffers must be 16-byte aligned");
+    const float3 b = make_float3(bg[0], bg[1], bg[2]);
+    return hip_check(gs::launch_composite_fwd(*cam, ranges, point_list, (const float4*)xy_depth,
+                                              (const float4*)conic_op, (const float4*)rgb, b, image,
+                                              final_T, n_contrib, n_examined, tile_order, (float4*)ckpt,
+                                              (uint32_t)capacity, (hipStream_t)stream),
                      "composite fwd launch");
 }
 
@@ -357,7 +401,35 @@ gs_status gs_composite_bwd(const gs_camera* cam, int32_t n, const uint32_t* rang
                                               (const float4*)conic_op, (const float4*)rgb, b, final_T,
                                               n_contrib, dL_dimage, (float2*)grad_mean2d,
                                               (float4*)grad_conic_op, (float4*)grad_rgb, tile_order,
-                                              (hipStream_t)stream),
+                                              nullptr, 0u, nullptr, nullptr, (hipStream_t)stream),
+                     "composite bwd launch");
+}
+
+gs_status gs_composite_bwd_ex(const gs_camera* cam, int32_t n, const uint32_t* ranges,
+                              const uint32_t* point_list, const uint32_t* chunks, int64_t capacity,
+                              const float* xy_depth, const float* conic_op, const float* rgb,
+                              const float bg[3], const float* image, const float* final_T,
+                              const uint32_t* n_contrib, const float* ckpt, const float* dL_dimage,
+                              float* grad_mean2d, float* grad_conic_op, float* grad_rgb, void* stream) {
+    g_last_error.clear();
+    if (gs_status s = check_camera(cam)) return s;
+    if (n < 0 || n > GS_MAX_GAUSSIANS) return fail(GS_ERR_INVALID, "n = %d outside [0, %d]", n, GS_MAX_GAUSSIANS);
+    if (capacity < 0 || capacity > (int64_t)UINT32_MAX)
+        return fail(GS_ERR_INVALID, "gs_composite_bwd_ex: capacity %lld outside [0, 2^32 - 1]", (long long)capacity);
+    if (!ranges || !bg || !final_T || !n_contrib || !dL_dimage || !image || !chunks)
+        return fail(GS_ERR_INVALID, "gs_composite_bwd_ex: a required pointer is NULL");
+    if (capacity > 0 && !ckpt) return fail(GS_ERR_INVALID, "gs_composite_bwd_ex: ckpt is NULL");
+    if (n > 0 && (!grad_mean2d || !grad_conic_op || !grad_rgb))
+        return fail(GS_ERR_INVALID, "gs_composite_bwd_ex: a gradient pointer is NULL");
+    if (((uintptr_t)xy_depth | (uintptr_t)conic_op | (uintptr_t)rgb | (uintptr_t)grad_conic_op |
+         (uintptr_t)grad_rgb | (uintptr_t)ckpt | (uintptr_t)chunks) & 15 || ((uintptr_t)grad_mean2d & 7))
+        return fail(GS_ERR_INVALID, "gs_composite_bwd_ex: misaligned vector buffer");
+    const float3 b = make_float3(bg[0], bg[1], bg[2]);
+    return hip_check(gs::launch_composite_bwd(*cam, n, ranges, point_list, (const float4*)xy_depth,
+                                              (const float4*)conic_op, (const float4*)rgb, b, final_T,
+                                              n_contrib, dL_dimage, (float2*)grad_mean2d,
+                                              (float4*)grad_conic_op, (float4*)grad_rgb, nullptr, chunks,
+                                              (uint32_t)capacity, (const float4*)ckpt, image, (hipStream_t)stream),
                      "composite bwd launch");
 }
 

@@ -573,39 +573,93 @@ __device__ __forceinline__ uint32_t heavy_first_key(uint32_t len) {
 }
 
 // order = the tiles in descending order of list length (by class; the
-// order within a class is unspecified). One workgroup of 1024 threads:
-// class histogram, exclusive scan, scatter through per-class cursors.
+// order within a class is unspecified). chunks = the work items of the
+// chunked backward after a count (padded to 16 bytes), each (tile, chunk
+// index, list start, list length). When the lists average more than one
+// chunk (E > kChunk tiles) they are cut into kChunk-entry chunks, in
+// descending order of the list length from the chunk's start to the list's
+// end: the front chunks of the longest lists first, since a pixel that
+// stops early leaves the later chunks of its list little to do. Otherwise
+// the tiles alone give the launch enough workgroups, and every non-empty
+// list is one item (chunk index kWholeList), in the order of `order`. One
+// workgroup of 1024 threads: class histograms, exclusive scans, scatter
+// through per-class cursors. order and chunks may be NULL.
 __global__ __launch_bounds__(1024) void k_tile_order(const uint32_t* __restrict__ ranges, int n_tiles,
-                                                     uint32_t* __restrict__ order) {
-    __shared__ uint32_t s_hist[kRadix];
-    __shared__ uint32_t s_wsum[kRadix / 64];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    if (tid < kRadix) s_hist[tid] = 0u;
+                                                     const uint64_t* __restrict__ total, uint32_t n_entries,
+                                                     uint32_t capacity, uint32_t* __restrict__ order,
+                                                     uint32_t* __restrict__ chunks) {
+    constexpr int kSweep = 8;  // tiles per thread per sweep, their ranges loaded together
+    __shared__ uint32_t s_hist[2][kRadix];  // tiles, chunks per class; then the class cursors
+    __shared__ uint32_t s_wsum[2][kRadix / 64];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const uint2* const r2 = reinterpret_cast<const uint2*>(ranges);
+    const uint32_t E = total ? usable_entries(total, capacity) : n_entries;
+    const bool split = chunks && (uint64_t)E > (uint64_t)kChunk * (uint64_t)n_tiles;
+    const bool by_tile = order || (chunks && !split);  // the tile classes are needed
+    if (tid < 2 * kRadix) (&s_hist[0][0])[tid] = 0u;
     __syncthreads();
-    for (int t = tid; t < n_tiles; t += 1024)
-        atomicAdd(&s_hist[heavy_first_key(ranges[2 * t + 1] - ranges[2 * t])], 1u);
+    for (int base = 0; base < n_tiles; base += 1024 * kSweep) {
+        uint2 r[kSweep];
+#pragma unroll
+        for (int k = 0; k < kSweep; ++k) {
+            const int t = base + k * 1024 + tid;
+            r[k] = t < n_tiles ? r2[t] : make_uint2(0u, 0u);
+        }
+#pragma unroll
+        for (int k = 0; k < kSweep; ++k) {
+            const int t = base + k * 1024 + tid;
+            const uint32_t len = r[k].y - r[k].x;
+            if (by_tile && t < n_tiles) atomicAdd(&s_hist[0][heavy_first_key(len)], 1u);
+            if (split)
+                for (uint32_t at = 0; at < len; at += kChunk) atomicAdd(&s_hist[1][heavy_first_key(len - at)], 1u);
+        }
+    }
     __syncthreads();
+    // waves 0..3 scan the tile classes, waves 4..7 the chunk classes
+    const int which = tid >> 8, cls = tid & (kRadix - 1), w4 = (tid >> 6) & 3;
     uint32_t h = 0, incl = 0;
-    if (tid < kRadix) {  // waves 0..3: exclusive scan of the 256 class counts
-        h = s_hist[tid];
+    if (tid < 2 * kRadix) {
+        h = s_hist[which][cls];
         incl = h;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
             const uint32_t y = (uint32_t)__shfl_up((int)incl, off, 64);
             if (lane >= off) incl += y;
         }
-        if (lane == 63) s_wsum[wave] = incl;
+        if (lane == 63) s_wsum[which][w4] = incl;
     }
     __syncthreads();
-    if (tid < kRadix) {
+    if (tid < 2 * kRadix) {
         uint32_t pre = 0;
-        for (int w = 0; w < wave; ++w) pre += s_wsum[w];
-        s_hist[tid] = pre + incl - h;  // now the class cursors
+        for (int w = 0; w < w4; ++w) pre += s_wsum[which][w];
+        s_hist[which][cls] = pre + incl - h;  // now the class cursors
+        // the item count: every chunk, or the non-empty tiles (those before
+        // the empty class, the last one)
+        if (chunks && tid == (split ? 2 * kRadix - 1 : kRadix - 1)) chunks[0] = split ? pre + incl : pre + incl - h;
     }
     __syncthreads();
-    for (int t = tid; t < n_tiles; t += 1024) {
-        const uint32_t c = heavy_first_key(ranges[2 * t + 1] - ranges[2 * t]);
-        order[atomicAdd(&s_hist[c], 1u)] = (uint32_t)t;
+    uint4* const items = chunks ? reinterpret_cast<uint4*>(chunks + 4) : nullptr;
+    for (int base = 0; base < n_tiles; base += 1024 * kSweep) {
+        uint2 r[kSweep];
+#pragma unroll
+        for (int k = 0; k < kSweep; ++k) {
+            const int t = base + k * 1024 + tid;
+            r[k] = t < n_tiles ? r2[t] : make_uint2(0u, 0u);
+        }
+#pragma unroll
+        for (int k = 0; k < kSweep; ++k) {
+            const int t = base + k * 1024 + tid;
+            const uint32_t start = r[k].x, len = r[k].y - r[k].x;
+            if (by_tile && t < n_tiles) {
+                const uint32_t pos = atomicAdd(&s_hist[0][heavy_first_key(len)], 1u);
+                if (order) order[pos] = (uint32_t)t;
+                if (chunks && !split && len != 0u) items[pos] = make_uint4((uint32_t)t, kWholeList, start, len);
+            }
+            if (split)
+                for (uint32_t at = 0, b = 0; at < len; at += kChunk, ++b)
+                    items[atomicAdd(&s_hist[1][heavy_first_key(len - at)], 1u)] =
+                        make_uint4((uint32_t)t, b, start, len);
+        }
     }
 }
 
@@ -742,7 +796,8 @@ hipError_t launch_fill_u32(uint32_t* p, size_t words, uint32_t v, hipStream_t st
 }
 
 hipError_t launch_tile_ranges(const uint64_t* keys, uint32_t n_entries, const uint64_t* n_dev, uint32_t capacity,
-                              int n_tiles, uint32_t* ranges, uint32_t* tile_order, hipStream_t stream) {
+                              int n_tiles, uint32_t* ranges, uint32_t* tile_order, uint32_t* chunks,
+                              hipStream_t stream) {
     // clear every tile (empty tiles keep (0, 0)), then mark the run boundaries
     const size_t words = 2 * (size_t)n_tiles;
     hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, stream,
@@ -751,8 +806,9 @@ hipError_t launch_tile_ranges(const uint64_t* keys, uint32_t n_entries, const ui
     if (grid_n > 0)
         hipLaunchKernelGGL(k_ranges, dim3((grid_n + 255) / 256), dim3(256), 0, stream, keys, n_entries, n_dev,
                            capacity, ranges);
-    if (tile_order)
-        hipLaunchKernelGGL(k_tile_order, dim3(1), dim3(1024), 0, stream, (const uint32_t*)ranges, n_tiles, tile_order);
+    if (tile_order || chunks)
+        hipLaunchKernelGGL(k_tile_order, dim3(1), dim3(1024), 0, stream, (const uint32_t*)ranges, n_tiles, n_dev,
+                           n_entries, capacity, tile_order, chunks);
     return hipGetLastError();
 }
 

@@ -61,6 +61,7 @@ namespace gs {
 namespace {
 
 constexpr int kBatch = 256;
+static_assert(kChunk == kBatch, "checkpoints are taken at the forward's batch boundaries");
 constexpr int kIlpF = 3;  // splats per step of the forward walk
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -169,7 +170,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
     const uint32_t* __restrict__ point_list, const float4* __restrict__ xy_depth,
     const float4* __restrict__ conic_op, const float4* __restrict__ rgb, const float3 bg,
     float* __restrict__ image, float* __restrict__ final_T, uint32_t* __restrict__ n_contrib,
-    uint32_t* __restrict__ n_examined, const uint32_t* __restrict__ tile_order) {
+    uint32_t* __restrict__ n_examined, const uint32_t* __restrict__ tile_order, float4* __restrict__ ckpt,
+    const uint32_t ckpt_slots) {
     __shared__ float4 s_conic[kBatch];  // -A/2, B, -C/2, opacity
     __shared__ float4 s_xyc[kBatch];    // u, v, r, g
     __shared__ float4 s_bl[kBatch];     // b, live blocks (as bits), -, -: one address with the two above
@@ -194,6 +196,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
     uint32_t last = 0;
 
     for (uint32_t base = start; base < end; base += kBatch) {
+        // the state in front of this batch, for a backward chunk that ends
+        // here; boundaries inside one list are 256 apart and those of the next
+        // list lie more than 256 beyond, so base / 256 is a slot of its own
+        if (base != start && base / kChunk < ckpt_slots)
+            ckpt[(size_t)(base / kChunk) * kChunk + tid] = make_float4(T, C0, C1, C2);
         if (__syncthreads_count(T < kTStop) == 256) break;
         const uint32_t j = base + tid;
         if (j < end) {
@@ -345,13 +352,23 @@ constexpr int kBwdStage = 128;
 constexpr int kParts = 16;  // 4 waves x 4 rows
 __host__ __device__ constexpr int part_swizzle(int t) { return t < 8 ? ((t & 2) << 1) | ((t & 4) << 1) : 0; }
 
+// Work items. Whole lists (kChunked false): item i is tile tile_order[i].
+// Scheduled (kChunked true): item i is entry i of the schedule `chunks` (a
+// count, then (tile, chunk b, list start, list length)), chunk b covering
+// tile-relative list positions [256 b, 256 b + 256), or the whole list when
+// b is kWholeList. A chunk starts each pixel from the final state when the
+// pixel composited nothing past the chunk's end, else from the forward's
+// checkpoint there: T, and g.R = g.(image - accumulated colour).
+template <bool kChunked>
 __global__ __launch_bounds__(256) void k_composite_bwd(
     const int W, const int H, const int TX, const uint32_t* __restrict__ ranges,
     const uint32_t* __restrict__ point_list, const float4* __restrict__ xy_depth,
     const float4* __restrict__ conic_op, const float4* __restrict__ rgb, const float3 bg,
     const float* __restrict__ final_T, const uint32_t* __restrict__ n_contrib,
     const float* __restrict__ dL_dimage, float* __restrict__ grad_mean2d,
-    float* __restrict__ grad_conic_op, float* __restrict__ grad_rgb, const uint32_t* __restrict__ tile_order) {
+    float* __restrict__ grad_conic_op, float* __restrict__ grad_rgb, const uint32_t* __restrict__ tile_order,
+    const uint32_t* __restrict__ chunks, const uint32_t n_slots, const uint32_t n_tiles,
+    const float4* __restrict__ ckpt, const float* __restrict__ image) {
     __shared__ float4 s_conic[kBwdStage];  // -A/2, B, -C/2, opacity
     __shared__ float4 s_xyc[kBwdStage];    // u, v, r, g
     __shared__ float4 s_aux[kBwdStage];    // b, Gaussian id, -, -: one address with the two above
@@ -360,7 +377,24 @@ __global__ __launch_bounds__(256) void k_composite_bwd(
     __shared__ float s_epoch[4][kBwdBatch];  // batch (as int bits) whose partials of slot k wave w wrote last
     __shared__ uint32_t s_maxnc[4];
 
-    const int tile = tile_order ? (int)tile_order[blockIdx.x] : (int)blockIdx.x;
+    int tile;
+    int lo = 0;  // first tile-relative position of this item
+    bool whole_item = true;
+    uint32_t start, len;
+    if (kChunked) {
+        const uint32_t count = chunks[0];
+        const uint4 item = reinterpret_cast<const uint4*>(chunks + 4)[blockIdx.x];
+        if (blockIdx.x >= count || item.x >= n_tiles) return;
+        tile = (int)item.x;
+        whole_item = item.y == kWholeList;
+        lo = whole_item ? 0 : (int)(item.y * (uint32_t)kChunk);
+        start = item.z;
+        len = item.w;
+    } else {
+        tile = tile_order ? (int)tile_order[blockIdx.x] : (int)blockIdx.x;
+        start = ranges[2 * tile];
+        len = ranges[2 * tile + 1] - start;
+    }
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -379,9 +413,12 @@ __global__ __launch_bounds__(256) void k_composite_bwd(
     const int store_stride = lane == 9 ? 1 : 9 * kParts;
     const bool inside = px < W && py < H;
     const float fx = (float)px, fy = (float)py;
-    const uint32_t start = ranges[2 * tile], len = ranges[2 * tile + 1] - start;
-
-    float T = 1.0f, g0 = 0.0f, g1 = 0.0f, g2 = 0.0f;
+    // g.R: the upstream gradient dotted with the radiance from behind the
+    // splats walked so far (their c alpha T, plus the background's T_final
+    // bg). With it dL/dalpha_j = T_j (g.c_j) - (g.R_j) / (1 - alpha_j): the
+    // colour behind splat j is R_j / T_(j+1), and T_(j+1) = T_j (1 - alpha_j).
+    const int hi_item = whole_item ? (int)len : min(lo + kChunk, (int)len);  // this item walks [lo, hi_item)
+    float T = 1.0f, g0 = 0.0f, g1 = 0.0f, g2 = 0.0f, gR = 0.0f;
     uint32_t nc = 0;
     if (inside) {
         const size_t p = (size_t)py * W + px;
@@ -391,12 +428,16 @@ __global__ __launch_bounds__(256) void k_composite_bwd(
         g0 = dL_dimage[p];
         g1 = dL_dimage[plane + p];
         g2 = dL_dimage[2 * plane + p];
+        gR = T * __builtin_fmaf(g2, bg.z, __builtin_fmaf(g1, bg.y, g0 * bg.x));
+        const uint32_t ck_slot = (start + (uint32_t)hi_item) / kChunk;
+        if (kChunked && (int)nc > hi_item && ck_slot < n_slots) {
+            // composited past the chunk: resume from the forward's state there
+            const float4 ck = ckpt[(size_t)ck_slot * kChunk + tid];
+            T = ck.x;
+            gR = __builtin_fmaf(g2, image[2 * plane + p] - ck.w,
+                                __builtin_fmaf(g1, image[plane + p] - ck.z, g0 * (image[p] - ck.y)));
+        }
     }
-    // g.R: the upstream gradient dotted with the radiance from behind the
-    // splats walked so far (their c alpha T, plus the background's T_final
-    // bg). With it dL/dalpha_j = T_j (g.c_j) - (g.R_j) / (1 - alpha_j): the
-    // colour behind splat j is R_j / T_(j+1), and T_(j+1) = T_j (1 - alpha_j).
-    float gR = T * __builtin_fmaf(g2, bg.z, __builtin_fmaf(g1, bg.y, g0 * bg.x));
     if (tid < 4 * kBwdBatch) (&s_epoch[0][0])[tid] = __int_as_float(-1);
 
     // per-wave and per-tile maximum of n_contrib
@@ -409,8 +450,8 @@ __global__ __launch_bounds__(256) void k_composite_bwd(
     const int wave_maxnc = (int)wmax;
 
     int batch = 0;
-    for (int send = maxnc; send > 0; send -= kBwdStage) {  // rounds, back to front
-        const int sstart = send > kBwdStage ? send - kBwdStage : 0;
+    for (int send = min(maxnc, hi_item); send > lo; send -= kBwdStage) {  // rounds, back to front
+        const int sstart = send - kBwdStage > lo ? send - kBwdStage : lo;
         __syncthreads();  // the previous round is fully consumed
         if (tid < send - sstart) {
             const uint32_t g = point_list[start + sstart + tid];
@@ -548,11 +589,13 @@ hipError_t launch_composite_fwd(const gs_camera& cam, const uint32_t* ranges,
                                 const uint32_t* point_list, const float4* xy_depth,
                                 const float4* conic_op, const float4* rgb, float3 bg,
                                 float* image, float* final_T, uint32_t* n_contrib,
-                                uint32_t* n_examined, const uint32_t* tile_order, hipStream_t stream) {
+                                uint32_t* n_examined, const uint32_t* tile_order, float4* ckpt,
+                                uint32_t capacity, hipStream_t stream) {
     const int TX = tiles_x(cam), TY = tiles_y(cam);
+    const uint32_t slots = ckpt ? (uint32_t)((capacity + (uint32_t)kChunk - 1u) / (uint32_t)kChunk) : 0u;
     hipLaunchKernelGGL(k_composite_fwd, dim3(TX * TY), dim3(256), 0, stream, cam.width, cam.height,
                        TX, ranges, point_list, xy_depth, conic_op, rgb, bg, image, final_T,
-                       n_contrib, n_examined, tile_order);
+                       n_contrib, n_examined, tile_order, ckpt, slots);
     return hipGetLastError();
 }
 
@@ -562,14 +605,26 @@ hipError_t launch_composite_bwd(const gs_camera& cam, int n, const uint32_t* ran
                                 const float* final_T, const uint32_t* n_contrib,
                                 const float* dL_dimage, float2* grad_mean2d,
                                 float4* grad_conic_op, float4* grad_rgb, const uint32_t* tile_order,
-                                hipStream_t stream) {
+                                const uint32_t* chunks, uint32_t capacity, const float4* ckpt,
+                                const float* image, hipStream_t stream) {
     if (n > 0)
         hipLaunchKernelGGL(k_zero_grads, dim3((n + 255) / 256), dim3(256), 0, stream, grad_mean2d,
                            grad_conic_op, grad_rgb, n);
     const int TX = tiles_x(cam), TY = tiles_y(cam);
-    hipLaunchKernelGGL(k_composite_bwd, dim3(TX * TY), dim3(256), 0, stream, cam.width, cam.height,
-                       TX, ranges, point_list, xy_depth, conic_op, rgb, bg, final_T, n_contrib,
-                       dL_dimage, (float*)grad_mean2d, (float*)grad_conic_op, (float*)grad_rgb, tile_order);
+    const uint32_t n_tiles = (uint32_t)(TX * TY);
+    if (chunks) {
+        // at most one chunk per non-empty list beyond its full ones
+        const uint32_t slots = (uint32_t)((capacity + (uint32_t)kChunk - 1u) / (uint32_t)kChunk);
+        hipLaunchKernelGGL(k_composite_bwd<true>, dim3(slots + n_tiles), dim3(256), 0, stream, cam.width,
+                           cam.height, TX, ranges, point_list, xy_depth, conic_op, rgb, bg, final_T, n_contrib,
+                           dL_dimage, (float*)grad_mean2d, (float*)grad_conic_op, (float*)grad_rgb, tile_order,
+                           chunks, slots, n_tiles, ckpt, image);
+    } else {
+        hipLaunchKernelGGL(k_composite_bwd<false>, dim3(n_tiles), dim3(256), 0, stream, cam.width, cam.height,
+                           TX, ranges, point_list, xy_depth, conic_op, rgb, bg, final_T, n_contrib, dL_dimage,
+                           (float*)grad_mean2d, (float*)grad_conic_op, (float*)grad_rgb, tile_order,
+                           (const uint32_t*)nullptr, 0u, n_tiles, (const float4*)nullptr, (const float*)nullptr);
+    }
     return hipGetLastError();
 }
 

@@ -21,6 +21,11 @@ constexpr float kSigma = 3.0f;
 constexpr float kAlphaMin = 1.0f / 255.0f;
 constexpr float kAlphaMax = 0.99f;
 constexpr float kTStop = 1e-4f;
+// Entries per chunk of a tile's list: the forward keeps each pixel's state
+// at these boundaries and the chunked backward walks one chunk per workgroup.
+constexpr int kChunk = 256;
+// Chunk index of a work item that is a whole list.
+constexpr uint32_t kWholeList = 0xffffffffu;
 
 inline int tiles_x(const gs_camera& c) { return (c.width + kTile - 1) / kTile; }
 inline int tiles_y(const gs_camera& c) { return (c.height + kTile - 1) / kTile; }
@@ -159,15 +164,22 @@ hipError_t launch_fill_u32(uint32_t* p, size_t words, uint32_t v, hipStream_t st
 
 // Per-tile ranges. The entry count is n_entries, or, when n_dev is given,
 // *n_dev if it does not exceed capacity and 0 otherwise. If tile_order is
-// given it receives the tiles, heaviest list first.
+// given it receives the tiles, heaviest list first; if chunks is given, the
+// count and (tile, chunk) pairs of every kChunk-entry chunk of every list.
 hipError_t launch_tile_ranges(const uint64_t* keys, uint32_t n_entries, const uint64_t* n_dev, uint32_t capacity,
-                              int n_tiles, uint32_t* ranges, uint32_t* tile_order, hipStream_t stream);
+                              int n_tiles, uint32_t* ranges, uint32_t* tile_order, uint32_t* chunks,
+                              hipStream_t stream);
 
+// Compositing. With ckpt, the forward also stores the per-pixel state at
+// every kChunk-entry boundary of a list and the backward runs one workgroup
+// per chunk of the schedule `chunks` (capacity: length of the sorted entry
+// arrays).
 hipError_t launch_composite_fwd(const gs_camera& cam, const uint32_t* ranges,
                                 const uint32_t* point_list, const float4* xy_depth,
                                 const float4* conic_op, const float4* rgb, float3 bg,
                                 float* image, float* final_T, uint32_t* n_contrib,
-                                uint32_t* n_examined, const uint32_t* tile_order, hipStream_t stream);
+                                uint32_t* n_examined, const uint32_t* tile_order, float4* ckpt,
+                                uint32_t capacity, hipStream_t stream);
 
 hipError_t launch_composite_bwd(const gs_camera& cam, int n, const uint32_t* ranges,
                                 const uint32_t* point_list, const float4* xy_depth,
@@ -175,7 +187,8 @@ hipError_t launch_composite_bwd(const gs_camera& cam, int n, const uint32_t* ran
                                 const float* final_T, const uint32_t* n_contrib,
                                 const float* dL_dimage, float2* grad_mean2d,
                                 float4* grad_conic_op, float4* grad_rgb, const uint32_t* tile_order,
-                                hipStream_t stream);
+                                const uint32_t* chunks, uint32_t capacity, const float4* ckpt,
+                                const float* image, hipStream_t stream);
 
 // Appearance MLP: parameter count, backward scratch (per-workgroup partial
 // weight gradients) and launchers.

@@ -248,37 +248,74 @@ def bin_and_sort_async(cam, xy_depth, tiles_touched, buffers: BinBuffers, stream
     return buffers.keys, buffers.point_list
 
 
-def tile_ranges_async(cam, buffers: BinBuffers, out=None, order=None, stream=None):
+def _check_chunks(chunks, cam, capacity):
+    need = chunk_words(cam, capacity)
+    if chunks.dtype != torch.int32 or chunks.numel() < need:
+        raise ValueError(f"chunks must be int32 with at least {need} elements")
+
+
+def tile_ranges_async(cam, buffers: BinBuffers, out=None, order=None, stream=None, chunks=None):
     """gs_tile_ranges_async over the last asynchronous binning into buffers.
-    `order` (int32 [TX*TY]) receives the heaviest-first tile schedule if given."""
+    `order` (int32 [TX*TY]) receives the heaviest-first tile schedule if given;
+    `chunks` (int32 [chunk_words(cam, buffers.capacity)]) the chunk schedule of
+    the chunked backward (gs_tile_ranges_ex)."""
     c = _cam(cam)
     if out is None:
         TX, TY = tiles_xy(dict(width=c.width, height=c.height))
         out = torch.empty((TX * TY, 2), dtype=torch.int32, device=buffers.keys.device)
+    if chunks is not None:
+        _check_chunks(chunks, cam, buffers.capacity)
+        _lib.check(_lib.load().gs_tile_ranges_ex(ctypes.byref(c), _ptr(buffers.keys), 0,
+                                                 _ptr(buffers.n_entries_dev), buffers.capacity,
+                                                 _ptr(out, torch.int32), _ptr(order, torch.int32, "order"),
+                                                 _ptr(chunks, torch.int32, "chunks"), _stream(stream)))
+        return out
     _lib.check(_lib.load().gs_tile_ranges_async(ctypes.byref(c), _ptr(buffers.keys), _ptr(buffers.n_entries_dev),
                                                 buffers.capacity, _ptr(out, torch.int32),
                                                 _ptr(order, torch.int32, "order"), _stream(stream)))
     return out
 
 
-def tile_ranges(cam, keys, n_entries: int, out=None, order=None, stream=None):
+def tile_ranges(cam, keys, n_entries: int, out=None, order=None, stream=None, chunks=None):
     """gs_tile_ranges. Returns ranges int32 [TX*TY, 2] (uint32 values); `order`
-    (int32 [TX*TY]) receives the heaviest-first tile schedule if given."""
+    (int32 [TX*TY]) receives the heaviest-first tile schedule if given; `chunks`
+    (int32 [chunk_words(cam, len(keys))]) the chunk schedule of the chunked
+    backward (gs_tile_ranges_ex)."""
     TX, TY = tiles_xy(cam if isinstance(cam, dict) else
                       dict(width=cam.width, height=cam.height))
     if out is None:
         out = torch.empty((TX * TY, 2), dtype=torch.int32, device=keys.device)
     c = _cam(cam)
+    if chunks is not None:
+        _check_chunks(chunks, cam, keys.numel())
+        _lib.check(_lib.load().gs_tile_ranges_ex(ctypes.byref(c), _ptr(keys, torch.int64, "keys"), int(n_entries),
+                                                 None, int(keys.numel()), _ptr(out, torch.int32),
+                                                 _ptr(order, torch.int32, "order"),
+                                                 _ptr(chunks, torch.int32, "chunks"), _stream(stream)))
+        return out
     _lib.check(_lib.load().gs_tile_ranges(ctypes.byref(c), _ptr(keys, torch.int64, "keys"),
                                           int(n_entries), _ptr(out, torch.int32),
                                           _ptr(order, torch.int32, "order"), _stream(stream)))
     return out
 
 
+def ckpt_rows(capacity: int) -> int:
+    """Rows of the checkpoint buffer gs_composite_fwd_ex needs for `capacity` entries."""
+    return (int(capacity) + 255) // 256 * 256
+
+
+def chunk_words(cam, capacity: int) -> int:
+    """Length of the chunk schedule gs_tile_ranges_ex writes for `capacity` entries."""
+    TX, TY = tiles_xy(cam if isinstance(cam, dict) else dict(width=cam.width, height=cam.height))
+    return 4 + 4 * (TX * TY + (int(capacity) + 255) // 256)
+
+
 def composite_fwd(cam, ranges, point_list, xy_depth, conic_op, rgb, bg=(0.0, 0.0, 0.0),
-                  with_examined=False, out=None, order=None, stream=None):
-    """gs_composite_fwd. Returns dict image [3,H,W], final_T [H,W], n_contrib [H,W] (int32),
-    and n_examined [H,W] when requested."""
+                  with_examined=False, out=None, order=None, stream=None, ckpt=None, capacity=None):
+    """gs_composite_fwd, or gs_composite_fwd_ex when `ckpt` (float32 [ckpt_rows(capacity), 4]) is
+    given: it then also receives the per-pixel state at every 256-entry boundary, for
+    composite_bwd's chunked walk; capacity defaults to point_list's length. Returns dict
+    image [3,H,W], final_T [H,W], n_contrib [H,W] (int32), and n_examined [H,W] when requested."""
     W, H = (cam["width"], cam["height"]) if isinstance(cam, dict) else (cam.width, cam.height)
     dev = xy_depth.device
     if out is None:
@@ -289,6 +326,17 @@ def composite_fwd(cam, ranges, point_list, xy_depth, conic_op, rgb, bg=(0.0, 0.0
             out["n_examined"] = torch.empty((H, W), dtype=torch.int32, device=dev)
     bgc = (ctypes.c_float * 3)(*[float(x) for x in bg])
     c = _cam(cam)
+    if ckpt is not None:
+        nk = int(point_list.numel() if capacity is None else capacity)
+        if ckpt.dtype != torch.float32 or ckpt.numel() < 4 * ckpt_rows(nk):
+            raise ValueError(f"ckpt must be float32 with at least {ckpt_rows(nk)} rows of 4")
+        _lib.check(_lib.load().gs_composite_fwd_ex(
+            ctypes.byref(c), _ptr(ranges, torch.int32, "ranges"), _ptr(point_list, torch.int32, "point_list"),
+            _ptr(xy_depth, torch.float32), _ptr(conic_op, torch.float32), _ptr(rgb, torch.float32),
+            ctypes.cast(bgc, ctypes.c_void_p), _ptr(out["image"]), _ptr(out["final_T"]),
+            _ptr(out["n_contrib"]), _ptr(out.get("n_examined")), _ptr(order, torch.int32, "order"), nk,
+            _ptr(ckpt, torch.float32, "ckpt"), _stream(stream)))
+        return out
     _lib.check(_lib.load().gs_composite_fwd(
         ctypes.byref(c), _ptr(ranges, torch.int32, "ranges"), _ptr(point_list, torch.int32, "point_list"),
         _ptr(xy_depth, torch.float32), _ptr(conic_op, torch.float32), _ptr(rgb, torch.float32),
@@ -299,8 +347,12 @@ def composite_fwd(cam, ranges, point_list, xy_depth, conic_op, rgb, bg=(0.0, 0.0
 
 
 def composite_bwd(cam, n, ranges, point_list, xy_depth, conic_op, rgb, final_T, n_contrib,
-                  dL_dimage, bg=(0.0, 0.0, 0.0), out=None, order=None, stream=None):
-    """gs_composite_bwd. Returns dict grad_mean2d [n,2], grad_conic_op [n,4], grad_rgb [n,4]."""
+                  dL_dimage, bg=(0.0, 0.0, 0.0), out=None, order=None, stream=None, chunks=None, image=None,
+                  ckpt=None, capacity=None):
+    """gs_composite_bwd, or gs_composite_bwd_ex (one workgroup per 256-entry chunk of a list)
+    when `chunks` is given, with the `image` and `ckpt` of the same frame's
+    composite_fwd(ckpt=..., capacity=...) and that capacity (default: point_list's length).
+    Returns dict grad_mean2d [n,2], grad_conic_op [n,4], grad_rgb [n,4]."""
     dev = xy_depth.device
     if out is None:
         out = dict(grad_mean2d=torch.empty((n, 2), dtype=torch.float32, device=dev),
@@ -308,6 +360,22 @@ def composite_bwd(cam, n, ranges, point_list, xy_depth, conic_op, rgb, final_T, 
                    grad_rgb=torch.empty((n, 4), dtype=torch.float32, device=dev))
     bgc = (ctypes.c_float * 3)(*[float(x) for x in bg])
     c = _cam(cam)
+    if chunks is not None:
+        if ckpt is None or image is None:
+            raise ValueError("the chunked backward needs the forward's image and ckpt")
+        cap = int(point_list.numel() if capacity is None else capacity)
+        _check_chunks(chunks, cam, cap)
+        if ckpt.dtype != torch.float32 or ckpt.numel() < 4 * ckpt_rows(cap):
+            raise ValueError(f"ckpt must be float32 with at least {ckpt_rows(cap)} rows of 4")
+        _lib.check(_lib.load().gs_composite_bwd_ex(
+            ctypes.byref(c), int(n), _ptr(ranges, torch.int32, "ranges"),
+            _ptr(point_list, torch.int32, "point_list"), _ptr(chunks, torch.int32, "chunks"), cap,
+            _ptr(xy_depth, torch.float32), _ptr(conic_op, torch.float32), _ptr(rgb, torch.float32),
+            ctypes.cast(bgc, ctypes.c_void_p), _ptr(image, torch.float32, "image"),
+            _ptr(final_T, torch.float32, "final_T"), _ptr(n_contrib, torch.int32, "n_contrib"),
+            _ptr(ckpt, torch.float32, "ckpt"), _ptr(dL_dimage, torch.float32, "dL_dimage"),
+            _ptr(out["grad_mean2d"]), _ptr(out["grad_conic_op"]), _ptr(out["grad_rgb"]), _stream(stream)))
+        return out
     _lib.check(_lib.load().gs_composite_bwd(
         ctypes.byref(c), int(n), _ptr(ranges, torch.int32, "ranges"),
         _ptr(point_list, torch.int32, "point_list"), _ptr(xy_depth, torch.float32),
@@ -349,7 +417,12 @@ class Rasterizer:
         self.bins = BinBuffers(self.device, capacity)
         self.tile_test = int(tile_test)
 
-    def forward(self, cam: dict, scene: Scene, bg=(0.0, 0.0, 0.0), with_examined=False):
+    def forward(self, cam: dict, scene: Scene, bg=(0.0, 0.0, 0.0), with_examined=False,
+                checkpoints=True):
+        """Render one view. With checkpoints (the default) the forward keeps the
+        per-pixel state at every 256-entry boundary, and backward() then walks
+        each list in 256-entry chunks in parallel; without, backward() walks
+        each list whole."""
         c = camera(cam)
         pre = preprocess(c, scene.means, scene.scales, scene.quats, scene.opacity, scene.sh,
                          scene.sh_degree, scene.rgb, tile_test=self.tile_test)
@@ -357,9 +430,14 @@ class Rasterizer:
                                            conic_op=pre["conic_op"], tile_test=self.tile_test)
         TX, TY = tiles_xy(cam)
         order = torch.empty((TX * TY,), dtype=torch.int32, device=self.device)
-        ranges = tile_ranges(cam, keys, E, order=order)
+        chunks = (torch.empty((chunk_words(cam, E),), dtype=torch.int32, device=self.device)
+                  if checkpoints else None)
+        ranges = tile_ranges(cam, keys, E, order=order, chunks=chunks)
+        ckpt = torch.empty((ckpt_rows(E), 4), dtype=torch.float32, device=self.device) if checkpoints else None
         fwd = composite_fwd(cam, ranges, point_list, pre["xy_depth"], pre["conic_op"], pre["rgb"], bg,
-                            with_examined=with_examined, order=order)
+                            with_examined=with_examined, order=order, ckpt=ckpt, capacity=E)
+        if checkpoints:
+            fwd.update(ckpt=ckpt, chunks=chunks)
         out = dict(pre)
         out.update(keys=keys, point_list=point_list, n_entries=E, ranges=ranges, tile_order=order, **fwd)
         return out
@@ -368,9 +446,11 @@ class Rasterizer:
                  to_parameters=False):
         """Gradients of the splat records (grad_mean2d, grad_conic_op, grad_rgb); with
         to_parameters, also those of the Gaussians' parameters (gs_preprocess_bwd)."""
+        ch = fwd.get("chunks")
         g = composite_bwd(cam, scene.n, fwd["ranges"], fwd["point_list"], fwd["xy_depth"],
                           fwd["conic_op"], fwd["rgb"], fwd["final_T"], fwd["n_contrib"], dL_dimage, bg,
-                          order=fwd.get("tile_order"))
+                          order=fwd.get("tile_order"), chunks=ch, image=fwd["image"] if ch is not None else None,
+                          ckpt=fwd.get("ckpt"), capacity=fwd["n_entries"])
         if to_parameters:
             g.update(preprocess_bwd(cam, scene.means, scene.scales, scene.quats, scene.sh, scene.sh_degree,
                                     fwd["tiles_touched"], g["grad_mean2d"], g["grad_conic_op"], g["grad_rgb"]))
@@ -395,7 +475,7 @@ class ViewBatch:
     """
 
     def __init__(self, cams, scene: "Scene", capacity: int, device="cuda", bg=(0.0, 0.0, 0.0),
-                 tile_order=True, streams: int = 1, tile_test: int = 0):
+                 tile_order=True, streams: int = 1, tile_test: int = 0, chunked: bool = True):
         self.device = torch.device(device)
         self.scene = scene
         self.bg = bg
@@ -423,6 +503,9 @@ class ViewBatch:
                 fwd=dict(image=torch.empty((3, H, W), dtype=f32, device=self.device),
                          final_T=torch.empty((H, W), dtype=f32, device=self.device),
                          n_contrib=torch.empty((H, W), dtype=i32, device=self.device)),
+                # forward state at 256-entry boundaries and the chunk schedule, for the chunked backward
+                ckpt=torch.empty((ckpt_rows(capacity), 4), dtype=f32, device=self.device) if chunked else None,
+                chunks=torch.empty((chunk_words(cam, capacity),), dtype=i32, device=self.device) if chunked else None,
                 dL_dimage=torch.zeros((3, H, W), dtype=f32, device=self.device),
                 grads=dict(grad_mean2d=torch.empty((n, 2), dtype=f32, device=self.device),
                            grad_conic_op=torch.empty((n, 4), dtype=f32, device=self.device),
@@ -457,14 +540,15 @@ class ViewBatch:
                    tile_test=self.tile_test)
         keys, pl = bin_and_sort_async(c, pre["xy_depth"], pre["tiles_touched"], bins, conic_op=pre["conic_op"],
                                       tile_test=self.tile_test)
-        tile_ranges_async(c, bins, out=v["ranges"], order=v["order"])
+        tile_ranges_async(c, bins, out=v["ranges"], order=v["order"], chunks=v["chunks"])
         composite_fwd(c, v["ranges"], pl, pre["xy_depth"], pre["conic_op"], pre["rgb"], self.bg,
-                      out=v["fwd"], order=v["order"])
+                      out=v["fwd"], order=v["order"], ckpt=v["ckpt"], capacity=bins.capacity)
         if loss_grad is not None:
             loss_grad(i, v["fwd"]["image"], v["dL_dimage"])
         composite_bwd(c, sc.n, v["ranges"], pl, pre["xy_depth"], pre["conic_op"], pre["rgb"],
                       v["fwd"]["final_T"], v["fwd"]["n_contrib"], v["dL_dimage"], self.bg,
-                      out=v["grads"], order=v["order"])
+                      out=v["grads"], order=v["order"], chunks=v["chunks"], image=v["fwd"]["image"],
+                      ckpt=v["ckpt"], capacity=bins.capacity)
 
     def capture(self, loss_grad=None, warmup: int = 1):
         """Record enqueue(loss_grad) as one HIP graph (after `warmup` eager runs

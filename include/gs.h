@@ -297,6 +297,31 @@ gs_status gs_tile_ranges_async(const gs_camera* cam, const uint64_t* keys, const
                                int64_t capacity, uint32_t* ranges, uint32_t* tile_order, void* stream);
 
 /* ---------------------------------------------------------------------
+ * gs_tile_ranges_ex - gs_tile_ranges (n_entries_dev NULL: E = n_entries)
+ * or gs_tile_ranges_async (E = *n_entries_dev, every tile empty when it
+ * exceeds capacity), optionally with the chunk schedule of the chunked
+ * backward (gs_composite_bwd_ex).
+ *
+ *   keys, ranges, tile_order  as gs_tile_ranges / gs_tile_ranges_async
+ *   capacity    length of keys; n_entries <= capacity when n_entries_dev is
+ *               NULL
+ *   chunks      out uint32 [4 + 4 (TX*TY + ceil(capacity / 256))], 16-byte
+ *               aligned, or NULL: the work items of gs_composite_bwd_ex.
+ *               chunks[0] = the item count; words 1-3 unused; from word 4,
+ *               for each item, (tile, k, list start, L). When the lists
+ *               average more than 256 entries (E > 256 TX TY), every list is
+ *               cut into ceil(L / 256) chunks, chunk k covering list
+ *               positions [256 k, min(256 k + 256, L)), in descending order
+ *               of L - 256 k, the list length from the chunk on (classes as
+ *               tile_order's). Otherwise the tiles alone give the backward
+ *               enough workgroups: every non-empty list is one item with
+ *               k = 0xffffffff (the whole list), in tile_order's order.
+ * ------------------------------------------------------------------- */
+gs_status gs_tile_ranges_ex(const gs_camera* cam, const uint64_t* keys, int64_t n_entries,
+                            const uint64_t* n_entries_dev, int64_t capacity, uint32_t* ranges,
+                            uint32_t* tile_order, uint32_t* chunks, void* stream);
+
+/* ---------------------------------------------------------------------
  * gs_composite_fwd - front-to-back alpha compositing per tile.
  * ("rigel" README "Rasterization"; zenn 4.5; learn-gs "The kernel".)
  *
@@ -357,6 +382,60 @@ gs_status gs_composite_bwd(const gs_camera* cam, int32_t n, const uint32_t* rang
                            const float* final_T, const uint32_t* n_contrib,
                            const float* dL_dimage, float* grad_mean2d, float* grad_conic_op,
                            float* grad_rgb, const uint32_t* tile_order, void* stream);
+
+/* ---------------------------------------------------------------------
+ * gs_composite_fwd_ex - gs_composite_fwd that also keeps, for the chunked
+ * backward (gs_composite_bwd_ex), each pixel's state at every 256-entry
+ * boundary of its tile's list. The compositing and every other output are
+ * those of gs_composite_fwd ("rigel" README "Rasterization").
+ *
+ *   capacity  length of the sorted entry arrays (keys, point_list): the
+ *             entry count E, or the capacity the asynchronous binning used;
+ *             every tile range must lie in [0, capacity)
+ *   ckpt      out float32 [ceil(capacity / 256) * 256][4], or NULL (then this
+ *             is gs_composite_fwd). For tile t and a boundary b = start_t +
+ *             256 k (k >= 1, b < end_t) that the compositing reached, row
+ *             (b / 256) * 256 + q holds (T, C_r, C_g, C_b) of the tile's pixel
+ *             q in front of entry b, C the colour accumulated so far;
+ *             q = 64 w + 8 r + c is pixel (8 (w & 1) + c, 8 (w >> 1) + r) of
+ *             the tile. Distinct boundaries never share a row (those of one
+ *             list are 256 apart, the next list's lie more than 256 further
+ *             on). Other rows are left as they were.
+ * Other arguments as gs_composite_fwd.
+ * ------------------------------------------------------------------- */
+gs_status gs_composite_fwd_ex(const gs_camera* cam, const uint32_t* ranges, const uint32_t* point_list,
+                              const float* xy_depth, const float* conic_op, const float* rgb,
+                              const float bg[3], float* image, float* final_T, uint32_t* n_contrib,
+                              uint32_t* n_examined, const uint32_t* tile_order, int64_t capacity,
+                              float* ckpt, void* stream);
+
+/* ---------------------------------------------------------------------
+ * gs_composite_bwd_ex - gs_composite_bwd over the work items of the
+ * schedule from gs_tile_ranges_ex: 256-entry chunks of the lists, one
+ * workgroup per chunk, so that a long list is walked by several workgroups
+ * at once (or whole lists, when the schedule says so). Same gradients as
+ * gs_composite_bwd
+ * ("rigel" README "Backward"), up to float32 rounding: for a chunk that a
+ * pixel composited past, the pixel starts from the forward's state at the
+ * chunk's end (T from ckpt, and the radiance from behind as image minus the
+ * colour accumulated in front: an exact identity that in float32 loses a
+ * few bits where little light is left, T near 1e-4); other pixels start
+ * from final_T as in gs_composite_bwd.
+ *
+ *   chunks    the schedule gs_tile_ranges_ex wrote for this frame's ranges
+ *   capacity  as gs_composite_fwd_ex (the same value)
+ *   image     [3][H][W] the image gs_composite_fwd_ex wrote
+ *   ckpt      the checkpoints gs_composite_fwd_ex wrote in the same frame
+ *             (may be NULL only when capacity is 0)
+ * Other arguments as gs_composite_bwd; every input must come from the same
+ * frame (ranges, chunks, the forward's outputs).
+ * ------------------------------------------------------------------- */
+gs_status gs_composite_bwd_ex(const gs_camera* cam, int32_t n, const uint32_t* ranges,
+                              const uint32_t* point_list, const uint32_t* chunks, int64_t capacity,
+                              const float* xy_depth, const float* conic_op, const float* rgb,
+                              const float bg[3], const float* image, const float* final_T,
+                              const uint32_t* n_contrib, const float* ckpt, const float* dL_dimage,
+                              float* grad_mean2d, float* grad_conic_op, float* grad_rgb, void* stream);
 
 /* ---------------------------------------------------------------------
  * gs_appearance_fwd - colour of every Gaussian from a latent code and the

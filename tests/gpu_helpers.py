@@ -29,7 +29,7 @@ def gpu_forward(cam, scene_np, bg=(0.0, 0.0, 0.0), capacity=1 << 16, rast=None):
     r = rast or gs.Rasterizer(capacity=capacity)
     out = r.forward(cam, sc, bg=bg, with_examined=True)
     torch.cuda.synchronize()
-    res = {k: to_np(v) for k, v in out.items() if hasattr(v, "detach")}
+    res = {k: to_np(v) for k, v in out.items() if hasattr(v, "detach") and k not in ("ckpt", "chunks")}
     res["n_entries"] = out["n_entries"]
     res["keys"] = res["keys"].view(np.uint64)
     for k in ("point_list", "ranges", "tiles_touched", "n_contrib", "n_examined"):
@@ -37,16 +37,22 @@ def gpu_forward(cam, scene_np, bg=(0.0, 0.0, 0.0), capacity=1 << 16, rast=None):
     return res, out, sc, r
 
 
-def gpu_backward(cam, sc, out, dLdI, bg=(0.0, 0.0, 0.0), final_T=None, n_contrib=None):
+def gpu_backward(cam, sc, out, dLdI, bg=(0.0, 0.0, 0.0), final_T=None, n_contrib=None, chunked=False):
+    """gs_composite_bwd on the forward's state (or the given final_T and
+    n_contrib); with chunked, gs_composite_bwd_ex on the forward's checkpoints."""
     import gaussian_splatting_tile_amd as gs
     import torch
     dev = out["xy_depth"].device
+    if chunked:
+        assert final_T is None and n_contrib is None, "chunks start from the forward's own state"
     fT = out["final_T"] if final_T is None else torch.from_numpy(np.ascontiguousarray(final_T)).to(dev)
     nc = out["n_contrib"] if n_contrib is None else torch.from_numpy(
         np.ascontiguousarray(n_contrib).view(np.int32)).to(dev)
     g = torch.from_numpy(np.ascontiguousarray(dLdI, np.float32)).to(dev)
     grads = gs.composite_bwd(cam, sc.n, out["ranges"], out["point_list"], out["xy_depth"], out["conic_op"],
-                             out["rgb"], fT, nc, g, bg)
+                             out["rgb"], fT, nc, g, bg, chunks=out["chunks"] if chunked else None,
+                             image=out["image"] if chunked else None, ckpt=out["ckpt"] if chunked else None,
+                             capacity=out["n_entries"])
     torch.cuda.synchronize()
     return {k: to_np(v).astype(np.float64) for k, v in grads.items()}
 

@@ -211,3 +211,39 @@ def test_async_entry_points_validate(gs):
     assert gs.gs_tile_ranges_async(ctypes.byref(c), P(256), None, 10, P(256), None, None) == _lib.GS_ERR_INVALID
     assert gs.gs_tile_ranges_async(ctypes.byref(c), P(256), P(260), 10, P(256), None, None) == _lib.GS_ERR_INVALID
     assert gs.gs_tile_ranges_async(ctypes.byref(c), P(256), P(256), -1, P(256), None, None) == _lib.GS_ERR_INVALID
+
+
+def test_chunked_composite_validates_before_launch(gs):
+    from gaussian_splatting_tile_amd import _lib
+    P = ctypes.c_void_p
+    d = P(256)  # never dereferenced: validation fails first
+    c = _cam()
+    bg = (ctypes.c_float * 3)()
+    fwd = lambda cap=100, ckpt=d, rgb=d: gs.gs_composite_fwd_ex(
+        ctypes.byref(c), d, d, d, d, rgb, bg, d, d, d, None, None, cap, ckpt, None)
+    assert fwd(cap=-1) == _lib.GS_ERR_INVALID
+    assert b"capacity" in gs.gs_last_error()
+    assert fwd(cap=1 << 32) == _lib.GS_ERR_INVALID
+    assert fwd(ckpt=P(264)) == _lib.GS_ERR_INVALID  # checkpoints are float4 rows
+    assert b"aligned" in gs.gs_last_error()
+    bwd = lambda n=4, chunks=d, cap=100, image=d, ckpt=d, gm=d: gs.gs_composite_bwd_ex(
+        ctypes.byref(c), n, d, d, chunks, cap, d, d, d, bg, image, d, d, ckpt, d, gm, d, d, None)
+    assert bwd(ckpt=None) == _lib.GS_ERR_INVALID  # the chunked walk needs the checkpoints
+    assert b"ckpt" in gs.gs_last_error()
+    assert bwd(image=None) == _lib.GS_ERR_INVALID
+    assert bwd(chunks=None) == _lib.GS_ERR_INVALID
+    assert bwd(cap=-5) == _lib.GS_ERR_INVALID
+    assert bwd(n=-1) == _lib.GS_ERR_INVALID
+    assert bwd(gm=None) == _lib.GS_ERR_INVALID
+    assert bwd(chunks=P(264)) == _lib.GS_ERR_INVALID
+    assert bwd(ckpt=P(264)) == _lib.GS_ERR_INVALID
+    rng = lambda n_e=10, n_dev=None, cap=100, keys=d, ranges=d, chunks=d: gs.gs_tile_ranges_ex(
+        ctypes.byref(c), keys, n_e, n_dev, cap, ranges, None, chunks, None)
+    assert rng(n_e=101) == _lib.GS_ERR_INVALID  # more entries than the keys hold
+    assert b"n_entries" in gs.gs_last_error()
+    assert rng(n_e=-1) == _lib.GS_ERR_INVALID
+    assert rng(cap=-1) == _lib.GS_ERR_INVALID
+    assert rng(ranges=None) == _lib.GS_ERR_INVALID
+    assert rng(keys=None) == _lib.GS_ERR_INVALID
+    assert rng(chunks=P(264)) == _lib.GS_ERR_INVALID
+    assert rng(n_dev=P(516)) == _lib.GS_ERR_INVALID

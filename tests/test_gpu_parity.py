@@ -65,6 +65,9 @@ def test_workload_backward_parity(orc, name):
     grads = gpu_backward(cam, sc, out, dLdI)
     rep = compare_gradients(grads, obwd)
     say(f"[{name}] end-to-end grads {rep}")
+    # lists walked in 256-entry chunks from the forward's checkpoints
+    rep_c = compare_gradients(gpu_backward(cam, sc, out, dLdI, chunked=True), obwd)
+    say(f"[{name}] chunked grads {rep_c}")
     # stage-isolated: the oracle's forward state fed to the GPU backward
     iso = gpu_backward(cam, sc, out, dLdI, final_T=ofwd["final_T"], n_contrib=ofwd["n_contrib"])
     rep2 = compare_gradients(iso, obwd)
@@ -89,6 +92,7 @@ def test_multiview_training_shape(orc):
         assert_binning_equal(g, ofwd)
         compare_forward(g, ofwd)
         compare_gradients(gpu_backward(cam, sc, out, dLdI), obwd)
+        compare_gradients(gpu_backward(cam, sc, out, dLdI, chunked=True), obwd)
 
 
 def _random_case(orc, W, H, n, seed, sh_degree=None, bg=(0.0, 0.0, 0.0), **kw):
@@ -111,6 +115,7 @@ def test_ragged_and_sh_degrees(orc, W, H, n, deg):
     dLdI = synth.upstream_gradient(n, W, H)
     obwd = oracle_backward(orc, cam, scene, ofwd, dLdI, bg)
     compare_gradients(gpu_backward(cam, sc, out, dLdI, bg), obwd)
+    compare_gradients(gpu_backward(cam, sc, out, dLdI, bg, chunked=True), obwd)
 
 
 def test_empty_and_fully_culled(orc):
@@ -127,9 +132,10 @@ def test_empty_and_fully_culled(orc):
     assert (g["ranges"] == 0).all()
     np.testing.assert_array_equal(g["image"], ofwd["image"])
     assert (g["final_T"] == 1).all() and not g["n_contrib"].any()
-    grads = gpu_backward(cam, sc, out, synth.upstream_gradient(0, 40, 24))
-    for v in grads.values():
-        assert not v.any()
+    for chunked in (False, True):
+        grads = gpu_backward(cam, sc, out, synth.upstream_gradient(0, 40, 24), chunked=chunked)
+        for v in grads.values():
+            assert not v.any()
     # n = 0 through every stage
     empty = dict(n=0, means=np.zeros((3, 0), np.float32), scales=np.zeros((3, 0), np.float32),
                  quats=np.zeros((4, 0), np.float32), opacity=np.zeros(0, np.float32),
@@ -181,6 +187,74 @@ def test_equal_depth_ties_keep_index_order(orc):
     g, out, sc, _ = gpu_forward(cam, scene)
     assert_binning_equal(g, ofwd)
     compare_forward(g, ofwd)
+
+
+def _sheet_camera(W, H):
+    return dict(R=np.eye(3, dtype=np.float32).reshape(9), t=np.zeros(3, np.float32),
+                campos=np.zeros(3, np.float32), fx=np.float32(50), fy=np.float32(50),
+                cx=np.float32(W / 2), cy=np.float32(H / 2), width=W, height=H)
+
+
+def _tile_confined_scene(cam, counts, opacity, seed):
+    """counts[t] splats of projected sigma <= 0.8 px (radius 3) centred in tile
+    t's interior of the top tile row, so each touches that tile alone and its
+    list holds exactly counts[t] entries; depths in [1, 1.5]."""
+    rng = np.random.default_rng(seed)
+    fx, cx, cy = float(cam["fx"]), float(cam["cx"]), float(cam["cy"])
+    cols = []
+    for t, k in enumerate(counts):
+        z = rng.uniform(1.0, 1.5, k)
+        u = 16 * t + rng.uniform(4.0, 12.0, k)
+        v = rng.uniform(4.0, 12.0, k)
+        cols.append(np.stack([(u - cx) * z / fx, (v - cy) * z / fx, z]))
+    means = np.concatenate(cols, axis=1).astype(np.float32)
+    n = means.shape[1]
+    return dict(n=n, means=means, scales=np.full((3, n), 0.016, np.float32),
+                quats=np.tile(np.float32([[1], [0], [0], [0]]), (1, n)),
+                opacity=rng.uniform(*opacity, n).astype(np.float32),
+                rgb=rng.uniform(0, 1, (3, n)).astype(np.float32), sh=None, sh_degree=0)
+
+
+def test_chunked_backward_at_list_boundaries(orc):
+    """The chunked backward on lists of 512 (a multiple of the chunk), 257 and
+    255 entries, the last tile ragged (40 px wide), and on a one-tile image
+    whose 600-entry list every pixel leaves within a few splats (the forward
+    stops before its first checkpoint, so the later chunks find nothing to
+    walk). Chunked and whole-list gradients both meet the bar against the
+    oracle."""
+    bg = (0.3, 0.6, 0.1)
+    cam = _sheet_camera(40, 16)
+    scene = _tile_confined_scene(cam, (512, 257, 255), (0.05, 0.5), seed=21)
+    ofwd = oracle_forward(orc, cam, scene, bg)
+    lens = (ofwd["ranges"][:, 1] - ofwd["ranges"][:, 0]).tolist()
+    assert lens == [512, 257, 255], lens
+    stopped = ofwd["final_T"] < 1e-4
+    assert stopped.any() and (~stopped).any()
+    assert ofwd["n_contrib"].max() > 256  # some pixel needs a checkpoint
+    dLdI = synth.upstream_gradient(7, 40, 16)
+    obwd = oracle_backward(orc, cam, scene, ofwd, dLdI, bg)
+    g, out, sc, _ = gpu_forward(cam, scene, bg=bg)
+    assert_binning_equal(g, ofwd)
+    compare_forward(g, ofwd)
+    compare_gradients(gpu_backward(cam, sc, out, dLdI, bg), obwd)
+    compare_gradients(gpu_backward(cam, sc, out, dLdI, bg, chunked=True), obwd)
+
+    cam1 = _sheet_camera(16, 16)
+    rng = np.random.default_rng(22)
+    n = 600
+    z = rng.uniform(1.0, 3.0, n)
+    means = np.stack([rng.uniform(-0.05, 0.05, n) * z, rng.uniform(-0.05, 0.05, n) * z, z]).astype(np.float32)
+    opaque = dict(n=n, means=means, scales=np.full((3, n), 0.3, np.float32),
+                  quats=np.tile(np.float32([[1], [0], [0], [0]]), (1, n)),
+                  opacity=rng.uniform(0.8, 0.95, n).astype(np.float32),
+                  rgb=rng.uniform(0, 1, (3, n)).astype(np.float32), sh=None, sh_degree=0)
+    o1 = oracle_forward(orc, cam1, opaque, bg)
+    assert o1["keys"].shape[0] == n and (o1["final_T"] < 1e-4).all() and o1["n_contrib"].max() < 256
+    dL1 = synth.upstream_gradient(8, 16, 16)
+    ob1 = oracle_backward(orc, cam1, opaque, o1, dL1, bg)
+    g1, out1, sc1, _ = gpu_forward(cam1, opaque, bg=bg)
+    compare_forward(g1, o1)
+    compare_gradients(gpu_backward(cam1, sc1, out1, dL1, bg, chunked=True), ob1)
 
 
 def test_repeat_runs_are_bit_identical(orc):
@@ -290,3 +364,66 @@ def test_tile_order_is_a_heaviest_first_schedule(orc):
     torch.cuda.synchronize()
     compare_gradients({k: to_np(v).astype(np.float64) for k, v in ordered.items()}, obwd)
     compare_gradients(grads, obwd)
+
+
+def _chunk_class(L):
+    msb = np.floor(np.log2(np.maximum(L, 1))).astype(np.int64)
+    frac = ((L << (31 - msb)) >> 27) & 15
+    return np.minimum(255, 1 + 16 * msb + frac)
+
+
+def _check_chunk_schedule(chunks, ranges):
+    """chunks: the schedule words; ranges [T, 2]. If the lists average more
+    than 256 entries: every (tile, k) with k < ceil(L / 256) exactly once, in
+    non-increasing class of L - 256 k; else every non-empty tile once as a
+    whole list, in non-increasing class of L. Returns whether it split."""
+    L = ranges[:, 1].astype(np.int64) - ranges[:, 0]
+    count = int(chunks[0])
+    items4 = chunks[4:4 + 4 * count].reshape(count, 4).astype(np.int64)
+    assert np.array_equal(items4[:, 2], ranges[items4[:, 0], 0])
+    assert np.array_equal(items4[:, 3], L[items4[:, 0]])
+    if L.sum() <= 256 * len(L):
+        assert (items4[:, 1] == 0xFFFFFFFF).all()
+        assert np.array_equal(np.sort(items4[:, 0]), np.nonzero(L)[0])
+        assert (np.diff(_chunk_class(L[items4[:, 0]])) <= 0).all()
+        return False
+    nch = (L + 255) // 256
+    assert count == int(nch.sum()), (count, int(nch.sum()))
+    items = items4[:, :2]
+    want = np.concatenate([np.stack([np.full(k, t), np.arange(k)], 1) for t, k in enumerate(nch) if k] or
+                          [np.zeros((0, 2), np.int64)])
+    got_sorted = items[np.lexsort((items[:, 1], items[:, 0]))]
+    assert np.array_equal(got_sorted, want)
+    if count:
+        rest = L[items[:, 0]] - 256 * items[:, 1]
+        assert (rest > 0).all()
+        assert (np.diff(_chunk_class(rest)) <= 0).all()
+    return True
+
+
+def test_chunk_schedule_covers_every_chunk(orc):
+    """The ranges call's schedule for the chunked backward, from a host entry
+    count and from a device count with spare capacity and with an overflow
+    (nothing to schedule): whole lists at cfg2 (lists average under 256
+    entries), chunks at cfg3."""
+    import gaussian_splatting_tile_amd as gs
+    import torch
+    from gpu_helpers import to_np
+    for name, split in (("cfg2", False), ("cfg3", True)):
+        say(f"[{name}] schedule")
+        scene, cam, _, ofwd, _ = workload(orc, name)
+        g, out, sc, r = gpu_forward(cam, scene, capacity=1 << 23)
+        assert _check_chunk_schedule(to_np(out["chunks"]).view(np.uint32), g["ranges"]) == split
+        c = gs.camera(cam)
+        for capacity in (g["n_entries"] + 5000, g["n_entries"] - 1):
+            bins = gs.BinBuffers(torch.device("cuda"), capacity)
+            gs.bin_and_sort_async(c, out["xy_depth"], out["tiles_touched"], bins)
+            chunks = torch.full((gs.chunk_words(cam, capacity),), -1, dtype=torch.int32, device="cuda")
+            ranges = gs.tile_ranges_async(c, bins, chunks=chunks)
+            torch.cuda.synchronize()
+            rg = to_np(ranges).view(np.uint32)
+            if capacity >= g["n_entries"]:
+                assert np.array_equal(rg, g["ranges"])
+                assert _check_chunk_schedule(to_np(chunks).view(np.uint32), rg) == split
+            else:
+                assert not rg.any() and int(to_np(chunks)[0]) == 0
