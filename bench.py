@@ -413,10 +413,10 @@ def main():
         "stage_ms_median": {s: round(v[0], 4) for s, v in stage_ms.items()},
         "timed_kernel_ms_mean": {"composite_fwd": round(fwd_s * 1e3, 4),
                                  "composite_bwd": round(bwd_s * 1e3, 4)},
-        "roofline": {"bound": "alu", "kernel": "k_composite_bwd",
+        "roofline": {"bound": "alu", "kernel": "k_composite_bwd<true>" if chunked else "k_composite_bwd<false>",
                      "achieved": round(achieved / 1e12, 4), "peak": PEAK_FP32_VECTOR / 1e12,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_VECTOR, 5),
-                     "traffic": measured_traffic(args.workload),
+                     "traffic": measured_traffic(args.workload) if chunked else None,
                      "per_unit": f"{FLOPS_PER_BWD_EVAL:.0f} flop per backward pixel-splat eval "
                                  f"x {evals_bwd} evals per launch"},
         "secondary": {

@@ -16,7 +16,8 @@ STATUS_NAMES = {0: "GS_OK", 1: "GS_ERR_INVALID", 2: "GS_ERR_CAPACITY", 3: "GS_ER
 EXPORTS = ("gs_constants", "gs_last_error", "gs_version", "gs_preprocess", "gs_preprocess_ex",
            "gs_preprocess_bwd", "gs_bin_and_sort", "gs_bin_and_sort_ex", "gs_bin_and_sort_async_ex",
            "gs_bin_and_sort_async", "gs_tile_ranges", "gs_tile_ranges_async", "gs_composite_fwd",
-           "gs_composite_bwd", "gs_composite_fwd_ex", "gs_composite_bwd_ex", "gs_tile_ranges_ex", "gs_appearance_fwd",
+           "gs_composite_bwd", "gs_composite_fwd_ex", "gs_composite_part_bytes", "gs_composite_bwd_ex", "gs_tile_ranges_ex",
+           "gs_appearance_fwd",
            "gs_appearance_bwd")
 
 
@@ -80,7 +81,9 @@ def load() -> ctypes.CDLL:
     lib.gs_composite_bwd.restype = ctypes.c_int
     lib.gs_composite_bwd.argtypes = [CAM, I32, P, P, P, P, P, P, P, P, P, P, P, P, P, P]
     lib.gs_composite_fwd_ex.restype = ctypes.c_int
-    lib.gs_composite_fwd_ex.argtypes = [CAM, P, P, P, P, P, P, P, P, P, P, P, I64, P, P]
+    lib.gs_composite_fwd_ex.argtypes = [CAM, P, P, P, P, P, P, P, P, P, P, P, I64, P, P, P, P]
+    lib.gs_composite_part_bytes.restype = ctypes.c_size_t
+    lib.gs_composite_part_bytes.argtypes = [CAM, I64]
     lib.gs_composite_bwd_ex.restype = ctypes.c_int
     lib.gs_composite_bwd_ex.argtypes = [CAM, I32, P, P, P, I64, P, P, P, P, P, P, P, P, P, P, P, P, P]
     lib.gs_tile_ranges_ex.restype = ctypes.c_int

@@ -352,7 +352,7 @@ gs_status gs_composite_fwd(const gs_camera* cam, const uint32_t* ranges, const u
     return hip_check(gs::launch_composite_fwd(*cam, ranges, point_list, (const float4*)xy_depth,
                                               (const float4*)conic_op, (const float4*)rgb, b, image,
                                               final_T, n_contrib, n_examined, tile_order, nullptr, 0u,
-                                              (hipStream_t)stream),
+                                              nullptr, nullptr, (hipStream_t)stream),
                      "composite fwd launch");
 }
 
@@ -360,24 +360,31 @@ gs_status gs_composite_fwd_ex(const gs_camera* cam, const uint32_t* ranges, cons
                               const float* xy_depth, const float* conic_op, const float* rgb,
                               const float bg[3], float* image, float* final_T, uint32_t* n_contrib,
                               uint32_t* n_examined, const uint32_t* tile_order, int64_t capacity,
-                              float* ckpt, void* stream) {
+                              float* ckpt, const uint32_t* chunks, void* part, void* stream) {
     g_last_error.clear();
-    if (!ckpt)
+    if (!ckpt && !chunks)
         return gs_composite_fwd(cam, ranges, point_list, xy_depth, conic_op, rgb, bg, image, final_T, n_contrib,
                                 n_examined, tile_order, stream);
     if (gs_status s = check_camera(cam)) return s;
     if (capacity < 0 || capacity > (int64_t)UINT32_MAX)
         return fail(GS_ERR_INVALID, "gs_composite_fwd_ex: capacity %lld outside [0, 2^32 - 1]", (long long)capacity);
-    if (!ranges || !bg || !image || !final_T || !n_contrib)
+    if (!bg || !image || !final_T || !n_contrib || (!chunks && !ranges))
         return fail(GS_ERR_INVALID, "gs_composite_fwd_ex: a required pointer is NULL");
-    if (((uintptr_t)xy_depth | (uintptr_t)conic_op | (uintptr_t)rgb | (uintptr_t)ckpt) & 15)
+    if (chunks && !part) return fail(GS_ERR_INVALID, "gs_composite_fwd_ex: chunks without the part workspace");
+    if (((uintptr_t)xy_depth | (uintptr_t)conic_op | (uintptr_t)rgb | (uintptr_t)ckpt | (uintptr_t)chunks |
+         (uintptr_t)part) & 15)
         return fail(GS_ERR_INVALID, "gs_composite_fwd_ex: float4 buffers must be 16-byte aligned");
     const float3 b = make_float3(bg[0], bg[1], bg[2]);
     return hip_check(gs::launch_composite_fwd(*cam, ranges, point_list, (const float4*)xy_depth,
                                               (const float4*)conic_op, (const float4*)rgb, b, image,
                                               final_T, n_contrib, n_examined, tile_order, (float4*)ckpt,
-                                              (uint32_t)capacity, (hipStream_t)stream),
+                                              (uint32_t)capacity, chunks, part, (hipStream_t)stream),
                      "composite fwd launch");
+}
+
+size_t gs_composite_part_bytes(const gs_camera* cam, int64_t capacity) {
+    if (!cam || check_camera(cam) != GS_OK || capacity < 0 || capacity > (int64_t)UINT32_MAX) return 0;
+    return gs::composite_part_bytes(*cam, (uint32_t)capacity);
 }
 
 gs_status gs_composite_bwd(const gs_camera* cam, int32_t n, const uint32_t* ranges,

@@ -574,14 +574,15 @@ __device__ __forceinline__ uint32_t heavy_first_key(uint32_t len) {
 
 // order = the tiles in descending order of list length (by class; the
 // order within a class is unspecified). chunks = the work items of the
-// chunked backward after a count (padded to 16 bytes), each (tile, chunk
-// index, list start, list length). When the lists average more than one
-// chunk (E > kChunk tiles) they are cut into kChunk-entry chunks, in
-// descending order of the list length from the chunk's start to the list's
-// end: the front chunks of the longest lists first, since a pixel that
-// stops early leaves the later chunks of its list little to do. Otherwise
-// the tiles alone give the launch enough workgroups, and every non-empty
-// list is one item (chunk index kWholeList), in the order of `order`. One
+// scheduled compositing after a count (padded to 16 bytes), each (tile,
+// chunk index, list start, list length). When the lists average more than
+// one chunk (E > kChunk tiles) every non-empty list is cut into
+// kChunk-entry chunks, in descending order of the list length from the
+// chunk's start to the list's end: the front chunks of the longest lists
+// first, since a pixel that stops early leaves the later chunks of its list
+// little to do; each empty list is one whole item, last. Otherwise the
+// tiles alone give a launch enough workgroups, and every list is one item
+// (chunk index kWholeList), in the order of `order`. One
 // workgroup of 1024 threads: class histograms, exclusive scans, scatter
 // through per-class cursors. order and chunks may be NULL.
 __global__ __launch_bounds__(1024) void k_tile_order(const uint32_t* __restrict__ ranges, int n_tiles,
@@ -610,8 +611,10 @@ __global__ __launch_bounds__(1024) void k_tile_order(const uint32_t* __restrict_
             const int t = base + k * 1024 + tid;
             const uint32_t len = r[k].y - r[k].x;
             if (by_tile && t < n_tiles) atomicAdd(&s_hist[0][heavy_first_key(len)], 1u);
-            if (split)
+            if (split && t < n_tiles) {
+                if (len == 0u) atomicAdd(&s_hist[1][heavy_first_key(0u)], 1u);  // an empty list: one whole item
                 for (uint32_t at = 0; at < len; at += kChunk) atomicAdd(&s_hist[1][heavy_first_key(len - at)], 1u);
+            }
         }
     }
     __syncthreads();
@@ -633,9 +636,8 @@ __global__ __launch_bounds__(1024) void k_tile_order(const uint32_t* __restrict_
         uint32_t pre = 0;
         for (int w = 0; w < w4; ++w) pre += s_wsum[which][w];
         s_hist[which][cls] = pre + incl - h;  // now the class cursors
-        // the item count: every chunk, or the non-empty tiles (those before
-        // the empty class, the last one)
-        if (chunks && tid == (split ? 2 * kRadix - 1 : kRadix - 1)) chunks[0] = split ? pre + incl : pre + incl - h;
+        // the item count: every chunk and empty list, or every tile
+        if (chunks && tid == (split ? 2 * kRadix - 1 : kRadix - 1)) chunks[0] = pre + incl;
     }
     __syncthreads();
     uint4* const items = chunks ? reinterpret_cast<uint4*>(chunks + 4) : nullptr;
@@ -653,12 +655,14 @@ __global__ __launch_bounds__(1024) void k_tile_order(const uint32_t* __restrict_
             if (by_tile && t < n_tiles) {
                 const uint32_t pos = atomicAdd(&s_hist[0][heavy_first_key(len)], 1u);
                 if (order) order[pos] = (uint32_t)t;
-                if (chunks && !split && len != 0u) items[pos] = make_uint4((uint32_t)t, kWholeList, start, len);
+                if (chunks && !split) items[pos] = make_uint4((uint32_t)t, kWholeList, start, len);
             }
-            if (split)
+            if (split && t < n_tiles) {
+                if (len == 0u) items[atomicAdd(&s_hist[1][heavy_first_key(0u)], 1u)] = make_uint4((uint32_t)t, kWholeList, 0u, 0u);
                 for (uint32_t at = 0, b = 0; at < len; at += kChunk, ++b)
                     items[atomicAdd(&s_hist[1][heavy_first_key(len - at)], 1u)] =
                         make_uint4((uint32_t)t, b, start, len);
+            }
         }
     }
 }

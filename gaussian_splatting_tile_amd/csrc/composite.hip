@@ -165,18 +165,152 @@ __device__ __forceinline__ uint32_t quadrant_blocks(int w) {
     return 0x33u << (2 * (w & 1) + 8 * (w >> 1));
 }
 
+// Stages list entries [base, min(base + kBatch, end)) into LDS, one per
+// thread: the conic with -1/2 folded in, the centre and colour, and the
+// 4 x 4 blocks of the tile the splat reaches.
+__device__ __forceinline__ void fwd_stage(uint32_t base, uint32_t end, int tid, int x0, int y0,
+                                          const uint32_t* __restrict__ point_list,
+                                          const float4* __restrict__ xy_depth, const float4* __restrict__ conic_op,
+                                          const float4* __restrict__ rgb, float4* s_conic, float4* s_xyc,
+                                          float4* s_bl) {
+    const uint32_t j = base + (uint32_t)tid;
+    if (j < end) {
+        const uint32_t g = point_list[j];
+        const float4 xy = xy_depth[g];
+        const float4 co = conic_op[g];
+        const float4 c = rgb[g];
+        s_conic[tid] = make_float4(-0.5f * co.x, co.y, -0.5f * co.z, co.w);
+        s_xyc[tid] = make_float4(xy.x, xy.y, c.x, c.y);
+        s_bl[tid] = make_float4(c.z, __uint_as_float(block_mask(co, xy.x, xy.y, x0, y0)), 0.0f, 0.0f);
+    }
+}
+
+// Composites the cnt staged splats (list positions pos0 ..) front to back
+// into this lane's (T, C, last). A lane whose T is below the stop threshold
+// has stopped and changes nothing. All 64 lanes of the wave take part.
+__device__ __forceinline__ void fwd_walk(int cnt, uint32_t pos0, uint32_t qblocks, int lane, float fx, float fy,
+                                         const float4* s_conic, const float4* s_xyc, const float4* s_bl,
+                                         float& T, float& C0, float& C1, float& C2, uint32_t& last) {
+    // this wave's live splats of the batch, as four 64-bit masks
+    uint64_t m[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int k = q * 64 + lane;
+        m[q] = __ballot(k < cnt && (__float_as_uint(s_bl[k].y) & qblocks) != 0u);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        uint64_t mq = m[q];
+        while (mq != 0ull) {
+            if (__ballot(T >= kTStop) == 0ull) { mq = 0ull; break; }
+            // kIlpF splats per step: independent alphas, then the ordered updates
+            int ks[kIlpF];
+            bool valid[kIlpF];
+#pragma unroll
+            for (int i = 0; i < kIlpF; ++i) {
+                valid[i] = mq != 0ull;
+                ks[i] = valid[i] ? q * 64 + (__ffsll((unsigned long long)mq) - 1) : (i ? ks[i - 1] : q * 64);
+                mq &= mq - 1ull;
+            }
+            float4 co[kIlpF], xc[kIlpF];
+            float cb[kIlpF], pw[kIlpF], G[kIlpF], oG[kIlpF], alpha[kIlpF];
+            bool near[kIlpF];
+            bool any_near = false;
+#pragma unroll
+            for (int i = 0; i < kIlpF; ++i) {
+                co[i] = s_conic[ks[i]];
+                xc[i] = s_xyc[ks[i]];
+                cb[i] = s_bl[ks[i]].x;
+            }
+#pragma unroll
+            for (int i = 0; i < kIlpF; ++i) {
+                near[i] = splat_alpha_fast(co[i].x, co[i].y, co[i].z, co[i].w, fx - xc[i].x, fy - xc[i].y, pw[i],
+                                           G[i], oG[i], alpha[i]);
+                any_near = any_near || near[i];
+            }
+            if (__builtin_expect(__ballot(any_near) != 0ull, 0)) {
+#pragma unroll
+                for (int i = 0; i < kIlpF; ++i)
+                    if (near[i]) splat_alpha_exact(pw[i], co[i].w, G[i], oG[i], alpha[i]);
+            }
+#pragma unroll
+            for (int i = 0; i < kIlpF; ++i) {
+                // branch-free update; stopped lanes and alphas below the floor change nothing
+                const bool use = valid[i] && T >= kTStop && alpha[i] >= kAlphaMin;
+                const float w = use ? alpha[i] * T : 0.0f;
+                C0 = __builtin_fmaf(xc[i].z, w, C0);
+                C1 = __builtin_fmaf(xc[i].w, w, C1);
+                C2 = __builtin_fmaf(cb[i], w, C2);
+                T = use ? T * (1.0f - alpha[i]) : T;
+                last = use ? pos0 + ks[i] + 1 : last;
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ void fwd_write(int W, int H, int px, int py, float3 bg, float T, float C0, float C1,
+                                          float C2, uint32_t last, uint32_t examined, float* __restrict__ image,
+                                          float* __restrict__ final_T, uint32_t* __restrict__ n_contrib,
+                                          uint32_t* __restrict__ n_examined) {
+    const size_t p = (size_t)py * W + px;
+    const size_t plane = (size_t)W * H;
+    image[p] = __builtin_fmaf(T, bg.x, C0);
+    image[plane + p] = __builtin_fmaf(T, bg.y, C1);
+    image[2 * plane + p] = __builtin_fmaf(T, bg.z, C2);
+    final_T[p] = T;
+    n_contrib[p] = last;
+    if (n_examined) n_examined[p] = examined;
+}
+
+// Row of the chunk partials of chunk b of a list (start, len): the
+// checkpoint slot of the chunk's end boundary, or, for the list's last
+// chunk, slot n_slots + tile.
+__device__ __forceinline__ size_t part_row(uint32_t start, uint32_t len, uint32_t b, uint32_t n_slots, int tile) {
+    const uint32_t end_rel = (b + 1u) * (uint32_t)kChunk;
+    return end_rel < len ? (size_t)((start + end_rel) / kChunk) : (size_t)n_slots + (size_t)tile;
+}
+
+// Forward compositing. Whole lists (kItems false): workgroup i takes tile
+// tile_order[i]. Scheduled (kItems true): workgroup i takes work item i of
+// `chunks` (see the backward): a whole list is composited as above; a chunk
+// is composited from T = 1 and C = 0 with the stop rule applied to that
+// local T, and its per-pixel (T, C, last) land in part / part_last for
+// k_composite_fwd_resolve, which writes the outputs of its pixels.
+template <bool kItems>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) void k_composite_fwd(
     const int W, const int H, const int TX, const uint32_t* __restrict__ ranges,
     const uint32_t* __restrict__ point_list, const float4* __restrict__ xy_depth,
     const float4* __restrict__ conic_op, const float4* __restrict__ rgb, const float3 bg,
     float* __restrict__ image, float* __restrict__ final_T, uint32_t* __restrict__ n_contrib,
     uint32_t* __restrict__ n_examined, const uint32_t* __restrict__ tile_order, float4* __restrict__ ckpt,
-    const uint32_t ckpt_slots) {
+    const uint32_t ckpt_slots, const uint32_t* __restrict__ chunks, const uint32_t n_tiles, const uint32_t n_slots,
+    float4* __restrict__ part, uint32_t* __restrict__ part_last) {
     __shared__ float4 s_conic[kBatch];  // -A/2, B, -C/2, opacity
     __shared__ float4 s_xyc[kBatch];    // u, v, r, g
     __shared__ float4 s_bl[kBatch];     // b, live blocks (as bits), -, -: one address with the two above
 
-    const int tile = tile_order ? (int)tile_order[blockIdx.x] : (int)blockIdx.x;
+    int tile;
+    uint32_t start, end, base0, len = 0, chunk = kWholeList;
+    if (kItems) {
+        const uint32_t count = chunks[0];
+        const uint4 item = reinterpret_cast<const uint4*>(chunks + 4)[blockIdx.x];
+        if (blockIdx.x >= count || item.x >= n_tiles) return;
+        tile = (int)item.x;
+        chunk = item.y;
+        start = item.z;
+        len = item.w;
+        end = start + len;
+        base0 = start;
+        if (chunk != kWholeList) {
+            base0 = start + chunk * (uint32_t)kChunk;
+            end = min(end, base0 + (uint32_t)kChunk);
+        }
+    } else {
+        tile = tile_order ? (int)tile_order[blockIdx.x] : (int)blockIdx.x;
+        start = ranges[2 * tile];
+        end = ranges[2 * tile + 1];
+        base0 = start;
+    }
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -186,7 +320,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
     const uint32_t qblocks = quadrant_blocks(wave);
     const bool inside = px < W && py < H;
     const float fx = (float)px, fy = (float)py;
-    const uint32_t start = ranges[2 * tile], end = ranges[2 * tile + 1];
 
     // A pixel has stopped exactly when its transmittance is below the stop
     // threshold (T only decreases, and compositing ends at the first splat
@@ -195,95 +328,115 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
     float T = inside ? 1.0f : 0.0f, C0 = 0.0f, C1 = 0.0f, C2 = 0.0f;
     uint32_t last = 0;
 
-    for (uint32_t base = start; base < end; base += kBatch) {
+    for (uint32_t base = base0; base < end; base += kBatch) {
         // the state in front of this batch, for a backward chunk that ends
         // here; boundaries inside one list are 256 apart and those of the next
         // list lie more than 256 beyond, so base / 256 is a slot of its own
-        if (base != start && base / kChunk < ckpt_slots)
+        if (chunk == kWholeList && base != start && base / kChunk < ckpt_slots)
             ckpt[(size_t)(base / kChunk) * kChunk + tid] = make_float4(T, C0, C1, C2);
         if (__syncthreads_count(T < kTStop) == 256) break;
-        const uint32_t j = base + tid;
-        if (j < end) {
-            const uint32_t g = point_list[j];
-            const float4 xy = xy_depth[g];
-            const float4 co = conic_op[g];
-            const float4 c = rgb[g];
-            s_conic[tid] = make_float4(-0.5f * co.x, co.y, -0.5f * co.z, co.w);
-            s_xyc[tid] = make_float4(xy.x, xy.y, c.x, c.y);
-            s_bl[tid] = make_float4(c.z, __uint_as_float(block_mask(co, xy.x, xy.y, tx * kTile, ty * kTile)),
-                                    0.0f, 0.0f);
-        }
+        fwd_stage(base, end, tid, tx * kTile, ty * kTile, point_list, xy_depth, conic_op, rgb, s_conic, s_xyc, s_bl);
         __syncthreads();
-        const int cnt = (int)min((uint32_t)kBatch, end - base);
-        const uint32_t pos0 = base - start;
-        // this wave's live splats of the batch, as four 64-bit masks
-        uint64_t m[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int k = q * 64 + lane;
-            m[q] = __ballot(k < cnt && (__float_as_uint(s_bl[k].y) & qblocks) != 0u);
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            uint64_t mq = m[q];
-            while (mq != 0ull) {
-                if (__ballot(T >= kTStop) == 0ull) { mq = 0ull; break; }
-                // kIlpF splats per step: independent alphas, then the ordered updates
-                int ks[kIlpF];
-                bool valid[kIlpF];
-#pragma unroll
-                for (int i = 0; i < kIlpF; ++i) {
-                    valid[i] = mq != 0ull;
-                    ks[i] = valid[i] ? q * 64 + (__ffsll((unsigned long long)mq) - 1) : (i ? ks[i - 1] : q * 64);
-                    mq &= mq - 1ull;
-                }
-                float4 co[kIlpF], xc[kIlpF];
-                float cb[kIlpF], pw[kIlpF], G[kIlpF], oG[kIlpF], alpha[kIlpF];
-                bool near[kIlpF];
-                bool any_near = false;
-#pragma unroll
-                for (int i = 0; i < kIlpF; ++i) {
-                    co[i] = s_conic[ks[i]];
-                    xc[i] = s_xyc[ks[i]];
-                    cb[i] = s_bl[ks[i]].x;
-                }
-#pragma unroll
-                for (int i = 0; i < kIlpF; ++i) {
-                    near[i] = splat_alpha_fast(co[i].x, co[i].y, co[i].z, co[i].w, fx - xc[i].x, fy - xc[i].y, pw[i],
-                                               G[i], oG[i], alpha[i]);
-                    any_near = any_near || near[i];
-                }
-                if (__builtin_expect(__ballot(any_near) != 0ull, 0)) {
-#pragma unroll
-                    for (int i = 0; i < kIlpF; ++i)
-                        if (near[i]) splat_alpha_exact(pw[i], co[i].w, G[i], oG[i], alpha[i]);
-                }
-#pragma unroll
-                for (int i = 0; i < kIlpF; ++i) {
-                    // branch-free update; stopped lanes and alphas below the floor change nothing
-                    const bool use = valid[i] && T >= kTStop && alpha[i] >= kAlphaMin;
-                    const float w = use ? alpha[i] * T : 0.0f;
-                    C0 = __builtin_fmaf(xc[i].z, w, C0);
-                    C1 = __builtin_fmaf(xc[i].w, w, C1);
-                    C2 = __builtin_fmaf(cb[i], w, C2);
-                    T = use ? T * (1.0f - alpha[i]) : T;
-                    last = use ? pos0 + ks[i] + 1 : last;
-                }
+        fwd_walk((int)min((uint32_t)kBatch, end - base), base - start, qblocks, lane, fx, fy, s_conic, s_xyc, s_bl, T,
+                 C0, C1, C2, last);
+    }
+
+    if (kItems && chunk != kWholeList) {
+        const size_t r = part_row(start, len, chunk, n_slots, tile) * kChunk + tid;
+        part[r] = make_float4(T, C0, C1, C2);
+        part_last[r] = last;
+    } else if (inside) {
+        // a pixel that stopped examined up to its last contributor; one that
+        // did not examined the whole list
+        fwd_write(W, H, px, py, bg, T, C0, C1, C2, last, T < kTStop ? last : end - start, image, final_T, n_contrib,
+                  n_examined);
+    }
+}
+
+// Outputs of the pixels whose lists were composited in chunks. Workgroup i
+// takes work item i of `chunks` when it is chunk b of a list (whole lists
+// are done): each pixel combines the partials of chunks 0 .. b-1 front to
+// back (T_in *= T_j, C += T_in C_j, in list order). A pixel whose
+// transmittance crosses the stop threshold inside an earlier chunk belongs
+// to that chunk's workgroup. A pixel still going stores the checkpoint at
+// the chunk's start; if the chunk's partial takes it below the threshold it
+// is composited again through the chunk from (T_in, C), splat by splat as
+// the whole-list walk does, stopping where that walk stops; if not and this
+// is the list's last chunk, the combined state is final.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) void k_composite_fwd_resolve(
+    const int W, const int H, const int TX, const uint32_t* __restrict__ point_list,
+    const float4* __restrict__ xy_depth, const float4* __restrict__ conic_op, const float4* __restrict__ rgb,
+    const float3 bg, float* __restrict__ image, float* __restrict__ final_T, uint32_t* __restrict__ n_contrib,
+    uint32_t* __restrict__ n_examined, float4* __restrict__ ckpt, const uint32_t* __restrict__ chunks,
+    const uint32_t n_tiles, const uint32_t n_slots, const float4* __restrict__ part,
+    const uint32_t* __restrict__ part_last) {
+    __shared__ float4 s_conic[kBatch];
+    __shared__ float4 s_xyc[kBatch];
+    __shared__ float4 s_bl[kBatch];
+
+    const uint32_t count = chunks[0];
+    const uint4 item = reinterpret_cast<const uint4*>(chunks + 4)[blockIdx.x];
+    if (blockIdx.x >= count || item.x >= n_tiles || item.y == kWholeList) return;
+    const int tile = (int)item.x;
+    const uint32_t b = item.y, start = item.z, len = item.w;
+    const uint32_t lo = b * (uint32_t)kChunk, hi = min(lo + (uint32_t)kChunk, len);
+    const bool last_chunk = hi == len;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int tx = tile % TX, ty = tile / TX;
+    const int px = tx * kTile + 8 * (wave & 1) + (lane & 7);
+    const int py = ty * kTile + 8 * (wave >> 1) + (lane >> 3);
+    const uint32_t qblocks = quadrant_blocks(wave);
+    const bool inside = px < W && py < H;
+    const float fx = (float)px, fy = (float)py;
+
+    float T = 1.0f, C0 = 0.0f, C1 = 0.0f, C2 = 0.0f;
+    uint32_t last = 0;
+    bool alive = inside;
+    for (uint32_t j = 0; j < b; ++j) {
+        if (alive) {
+            const size_t r = part_row(start, len, j, n_slots, tile) * kChunk + tid;
+            const float4 q = part[r];
+            const uint32_t lj = part_last[r];
+            const float Tn = T * q.x;
+            if (Tn < kTStop) {
+                alive = false;  // stops inside chunk j
+            } else {
+                C0 = __builtin_fmaf(T, q.y, C0);
+                C1 = __builtin_fmaf(T, q.z, C1);
+                C2 = __builtin_fmaf(T, q.w, C2);
+                T = Tn;
+                last = lj != 0u ? lj : last;
             }
         }
     }
-
-    if (inside) {
-        const size_t p = (size_t)py * W + px;
-        const size_t plane = (size_t)W * H;
-        image[p] = __builtin_fmaf(T, bg.x, C0);
-        image[plane + p] = __builtin_fmaf(T, bg.y, C1);
-        image[2 * plane + p] = __builtin_fmaf(T, bg.z, C2);
-        final_T[p] = T;
-        n_contrib[p] = last;
-        // a pixel that stopped examined up to its last contributor; one that
-        // did not examined the whole list
-        if (n_examined) n_examined[p] = T < kTStop ? last : end - start;
+    if (alive && b != 0u && ckpt && (start + lo) / kChunk < n_slots)
+        ckpt[(size_t)((start + lo) / kChunk) * kChunk + tid] = make_float4(T, C0, C1, C2);
+    bool walk = false;
+    if (alive) {
+        const size_t r = part_row(start, len, b, n_slots, tile) * kChunk + tid;
+        const float4 q = part[r];
+        const uint32_t lb = part_last[r];
+        const float Tn = T * q.x;
+        if (Tn < kTStop) {
+            walk = true;
+        } else if (last_chunk) {
+            fwd_write(W, H, px, py, bg, Tn, __builtin_fmaf(T, q.y, C0), __builtin_fmaf(T, q.z, C1),
+                      __builtin_fmaf(T, q.w, C2), lb != 0u ? lb : last, len, image, final_T, n_contrib, n_examined);
+        }
+    }
+    if (__syncthreads_or(walk)) {
+        fwd_stage(start + lo, start + hi, tid, tx * kTile, ty * kTile, point_list, xy_depth, conic_op, rgb, s_conic,
+                  s_xyc, s_bl);
+        __syncthreads();
+        float Tw = walk ? T : 0.0f;  // only these lanes composite
+        fwd_walk((int)(hi - lo), lo, qblocks, lane, fx, fy, s_conic, s_xyc, s_bl, Tw, C0, C1, C2, last);
+        // stopped here (or, if rounding kept it just above the threshold,
+        // ended with this chunk)
+        if (walk) fwd_write(W, H, px, py, bg, Tw, C0, C1, C2, last, Tw < kTStop ? last : hi, image, final_T, n_contrib,
+                            n_examined);
     }
 }
 
@@ -590,13 +743,33 @@ hipError_t launch_composite_fwd(const gs_camera& cam, const uint32_t* ranges,
                                 const float4* conic_op, const float4* rgb, float3 bg,
                                 float* image, float* final_T, uint32_t* n_contrib,
                                 uint32_t* n_examined, const uint32_t* tile_order, float4* ckpt,
-                                uint32_t capacity, hipStream_t stream) {
+                                uint32_t capacity, const uint32_t* chunks, void* part, hipStream_t stream) {
     const int TX = tiles_x(cam), TY = tiles_y(cam);
-    const uint32_t slots = ckpt ? (uint32_t)((capacity + (uint32_t)kChunk - 1u) / (uint32_t)kChunk) : 0u;
-    hipLaunchKernelGGL(k_composite_fwd, dim3(TX * TY), dim3(256), 0, stream, cam.width, cam.height,
-                       TX, ranges, point_list, xy_depth, conic_op, rgb, bg, image, final_T,
-                       n_contrib, n_examined, tile_order, ckpt, slots);
+    const uint32_t n_tiles = (uint32_t)(TX * TY);
+    const uint32_t slots = (uint32_t)((capacity + (uint32_t)kChunk - 1u) / (uint32_t)kChunk);
+    const uint32_t ckpt_slots = ckpt ? slots : 0u;
+    if (chunks) {
+        float4* const p4 = (float4*)part;
+        uint32_t* const pl = (uint32_t*)(p4 + (size_t)(slots + n_tiles) * kChunk);
+        hipLaunchKernelGGL(k_composite_fwd<true>, dim3(slots + n_tiles), dim3(256), 0, stream, cam.width, cam.height,
+                           TX, (const uint32_t*)nullptr, point_list, xy_depth, conic_op, rgb, bg, image, final_T,
+                           n_contrib, n_examined, (const uint32_t*)nullptr, ckpt, ckpt_slots, chunks, n_tiles, slots,
+                           p4, pl);
+        hipLaunchKernelGGL(k_composite_fwd_resolve, dim3(slots + n_tiles), dim3(256), 0, stream, cam.width,
+                           cam.height, TX, point_list, xy_depth, conic_op, rgb, bg, image, final_T, n_contrib,
+                           n_examined, ckpt, chunks, n_tiles, slots, (const float4*)p4, (const uint32_t*)pl);
+    } else {
+        hipLaunchKernelGGL(k_composite_fwd<false>, dim3(n_tiles), dim3(256), 0, stream, cam.width, cam.height,
+                           TX, ranges, point_list, xy_depth, conic_op, rgb, bg, image, final_T, n_contrib,
+                           n_examined, tile_order, ckpt, ckpt_slots, (const uint32_t*)nullptr, n_tiles, slots,
+                           (float4*)nullptr, (uint32_t*)nullptr);
+    }
     return hipGetLastError();
+}
+
+size_t composite_part_bytes(const gs_camera& cam, uint32_t capacity) {
+    const size_t slots = (capacity + (size_t)kChunk - 1) / kChunk;
+    return (slots + (size_t)tiles_x(cam) * tiles_y(cam)) * kChunk * (sizeof(float4) + sizeof(uint32_t));
 }
 
 hipError_t launch_composite_bwd(const gs_camera& cam, int n, const uint32_t* ranges,

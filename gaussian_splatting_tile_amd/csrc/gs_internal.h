@@ -179,7 +179,9 @@ hipError_t launch_composite_fwd(const gs_camera& cam, const uint32_t* ranges,
                                 const float4* conic_op, const float4* rgb, float3 bg,
                                 float* image, float* final_T, uint32_t* n_contrib,
                                 uint32_t* n_examined, const uint32_t* tile_order, float4* ckpt,
-                                uint32_t capacity, hipStream_t stream);
+                                uint32_t capacity, const uint32_t* chunks, void* part, hipStream_t stream);
+// Bytes of the chunk partials the scheduled forward needs.
+size_t composite_part_bytes(const gs_camera& cam, uint32_t capacity);
 
 hipError_t launch_composite_bwd(const gs_camera& cam, int n, const uint32_t* ranges,
                                 const uint32_t* point_list, const float4* xy_depth,

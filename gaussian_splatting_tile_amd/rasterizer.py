@@ -299,6 +299,18 @@ def tile_ranges(cam, keys, n_entries: int, out=None, order=None, stream=None, ch
     return out
 
 
+# Below this many tiles a frame cannot fill the GPU's workgroup slots with
+# whole lists, and the forward composites the chunk schedule instead.
+SCHEDULED_FORWARD_MAX_TILES = 2048
+
+
+def scheduled_forward(cam) -> bool:
+    """Whether Rasterizer and ViewBatch composite the forward by the chunk
+    schedule for this camera (small tile grids: few, long lists)."""
+    TX, TY = tiles_xy(cam if isinstance(cam, dict) else dict(width=cam.width, height=cam.height))
+    return TX * TY < SCHEDULED_FORWARD_MAX_TILES
+
+
 def ckpt_rows(capacity: int) -> int:
     """Rows of the checkpoint buffer gs_composite_fwd_ex needs for `capacity` entries."""
     return (int(capacity) + 255) // 256 * 256
@@ -310,12 +322,22 @@ def chunk_words(cam, capacity: int) -> int:
     return 4 + 4 * (TX * TY + (int(capacity) + 255) // 256)
 
 
+def part_bytes(cam, capacity: int) -> int:
+    """Bytes of the workspace the scheduled forward (composite_fwd with chunks) needs."""
+    c = _cam(cam)
+    return int(_lib.load().gs_composite_part_bytes(ctypes.byref(c), int(capacity)))
+
+
 def composite_fwd(cam, ranges, point_list, xy_depth, conic_op, rgb, bg=(0.0, 0.0, 0.0),
-                  with_examined=False, out=None, order=None, stream=None, ckpt=None, capacity=None):
-    """gs_composite_fwd, or gs_composite_fwd_ex when `ckpt` (float32 [ckpt_rows(capacity), 4]) is
-    given: it then also receives the per-pixel state at every 256-entry boundary, for
-    composite_bwd's chunked walk; capacity defaults to point_list's length. Returns dict
-    image [3,H,W], final_T [H,W], n_contrib [H,W] (int32), and n_examined [H,W] when requested."""
+                  with_examined=False, out=None, order=None, stream=None, ckpt=None, capacity=None,
+                  chunks=None, part=None):
+    """gs_composite_fwd, or gs_composite_fwd_ex when `ckpt` (float32 [ckpt_rows(capacity), 4]) or
+    `chunks` is given: ckpt then receives the per-pixel state at every 256-entry boundary, for
+    composite_bwd's chunked walk; with the schedule `chunks` (from tile_ranges) the lists are
+    composited as its work items, long ones in 256-entry chunks, in the workspace `part`
+    (uint8 [part_bytes(cam, capacity)]; allocated here if not given). capacity defaults to
+    point_list's length. Returns dict image [3,H,W], final_T [H,W], n_contrib [H,W] (int32), and
+    n_examined [H,W] when requested."""
     W, H = (cam["width"], cam["height"]) if isinstance(cam, dict) else (cam.width, cam.height)
     dev = xy_depth.device
     if out is None:
@@ -326,16 +348,24 @@ def composite_fwd(cam, ranges, point_list, xy_depth, conic_op, rgb, bg=(0.0, 0.0
             out["n_examined"] = torch.empty((H, W), dtype=torch.int32, device=dev)
     bgc = (ctypes.c_float * 3)(*[float(x) for x in bg])
     c = _cam(cam)
-    if ckpt is not None:
+    if ckpt is not None or chunks is not None:
         nk = int(point_list.numel() if capacity is None else capacity)
-        if ckpt.dtype != torch.float32 or ckpt.numel() < 4 * ckpt_rows(nk):
+        if ckpt is not None and (ckpt.dtype != torch.float32 or ckpt.numel() < 4 * ckpt_rows(nk)):
             raise ValueError(f"ckpt must be float32 with at least {ckpt_rows(nk)} rows of 4")
+        if chunks is not None:
+            _check_chunks(chunks, cam, nk)
+            need = part_bytes(cam, nk)
+            if part is None:
+                part = torch.empty((need,), dtype=torch.uint8, device=xy_depth.device)
+            elif part.numel() * part.element_size() < need:
+                raise ValueError(f"part must hold at least {need} bytes")
         _lib.check(_lib.load().gs_composite_fwd_ex(
             ctypes.byref(c), _ptr(ranges, torch.int32, "ranges"), _ptr(point_list, torch.int32, "point_list"),
             _ptr(xy_depth, torch.float32), _ptr(conic_op, torch.float32), _ptr(rgb, torch.float32),
             ctypes.cast(bgc, ctypes.c_void_p), _ptr(out["image"]), _ptr(out["final_T"]),
             _ptr(out["n_contrib"]), _ptr(out.get("n_examined")), _ptr(order, torch.int32, "order"), nk,
-            _ptr(ckpt, torch.float32, "ckpt"), _stream(stream)))
+            _ptr(ckpt, torch.float32, "ckpt"), _ptr(chunks, torch.int32, "chunks"),
+            _ptr(part if chunks is not None else None, None, "part"), _stream(stream)))
         return out
     _lib.check(_lib.load().gs_composite_fwd(
         ctypes.byref(c), _ptr(ranges, torch.int32, "ranges"), _ptr(point_list, torch.int32, "point_list"),
@@ -418,11 +448,13 @@ class Rasterizer:
         self.tile_test = int(tile_test)
 
     def forward(self, cam: dict, scene: Scene, bg=(0.0, 0.0, 0.0), with_examined=False,
-                checkpoints=True):
+                checkpoints=True, scheduled=None):
         """Render one view. With checkpoints (the default) the forward keeps the
         per-pixel state at every 256-entry boundary, and backward() then walks
-        each list in 256-entry chunks in parallel; without, backward() walks
-        each list whole."""
+        long lists in 256-entry chunks in parallel; without, backward() walks
+        each list whole. With scheduled, the forward too composites the work
+        items of the chunk schedule (long lists in chunks); by default it does
+        when the tile grid alone is small (see scheduled_forward)."""
         c = camera(cam)
         pre = preprocess(c, scene.means, scene.scales, scene.quats, scene.opacity, scene.sh,
                          scene.sh_degree, scene.rgb, tile_test=self.tile_test)
@@ -430,12 +462,15 @@ class Rasterizer:
                                            conic_op=pre["conic_op"], tile_test=self.tile_test)
         TX, TY = tiles_xy(cam)
         order = torch.empty((TX * TY,), dtype=torch.int32, device=self.device)
+        if scheduled is None:
+            scheduled = scheduled_forward(cam)
         chunks = (torch.empty((chunk_words(cam, E),), dtype=torch.int32, device=self.device)
-                  if checkpoints else None)
+                  if checkpoints or scheduled else None)
         ranges = tile_ranges(cam, keys, E, order=order, chunks=chunks)
         ckpt = torch.empty((ckpt_rows(E), 4), dtype=torch.float32, device=self.device) if checkpoints else None
         fwd = composite_fwd(cam, ranges, point_list, pre["xy_depth"], pre["conic_op"], pre["rgb"], bg,
-                            with_examined=with_examined, order=order, ckpt=ckpt, capacity=E)
+                            with_examined=with_examined, order=order, ckpt=ckpt, capacity=E,
+                            chunks=chunks if scheduled else None)
         if checkpoints:
             fwd.update(ckpt=ckpt, chunks=chunks)
         out = dict(pre)
@@ -475,7 +510,8 @@ class ViewBatch:
     """
 
     def __init__(self, cams, scene: "Scene", capacity: int, device="cuda", bg=(0.0, 0.0, 0.0),
-                 tile_order=True, streams: int = 1, tile_test: int = 0, chunked: bool = True):
+                 tile_order=True, streams: int = 1, tile_test: int = 0, chunked: bool = True,
+                 scheduled=None):
         self.device = torch.device(device)
         self.scene = scene
         self.bg = bg
@@ -506,6 +542,8 @@ class ViewBatch:
                 # forward state at 256-entry boundaries and the chunk schedule, for the chunked backward
                 ckpt=torch.empty((ckpt_rows(capacity), 4), dtype=f32, device=self.device) if chunked else None,
                 chunks=torch.empty((chunk_words(cam, capacity),), dtype=i32, device=self.device) if chunked else None,
+                part=(torch.empty((part_bytes(cam, capacity),), dtype=torch.uint8, device=self.device)
+                      if chunked and (scheduled_forward(cam) if scheduled is None else scheduled) else None),
                 dL_dimage=torch.zeros((3, H, W), dtype=f32, device=self.device),
                 grads=dict(grad_mean2d=torch.empty((n, 2), dtype=f32, device=self.device),
                            grad_conic_op=torch.empty((n, 4), dtype=f32, device=self.device),
@@ -542,7 +580,8 @@ class ViewBatch:
                                       tile_test=self.tile_test)
         tile_ranges_async(c, bins, out=v["ranges"], order=v["order"], chunks=v["chunks"])
         composite_fwd(c, v["ranges"], pl, pre["xy_depth"], pre["conic_op"], pre["rgb"], self.bg,
-                      out=v["fwd"], order=v["order"], ckpt=v["ckpt"], capacity=bins.capacity)
+                      out=v["fwd"], order=v["order"], ckpt=v["ckpt"], capacity=bins.capacity,
+                      chunks=v["chunks"] if v["part"] is not None else None, part=v["part"])
         if loss_grad is not None:
             loss_grad(i, v["fwd"]["image"], v["dL_dimage"])
         composite_bwd(c, sc.n, v["ranges"], pl, pre["xy_depth"], pre["conic_op"], pre["rgb"],

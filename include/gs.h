@@ -306,16 +306,18 @@ gs_status gs_tile_ranges_async(const gs_camera* cam, const uint64_t* keys, const
  *   capacity    length of keys; n_entries <= capacity when n_entries_dev is
  *               NULL
  *   chunks      out uint32 [4 + 4 (TX*TY + ceil(capacity / 256))], 16-byte
- *               aligned, or NULL: the work items of gs_composite_bwd_ex.
+ *               aligned, or NULL: the work items of gs_composite_fwd_ex and
+ *               gs_composite_bwd_ex.
  *               chunks[0] = the item count; words 1-3 unused; from word 4,
  *               for each item, (tile, k, list start, L). When the lists
  *               average more than 256 entries (E > 256 TX TY), every list is
  *               cut into ceil(L / 256) chunks, chunk k covering list
  *               positions [256 k, min(256 k + 256, L)), in descending order
  *               of L - 256 k, the list length from the chunk on (classes as
- *               tile_order's). Otherwise the tiles alone give the backward
- *               enough workgroups: every non-empty list is one item with
- *               k = 0xffffffff (the whole list), in tile_order's order.
+ *               tile_order's); each empty list is one item (k = 0xffffffff,
+ *               the whole list), last. Otherwise the tiles alone give the
+ *               compositing enough workgroups: every list is one item with
+ *               k = 0xffffffff, in tile_order's order.
  * ------------------------------------------------------------------- */
 gs_status gs_tile_ranges_ex(const gs_camera* cam, const uint64_t* keys, int64_t n_entries,
                             const uint64_t* n_entries_dev, int64_t capacity, uint32_t* ranges,
@@ -384,30 +386,53 @@ gs_status gs_composite_bwd(const gs_camera* cam, int32_t n, const uint32_t* rang
                            float* grad_rgb, const uint32_t* tile_order, void* stream);
 
 /* ---------------------------------------------------------------------
- * gs_composite_fwd_ex - gs_composite_fwd that also keeps, for the chunked
+ * gs_composite_fwd_ex - gs_composite_fwd that can keep, for the chunked
  * backward (gs_composite_bwd_ex), each pixel's state at every 256-entry
- * boundary of its tile's list. The compositing and every other output are
- * those of gs_composite_fwd ("rigel" README "Rasterization").
+ * boundary of its tile's list, and can composite long lists in 256-entry
+ * chunks in parallel. The compositing is that of gs_composite_fwd ("rigel"
+ * README "Rasterization").
  *
  *   capacity  length of the sorted entry arrays (keys, point_list): the
  *             entry count E, or the capacity the asynchronous binning used;
  *             every tile range must lie in [0, capacity)
- *   ckpt      out float32 [ceil(capacity / 256) * 256][4], or NULL (then this
- *             is gs_composite_fwd). For tile t and a boundary b = start_t +
- *             256 k (k >= 1, b < end_t) that the compositing reached, row
- *             (b / 256) * 256 + q holds (T, C_r, C_g, C_b) of the tile's pixel
- *             q in front of entry b, C the colour accumulated so far;
- *             q = 64 w + 8 r + c is pixel (8 (w & 1) + c, 8 (w >> 1) + r) of
- *             the tile. Distinct boundaries never share a row (those of one
- *             list are 256 apart, the next list's lie more than 256 further
- *             on). Other rows are left as they were.
- * Other arguments as gs_composite_fwd.
+ *   ckpt      out float32 [ceil(capacity / 256) * 256][4], or NULL. For tile
+ *             t and a boundary b = start_t + 256 k (k >= 1, b < end_t) that
+ *             the pixel's compositing reached, row (b / 256) * 256 + q holds
+ *             (T, C_r, C_g, C_b) of the tile's pixel q in front of entry b, C
+ *             the colour accumulated so far; q = 64 w + 8 r + c is pixel
+ *             (8 (w & 1) + c, 8 (w >> 1) + r) of the tile. Distinct boundaries
+ *             never share a row (those of one list are 256 apart, the next
+ *             list's lie more than 256 further on). Other rows are left as
+ *             they were.
+ *   chunks    the schedule gs_tile_ranges_ex wrote for this frame, or NULL
+ *             (tiles in tile_order, each list walked whole). With it every
+ *             work item is one workgroup: whole lists as without it; a chunk
+ *             is first composited on its own from T = 1 (a pixel stopping
+ *             where that local T falls below 1e-4), then each pixel combines
+ *             the chunks in front of it (T_in *= T_chunk, C += T_in C_chunk)
+ *             and, in the chunk where T_in T_chunk falls below 1e-4, is
+ *             composited again splat by splat from (T_in, C) and stops where
+ *             the whole-list walk stops. Results agree with gs_composite_fwd
+ *             to float32 rounding: T is a product in another grouping, so a
+ *             pixel whose T lands within rounding of 1e-4 may stop one splat
+ *             earlier or later, and one that the grouped product puts past
+ *             1e-4 but its own walk does not ends with that chunk.
+ *             ranges and tile_order are then not read.
+ *   part      workspace of gs_composite_part_bytes(cam, capacity) bytes,
+ *             16-byte aligned (required with chunks, else unused)
+ * Other arguments as gs_composite_fwd. ckpt and chunks may both be NULL:
+ * then this is gs_composite_fwd.
  * ------------------------------------------------------------------- */
 gs_status gs_composite_fwd_ex(const gs_camera* cam, const uint32_t* ranges, const uint32_t* point_list,
                               const float* xy_depth, const float* conic_op, const float* rgb,
                               const float bg[3], float* image, float* final_T, uint32_t* n_contrib,
                               uint32_t* n_examined, const uint32_t* tile_order, int64_t capacity,
-                              float* ckpt, void* stream);
+                              float* ckpt, const uint32_t* chunks, void* part, void* stream);
+
+/* gs_composite_part_bytes - bytes of the `part` workspace of
+ * gs_composite_fwd_ex for this camera and capacity: (ceil(capacity / 256) +
+ * TX*TY) * 256 * 20. 0 for an invalid camera or capacity. */
+size_t gs_composite_part_bytes(const gs_camera* cam, int64_t capacity);
 
 /* ---------------------------------------------------------------------
  * gs_composite_bwd_ex - gs_composite_bwd over the work items of the

@@ -22,12 +22,14 @@ def to_np(t):
     return t.detach().cpu().numpy()
 
 
-def gpu_forward(cam, scene_np, bg=(0.0, 0.0, 0.0), capacity=1 << 16, rast=None):
+def gpu_forward(cam, scene_np, bg=(0.0, 0.0, 0.0), capacity=1 << 16, rast=None, scheduled=None):
+    """Rasterizer.forward; scheduled None leaves the choice of the scheduled
+    (chunked) forward to the Rasterizer (small tile grids)."""
     import gaussian_splatting_tile_amd as gs
     import torch
     sc = gs.Scene.from_numpy(scene_np)
     r = rast or gs.Rasterizer(capacity=capacity)
-    out = r.forward(cam, sc, bg=bg, with_examined=True)
+    out = r.forward(cam, sc, bg=bg, with_examined=True, scheduled=scheduled)
     torch.cuda.synchronize()
     res = {k: to_np(v) for k, v in out.items() if hasattr(v, "detach") and k not in ("ckpt", "chunks")}
     res["n_entries"] = out["n_entries"]

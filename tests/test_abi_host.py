@@ -219,13 +219,24 @@ def test_chunked_composite_validates_before_launch(gs):
     d = P(256)  # never dereferenced: validation fails first
     c = _cam()
     bg = (ctypes.c_float * 3)()
-    fwd = lambda cap=100, ckpt=d, rgb=d: gs.gs_composite_fwd_ex(
-        ctypes.byref(c), d, d, d, d, rgb, bg, d, d, d, None, None, cap, ckpt, None)
+    fwd = lambda cap=100, ckpt=d, rgb=d, chunks=None, part=None, ranges=d: gs.gs_composite_fwd_ex(
+        ctypes.byref(c), ranges, d, d, d, rgb, bg, d, d, d, None, None, cap, ckpt, chunks, part, None)
     assert fwd(cap=-1) == _lib.GS_ERR_INVALID
     assert b"capacity" in gs.gs_last_error()
     assert fwd(cap=1 << 32) == _lib.GS_ERR_INVALID
     assert fwd(ckpt=P(264)) == _lib.GS_ERR_INVALID  # checkpoints are float4 rows
     assert b"aligned" in gs.gs_last_error()
+    assert fwd(chunks=d) == _lib.GS_ERR_INVALID  # the scheduled forward needs its workspace
+    assert b"part" in gs.gs_last_error()
+    assert fwd(chunks=P(264), part=d) == _lib.GS_ERR_INVALID
+    assert fwd(chunks=d, part=P(260)) == _lib.GS_ERR_INVALID
+    assert fwd(ranges=None) == _lib.GS_ERR_INVALID  # without a schedule the ranges are read
+    # the workspace size: (ceil(capacity / 256) + tiles) rows of 256 (float4 + uint32)
+    tiles = 4 * 4  # the 64 x 64 test camera
+    assert gs.gs_composite_part_bytes(ctypes.byref(c), 1000) == (4 + tiles) * 256 * 20
+    assert gs.gs_composite_part_bytes(ctypes.byref(c), 0) == tiles * 256 * 20
+    assert gs.gs_composite_part_bytes(ctypes.byref(c), -1) == 0
+    assert gs.gs_composite_part_bytes(None, 10) == 0
     bwd = lambda n=4, chunks=d, cap=100, image=d, ckpt=d, gm=d: gs.gs_composite_bwd_ex(
         ctypes.byref(c), n, d, d, chunks, cap, d, d, d, bg, image, d, d, ckpt, d, gm, d, d, None)
     assert bwd(ckpt=None) == _lib.GS_ERR_INVALID  # the chunked walk needs the checkpoints

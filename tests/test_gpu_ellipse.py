@@ -1,8 +1,11 @@
 """GPU parity of the ellipse tile test (GS_TILES_ELLIPSE) against the
 oracle's, and against the GPU's own square-span run: the preprocess,
 tiles_touched, keys, sorted order, ranges and E bit-exact with the oracle;
-the image and final_T bit-identical to the square-span run on the GPU (the
-dropped tiles hold no pixel the splat changes); gradients within the bar.
+the image and final_T bit-identical to the square-span run on the GPU when
+each list is walked whole (the dropped tiles hold no pixel the splat
+changes; the chunked forward groups T's product by list position, which the
+shorter lists shift, so there the two agree to rounding); gradients within
+the bar.
 """
 import sys
 
@@ -21,12 +24,12 @@ def say(*a):
     sys.stdout.flush()
 
 
-def _gpu_forward(cam, scene_np, tile_test, capacity=1 << 22):
+def _gpu_forward(cam, scene_np, tile_test, capacity=1 << 22, scheduled=None):
     import torch
     import gaussian_splatting_tile_amd as gs
     sc = gs.Scene.from_numpy(scene_np)
     r = gs.Rasterizer(capacity=capacity, tile_test=tile_test)
-    out = r.forward(cam, sc, with_examined=True)
+    out = r.forward(cam, sc, with_examined=True, scheduled=scheduled)
     torch.cuda.synchronize()
     res = {k: to_np(v) for k, v in out.items() if hasattr(v, "detach")}
     res["n_entries"] = out["n_entries"]
@@ -45,9 +48,10 @@ def test_ellipse_forward_parity(orc, name):
     assert_preprocess_equal(g, o)
     assert_binning_equal(g, o)
     rep = compare_forward(g, o)
-    sq, _, _ = _gpu_forward(cam, scene, 0)
+    whole, _, _ = _gpu_forward(cam, scene, 1, scheduled=False)
+    sq, _, _ = _gpu_forward(cam, scene, 0, scheduled=False)
     for k in ("image", "final_T"):
-        assert g[k].tobytes() == sq[k].tobytes(), k
+        assert whole[k].tobytes() == sq[k].tobytes(), k
     say(f"[ellipse {name}] E {sq['n_entries']} -> {g['n_entries']} {rep}")
 
 

@@ -74,6 +74,25 @@ def test_workload_backward_parity(orc, name):
     say(f"[{name}] isolated grads {rep2}")
 
 
+@pytest.mark.parametrize("name", ["cfg2", "cfg3"])
+def test_scheduled_forward_parity(orc, name):
+    """The forward over the chunk schedule at 1080p: cfg3's lists average
+    more than 256 entries, so they are composited in chunks and most pixels
+    stop inside one, composited again from the combined state; cfg2's are
+    whole items. Both against the oracle, with the chunked backward from
+    that forward's state."""
+    say(f"[{name}] scheduled forward")
+    scene, cam, dLdI, ofwd, obwd = workload(orc, name)
+    g, out, sc, r = gpu_forward(cam, scene, capacity=1 << 23, scheduled=True)
+    rep = compare_forward(g, ofwd)
+    stopped = ofwd["final_T"] < 1e-4
+    say(f"[{name}] scheduled forward {rep}, pixels stopped {int(stopped.sum())}")
+    if name == "cfg3":
+        assert stopped.sum() > 100_000  # the re-walk path is exercised (12% of the pixels stop)
+    rep_b = compare_gradients(gpu_backward(cam, sc, out, dLdI, chunked=True), obwd)
+    say(f"[{name}] chunked backward after it {rep_b}")
+
+
 def test_multiview_training_shape(orc):
     """Three of the sixteen 400x400 views over 300k Gaussians, dL/dI = sign(I - I_ref)
     with I and I_ref from the oracle."""
@@ -374,30 +393,34 @@ def _chunk_class(L):
 
 def _check_chunk_schedule(chunks, ranges):
     """chunks: the schedule words; ranges [T, 2]. If the lists average more
-    than 256 entries: every (tile, k) with k < ceil(L / 256) exactly once, in
-    non-increasing class of L - 256 k; else every non-empty tile once as a
-    whole list, in non-increasing class of L. Returns whether it split."""
+    than 256 entries: every (tile, k) with k < ceil(L / 256) exactly once and
+    every empty tile once as a whole item, in non-increasing class of
+    L - 256 k (empty tiles last); else every tile once as a whole item, in
+    non-increasing class of L. Returns whether it split."""
     L = ranges[:, 1].astype(np.int64) - ranges[:, 0]
     count = int(chunks[0])
     items4 = chunks[4:4 + 4 * count].reshape(count, 4).astype(np.int64)
     assert np.array_equal(items4[:, 2], ranges[items4[:, 0], 0])
     assert np.array_equal(items4[:, 3], L[items4[:, 0]])
+    whole = items4[:, 1] == 0xFFFFFFFF
     if L.sum() <= 256 * len(L):
-        assert (items4[:, 1] == 0xFFFFFFFF).all()
-        assert np.array_equal(np.sort(items4[:, 0]), np.nonzero(L)[0])
-        assert (np.diff(_chunk_class(L[items4[:, 0]])) <= 0).all()
+        assert whole.all()
+        assert np.array_equal(np.sort(items4[:, 0]), np.arange(len(L)))
+        cls = np.where(L[items4[:, 0]] == 0, -1, _chunk_class(L[items4[:, 0]]))
+        assert (np.diff(cls) <= 0).all()
         return False
     nch = (L + 255) // 256
-    assert count == int(nch.sum()), (count, int(nch.sum()))
-    items = items4[:, :2]
+    assert count == int(nch.sum()) + int((L == 0).sum()), (count, int(nch.sum()))
+    assert np.array_equal(np.sort(items4[whole, 0]), np.nonzero(L == 0)[0])
+    items = items4[~whole, :2]
     want = np.concatenate([np.stack([np.full(k, t), np.arange(k)], 1) for t, k in enumerate(nch) if k] or
                           [np.zeros((0, 2), np.int64)])
     got_sorted = items[np.lexsort((items[:, 1], items[:, 0]))]
     assert np.array_equal(got_sorted, want)
-    if count:
-        rest = L[items[:, 0]] - 256 * items[:, 1]
-        assert (rest > 0).all()
-        assert (np.diff(_chunk_class(rest)) <= 0).all()
+    rest = np.where(whole, 0, L[items4[:, 0]] - 256 * np.where(whole, 0, items4[:, 1]))
+    assert (rest[~whole] > 0).all()
+    cls = np.where(whole, -1, _chunk_class(np.maximum(rest, 1)))
+    assert (np.diff(cls) <= 0).all()
     return True
 
 
@@ -426,4 +449,6 @@ def test_chunk_schedule_covers_every_chunk(orc):
                 assert np.array_equal(rg, g["ranges"])
                 assert _check_chunk_schedule(to_np(chunks).view(np.uint32), rg) == split
             else:
-                assert not rg.any() and int(to_np(chunks)[0]) == 0
+                # every list empty: one whole item per tile
+                assert not rg.any()
+                assert _check_chunk_schedule(to_np(chunks).view(np.uint32), rg) is False
