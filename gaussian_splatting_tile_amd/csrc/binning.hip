@@ -576,11 +576,12 @@ __device__ __forceinline__ uint32_t heavy_first_key(uint32_t len) {
 // order within a class is unspecified). chunks = the work items of the
 // scheduled compositing after a count (padded to 16 bytes), each (tile,
 // chunk index, list start, list length). When the lists average more than
-// one chunk (E > kChunk tiles) every non-empty list is cut into
+// one chunk (E > kChunk tiles) every list longer than a chunk is cut into
 // kChunk-entry chunks, in descending order of the list length from the
 // chunk's start to the list's end: the front chunks of the longest lists
 // first, since a pixel that stops early leaves the later chunks of its list
-// little to do; each empty list is one whole item, last. Otherwise the
+// little to do; shorter lists (empty ones too) are whole items, placed by
+// their length in the same order. Otherwise the
 // tiles alone give a launch enough workgroups, and every list is one item
 // (chunk index kWholeList), in the order of `order`. One
 // workgroup of 1024 threads: class histograms, exclusive scans, scatter
@@ -612,8 +613,10 @@ __global__ __launch_bounds__(1024) void k_tile_order(const uint32_t* __restrict_
             const uint32_t len = r[k].y - r[k].x;
             if (by_tile && t < n_tiles) atomicAdd(&s_hist[0][heavy_first_key(len)], 1u);
             if (split && t < n_tiles) {
-                if (len == 0u) atomicAdd(&s_hist[1][heavy_first_key(0u)], 1u);  // an empty list: one whole item
-                for (uint32_t at = 0; at < len; at += kChunk) atomicAdd(&s_hist[1][heavy_first_key(len - at)], 1u);
+                if (len <= (uint32_t)kChunk)  // one chunk at most: a whole item
+                    atomicAdd(&s_hist[1][heavy_first_key(len)], 1u);
+                else
+                    for (uint32_t at = 0; at < len; at += kChunk) atomicAdd(&s_hist[1][heavy_first_key(len - at)], 1u);
             }
         }
     }
@@ -658,10 +661,13 @@ __global__ __launch_bounds__(1024) void k_tile_order(const uint32_t* __restrict_
                 if (chunks && !split) items[pos] = make_uint4((uint32_t)t, kWholeList, start, len);
             }
             if (split && t < n_tiles) {
-                if (len == 0u) items[atomicAdd(&s_hist[1][heavy_first_key(0u)], 1u)] = make_uint4((uint32_t)t, kWholeList, 0u, 0u);
-                for (uint32_t at = 0, b = 0; at < len; at += kChunk, ++b)
-                    items[atomicAdd(&s_hist[1][heavy_first_key(len - at)], 1u)] =
-                        make_uint4((uint32_t)t, b, start, len);
+                if (len <= (uint32_t)kChunk)
+                    items[atomicAdd(&s_hist[1][heavy_first_key(len)], 1u)] =
+                        make_uint4((uint32_t)t, kWholeList, start, len);
+                else
+                    for (uint32_t at = 0, b = 0; at < len; at += kChunk, ++b)
+                        items[atomicAdd(&s_hist[1][heavy_first_key(len - at)], 1u)] =
+                            make_uint4((uint32_t)t, b, start, len);
             }
         }
     }

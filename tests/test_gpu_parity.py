@@ -393,10 +393,11 @@ def _chunk_class(L):
 
 def _check_chunk_schedule(chunks, ranges):
     """chunks: the schedule words; ranges [T, 2]. If the lists average more
-    than 256 entries: every (tile, k) with k < ceil(L / 256) exactly once and
-    every empty tile once as a whole item, in non-increasing class of
-    L - 256 k (empty tiles last); else every tile once as a whole item, in
-    non-increasing class of L. Returns whether it split."""
+    than 256 entries: every (tile, k) with k < ceil(L / 256) of each list
+    longer than 256 exactly once and every other tile once as a whole item,
+    in non-increasing class of L - 256 k (k = 0 for whole items, empty tiles
+    last); else every tile once as a whole item, in non-increasing class of
+    L. Returns whether it split."""
     L = ranges[:, 1].astype(np.int64) - ranges[:, 0]
     count = int(chunks[0])
     items4 = chunks[4:4 + 4 * count].reshape(count, 4).astype(np.int64)
@@ -409,17 +410,17 @@ def _check_chunk_schedule(chunks, ranges):
         cls = np.where(L[items4[:, 0]] == 0, -1, _chunk_class(L[items4[:, 0]]))
         assert (np.diff(cls) <= 0).all()
         return False
-    nch = (L + 255) // 256
-    assert count == int(nch.sum()) + int((L == 0).sum()), (count, int(nch.sum()))
-    assert np.array_equal(np.sort(items4[whole, 0]), np.nonzero(L == 0)[0])
+    nch = np.where(L > 256, (L + 255) // 256, 0)
+    assert count == int(nch.sum()) + int((L <= 256).sum()), (count, int(nch.sum()))
+    assert np.array_equal(np.sort(items4[whole, 0]), np.nonzero(L <= 256)[0])
     items = items4[~whole, :2]
     want = np.concatenate([np.stack([np.full(k, t), np.arange(k)], 1) for t, k in enumerate(nch) if k] or
                           [np.zeros((0, 2), np.int64)])
     got_sorted = items[np.lexsort((items[:, 1], items[:, 0]))]
     assert np.array_equal(got_sorted, want)
-    rest = np.where(whole, 0, L[items4[:, 0]] - 256 * np.where(whole, 0, items4[:, 1]))
+    rest = L[items4[:, 0]] - 256 * np.where(whole, 0, items4[:, 1])
     assert (rest[~whole] > 0).all()
-    cls = np.where(whole, -1, _chunk_class(np.maximum(rest, 1)))
+    cls = np.where(rest == 0, -1, _chunk_class(np.maximum(rest, 1)))
     assert (np.diff(cls) <= 0).all()
     return True
 
