@@ -55,6 +55,15 @@
 //    splat per step their waves mostly wait on their own latency (measured
 //    per workgroup at 1080p: the backward's last 70 of 245 us then ran on
 //    under 5% of the workgroup slots).
+//  * Long lists in chunks. With a work schedule from the ranges call (see
+//    k_tile_order) a workgroup takes one 256-entry chunk of a list instead
+//    of the whole list, so a long list is walked by several workgroups at
+//    once. The forward stores each pixel's (T, C) at every 256-entry
+//    boundary; a backward chunk starts a pixel that composited past its end
+//    from that state (T, and the radiance from behind as image - C). The
+//    scheduled forward composites every chunk from T = 1, then combines the
+//    chunks in front of each pixel (T_in *= T_chunk, C += T_in C_chunk) and
+//    composites again, splat by splat, the chunk where the pixel stops.
 #include "gs_internal.h"
 
 namespace gs {

@@ -463,7 +463,9 @@ class Rasterizer:
         TX, TY = tiles_xy(cam)
         order = torch.empty((TX * TY,), dtype=torch.int32, device=self.device)
         if scheduled is None:
-            scheduled = scheduled_forward(cam)
+            # the schedule cuts lists only when they average more than a chunk
+            # (E known here); otherwise its items are the tiles themselves
+            scheduled = scheduled_forward(cam) and E > 256 * TX * TY
         chunks = (torch.empty((chunk_words(cam, E),), dtype=torch.int32, device=self.device)
                   if checkpoints or scheduled else None)
         ranges = tile_ranges(cam, keys, E, order=order, chunks=chunks)
