@@ -142,11 +142,20 @@ def bench_views(args):
         E_max = max(E_max, rast.forward(cam, sc)["n_entries"])
     torch.cuda.synchronize()
 
-    def loss_grad(i, image, out):
-        out.copy_(image).sub_(refs[i]).sign_()
+    if args.batch == "stack":
+        # the 16 views as bands of one stacked frame: one launch sequence per step
+        ref_all = torch.stack(refs)
 
-    batch = gs.ViewBatch(cams, sc, capacity=int(E_max * 1.25) + 1024, device=dev, streams=args.streams,
-                         chunked=args.backward == "chunked")
+        def loss_grad(image, out):
+            out.copy_(image).sub_(ref_all).sign_()
+
+        batch = gs.ViewStack(cams, sc, capacity=int(E_max * n_views * 1.25) + 1024, device=dev)
+    else:
+        def loss_grad(i, image, out):
+            out.copy_(image).sub_(refs[i]).sign_()
+
+        batch = gs.ViewBatch(cams, sc, capacity=int(E_max * 1.25) + 1024, device=dev, streams=args.streams,
+                             chunked=args.backward == "chunked")
     batch.enqueue(loss_grad)
     E = batch.check()
     st = torch.cuda.current_stream()
@@ -179,8 +188,9 @@ def bench_views(args):
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(1e3 * graph_s, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"cfg4: {WORKLOADS['cfg4']}", "n_gaussians": sc.n, "views_per_step": n_views,
-                   "streams": args.streams, "backward": args.backward,
-                   "width": 400, "height": 400, "entries_per_view": E},
+                   "batch": args.batch, "streams": args.streams if args.batch == "streams" else 1,
+                   "backward": args.backward,
+                   "width": 400, "height": 400, "entries_total": int(sum(E)) if isinstance(E, list) else int(E)},
         "secondary": {"eager_frames_per_s": round(n_views / eager_s, 3),
                       "graph_event_ms_per_step": round(e0.elapsed_time(e1) / args.steps, 4)},
     }
@@ -198,6 +208,9 @@ def main():
     ap.add_argument("--backward", choices=("chunked", "whole"), default="chunked",
                     help="backward compositing over 256-entry chunks of each list (from the forward's "
                          "checkpoints) or over whole lists (results agree to float32 rounding)")
+    ap.add_argument("--batch", choices=("stack", "streams"), default="stack",
+                    help="cfg4: the 16 views as bands of one stacked frame (one launch sequence), or one "
+                         "launch sequence per view spread over --streams streams")
     ap.add_argument("--streams", type=int, default=4,
                     help="cfg4: streams the 16 views are spread over (fork/join inside the graph)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,

@@ -17,7 +17,7 @@ EXPORTS = ("gs_constants", "gs_last_error", "gs_version", "gs_preprocess", "gs_p
            "gs_preprocess_bwd", "gs_bin_and_sort", "gs_bin_and_sort_ex", "gs_bin_and_sort_async_ex",
            "gs_bin_and_sort_async", "gs_tile_ranges", "gs_tile_ranges_async", "gs_composite_fwd",
            "gs_composite_bwd", "gs_composite_fwd_ex", "gs_composite_part_bytes", "gs_composite_bwd_ex", "gs_tile_ranges_ex",
-           "gs_appearance_fwd",
+           "gs_preprocess_views", "gs_bin_and_sort_views_async", "gs_appearance_fwd",
            "gs_appearance_bwd")
 
 
@@ -81,13 +81,18 @@ def load() -> ctypes.CDLL:
     lib.gs_composite_bwd.restype = ctypes.c_int
     lib.gs_composite_bwd.argtypes = [CAM, I32, P, P, P, P, P, P, P, P, P, P, P, P, P, P]
     lib.gs_composite_fwd_ex.restype = ctypes.c_int
-    lib.gs_composite_fwd_ex.argtypes = [CAM, P, P, P, P, P, P, P, P, P, P, P, I64, P, P, P, P]
+    lib.gs_composite_fwd_ex.argtypes = [CAM, I32, P, P, P, P, P, P, P, P, P, P, P, I64, P, P, P, P]
     lib.gs_composite_part_bytes.restype = ctypes.c_size_t
-    lib.gs_composite_part_bytes.argtypes = [CAM, I64]
+    lib.gs_composite_part_bytes.argtypes = [CAM, I32, I64]
+    lib.gs_preprocess_views.restype = ctypes.c_int
+    lib.gs_preprocess_views.argtypes = [P, I32, I32, P, P, P, P, P, I32, P, P, P, P, P, U32, P]
+    lib.gs_bin_and_sort_views_async.restype = ctypes.c_int
+    lib.gs_bin_and_sort_views_async.argtypes = [CAM, I32, I32, P, P, P, P, P, I64, P,
+                                                ctypes.POINTER(ctypes.c_size_t), P, U32, P]
     lib.gs_composite_bwd_ex.restype = ctypes.c_int
-    lib.gs_composite_bwd_ex.argtypes = [CAM, I32, P, P, P, I64, P, P, P, P, P, P, P, P, P, P, P, P, P]
+    lib.gs_composite_bwd_ex.argtypes = [CAM, I32, I32, P, P, P, I64, P, P, P, P, P, P, P, P, P, P, P, P, P]
     lib.gs_tile_ranges_ex.restype = ctypes.c_int
-    lib.gs_tile_ranges_ex.argtypes = [CAM, P, I64, P, I64, P, P, P, P]
+    lib.gs_tile_ranges_ex.argtypes = [CAM, I32, P, I64, P, I64, P, P, P, P]
     lib.gs_appearance_fwd.restype = ctypes.c_int
     lib.gs_appearance_fwd.argtypes = [CAM, I32, P, P, I32, I32, P, P, P]
     lib.gs_appearance_bwd.restype = ctypes.c_int

@@ -100,6 +100,40 @@ gs_status gs_preprocess(const gs_camera* cam, int32_t n, const float* means, con
                             rgb, tiles_touched, GS_TILES_SQUARE, stream);
 }
 
+gs_status gs_preprocess_views(const gs_camera* cams, int32_t n_views, int32_t n, const float* means,
+                              const float* scales, const float* quats, const float* opacity, const float* sh,
+                              int32_t sh_degree, const float* rgb_in, float* xy_depth, float* conic_op, float* rgb,
+                              uint32_t* tiles_touched, uint32_t flags, void* stream) {
+    g_last_error.clear();
+    if (!cams) return fail(GS_ERR_INVALID, "gs_preprocess_views: cams is NULL");
+    if (n_views < 1 || n_views > GS_MAX_VIEWS)
+        return fail(GS_ERR_INVALID, "gs_preprocess_views: n_views = %d outside [1, %d]", n_views, GS_MAX_VIEWS);
+    gs::CameraSet set{};
+    set.n = n_views;
+    for (int v = 0; v < n_views; ++v) {
+        if (gs_status s = check_camera(&cams[v])) return s;
+        if (cams[v].width != cams[0].width || cams[v].height != cams[0].height)
+            return fail(GS_ERR_INVALID, "gs_preprocess_views: camera %d is not %dx%d like camera 0", v,
+                        cams[0].width, cams[0].height);
+        set.cam[v] = cams[v];
+    }
+    if (n < 0 || (int64_t)n * n_views > GS_MAX_GAUSSIANS)
+        return fail(GS_ERR_INVALID, "n = %d (x %d views) outside [0, %d]", n, n_views, GS_MAX_GAUSSIANS);
+    if (sh && (sh_degree < 0 || sh_degree > 3))
+        return fail(GS_ERR_INVALID, "sh_degree %d outside [0, 3]", sh_degree);
+    if (flags & ~(uint32_t)GS_TILES_ELLIPSE) return fail(GS_ERR_INVALID, "gs_preprocess_views: unknown flags");
+    if (n == 0) return GS_OK;
+    if (!means || !scales || !quats || !opacity || (!sh && !rgb_in) || !xy_depth || !conic_op || !rgb ||
+        !tiles_touched)
+        return fail(GS_ERR_INVALID, "gs_preprocess_views: a required pointer is NULL");
+    if (((uintptr_t)xy_depth | (uintptr_t)conic_op | (uintptr_t)rgb) & 15)
+        return fail(GS_ERR_INVALID, "gs_preprocess_views: float4 outputs must be 16-byte aligned");
+    return hip_check(gs::launch_preprocess_views(set, n, means, scales, quats, opacity, sh, sh_degree, rgb_in,
+                                                 (float4*)xy_depth, (float4*)conic_op, (float4*)rgb, tiles_touched,
+                                                 flags, (hipStream_t)stream),
+                     "gs_preprocess_views launch");
+}
+
 gs_status gs_preprocess_bwd(const gs_camera* cam, int32_t n, const float* means, const float* scales,
                             const float* quats, const float* sh, int32_t sh_degree,
                             const uint32_t* tiles_touched, const float* grad_mean2d,
@@ -137,9 +171,16 @@ namespace {
 // on GS_OK with scratch != NULL, *s is laid out in scratch.
 gs_status bin_args(const char* fn, const gs_camera* cam, int32_t n, const float* xy_depth,
                    const uint32_t* tiles_touched, const uint64_t* keys, const uint32_t* point_list,
-                   int64_t capacity, void* scratch, size_t* scratch_bytes, bool* size_query, gs::BinScratch* s) {
+                   int64_t capacity, void* scratch, size_t* scratch_bytes, bool* size_query, gs::BinScratch* s,
+                   int32_t n_views = 1) {
     if (gs_status st = check_camera(cam)) return st;
-    if (n < 0 || n > GS_MAX_GAUSSIANS) return fail(GS_ERR_INVALID, "n = %d outside [0, %d]", n, GS_MAX_GAUSSIANS);
+    if (n_views < 1 || n_views > GS_MAX_VIEWS)
+        return fail(GS_ERR_INVALID, "%s: n_views = %d outside [1, %d]", fn, n_views, GS_MAX_VIEWS);
+    if (n < 0 || (int64_t)n * n_views > GS_MAX_GAUSSIANS)
+        return fail(GS_ERR_INVALID, "n = %d (x %d views) outside [0, %d]", n, n_views, GS_MAX_GAUSSIANS);
+    if ((int64_t)gs::tiles_x(*cam) * gs::tiles_y(*cam) * n_views > (1 << 24))
+        return fail(GS_ERR_INVALID, "%s: more than 2^24 tiles", fn);
+    n *= n_views;
     if (capacity < 0 || capacity > (int64_t)UINT32_MAX)
         return fail(GS_ERR_INVALID, "capacity %lld outside [0, 2^32 - 1]", (long long)capacity);
     if (!scratch_bytes) return fail(GS_ERR_INVALID, "%s: scratch_bytes is NULL", fn);
@@ -187,7 +228,7 @@ gs_status gs_bin_and_sort_ex(const gs_camera* cam, int32_t n, const float* xy_de
     *n_entries = 0;
     if (n == 0) return GS_OK;
     hipStream_t st = (hipStream_t)stream;
-    if (gs_status e = hip_check(gs::launch_bin_and_sort(*cam, n, (const float4*)xy_depth, (const float4*)conic_op,
+    if (gs_status e = hip_check(gs::launch_bin_and_sort(*cam, 1, n, (const float4*)xy_depth, (const float4*)conic_op,
                                                         tiles_touched, keys, point_list, (uint32_t)capacity, s,
                                                         nullptr, flags, st),
                                 "bin_and_sort launch"))
@@ -215,27 +256,36 @@ gs_status gs_bin_and_sort(const gs_camera* cam, int32_t n, const float* xy_depth
                               scratch_bytes, n_entries, GS_TILES_SQUARE, stream);
 }
 
-gs_status gs_bin_and_sort_async_ex(const gs_camera* cam, int32_t n, const float* xy_depth, const float* conic_op,
-                                   const uint32_t* tiles_touched, uint64_t* keys, uint32_t* point_list,
-                                   int64_t capacity, void* scratch, size_t* scratch_bytes,
-                                   uint64_t* n_entries_dev, uint32_t flags, void* stream) {
+gs_status gs_bin_and_sort_views_async(const gs_camera* cam, int32_t n_views, int32_t n, const float* xy_depth,
+                                      const float* conic_op, const uint32_t* tiles_touched, uint64_t* keys,
+                                      uint32_t* point_list, int64_t capacity, void* scratch, size_t* scratch_bytes,
+                                      uint64_t* n_entries_dev, uint32_t flags, void* stream) {
     g_last_error.clear();
     gs::BinScratch s{};
     bool query = false;
     if (gs_status e = bin_args("gs_bin_and_sort_async", cam, n, xy_depth, tiles_touched, keys, point_list,
-                               capacity, scratch, scratch_bytes, &query, &s))
+                               capacity, scratch, scratch_bytes, &query, &s, n_views))
         return e;
     if (query) return GS_OK;
-    if (gs_status e = tile_test_args("gs_bin_and_sort_async", n, conic_op, flags)) return e;
+    const int32_t n_all = n * n_views;
+    if (gs_status e = tile_test_args("gs_bin_and_sort_async", n_all, conic_op, flags)) return e;
     if (!n_entries_dev || ((uintptr_t)n_entries_dev & 7))
         return fail(GS_ERR_INVALID, "gs_bin_and_sort_async: n_entries_dev must be an 8-byte aligned device pointer");
     hipStream_t st = (hipStream_t)stream;
-    if (n == 0)
+    if (n_all == 0)
         return hip_check(gs::launch_fill_u32((uint32_t*)n_entries_dev, 2, 0u, st), "entry count clear");
-    return hip_check(gs::launch_bin_and_sort(*cam, n, (const float4*)xy_depth, (const float4*)conic_op,
+    return hip_check(gs::launch_bin_and_sort(*cam, n_views, n_all, (const float4*)xy_depth, (const float4*)conic_op,
                                              tiles_touched, keys, point_list, (uint32_t)capacity, s, n_entries_dev,
                                              flags, st),
                      "bin_and_sort launch");
+}
+
+gs_status gs_bin_and_sort_async_ex(const gs_camera* cam, int32_t n, const float* xy_depth, const float* conic_op,
+                                   const uint32_t* tiles_touched, uint64_t* keys, uint32_t* point_list,
+                                   int64_t capacity, void* scratch, size_t* scratch_bytes,
+                                   uint64_t* n_entries_dev, uint32_t flags, void* stream) {
+    return gs_bin_and_sort_views_async(cam, 1, n, xy_depth, conic_op, tiles_touched, keys, point_list, capacity,
+                                       scratch, scratch_bytes, n_entries_dev, flags, stream);
 }
 
 gs_status gs_bin_and_sort_async(const gs_camera* cam, int32_t n, const float* xy_depth,
@@ -319,11 +369,13 @@ gs_status gs_tile_ranges_async(const gs_camera* cam, const uint64_t* keys, const
                      "tile ranges launch");
 }
 
-gs_status gs_tile_ranges_ex(const gs_camera* cam, const uint64_t* keys, int64_t n_entries,
+gs_status gs_tile_ranges_ex(const gs_camera* cam, int32_t n_views, const uint64_t* keys, int64_t n_entries,
                             const uint64_t* n_entries_dev, int64_t capacity, uint32_t* ranges,
                             uint32_t* tile_order, uint32_t* chunks, void* stream) {
     g_last_error.clear();
     if (gs_status s = check_camera(cam)) return s;
+    if (n_views < 1 || n_views > GS_MAX_VIEWS)
+        return fail(GS_ERR_INVALID, "gs_tile_ranges_ex: n_views = %d outside [1, %d]", n_views, GS_MAX_VIEWS);
     if (capacity < 0 || capacity > (int64_t)UINT32_MAX)
         return fail(GS_ERR_INVALID, "capacity %lld outside [0, 2^32 - 1]", (long long)capacity);
     if (!n_entries_dev && (n_entries < 0 || n_entries > capacity))
@@ -331,7 +383,7 @@ gs_status gs_tile_ranges_ex(const gs_camera* cam, const uint64_t* keys, int64_t 
                     (long long)capacity);
     if (!ranges || (capacity > 0 && !keys) || ((uintptr_t)n_entries_dev & 7) || ((uintptr_t)chunks & 15))
         return fail(GS_ERR_INVALID, "gs_tile_ranges_ex: NULL or misaligned pointer");
-    const int n_tiles = gs::tiles_x(*cam) * gs::tiles_y(*cam);
+    const int n_tiles = gs::tiles_x(*cam) * gs::tiles_y(*cam) * n_views;
     return hip_check(gs::launch_tile_ranges(keys, n_entries_dev ? 0u : (uint32_t)n_entries, n_entries_dev,
                                             (uint32_t)capacity, n_tiles, ranges, tile_order, chunks,
                                             (hipStream_t)stream),
@@ -349,20 +401,22 @@ gs_status gs_composite_fwd(const gs_camera* cam, const uint32_t* ranges, const u
     if (((uintptr_t)xy_depth | (uintptr_t)conic_op | (uintptr_t)rgb) & 15)
         return fail(GS_ERR_INVALID, "gs_composite_fwd: float4 inputs must be 16-byte aligned");
     const float3 b = make_float3(bg[0], bg[1], bg[2]);
-    return hip_check(gs::launch_composite_fwd(*cam, ranges, point_list, (const float4*)xy_depth,
+    return hip_check(gs::launch_composite_fwd(*cam, 1, ranges, point_list, (const float4*)xy_depth,
                                               (const float4*)conic_op, (const float4*)rgb, b, image,
                                               final_T, n_contrib, n_examined, tile_order, nullptr, 0u,
                                               nullptr, nullptr, (hipStream_t)stream),
                      "composite fwd launch");
 }
 
-gs_status gs_composite_fwd_ex(const gs_camera* cam, const uint32_t* ranges, const uint32_t* point_list,
-                              const float* xy_depth, const float* conic_op, const float* rgb,
-                              const float bg[3], float* image, float* final_T, uint32_t* n_contrib,
+gs_status gs_composite_fwd_ex(const gs_camera* cam, int32_t n_views, const uint32_t* ranges,
+                              const uint32_t* point_list, const float* xy_depth, const float* conic_op,
+                              const float* rgb, const float bg[3], float* image, float* final_T, uint32_t* n_contrib,
                               uint32_t* n_examined, const uint32_t* tile_order, int64_t capacity,
                               float* ckpt, const uint32_t* chunks, void* part, void* stream) {
     g_last_error.clear();
-    if (!ckpt && !chunks)
+    if (n_views < 1 || n_views > GS_MAX_VIEWS)
+        return fail(GS_ERR_INVALID, "gs_composite_fwd_ex: n_views = %d outside [1, %d]", n_views, GS_MAX_VIEWS);
+    if (!ckpt && !chunks && n_views == 1)
         return gs_composite_fwd(cam, ranges, point_list, xy_depth, conic_op, rgb, bg, image, final_T, n_contrib,
                                 n_examined, tile_order, stream);
     if (gs_status s = check_camera(cam)) return s;
@@ -375,16 +429,17 @@ gs_status gs_composite_fwd_ex(const gs_camera* cam, const uint32_t* ranges, cons
          (uintptr_t)part) & 15)
         return fail(GS_ERR_INVALID, "gs_composite_fwd_ex: float4 buffers must be 16-byte aligned");
     const float3 b = make_float3(bg[0], bg[1], bg[2]);
-    return hip_check(gs::launch_composite_fwd(*cam, ranges, point_list, (const float4*)xy_depth,
+    return hip_check(gs::launch_composite_fwd(*cam, n_views, ranges, point_list, (const float4*)xy_depth,
                                               (const float4*)conic_op, (const float4*)rgb, b, image,
                                               final_T, n_contrib, n_examined, tile_order, (float4*)ckpt,
                                               (uint32_t)capacity, chunks, part, (hipStream_t)stream),
                      "composite fwd launch");
 }
 
-size_t gs_composite_part_bytes(const gs_camera* cam, int64_t capacity) {
+size_t gs_composite_part_bytes(const gs_camera* cam, int32_t n_views, int64_t capacity) {
     if (!cam || check_camera(cam) != GS_OK || capacity < 0 || capacity > (int64_t)UINT32_MAX) return 0;
-    return gs::composite_part_bytes(*cam, (uint32_t)capacity);
+    if (n_views < 1 || n_views > GS_MAX_VIEWS) return 0;
+    return gs::composite_part_bytes(*cam, n_views, (uint32_t)capacity);
 }
 
 gs_status gs_composite_bwd(const gs_camera* cam, int32_t n, const uint32_t* ranges,
@@ -404,7 +459,7 @@ gs_status gs_composite_bwd(const gs_camera* cam, int32_t n, const uint32_t* rang
          (uintptr_t)grad_rgb) & 15 || ((uintptr_t)grad_mean2d & 7))
         return fail(GS_ERR_INVALID, "gs_composite_bwd: misaligned vector buffer");
     const float3 b = make_float3(bg[0], bg[1], bg[2]);
-    return hip_check(gs::launch_composite_bwd(*cam, n, ranges, point_list, (const float4*)xy_depth,
+    return hip_check(gs::launch_composite_bwd(*cam, 1, n, ranges, point_list, (const float4*)xy_depth,
                                               (const float4*)conic_op, (const float4*)rgb, b, final_T,
                                               n_contrib, dL_dimage, (float2*)grad_mean2d,
                                               (float4*)grad_conic_op, (float4*)grad_rgb, tile_order,
@@ -412,7 +467,7 @@ gs_status gs_composite_bwd(const gs_camera* cam, int32_t n, const uint32_t* rang
                      "composite bwd launch");
 }
 
-gs_status gs_composite_bwd_ex(const gs_camera* cam, int32_t n, const uint32_t* ranges,
+gs_status gs_composite_bwd_ex(const gs_camera* cam, int32_t n_views, int32_t n, const uint32_t* ranges,
                               const uint32_t* point_list, const uint32_t* chunks, int64_t capacity,
                               const float* xy_depth, const float* conic_op, const float* rgb,
                               const float bg[3], const float* image, const float* final_T,
@@ -420,6 +475,8 @@ gs_status gs_composite_bwd_ex(const gs_camera* cam, int32_t n, const uint32_t* r
                               float* grad_mean2d, float* grad_conic_op, float* grad_rgb, void* stream) {
     g_last_error.clear();
     if (gs_status s = check_camera(cam)) return s;
+    if (n_views < 1 || n_views > GS_MAX_VIEWS)
+        return fail(GS_ERR_INVALID, "gs_composite_bwd_ex: n_views = %d outside [1, %d]", n_views, GS_MAX_VIEWS);
     if (n < 0 || n > GS_MAX_GAUSSIANS) return fail(GS_ERR_INVALID, "n = %d outside [0, %d]", n, GS_MAX_GAUSSIANS);
     if (capacity < 0 || capacity > (int64_t)UINT32_MAX)
         return fail(GS_ERR_INVALID, "gs_composite_bwd_ex: capacity %lld outside [0, 2^32 - 1]", (long long)capacity);
@@ -432,7 +489,7 @@ gs_status gs_composite_bwd_ex(const gs_camera* cam, int32_t n, const uint32_t* r
          (uintptr_t)grad_rgb | (uintptr_t)ckpt | (uintptr_t)chunks) & 15 || ((uintptr_t)grad_mean2d & 7))
         return fail(GS_ERR_INVALID, "gs_composite_bwd_ex: misaligned vector buffer");
     const float3 b = make_float3(bg[0], bg[1], bg[2]);
-    return hip_check(gs::launch_composite_bwd(*cam, n, ranges, point_list, (const float4*)xy_depth,
+    return hip_check(gs::launch_composite_bwd(*cam, n_views, n, ranges, point_list, (const float4*)xy_depth,
                                               (const float4*)conic_op, (const float4*)rgb, b, final_T,
                                               n_contrib, dL_dimage, (float2*)grad_mean2d,
                                               (float4*)grad_conic_op, (float4*)grad_rgb, nullptr, chunks,

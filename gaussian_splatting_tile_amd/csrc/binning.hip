@@ -160,7 +160,7 @@ template <bool ELLIPSE>
 __global__ __launch_bounds__(kDupThreads) void k_duplicate(
     const float4* __restrict__ xy_depth, const float4* __restrict__ conic_op, const uint32_t* __restrict__ offsets,
     const uint32_t* __restrict__ perm, const uint32_t* __restrict__ first_owner, int n,
-    const uint64_t* __restrict__ total, uint32_t capacity, int TX, int TY, int passes,
+    const uint64_t* __restrict__ total, uint32_t capacity, int TX, int TY, uint32_t n_view, int passes,
     uint64_t* __restrict__ keys, uint32_t* __restrict__ values, uint32_t* __restrict__ counts) {
     constexpr int kPer = kDupTile / kDupThreads;  // slots per thread in the scan
     __shared__ uint32_t s_owner[kDupTile];
@@ -243,7 +243,9 @@ __global__ __launch_bounds__(kDupThreads) void k_duplicate(
                 tx = (uint32_t)sp.x0 + (uint32_t)r;
                 ty = (uint32_t)sp.y0 + q;
             }
-            t = ty * (uint32_t)TX + tx;
+            // splat g of view g / n_view lists its tiles in that view's band
+            const uint32_t band = g / n_view;
+            t = (band * (uint32_t)TY + ty) * (uint32_t)TX + tx;
             keys[e] = ((uint64_t)t << 32) | (uint64_t)__float_as_uint(rec.z);
             values[e] = g;
         }
@@ -340,21 +342,27 @@ __global__ __launch_bounds__(kSortThreads) void k_count_digits(const K* __restri
 // One pass's 256 rows of per-tile digit counts (row d at counts + d *
 // stride): hist[d] = the total of the row's first nblk tiles, and the row is
 // replaced in place by its exclusive prefix over tiles. nblk covers the
-// usable entries (*total, capacity) when total is given. One wave per row.
+// usable entries (*total, capacity) when total is given. One workgroup of
+// kScanThreads per row, each thread a run of consecutive tiles (a row can
+// be tens of thousands of tiles long when many views are binned at once).
 // If tt_counts is given (the last depth pass), its rows are scanned the same
 // way in 64 bits into tt_prefix, with totals in tt_hist.
-__global__ __launch_bounds__(256) void k_count_scan(uint32_t* __restrict__ counts, int stride, int nblk,
-                                                    const uint64_t* __restrict__ total, uint32_t capacity,
-                                                    int tile_keys, uint32_t* __restrict__ hist,
-                                                    const uint32_t* __restrict__ tt_counts,
-                                                    uint64_t* __restrict__ tt_prefix,
-                                                    uint64_t* __restrict__ tt_hist) {
-    const int lane = threadIdx.x & 63;
-    const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+constexpr int kScanThreads = 1024;
+__global__ __launch_bounds__(kScanThreads) void k_count_scan(uint32_t* __restrict__ counts, int stride, int nblk,
+                                                             const uint64_t* __restrict__ total, uint32_t capacity,
+                                                             int tile_keys, uint32_t* __restrict__ hist,
+                                                             const uint32_t* __restrict__ tt_counts,
+                                                             uint64_t* __restrict__ tt_prefix,
+                                                             uint64_t* __restrict__ tt_hist) {
+    constexpr int kWaves = kScanThreads / 64;
+    __shared__ uint32_t s_w[kWaves];
+    __shared__ uint64_t s_w64[kWaves];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r = blockIdx.x;
     if (total) nblk = (int)((usable_entries(total, capacity) + (uint32_t)tile_keys - 1) / (uint32_t)tile_keys);
     uint32_t* row = counts + (size_t)r * stride;
-    const int per = (nblk + 63) / 64;
-    const int i0 = min(lane * per, nblk), i1 = min(i0 + per, nblk);
+    const int per = (nblk + kScanThreads - 1) / kScanThreads;
+    const int i0 = min(tid * per, nblk), i1 = min(i0 + per, nblk);
     uint32_t sum = 0;
     for (int i = i0; i < i1; ++i) sum += row[i];
     uint32_t incl = sum;
@@ -363,14 +371,21 @@ __global__ __launch_bounds__(256) void k_count_scan(uint32_t* __restrict__ count
         const uint32_t y = (uint32_t)__shfl_up((int)incl, off, 64);
         if (lane >= off) incl += y;
     }
-    uint32_t run = incl - sum;
+    if (lane == 63) s_w[wave] = incl;
+    __syncthreads();
+    uint32_t pre = 0, row_total = 0;
+    for (int w = 0; w < kWaves; ++w) {
+        const uint32_t x = s_w[w];
+        pre += w < wave ? x : 0u;
+        row_total += x;
+    }
+    uint32_t run = pre + incl - sum;
     for (int i = i0; i < i1; ++i) {
         const uint32_t c = row[i];
         row[i] = run;
         run += c;
     }
-    const uint32_t row_total = (uint32_t)__shfl((int)incl, 63, 64);
-    if (lane == 0) hist[r] = row_total;
+    if (tid == 0) hist[r] = row_total;
     if (tt_counts) {
         const uint32_t* trow = tt_counts + (size_t)r * stride;
         uint64_t* prow = tt_prefix + (size_t)r * stride;
@@ -382,12 +397,20 @@ __global__ __launch_bounds__(256) void k_count_scan(uint32_t* __restrict__ count
             const uint64_t y = shfl_up_u64(tincl, off);
             if (lane >= off) tincl += y;
         }
-        uint64_t trun = tincl - tsum;
+        if (lane == 63) s_w64[wave] = tincl;
+        __syncthreads();
+        uint64_t tpre = 0, ttot = 0;
+        for (int w = 0; w < kWaves; ++w) {
+            const uint64_t x = s_w64[w];
+            tpre += w < wave ? x : 0ull;
+            ttot += x;
+        }
+        uint64_t trun = tpre + tincl - tsum;
         for (int i = i0; i < i1; ++i) {
             prow[i] = trun;
             trun += trow[i];
         }
-        if (lane == 63) tt_hist[r] = tincl;
+        if (tid == 0) tt_hist[r] = ttot;
     }
 }
 
@@ -724,7 +747,7 @@ size_t bin_scratch_layout(int n, int64_t capacity, BinScratch* out, void* base) 
     return off;
 }
 
-hipError_t launch_bin_and_sort(const gs_camera& cam, int n, const float4* xy_depth,
+hipError_t launch_bin_and_sort(const gs_camera& cam, int n_views, int n, const float4* xy_depth,
                                const float4* conic_op, const uint32_t* tiles_touched, uint64_t* keys,
                                uint32_t* values, uint32_t capacity, const BinScratch& s, uint64_t* n_dev,
                                uint32_t flags, hipStream_t stream) {
@@ -748,7 +771,7 @@ hipError_t launch_bin_and_sort(const gs_camera& cam, int n, const float4* xy_dep
             hipLaunchKernelGGL((k_count_digits<uint32_t, kGaussItems, false>), dim3(nbg), dim3(kSortThreads), 0,
                                stream, s.gk[src], (uint32_t)n, (const uint64_t*)nullptr, 0u, 8 * p, cnt,
                                (const uint32_t*)nullptr, (const uint32_t*)nullptr, (uint32_t*)nullptr);
-        hipLaunchKernelGGL(k_count_scan, dim3(kRadix / 4), dim3(256), 0, stream, cnt, (int)nbg, (int)nbg,
+        hipLaunchKernelGGL(k_count_scan, dim3(kRadix), dim3(kScanThreads), 0, stream, cnt, (int)nbg, (int)nbg,
                            (const uint64_t*)nullptr, 0u, kGaussTile, s.gauss_hist + p * kRadix,
                            last ? (const uint32_t*)s.tt_counts : nullptr, last ? s.tt_prefix : nullptr,
                            last ? s.tt_hist : nullptr);
@@ -765,7 +788,8 @@ hipError_t launch_bin_and_sort(const gs_camera& cam, int n, const float4* xy_dep
     // capacity; the kernels read E and do nothing when it exceeds capacity.
     if (nbe == 0) return hipGetLastError();
     int tile_bits = 0;
-    while ((1 << tile_bits) < tiles_x(cam) * tiles_y(cam)) ++tile_bits;
+    while ((int64_t)1 << tile_bits < (int64_t)tiles_x(cam) * tiles_y(cam) * n_views) ++tile_bits;
+    const uint32_t n_view = (uint32_t)max(1, n / n_views);  // splats per view (n_views divides n)
     const int passes = tile_pass_count(tile_bits);
     // entries start in the tmp pair when the pass count is odd, so the last
     // pass always writes (keys, values)
@@ -776,18 +800,18 @@ hipError_t launch_bin_and_sort(const gs_camera& cam, int n, const float4* xy_dep
     if (flags & kTilesEllipse)
         hipLaunchKernelGGL(k_duplicate<true>, dim3(nbe), dim3(kDupThreads), 0, stream, xy_depth, conic_op,
                            s.offsets, s.gv[0], s.first_owner, n, (const uint64_t*)s.total, capacity, tiles_x(cam),
-                           tiles_y(cam), passes, kin, vin, s.entry_counts);
+                           tiles_y(cam), n_view, passes, kin, vin, s.entry_counts);
     else
         hipLaunchKernelGGL(k_duplicate<false>, dim3(nbe), dim3(kDupThreads), 0, stream, xy_depth, conic_op,
                            s.offsets, s.gv[0], s.first_owner, n, (const uint64_t*)s.total, capacity, tiles_x(cam),
-                           tiles_y(cam), passes, kin, vin, s.entry_counts);
+                           tiles_y(cam), n_view, passes, kin, vin, s.entry_counts);
     for (int p = 0; p < passes; ++p) {
         uint32_t* cnt = s.entry_counts + (size_t)p * kRadix * nbe;
         if (p > 0)
             hipLaunchKernelGGL((k_count_digits<uint64_t, kEntryItems, false>), dim3(nbe), dim3(kSortThreads), 0,
                                stream, kin, 0u, (const uint64_t*)s.total, capacity, 32 + 8 * p, cnt,
                                (const uint32_t*)nullptr, (const uint32_t*)nullptr, (uint32_t*)nullptr);
-        hipLaunchKernelGGL(k_count_scan, dim3(kRadix / 4), dim3(256), 0, stream, cnt, (int)nbe, 0,
+        hipLaunchKernelGGL(k_count_scan, dim3(kRadix), dim3(kScanThreads), 0, stream, cnt, (int)nbe, 0,
                            (const uint64_t*)s.total, capacity, kEntryTile, s.entry_hist + p * kRadix,
                            (const uint32_t*)nullptr, (uint64_t*)nullptr, (uint64_t*)nullptr);
         hipLaunchKernelGGL((k_radix_pass<uint64_t, kEntryItems, false>), dim3(nbe), dim3(kSortThreads), 0, stream,

@@ -174,6 +174,19 @@ __device__ __forceinline__ uint32_t quadrant_blocks(int w) {
     return 0x33u << (2 * (w & 1) + 8 * (w >> 1));
 }
 
+// A stack of views shares one tile grid: view b is the band of tile rows
+// [b TYb, b TYb + TYb), and its pixels keep their own coordinates (the
+// splat records of a view are in that view's pixels). Tile column, row
+// within the band, and band of a tile id.
+struct TileAt {
+    int tx, ty, band;
+};
+__device__ __forceinline__ TileAt tile_at(int tile, int TX, int TYb) {
+    const int row = tile / TX;
+    const int band = row / TYb;
+    return {tile - row * TX, row - band * TYb, band};
+}
+
 // Stages list entries [base, min(base + kBatch, end)) into LDS, one per
 // thread: the conic with -1/2 folded in, the centre and colour, and the
 // 4 x 4 blocks of the tile the splat reaches.
@@ -287,7 +300,7 @@ __device__ __forceinline__ size_t part_row(uint32_t start, uint32_t len, uint32_
 // k_composite_fwd_resolve, which writes the outputs of its pixels.
 template <bool kItems>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) void k_composite_fwd(
-    const int W, const int H, const int TX, const uint32_t* __restrict__ ranges,
+    const int W, const int H, const int TX, const int TYb, const uint32_t* __restrict__ ranges,
     const uint32_t* __restrict__ point_list, const float4* __restrict__ xy_depth,
     const float4* __restrict__ conic_op, const float4* __restrict__ rgb, const float3 bg,
     float* __restrict__ image, float* __restrict__ final_T, uint32_t* __restrict__ n_contrib,
@@ -323,7 +336,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int tx = tile % TX, ty = tile / TX;
+    const TileAt ta = tile_at(tile, TX, TYb);
+    const int tx = ta.tx, ty = ta.ty;
+    {  // this view's outputs
+        const size_t view_px = (size_t)W * H;
+        image += (size_t)ta.band * 3 * view_px;
+        final_T += (size_t)ta.band * view_px;
+        n_contrib += (size_t)ta.band * view_px;
+        if (n_examined) n_examined += (size_t)ta.band * view_px;
+    }
     const int px = tx * kTile + 8 * (wave & 1) + (lane & 7);
     const int py = ty * kTile + 8 * (wave >> 1) + (lane >> 3);
     const uint32_t qblocks = quadrant_blocks(wave);
@@ -373,7 +394,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
 // the whole-list walk does, stopping where that walk stops; if not and this
 // is the list's last chunk, the combined state is final.
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) void k_composite_fwd_resolve(
-    const int W, const int H, const int TX, const uint32_t* __restrict__ point_list,
+    const int W, const int H, const int TX, const int TYb, const uint32_t* __restrict__ point_list,
     const float4* __restrict__ xy_depth, const float4* __restrict__ conic_op, const float4* __restrict__ rgb,
     const float3 bg, float* __restrict__ image, float* __restrict__ final_T, uint32_t* __restrict__ n_contrib,
     uint32_t* __restrict__ n_examined, float4* __restrict__ ckpt, const uint32_t* __restrict__ chunks,
@@ -394,7 +415,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int tx = tile % TX, ty = tile / TX;
+    const TileAt ta = tile_at(tile, TX, TYb);
+    const int tx = ta.tx, ty = ta.ty;
+    {  // this view's outputs
+        const size_t view_px = (size_t)W * H;
+        image += (size_t)ta.band * 3 * view_px;
+        final_T += (size_t)ta.band * view_px;
+        n_contrib += (size_t)ta.band * view_px;
+        if (n_examined) n_examined += (size_t)ta.band * view_px;
+    }
     const int px = tx * kTile + 8 * (wave & 1) + (lane & 7);
     const int py = ty * kTile + 8 * (wave >> 1) + (lane >> 3);
     const uint32_t qblocks = quadrant_blocks(wave);
@@ -523,7 +552,7 @@ __host__ __device__ constexpr int part_swizzle(int t) { return t < 8 ? ((t & 2) 
 // checkpoint there: T, and g.R = g.(image - accumulated colour).
 template <bool kChunked>
 __global__ __launch_bounds__(256) void k_composite_bwd(
-    const int W, const int H, const int TX, const uint32_t* __restrict__ ranges,
+    const int W, const int H, const int TX, const int TYb, const uint32_t* __restrict__ ranges,
     const uint32_t* __restrict__ point_list, const float4* __restrict__ xy_depth,
     const float4* __restrict__ conic_op, const float4* __restrict__ rgb, const float3 bg,
     const float* __restrict__ final_T, const uint32_t* __restrict__ n_contrib,
@@ -562,7 +591,15 @@ __global__ __launch_bounds__(256) void k_composite_bwd(
     const int wave = tid >> 6;
     const bool lane_b0 = (lane & 1) != 0, lane_b1 = (lane & 2) != 0, lane_b2 = (lane & 4) != 0,
                lane_b3 = (lane & 8) != 0;
-    const int tx = tile % TX, ty = tile / TX;
+    const TileAt ta = tile_at(tile, TX, TYb);
+    const int tx = ta.tx, ty = ta.ty;
+    {  // this view's pixels
+        const size_t view_px = (size_t)W * H;
+        final_T += (size_t)ta.band * view_px;
+        n_contrib += (size_t)ta.band * view_px;
+        dL_dimage += (size_t)ta.band * 3 * view_px;
+        if (image) image += (size_t)ta.band * 3 * view_px;
+    }
     const int px = tx * kTile + 8 * (wave & 1) + (lane & 7);
     const int py = ty * kTile + 8 * (wave >> 1) + (lane >> 3);
     const uint32_t qblocks = quadrant_blocks(wave);
@@ -747,41 +784,41 @@ __global__ __launch_bounds__(256) void k_composite_bwd(
 
 }  // namespace
 
-hipError_t launch_composite_fwd(const gs_camera& cam, const uint32_t* ranges,
+hipError_t launch_composite_fwd(const gs_camera& cam, int n_views, const uint32_t* ranges,
                                 const uint32_t* point_list, const float4* xy_depth,
                                 const float4* conic_op, const float4* rgb, float3 bg,
                                 float* image, float* final_T, uint32_t* n_contrib,
                                 uint32_t* n_examined, const uint32_t* tile_order, float4* ckpt,
                                 uint32_t capacity, const uint32_t* chunks, void* part, hipStream_t stream) {
-    const int TX = tiles_x(cam), TY = tiles_y(cam);
-    const uint32_t n_tiles = (uint32_t)(TX * TY);
+    const int TX = tiles_x(cam), TYb = tiles_y(cam);
+    const uint32_t n_tiles = (uint32_t)(TX * TYb * n_views);
     const uint32_t slots = (uint32_t)((capacity + (uint32_t)kChunk - 1u) / (uint32_t)kChunk);
     const uint32_t ckpt_slots = ckpt ? slots : 0u;
     if (chunks) {
         float4* const p4 = (float4*)part;
         uint32_t* const pl = (uint32_t*)(p4 + (size_t)(slots + n_tiles) * kChunk);
         hipLaunchKernelGGL(k_composite_fwd<true>, dim3(slots + n_tiles), dim3(256), 0, stream, cam.width, cam.height,
-                           TX, (const uint32_t*)nullptr, point_list, xy_depth, conic_op, rgb, bg, image, final_T,
-                           n_contrib, n_examined, (const uint32_t*)nullptr, ckpt, ckpt_slots, chunks, n_tiles, slots,
-                           p4, pl);
+                           TX, TYb, (const uint32_t*)nullptr, point_list, xy_depth, conic_op, rgb, bg, image,
+                           final_T, n_contrib, n_examined, (const uint32_t*)nullptr, ckpt, ckpt_slots, chunks,
+                           n_tiles, slots, p4, pl);
         hipLaunchKernelGGL(k_composite_fwd_resolve, dim3(slots + n_tiles), dim3(256), 0, stream, cam.width,
-                           cam.height, TX, point_list, xy_depth, conic_op, rgb, bg, image, final_T, n_contrib,
+                           cam.height, TX, TYb, point_list, xy_depth, conic_op, rgb, bg, image, final_T, n_contrib,
                            n_examined, ckpt, chunks, n_tiles, slots, (const float4*)p4, (const uint32_t*)pl);
     } else {
         hipLaunchKernelGGL(k_composite_fwd<false>, dim3(n_tiles), dim3(256), 0, stream, cam.width, cam.height,
-                           TX, ranges, point_list, xy_depth, conic_op, rgb, bg, image, final_T, n_contrib,
+                           TX, TYb, ranges, point_list, xy_depth, conic_op, rgb, bg, image, final_T, n_contrib,
                            n_examined, tile_order, ckpt, ckpt_slots, (const uint32_t*)nullptr, n_tiles, slots,
                            (float4*)nullptr, (uint32_t*)nullptr);
     }
     return hipGetLastError();
 }
 
-size_t composite_part_bytes(const gs_camera& cam, uint32_t capacity) {
+size_t composite_part_bytes(const gs_camera& cam, int n_views, uint32_t capacity) {
     const size_t slots = (capacity + (size_t)kChunk - 1) / kChunk;
-    return (slots + (size_t)tiles_x(cam) * tiles_y(cam)) * kChunk * (sizeof(float4) + sizeof(uint32_t));
+    return (slots + (size_t)tiles_x(cam) * tiles_y(cam) * n_views) * kChunk * (sizeof(float4) + sizeof(uint32_t));
 }
 
-hipError_t launch_composite_bwd(const gs_camera& cam, int n, const uint32_t* ranges,
+hipError_t launch_composite_bwd(const gs_camera& cam, int n_views, int n, const uint32_t* ranges,
                                 const uint32_t* point_list, const float4* xy_depth,
                                 const float4* conic_op, const float4* rgb, float3 bg,
                                 const float* final_T, const uint32_t* n_contrib,
@@ -792,18 +829,18 @@ hipError_t launch_composite_bwd(const gs_camera& cam, int n, const uint32_t* ran
     if (n > 0)
         hipLaunchKernelGGL(k_zero_grads, dim3((n + 255) / 256), dim3(256), 0, stream, grad_mean2d,
                            grad_conic_op, grad_rgb, n);
-    const int TX = tiles_x(cam), TY = tiles_y(cam);
-    const uint32_t n_tiles = (uint32_t)(TX * TY);
+    const int TX = tiles_x(cam), TYb = tiles_y(cam);
+    const uint32_t n_tiles = (uint32_t)(TX * TYb * n_views);
     if (chunks) {
         // at most one chunk per non-empty list beyond its full ones
         const uint32_t slots = (uint32_t)((capacity + (uint32_t)kChunk - 1u) / (uint32_t)kChunk);
         hipLaunchKernelGGL(k_composite_bwd<true>, dim3(slots + n_tiles), dim3(256), 0, stream, cam.width,
-                           cam.height, TX, ranges, point_list, xy_depth, conic_op, rgb, bg, final_T, n_contrib,
+                           cam.height, TX, TYb, ranges, point_list, xy_depth, conic_op, rgb, bg, final_T, n_contrib,
                            dL_dimage, (float*)grad_mean2d, (float*)grad_conic_op, (float*)grad_rgb, tile_order,
                            chunks, slots, n_tiles, ckpt, image);
     } else {
         hipLaunchKernelGGL(k_composite_bwd<false>, dim3(n_tiles), dim3(256), 0, stream, cam.width, cam.height,
-                           TX, ranges, point_list, xy_depth, conic_op, rgb, bg, final_T, n_contrib, dL_dimage,
+                           TX, TYb, ranges, point_list, xy_depth, conic_op, rgb, bg, final_T, n_contrib, dL_dimage,
                            (float*)grad_mean2d, (float*)grad_conic_op, (float*)grad_rgb, tile_order,
                            (const uint32_t*)nullptr, 0u, n_tiles, (const float4*)nullptr, (const float*)nullptr);
     }

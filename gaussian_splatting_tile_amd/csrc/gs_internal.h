@@ -117,6 +117,16 @@ constexpr uint32_t kTilesEllipse = 1u;
 
 // ---- launchers (each returns the launch's hipError_t) ----
 
+// A stack of cameras passed by value to a kernel (at most GS_MAX_VIEWS).
+struct CameraSet {
+    gs_camera cam[GS_MAX_VIEWS];
+    int n;
+};
+// Records of n Gaussians for every camera of the set, camera v's at v n + g.
+hipError_t launch_preprocess_views(const CameraSet& cams, int n, const float* means, const float* scales,
+                                   const float* quats, const float* opacity, const float* sh, int sh_degree,
+                                   const float* rgb_in, float4* xy_depth, float4* conic_op, float4* rgb,
+                                   uint32_t* tiles_touched, uint32_t flags, hipStream_t stream);
 hipError_t launch_preprocess(const gs_camera& cam, int n, const float* means, const float* scales,
                              const float* quats, const float* opacity, const float* sh,
                              int sh_degree, const float* rgb_in, float4* xy_depth,
@@ -154,8 +164,10 @@ size_t bin_scratch_layout(int n, int64_t capacity, BinScratch* out, void* base);
 // The whole binning: stable depth order of the splats with the scan of
 // their tile counts in that order (E -> *s.total, and *n_dev if given), duplication,
 // stable sort on the tile-id bits into (keys, values). Never waits on the
-// host. When E > capacity nothing is written to keys/values.
-hipError_t launch_bin_and_sort(const gs_camera& cam, int n, const float4* xy_depth,
+// host. When E > capacity nothing is written to keys/values. The n splats
+// may be a stack of n_views views of cam's size (n / n_views each, view v's
+// tiles in the band of rows [v TY, v TY + TY)).
+hipError_t launch_bin_and_sort(const gs_camera& cam, int n_views, int n, const float4* xy_depth,
                                const float4* conic_op, const uint32_t* tiles_touched, uint64_t* keys,
                                uint32_t* values, uint32_t capacity, const BinScratch& s, uint64_t* n_dev,
                                uint32_t flags, hipStream_t stream);
@@ -170,20 +182,22 @@ hipError_t launch_tile_ranges(const uint64_t* keys, uint32_t n_entries, const ui
                               int n_tiles, uint32_t* ranges, uint32_t* tile_order, uint32_t* chunks,
                               hipStream_t stream);
 
-// Compositing. With ckpt, the forward also stores the per-pixel state at
+// Compositing over a stack of n_views views of cam's size (each a band of
+// tiles_y(cam) tile rows; per-view planes one after another). With ckpt,
+// the forward also stores the per-pixel state at
 // every kChunk-entry boundary of a list and the backward runs one workgroup
 // per chunk of the schedule `chunks` (capacity: length of the sorted entry
 // arrays).
-hipError_t launch_composite_fwd(const gs_camera& cam, const uint32_t* ranges,
+hipError_t launch_composite_fwd(const gs_camera& cam, int n_views, const uint32_t* ranges,
                                 const uint32_t* point_list, const float4* xy_depth,
                                 const float4* conic_op, const float4* rgb, float3 bg,
                                 float* image, float* final_T, uint32_t* n_contrib,
                                 uint32_t* n_examined, const uint32_t* tile_order, float4* ckpt,
                                 uint32_t capacity, const uint32_t* chunks, void* part, hipStream_t stream);
 // Bytes of the chunk partials the scheduled forward needs.
-size_t composite_part_bytes(const gs_camera& cam, uint32_t capacity);
+size_t composite_part_bytes(const gs_camera& cam, int n_views, uint32_t capacity);
 
-hipError_t launch_composite_bwd(const gs_camera& cam, int n, const uint32_t* ranges,
+hipError_t launch_composite_bwd(const gs_camera& cam, int n_views, int n, const uint32_t* ranges,
                                 const uint32_t* point_list, const float4* xy_depth,
                                 const float4* conic_op, const float4* rgb, float3 bg,
                                 const float* final_T, const uint32_t* n_contrib,

@@ -30,24 +30,25 @@ constexpr float kSh3c = 0.4570457994644658f;   // sqrt(21 / (2 pi)) / 4
 constexpr float kSh3d = 0.3731763325901154f;   // sqrt(7 / pi) / 4
 constexpr float kSh3e = 1.445305721320277f;    // sqrt(105 / pi) / 4
 
-__global__ __launch_bounds__(256) void k_preprocess(
-    const gs_camera cam, const int n, const float* __restrict__ means,
-    const float* __restrict__ scales, const float* __restrict__ quats,
-    const float* __restrict__ opacity, const float* __restrict__ sh, const int n_coef,
-    const float* __restrict__ rgb_in, float4* __restrict__ xy_depth, float4* __restrict__ conic_op,
-    float4* __restrict__ rgb_out, uint32_t* __restrict__ tiles_touched, const uint32_t flags) {
-    const int g = blockIdx.x * blockDim.x + threadIdx.x;
-    if (g >= n) return;
+// The splat record of Gaussian g seen by camera cam. The Gaussian's inputs
+// come from `in` (in.mean(c), in.quat(c), in.scale(c), in.opacity(),
+// in.sh(row), in.rgb(c)), read only once the splat survives the culls
+// before them; outputs are (0, 0, 0, 0) records and count 0 when culled.
+template <class In>
+__device__ __forceinline__ void project_splat(const gs_camera& cam, const In& in, const bool has_sh, const int n_coef,
+                                              const uint32_t flags, float4& o_xy, float4& o_co, float4& o_rgb,
+                                              uint32_t& count) {
     const int TX = (cam.width + kTile - 1) / kTile;
     const int TY = (cam.height + kTile - 1) / kTile;
     const float* W = cam.R;
 
-    float4 o_xy = make_float4(0.f, 0.f, 0.f, 0.f);
-    float4 o_co = o_xy, o_rgb = o_xy;
-    uint32_t count = 0;
+    o_xy = make_float4(0.f, 0.f, 0.f, 0.f);
+    o_co = o_xy;
+    o_rgb = o_xy;
+    count = 0;
 
     do {
-        const float mx = means[g], my = means[n + g], mz = means[2 * n + g];
+        const float mx = in.mean(0), my = in.mean(1), mz = in.mean(2);
 
         // World to camera.
         const float px = ((W[0] * mx + W[1] * my) + W[2] * mz) + cam.t[0];
@@ -72,7 +73,7 @@ __global__ __launch_bounds__(256) void k_preprocess(
         const float J12 = -(cam.fy * yj) / zz;
 
         // Normalised quaternion (w, x, y, z) to rotation.
-        float qw = quats[g], qx = quats[n + g], qy = quats[2 * n + g], qz = quats[3 * n + g];
+        float qw = in.quat(0), qx = in.quat(1), qy = in.quat(2), qz = in.quat(3);
         const float qn = sqrtf(((qw * qw + qx * qx) + qy * qy) + qz * qz);
         if (!(qn > 0.0f)) break;
         qw = qw / qn;
@@ -90,7 +91,7 @@ __global__ __launch_bounds__(256) void k_preprocess(
         const float r22 = 1.0f - 2.0f * (qx * qx + qy * qy);
 
         // M = R(q) S, Sigma = M M^T (symmetric; six distinct entries).
-        const float sx = scales[g], sy = scales[n + g], sz = scales[2 * n + g];
+        const float sx = in.scale(0), sy = in.scale(1), sz = in.scale(2);
         const float m00 = r00 * sx, m01 = r01 * sy, m02 = r02 * sz;
         const float m10 = r10 * sx, m11 = r11 * sy, m12 = r12 * sz;
         const float m20 = r20 * sx, m21 = r21 * sy, m22 = r22 * sz;
@@ -145,7 +146,7 @@ __global__ __launch_bounds__(256) void k_preprocess(
 
         // Colour.
         float col0, col1, col2;
-        if (sh != nullptr) {
+        if (has_sh) {
             float dx = mx - cam.campos[0], dy = my - cam.campos[1], dz = mz - cam.campos[2];
             const float dn = sqrtf((dx * dx + dy * dy) + dz * dz);
             const float x = dx / dn, y = dy / dn, z = dz / dn;
@@ -167,24 +168,23 @@ __global__ __launch_bounds__(256) void k_preprocess(
             Y[13] = -kSh3c * (x * ((4.0f * zz2 - xx) - yy));
             Y[14] = kSh3e * ((xx - yy) * z);
             Y[15] = -kSh3a * (x * (xx - 3.0f * yy));
-            const size_t stride = (size_t)n;
-            col0 = sh[0 * stride + g] * Y[0];
-            col1 = sh[1 * stride + g] * Y[0];
-            col2 = sh[2 * stride + g] * Y[0];
+            col0 = in.sh(0) * Y[0];
+            col1 = in.sh(1) * Y[0];
+            col2 = in.sh(2) * Y[0];
 #pragma unroll
             for (int k = 1; k < 16; ++k) {
                 if (k < n_coef) {
-                    col0 = col0 + sh[(size_t)(3 * k + 0) * stride + g] * Y[k];
-                    col1 = col1 + sh[(size_t)(3 * k + 1) * stride + g] * Y[k];
-                    col2 = col2 + sh[(size_t)(3 * k + 2) * stride + g] * Y[k];
+                    col0 = col0 + in.sh(3 * k + 0) * Y[k];
+                    col1 = col1 + in.sh(3 * k + 1) * Y[k];
+                    col2 = col2 + in.sh(3 * k + 2) * Y[k];
                 }
             }
         } else {
-            col0 = rgb_in[g];
-            col1 = rgb_in[n + g];
-            col2 = rgb_in[2 * n + g];
+            col0 = in.rgb(0);
+            col1 = in.rgb(1);
+            col2 = in.rgb(2);
         }
-        const float op = opacity[g];
+        const float op = in.opacity();
         if (!isfinite(op) || !isfinite(col0) || !isfinite(col1) || !isfinite(col2)) break;
 
         o_xy = make_float4(u, v, pz, r);
@@ -192,12 +192,93 @@ __global__ __launch_bounds__(256) void k_preprocess(
         o_rgb = make_float4(col0, col1, col2, 0.0f);
         count = (uint32_t)cnt;
     } while (false);
+}
 
+// Inputs read from the SoA arrays where they are needed.
+struct GlobalIn {
+    const float* __restrict__ means;
+    const float* __restrict__ scales;
+    const float* __restrict__ quats;
+    const float* __restrict__ opac;
+    const float* __restrict__ shs;
+    const float* __restrict__ rgbs;
+    size_t n, g;
+    __device__ float mean(int c) const { return means[c * n + g]; }
+    __device__ float scale(int c) const { return scales[c * n + g]; }
+    __device__ float quat(int c) const { return quats[c * n + g]; }
+    __device__ float opacity() const { return opac[g]; }
+    __device__ float sh(int row) const { return shs[row * n + g]; }
+    __device__ float rgb(int c) const { return rgbs[c * n + g]; }
+};
+
+// Inputs held in registers, read once for every camera of a stack.
+struct RegIn {
+    float m[3], s[3], q[4], o, c[48];
+    __device__ float mean(int i) const { return m[i]; }
+    __device__ float scale(int i) const { return s[i]; }
+    __device__ float quat(int i) const { return q[i]; }
+    __device__ float opacity() const { return o; }
+    __device__ float sh(int row) const { return c[row]; }
+    __device__ float rgb(int i) const { return c[i]; }
+};
+
+__global__ __launch_bounds__(256) void k_preprocess(
+    const gs_camera cam, const int n, const float* __restrict__ means,
+    const float* __restrict__ scales, const float* __restrict__ quats,
+    const float* __restrict__ opacity, const float* __restrict__ sh, const int n_coef,
+    const float* __restrict__ rgb_in, float4* __restrict__ xy_depth, float4* __restrict__ conic_op,
+    float4* __restrict__ rgb_out, uint32_t* __restrict__ tiles_touched, const uint32_t flags) {
+    const int g = blockIdx.x * blockDim.x + threadIdx.x;
+    if (g >= n) return;
+    const GlobalIn in{means, scales, quats, opacity, sh, rgb_in, (size_t)n, (size_t)g};
+    float4 o_xy, o_co, o_rgb;
+    uint32_t count;
+    project_splat(cam, in, sh != nullptr, n_coef, flags, o_xy, o_co, o_rgb, count);
     xy_depth[g] = o_xy;
     conic_op[g] = o_co;
     rgb_out[g] = o_rgb;
     tiles_touched[g] = count;
 }
+
+// One thread per Gaussian for a stack of cameras: the Gaussian's inputs are
+// read once, its record for camera v lands at v n + g.
+__global__ __launch_bounds__(256) void k_preprocess_views(
+    const CameraSet cams, const int n, const float* __restrict__ means,
+    const float* __restrict__ scales, const float* __restrict__ quats,
+    const float* __restrict__ opacity, const float* __restrict__ sh, const int n_coef,
+    const float* __restrict__ rgb_in, float4* __restrict__ xy_depth, float4* __restrict__ conic_op,
+    float4* __restrict__ rgb_out, uint32_t* __restrict__ tiles_touched, const uint32_t flags) {
+    const int g = blockIdx.x * blockDim.x + threadIdx.x;
+    if (g >= n) return;
+    RegIn in;
+#pragma unroll
+    for (int c = 0; c < 3; ++c) {
+        in.m[c] = means[(size_t)c * n + g];
+        in.s[c] = scales[(size_t)c * n + g];
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) in.q[c] = quats[(size_t)c * n + g];
+    in.o = opacity[g];
+    if (sh) {
+#pragma unroll
+        for (int row = 0; row < 48; ++row)
+            in.c[row] = row < 3 * n_coef ? sh[(size_t)row * n + g] : 0.0f;
+    } else {
+#pragma unroll
+        for (int c = 0; c < 3; ++c) in.c[c] = rgb_in[(size_t)c * n + g];
+    }
+    for (int v = 0; v < cams.n; ++v) {
+        float4 o_xy, o_co, o_rgb;
+        uint32_t count;
+        project_splat(cams.cam[v], in, sh != nullptr, n_coef, flags, o_xy, o_co, o_rgb, count);
+        const size_t i = (size_t)v * n + g;
+        xy_depth[i] = o_xy;
+        conic_op[i] = o_co;
+        rgb_out[i] = o_rgb;
+        tiles_touched[i] = count;
+    }
+}
+
 
 }  // namespace
 
@@ -211,6 +292,18 @@ hipError_t launch_preprocess(const gs_camera& cam, int n, const float* means, co
     const int blocks = (n + 255) / 256;
     hipLaunchKernelGGL(k_preprocess, dim3(blocks), dim3(256), 0, stream, cam, n, means, scales,
                        quats, opacity, sh, n_coef, rgb_in, xy_depth, conic_op, rgb, tiles_touched, flags);
+    return hipGetLastError();
+}
+
+hipError_t launch_preprocess_views(const CameraSet& cams, int n, const float* means, const float* scales,
+                                   const float* quats, const float* opacity, const float* sh, int sh_degree,
+                                   const float* rgb_in, float4* xy_depth, float4* conic_op, float4* rgb,
+                                   uint32_t* tiles_touched, uint32_t flags, hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    const int n_coef = sh ? (sh_degree + 1) * (sh_degree + 1) : 0;
+    const int blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(k_preprocess_views, dim3(blocks), dim3(256), 0, stream, cams, n, means, scales, quats,
+                       opacity, sh, n_coef, rgb_in, xy_depth, conic_op, rgb, tiles_touched, flags);
     return hipGetLastError();
 }
 

@@ -91,6 +91,30 @@ def preprocess(cam, means, scales, quats, opacity, sh=None, sh_degree=0, rgb_in=
     return out
 
 
+def preprocess_views(cams, means, scales, quats, opacity, sh=None, sh_degree=0, rgb_in=None, out=None,
+                     stream=None, tile_test=0):
+    """gs_preprocess_views: the records of n Gaussians for every camera of `cams` (one size).
+    Returns dict xy_depth [V*n,4], conic_op [V*n,4], rgb [V*n,4], tiles_touched [V*n], camera
+    v's records at v*n + g."""
+    n = int(opacity.shape[0])
+    V = len(cams)
+    dev = opacity.device
+    if out is None:
+        out = dict(xy_depth=torch.empty((V * n, 4), dtype=torch.float32, device=dev),
+                   conic_op=torch.empty((V * n, 4), dtype=torch.float32, device=dev),
+                   rgb=torch.empty((V * n, 4), dtype=torch.float32, device=dev),
+                   tiles_touched=torch.empty((V * n,), dtype=torch.int32, device=dev))
+    f32, i32 = torch.float32, torch.int32
+    arr = (_lib.GsCamera * V)(*[_cam(c) for c in cams])
+    _lib.check(_lib.load().gs_preprocess_views(
+        ctypes.cast(arr, ctypes.c_void_p), V, n, _ptr(means, f32, "means"), _ptr(scales, f32, "scales"),
+        _ptr(quats, f32, "quats"), _ptr(opacity, f32, "opacity"), _ptr(sh, f32, "sh"),
+        int(sh_degree), _ptr(rgb_in, f32, "rgb_in"), _ptr(out["xy_depth"], f32),
+        _ptr(out["conic_op"], f32), _ptr(out["rgb"], f32), _ptr(out["tiles_touched"], i32),
+        int(tile_test), _stream(stream)))
+    return out
+
+
 def preprocess_bwd(cam, means, scales=None, quats=None, sh=None, sh_degree=0, tiles_touched=None,
                    grad_mean2d=None, grad_conic_op=None, grad_rgb=None, out=None, stream=None):
     """gs_preprocess_bwd. Returns dict grad_means [3,n], grad_scales [3,n], grad_quats [4,n],
@@ -248,24 +272,45 @@ def bin_and_sort_async(cam, xy_depth, tiles_touched, buffers: BinBuffers, stream
     return buffers.keys, buffers.point_list
 
 
-def _check_chunks(chunks, cam, capacity):
-    need = chunk_words(cam, capacity)
+def _check_chunks(chunks, cam, capacity, n_views=1):
+    need = chunk_words(cam, capacity, n_views)
     if chunks.dtype != torch.int32 or chunks.numel() < need:
         raise ValueError(f"chunks must be int32 with at least {need} elements")
 
 
-def tile_ranges_async(cam, buffers: BinBuffers, out=None, order=None, stream=None, chunks=None):
+def bin_and_sort_views_async(cam, n_views: int, xy_depth, tiles_touched, buffers: BinBuffers, stream=None,
+                             conic_op=None, tile_test=0):
+    """gs_bin_and_sort_views_async: one binning of a stack of n_views views of cam's size
+    (records from preprocess_views). Returns (keys, point_list), both [capacity]; E lands in
+    buffers.n_entries_dev."""
+    c = _cam(cam)
+    n_all = int(tiles_touched.shape[0])
+    if n_all % n_views:
+        raise ValueError("the records must hold n_views equal views")
+    scratch = buffers.scratch_for(c, n_all)
+    nbytes = ctypes.c_size_t(scratch.numel())
+    _lib.check(_lib.load().gs_bin_and_sort_views_async(
+        ctypes.byref(c), int(n_views), n_all // n_views, _ptr(xy_depth, torch.float32, "xy_depth"),
+        _ptr(conic_op, torch.float32, "conic_op"), _ptr(tiles_touched, torch.int32, "tiles_touched"),
+        _ptr(buffers.keys), _ptr(buffers.point_list), buffers.capacity, _ptr(scratch), ctypes.byref(nbytes),
+        _ptr(buffers.n_entries_dev), int(tile_test), _stream(stream)))
+    return buffers.keys, buffers.point_list
+
+
+def tile_ranges_async(cam, buffers: BinBuffers, out=None, order=None, stream=None, chunks=None, n_views=1):
     """gs_tile_ranges_async over the last asynchronous binning into buffers.
     `order` (int32 [TX*TY]) receives the heaviest-first tile schedule if given;
     `chunks` (int32 [chunk_words(cam, buffers.capacity)]) the chunk schedule of
-    the chunked backward (gs_tile_ranges_ex)."""
+    the chunked backward (gs_tile_ranges_ex); n_views > 1: the tiles of a view
+    stack (bin_and_sort_views_async)."""
     c = _cam(cam)
     if out is None:
         TX, TY = tiles_xy(dict(width=c.width, height=c.height))
-        out = torch.empty((TX * TY, 2), dtype=torch.int32, device=buffers.keys.device)
-    if chunks is not None:
-        _check_chunks(chunks, cam, buffers.capacity)
-        _lib.check(_lib.load().gs_tile_ranges_ex(ctypes.byref(c), _ptr(buffers.keys), 0,
+        out = torch.empty((TX * TY * n_views, 2), dtype=torch.int32, device=buffers.keys.device)
+    if chunks is not None or n_views != 1:
+        if chunks is not None:
+            _check_chunks(chunks, cam, buffers.capacity, n_views)
+        _lib.check(_lib.load().gs_tile_ranges_ex(ctypes.byref(c), int(n_views), _ptr(buffers.keys), 0,
                                                  _ptr(buffers.n_entries_dev), buffers.capacity,
                                                  _ptr(out, torch.int32), _ptr(order, torch.int32, "order"),
                                                  _ptr(chunks, torch.int32, "chunks"), _stream(stream)))
@@ -288,7 +333,7 @@ def tile_ranges(cam, keys, n_entries: int, out=None, order=None, stream=None, ch
     c = _cam(cam)
     if chunks is not None:
         _check_chunks(chunks, cam, keys.numel())
-        _lib.check(_lib.load().gs_tile_ranges_ex(ctypes.byref(c), _ptr(keys, torch.int64, "keys"), int(n_entries),
+        _lib.check(_lib.load().gs_tile_ranges_ex(ctypes.byref(c), 1, _ptr(keys, torch.int64, "keys"), int(n_entries),
                                                  None, int(keys.numel()), _ptr(out, torch.int32),
                                                  _ptr(order, torch.int32, "order"),
                                                  _ptr(chunks, torch.int32, "chunks"), _stream(stream)))
@@ -316,21 +361,21 @@ def ckpt_rows(capacity: int) -> int:
     return (int(capacity) + 255) // 256 * 256
 
 
-def chunk_words(cam, capacity: int) -> int:
+def chunk_words(cam, capacity: int, n_views: int = 1) -> int:
     """Length of the chunk schedule gs_tile_ranges_ex writes for `capacity` entries."""
     TX, TY = tiles_xy(cam if isinstance(cam, dict) else dict(width=cam.width, height=cam.height))
-    return 4 + 4 * (TX * TY + (int(capacity) + 255) // 256)
+    return 4 + 4 * (TX * TY * n_views + (int(capacity) + 255) // 256)
 
 
-def part_bytes(cam, capacity: int) -> int:
+def part_bytes(cam, capacity: int, n_views: int = 1) -> int:
     """Bytes of the workspace the scheduled forward (composite_fwd with chunks) needs."""
     c = _cam(cam)
-    return int(_lib.load().gs_composite_part_bytes(ctypes.byref(c), int(capacity)))
+    return int(_lib.load().gs_composite_part_bytes(ctypes.byref(c), int(n_views), int(capacity)))
 
 
 def composite_fwd(cam, ranges, point_list, xy_depth, conic_op, rgb, bg=(0.0, 0.0, 0.0),
                   with_examined=False, out=None, order=None, stream=None, ckpt=None, capacity=None,
-                  chunks=None, part=None):
+                  chunks=None, part=None, n_views=1):
     """gs_composite_fwd, or gs_composite_fwd_ex when `ckpt` (float32 [ckpt_rows(capacity), 4]) or
     `chunks` is given: ckpt then receives the per-pixel state at every 256-entry boundary, for
     composite_bwd's chunked walk; with the schedule `chunks` (from tile_ranges) the lists are
@@ -341,26 +386,28 @@ def composite_fwd(cam, ranges, point_list, xy_depth, conic_op, rgb, bg=(0.0, 0.0
     W, H = (cam["width"], cam["height"]) if isinstance(cam, dict) else (cam.width, cam.height)
     dev = xy_depth.device
     if out is None:
-        out = dict(image=torch.empty((3, H, W), dtype=torch.float32, device=dev),
-                   final_T=torch.empty((H, W), dtype=torch.float32, device=dev),
-                   n_contrib=torch.empty((H, W), dtype=torch.int32, device=dev))
+        lead = (n_views,) if n_views != 1 else ()
+        out = dict(image=torch.empty(lead + (3, H, W), dtype=torch.float32, device=dev),
+                   final_T=torch.empty(lead + (H, W), dtype=torch.float32, device=dev),
+                   n_contrib=torch.empty(lead + (H, W), dtype=torch.int32, device=dev))
         if with_examined:
-            out["n_examined"] = torch.empty((H, W), dtype=torch.int32, device=dev)
+            out["n_examined"] = torch.empty(lead + (H, W), dtype=torch.int32, device=dev)
     bgc = (ctypes.c_float * 3)(*[float(x) for x in bg])
     c = _cam(cam)
-    if ckpt is not None or chunks is not None:
+    if ckpt is not None or chunks is not None or n_views != 1:
         nk = int(point_list.numel() if capacity is None else capacity)
         if ckpt is not None and (ckpt.dtype != torch.float32 or ckpt.numel() < 4 * ckpt_rows(nk)):
             raise ValueError(f"ckpt must be float32 with at least {ckpt_rows(nk)} rows of 4")
         if chunks is not None:
-            _check_chunks(chunks, cam, nk)
-            need = part_bytes(cam, nk)
+            _check_chunks(chunks, cam, nk, n_views)
+            need = part_bytes(cam, nk, n_views)
             if part is None:
                 part = torch.empty((need,), dtype=torch.uint8, device=xy_depth.device)
             elif part.numel() * part.element_size() < need:
                 raise ValueError(f"part must hold at least {need} bytes")
         _lib.check(_lib.load().gs_composite_fwd_ex(
-            ctypes.byref(c), _ptr(ranges, torch.int32, "ranges"), _ptr(point_list, torch.int32, "point_list"),
+            ctypes.byref(c), int(n_views), _ptr(ranges, torch.int32, "ranges"),
+            _ptr(point_list, torch.int32, "point_list"),
             _ptr(xy_depth, torch.float32), _ptr(conic_op, torch.float32), _ptr(rgb, torch.float32),
             ctypes.cast(bgc, ctypes.c_void_p), _ptr(out["image"]), _ptr(out["final_T"]),
             _ptr(out["n_contrib"]), _ptr(out.get("n_examined")), _ptr(order, torch.int32, "order"), nk,
@@ -378,7 +425,7 @@ def composite_fwd(cam, ranges, point_list, xy_depth, conic_op, rgb, bg=(0.0, 0.0
 
 def composite_bwd(cam, n, ranges, point_list, xy_depth, conic_op, rgb, final_T, n_contrib,
                   dL_dimage, bg=(0.0, 0.0, 0.0), out=None, order=None, stream=None, chunks=None, image=None,
-                  ckpt=None, capacity=None):
+                  ckpt=None, capacity=None, n_views=1):
     """gs_composite_bwd, or gs_composite_bwd_ex (one workgroup per 256-entry chunk of a list)
     when `chunks` is given, with the `image` and `ckpt` of the same frame's
     composite_fwd(ckpt=..., capacity=...) and that capacity (default: point_list's length).
@@ -390,15 +437,17 @@ def composite_bwd(cam, n, ranges, point_list, xy_depth, conic_op, rgb, final_T, 
                    grad_rgb=torch.empty((n, 4), dtype=torch.float32, device=dev))
     bgc = (ctypes.c_float * 3)(*[float(x) for x in bg])
     c = _cam(cam)
+    if n_views != 1 and chunks is None:
+        raise ValueError("the backward of a view stack takes the schedule (chunks)")
     if chunks is not None:
         if ckpt is None or image is None:
             raise ValueError("the chunked backward needs the forward's image and ckpt")
         cap = int(point_list.numel() if capacity is None else capacity)
-        _check_chunks(chunks, cam, cap)
+        _check_chunks(chunks, cam, cap, n_views)
         if ckpt.dtype != torch.float32 or ckpt.numel() < 4 * ckpt_rows(cap):
             raise ValueError(f"ckpt must be float32 with at least {ckpt_rows(cap)} rows of 4")
         _lib.check(_lib.load().gs_composite_bwd_ex(
-            ctypes.byref(c), int(n), _ptr(ranges, torch.int32, "ranges"),
+            ctypes.byref(c), int(n_views), int(n), _ptr(ranges, torch.int32, "ranges"),
             _ptr(point_list, torch.int32, "point_list"), _ptr(chunks, torch.int32, "chunks"), cap,
             _ptr(xy_depth, torch.float32), _ptr(conic_op, torch.float32), _ptr(rgb, torch.float32),
             ctypes.cast(bgc, ctypes.c_void_p), _ptr(image, torch.float32, "image"),
@@ -620,4 +669,105 @@ class ViewBatch:
         over = [(i, e) for i, e in enumerate(E) if e > self.views[i]["bins"].capacity]
         if over:
             raise GsError(_lib.GS_ERR_CAPACITY, f"views over capacity (view, entries): {over}")
+        return E
+
+
+class ViewStack:
+    """A batch of views of one size composited as one frame: view v is the
+    band of tile rows [v TY, v TY + TY) of a stacked tile grid, so each stage
+    (one preprocess for all cameras, one binning, one ranges call, one
+    forward, one backward) is a single launch sequence over the whole batch
+    instead of one per view. Images are [V, 3, H, W], per-pixel buffers
+    [V, H, W], splat records and their gradients [V*n, ...] (view v's at
+    v*n + g). No host synchronisation; `check()` reports an overflow of
+    `capacity` (the batch then renders the background).
+
+    loss_grad(image, out): writes dL/dI ([V, 3, H, W]) from the rendered
+    images; enqueued between the forward and the backward.
+    """
+
+    def __init__(self, cams, scene: "Scene", capacity: int, device="cuda", bg=(0.0, 0.0, 0.0),
+                 tile_test: int = 0, scheduled=None):
+        self.device = torch.device(device)
+        self.scene, self.bg, self.tile_test = scene, bg, int(tile_test)
+        self.cams = list(cams)
+        self.V = V = len(self.cams)
+        W, H = int(self.cams[0]["width"]), int(self.cams[0]["height"])
+        if any(int(c["width"]) != W or int(c["height"]) != H for c in self.cams):
+            raise ValueError("a view stack needs cameras of one size")
+        self.c = camera(self.cams[0])  # the size of one view
+        n = scene.n
+        TX, TY = tiles_xy(self.cams[0])
+        f32, i32, dev = torch.float32, torch.int32, self.device
+        self.bins = BinBuffers(dev, capacity)
+        self.bins.scratch_for(self.c, V * n)
+        self.pre = dict(xy_depth=torch.empty((V * n, 4), dtype=f32, device=dev),
+                        conic_op=torch.empty((V * n, 4), dtype=f32, device=dev),
+                        rgb=torch.empty((V * n, 4), dtype=f32, device=dev),
+                        tiles_touched=torch.empty((V * n,), dtype=i32, device=dev))
+        self.ranges = torch.empty((V * TX * TY, 2), dtype=i32, device=dev)
+        self.order = torch.empty((V * TX * TY,), dtype=i32, device=dev)
+        self.chunks = torch.empty((chunk_words(self.c, capacity, V),), dtype=i32, device=dev)
+        self.ckpt = torch.empty((ckpt_rows(capacity), 4), dtype=f32, device=dev)
+        # the scheduled forward when the stacked grid is small (few, long lists)
+        if scheduled is None:
+            scheduled = V * TX * TY < SCHEDULED_FORWARD_MAX_TILES
+        self.part = (torch.empty((part_bytes(self.c, capacity, V),), dtype=torch.uint8, device=dev)
+                     if scheduled else None)
+        self.fwd = dict(image=torch.empty((V, 3, H, W), dtype=f32, device=dev),
+                        final_T=torch.empty((V, H, W), dtype=f32, device=dev),
+                        n_contrib=torch.empty((V, H, W), dtype=i32, device=dev))
+        self.dL_dimage = torch.zeros((V, 3, H, W), dtype=f32, device=dev)
+        self.grads = dict(grad_mean2d=torch.empty((V * n, 2), dtype=f32, device=dev),
+                          grad_conic_op=torch.empty((V * n, 4), dtype=f32, device=dev),
+                          grad_rgb=torch.empty((V * n, 4), dtype=f32, device=dev))
+        self.graph = None
+
+    def enqueue(self, loss_grad=None):
+        """Enqueue the batch on the current stream: preprocess, binning, ranges and
+        schedule, forward, loss_grad (if given), backward. Nothing waits on the host."""
+        sc, V, c = self.scene, self.V, self.c
+        preprocess_views(self.cams, sc.means, sc.scales, sc.quats, sc.opacity, sc.sh, sc.sh_degree, sc.rgb,
+                         out=self.pre, tile_test=self.tile_test)
+        keys, pl = bin_and_sort_views_async(c, V, self.pre["xy_depth"], self.pre["tiles_touched"], self.bins,
+                                            conic_op=self.pre["conic_op"], tile_test=self.tile_test)
+        tile_ranges_async(c, self.bins, out=self.ranges, order=self.order, chunks=self.chunks, n_views=V)
+        composite_fwd(c, self.ranges, pl, self.pre["xy_depth"], self.pre["conic_op"], self.pre["rgb"], self.bg,
+                      out=self.fwd, order=self.order, ckpt=self.ckpt, capacity=self.bins.capacity,
+                      chunks=self.chunks if self.part is not None else None, part=self.part, n_views=V)
+        if loss_grad is not None:
+            loss_grad(self.fwd["image"], self.dL_dimage)
+        composite_bwd(c, V * sc.n, self.ranges, pl, self.pre["xy_depth"], self.pre["conic_op"], self.pre["rgb"],
+                      self.fwd["final_T"], self.fwd["n_contrib"], self.dL_dimage, self.bg, out=self.grads,
+                      chunks=self.chunks, image=self.fwd["image"], ckpt=self.ckpt, capacity=self.bins.capacity,
+                      n_views=V)
+
+    def capture(self, loss_grad=None, warmup: int = 1):
+        """Record enqueue(loss_grad) as one HIP graph (after `warmup` eager runs on a side
+        stream, as graph capture requires)."""
+        s = torch.cuda.Stream(device=self.device)
+        s.wait_stream(torch.cuda.current_stream(self.device))
+        with torch.cuda.stream(s):
+            for _ in range(warmup):
+                self.enqueue(loss_grad)
+        torch.cuda.current_stream(self.device).wait_stream(s)
+        torch.cuda.synchronize(self.device)
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self.enqueue(loss_grad)
+        return self.graph
+
+    def replay(self):
+        if self.graph is None:
+            raise RuntimeError("ViewStack.replay: capture() first")
+        self.graph.replay()
+
+    def entries(self) -> int:
+        """Entries of the whole batch after the last run (waits for the stream)."""
+        return self.bins.entries()
+
+    def check(self) -> int:
+        E = self.entries()
+        if E > self.bins.capacity:
+            raise GsError(_lib.GS_ERR_CAPACITY, f"the batch's {E} entries exceed the capacity {self.bins.capacity}")
         return E

@@ -49,6 +49,7 @@ extern "C" {
 #define GS_TILE 16
 #define GS_MAX_GAUSSIANS (1 << 24) /* prefix-scan capacity, 256^3 */
 #define GS_MAX_DIM 16384
+#define GS_MAX_VIEWS 32 /* cameras of one view stack */
 
 /* Tile tests (the flags of the _ex entry points). GS_TILES_SQUARE: a splat
  * is listed in every tile of its span rectangle. GS_TILES_ELLIPSE: only in
@@ -154,6 +155,26 @@ gs_status gs_preprocess_ex(const gs_camera* cam, int32_t n, const float* means, 
                            const float* quats, const float* opacity, const float* sh,
                            int32_t sh_degree, const float* rgb_in, float* xy_depth, float* conic_op,
                            float* rgb, uint32_t* tiles_touched, uint32_t flags, void* stream);
+
+/* ---------------------------------------------------------------------
+ * gs_preprocess_views - gs_preprocess_ex for a stack of n_views cameras of
+ * one size at once: each Gaussian's inputs are read once and its record for
+ * camera v is written at index v n + g of every output (xy_depth, conic_op,
+ * rgb [n_views n][4], tiles_touched [n_views n]), the same bits
+ * gs_preprocess_ex writes for that camera alone. Such a stack is binned,
+ * ranged and composited as one frame whose view v owns the band of tile
+ * rows [v TY, v TY + TY) (gs_bin_and_sort_views_async, gs_tile_ranges_ex,
+ * gs_composite_fwd_ex, gs_composite_bwd_ex with n_views).
+ *
+ *   cams       (host) n_views cameras, 1 <= n_views <= GS_MAX_VIEWS, all of
+ *              the same width and height
+ *   n          Gaussians; n_views n <= GS_MAX_GAUSSIANS
+ * Other arguments as gs_preprocess_ex.
+ * ------------------------------------------------------------------- */
+gs_status gs_preprocess_views(const gs_camera* cams, int32_t n_views, int32_t n, const float* means,
+                              const float* scales, const float* quats, const float* opacity, const float* sh,
+                              int32_t sh_degree, const float* rgb_in, float* xy_depth, float* conic_op, float* rgb,
+                              uint32_t* tiles_touched, uint32_t flags, void* stream);
 
 /* ---------------------------------------------------------------------
  * gs_preprocess_bwd - gradients of gs_preprocess's outputs with respect to
@@ -266,6 +287,19 @@ gs_status gs_bin_and_sort_async_ex(const gs_camera* cam, int32_t n, const float*
                                    int64_t capacity, void* scratch, size_t* scratch_bytes,
                                    uint64_t* n_entries_dev, uint32_t flags, void* stream);
 
+/* gs_bin_and_sort_views_async - gs_bin_and_sort_async_ex over a stack of
+ * n_views views (see gs_preprocess_views): xy_depth, conic_op and
+ * tiles_touched hold n_views n records, view v's at v n + g; an entry's
+ * tile id is v TX TY + ty TX + tx for the tile (tx, ty) of its own view,
+ * and its value the record index v n + g. Within each view's band the
+ * lists are exactly those of gs_bin_and_sort_async_ex for that view alone.
+ * cam gives the size of one view; TX TY n_views <= 2^24. The scratch size
+ * is that of gs_bin_and_sort(_async) for n_views n Gaussians. */
+gs_status gs_bin_and_sort_views_async(const gs_camera* cam, int32_t n_views, int32_t n, const float* xy_depth,
+                                      const float* conic_op, const uint32_t* tiles_touched, uint64_t* keys,
+                                      uint32_t* point_list, int64_t capacity, void* scratch, size_t* scratch_bytes,
+                                      uint64_t* n_entries_dev, uint32_t flags, void* stream);
+
 /* ---------------------------------------------------------------------
  * gs_tile_ranges - per-tile [start, end) of the sorted entries.
  * (zenn 4.4.1-4.4.2; "rigel" README "Binning": the range kernel.)
@@ -302,6 +336,8 @@ gs_status gs_tile_ranges_async(const gs_camera* cam, const uint64_t* keys, const
  * exceeds capacity), optionally with the chunk schedule of the chunked
  * backward (gs_composite_bwd_ex).
  *
+ *   n_views     1, or the views of a stack (gs_bin_and_sort_views_async):
+ *               the tiles are then the TX TY n_views of the stack
  *   keys, ranges, tile_order  as gs_tile_ranges / gs_tile_ranges_async
  *   capacity    length of keys; n_entries <= capacity when n_entries_dev is
  *               NULL
@@ -321,7 +357,7 @@ gs_status gs_tile_ranges_async(const gs_camera* cam, const uint64_t* keys, const
  *               every list is one item with k = 0xffffffff, in tile_order's
  *               order.
  * ------------------------------------------------------------------- */
-gs_status gs_tile_ranges_ex(const gs_camera* cam, const uint64_t* keys, int64_t n_entries,
+gs_status gs_tile_ranges_ex(const gs_camera* cam, int32_t n_views, const uint64_t* keys, int64_t n_entries,
                             const uint64_t* n_entries_dev, int64_t capacity, uint32_t* ranges,
                             uint32_t* tile_order, uint32_t* chunks, void* stream);
 
@@ -394,6 +430,10 @@ gs_status gs_composite_bwd(const gs_camera* cam, int32_t n, const uint32_t* rang
  * chunks in parallel. The compositing is that of gs_composite_fwd ("rigel"
  * README "Rasterization").
  *
+ *   n_views   1, or the views of a stack: cam gives one view's size, the
+ *             tiles, ranges and schedule cover the stack, and image
+ *             [n_views][3][H][W], final_T, n_contrib, n_examined
+ *             [n_views][H][W] hold view after view
  *   capacity  length of the sorted entry arrays (keys, point_list): the
  *             entry count E, or the capacity the asynchronous binning used;
  *             every tile range must lie in [0, capacity)
@@ -422,19 +462,20 @@ gs_status gs_composite_bwd(const gs_camera* cam, int32_t n, const uint32_t* rang
  *             ranges and tile_order are then not read.
  *   part      workspace of gs_composite_part_bytes(cam, capacity) bytes,
  *             16-byte aligned (required with chunks, else unused)
- * Other arguments as gs_composite_fwd. ckpt and chunks may both be NULL:
- * then this is gs_composite_fwd.
+ * Other arguments as gs_composite_fwd. With n_views 1 and ckpt and chunks
+ * both NULL this is gs_composite_fwd.
  * ------------------------------------------------------------------- */
-gs_status gs_composite_fwd_ex(const gs_camera* cam, const uint32_t* ranges, const uint32_t* point_list,
-                              const float* xy_depth, const float* conic_op, const float* rgb,
-                              const float bg[3], float* image, float* final_T, uint32_t* n_contrib,
+gs_status gs_composite_fwd_ex(const gs_camera* cam, int32_t n_views, const uint32_t* ranges,
+                              const uint32_t* point_list, const float* xy_depth, const float* conic_op,
+                              const float* rgb, const float bg[3], float* image, float* final_T, uint32_t* n_contrib,
                               uint32_t* n_examined, const uint32_t* tile_order, int64_t capacity,
                               float* ckpt, const uint32_t* chunks, void* part, void* stream);
 
 /* gs_composite_part_bytes - bytes of the `part` workspace of
- * gs_composite_fwd_ex for this camera and capacity: (ceil(capacity / 256) +
- * TX*TY) * 256 * 20. 0 for an invalid camera or capacity. */
-size_t gs_composite_part_bytes(const gs_camera* cam, int64_t capacity);
+ * gs_composite_fwd_ex for this camera, view count and capacity:
+ * (ceil(capacity / 256) + TX TY n_views) * 256 * 20. 0 for invalid
+ * arguments. */
+size_t gs_composite_part_bytes(const gs_camera* cam, int32_t n_views, int64_t capacity);
 
 /* ---------------------------------------------------------------------
  * gs_composite_bwd_ex - gs_composite_bwd over the work items of the
@@ -449,6 +490,8 @@ size_t gs_composite_part_bytes(const gs_camera* cam, int64_t capacity);
  * few bits where little light is left, T near 1e-4); other pixels start
  * from final_T as in gs_composite_bwd.
  *
+ *   n_views   as gs_composite_fwd_ex (dL_dimage [n_views][3][H][W]; n
+ *             counts the records of the whole stack)
  *   chunks    the schedule gs_tile_ranges_ex wrote for this frame's ranges
  *   capacity  as gs_composite_fwd_ex (the same value)
  *   image     [3][H][W] the image gs_composite_fwd_ex wrote
@@ -457,7 +500,7 @@ size_t gs_composite_part_bytes(const gs_camera* cam, int64_t capacity);
  * Other arguments as gs_composite_bwd; every input must come from the same
  * frame (ranges, chunks, the forward's outputs).
  * ------------------------------------------------------------------- */
-gs_status gs_composite_bwd_ex(const gs_camera* cam, int32_t n, const uint32_t* ranges,
+gs_status gs_composite_bwd_ex(const gs_camera* cam, int32_t n_views, int32_t n, const uint32_t* ranges,
                               const uint32_t* point_list, const uint32_t* chunks, int64_t capacity,
                               const float* xy_depth, const float* conic_op, const float* rgb,
                               const float bg[3], const float* image, const float* final_T,

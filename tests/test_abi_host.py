@@ -219,8 +219,8 @@ def test_chunked_composite_validates_before_launch(gs):
     d = P(256)  # never dereferenced: validation fails first
     c = _cam()
     bg = (ctypes.c_float * 3)()
-    fwd = lambda cap=100, ckpt=d, rgb=d, chunks=None, part=None, ranges=d: gs.gs_composite_fwd_ex(
-        ctypes.byref(c), ranges, d, d, d, rgb, bg, d, d, d, None, None, cap, ckpt, chunks, part, None)
+    fwd = lambda cap=100, ckpt=d, rgb=d, chunks=None, part=None, ranges=d, views=1: gs.gs_composite_fwd_ex(
+        ctypes.byref(c), views, ranges, d, d, d, rgb, bg, d, d, d, None, None, cap, ckpt, chunks, part, None)
     assert fwd(cap=-1) == _lib.GS_ERR_INVALID
     assert b"capacity" in gs.gs_last_error()
     assert fwd(cap=1 << 32) == _lib.GS_ERR_INVALID
@@ -231,14 +231,19 @@ def test_chunked_composite_validates_before_launch(gs):
     assert fwd(chunks=P(264), part=d) == _lib.GS_ERR_INVALID
     assert fwd(chunks=d, part=P(260)) == _lib.GS_ERR_INVALID
     assert fwd(ranges=None) == _lib.GS_ERR_INVALID  # without a schedule the ranges are read
+    for bad in (0, -1, 33):
+        assert fwd(views=bad) == _lib.GS_ERR_INVALID
+        assert b"n_views" in gs.gs_last_error()
     # the workspace size: (ceil(capacity / 256) + tiles) rows of 256 (float4 + uint32)
     tiles = 4 * 4  # the 64 x 64 test camera
-    assert gs.gs_composite_part_bytes(ctypes.byref(c), 1000) == (4 + tiles) * 256 * 20
-    assert gs.gs_composite_part_bytes(ctypes.byref(c), 0) == tiles * 256 * 20
-    assert gs.gs_composite_part_bytes(ctypes.byref(c), -1) == 0
-    assert gs.gs_composite_part_bytes(None, 10) == 0
-    bwd = lambda n=4, chunks=d, cap=100, image=d, ckpt=d, gm=d: gs.gs_composite_bwd_ex(
-        ctypes.byref(c), n, d, d, chunks, cap, d, d, d, bg, image, d, d, ckpt, d, gm, d, d, None)
+    assert gs.gs_composite_part_bytes(ctypes.byref(c), 1, 1000) == (4 + tiles) * 256 * 20
+    assert gs.gs_composite_part_bytes(ctypes.byref(c), 3, 1000) == (4 + 3 * tiles) * 256 * 20
+    assert gs.gs_composite_part_bytes(ctypes.byref(c), 1, 0) == tiles * 256 * 20
+    assert gs.gs_composite_part_bytes(ctypes.byref(c), 1, -1) == 0
+    assert gs.gs_composite_part_bytes(ctypes.byref(c), 0, 10) == 0
+    assert gs.gs_composite_part_bytes(None, 1, 10) == 0
+    bwd = lambda n=4, chunks=d, cap=100, image=d, ckpt=d, gm=d, views=1: gs.gs_composite_bwd_ex(
+        ctypes.byref(c), views, n, d, d, chunks, cap, d, d, d, bg, image, d, d, ckpt, d, gm, d, d, None)
     assert bwd(ckpt=None) == _lib.GS_ERR_INVALID  # the chunked walk needs the checkpoints
     assert b"ckpt" in gs.gs_last_error()
     assert bwd(image=None) == _lib.GS_ERR_INVALID
@@ -248,8 +253,9 @@ def test_chunked_composite_validates_before_launch(gs):
     assert bwd(gm=None) == _lib.GS_ERR_INVALID
     assert bwd(chunks=P(264)) == _lib.GS_ERR_INVALID
     assert bwd(ckpt=P(264)) == _lib.GS_ERR_INVALID
-    rng = lambda n_e=10, n_dev=None, cap=100, keys=d, ranges=d, chunks=d: gs.gs_tile_ranges_ex(
-        ctypes.byref(c), keys, n_e, n_dev, cap, ranges, None, chunks, None)
+    assert bwd(views=0) == _lib.GS_ERR_INVALID and b"n_views" in gs.gs_last_error()
+    rng = lambda n_e=10, n_dev=None, cap=100, keys=d, ranges=d, chunks=d, views=1: gs.gs_tile_ranges_ex(
+        ctypes.byref(c), views, keys, n_e, n_dev, cap, ranges, None, chunks, None)
     assert rng(n_e=101) == _lib.GS_ERR_INVALID  # more entries than the keys hold
     assert b"n_entries" in gs.gs_last_error()
     assert rng(n_e=-1) == _lib.GS_ERR_INVALID
@@ -258,3 +264,41 @@ def test_chunked_composite_validates_before_launch(gs):
     assert rng(keys=None) == _lib.GS_ERR_INVALID
     assert rng(chunks=P(264)) == _lib.GS_ERR_INVALID
     assert rng(n_dev=P(516)) == _lib.GS_ERR_INVALID
+    assert rng(views=33) == _lib.GS_ERR_INVALID and b"n_views" in gs.gs_last_error()
+
+
+def test_view_stack_validates_before_launch(gs):
+    """gs_preprocess_views and gs_bin_and_sort_views_async check the stack
+    (camera count and sizes, the splat total, the tile count) before any
+    launch."""
+    from gaussian_splatting_tile_amd import _lib
+    P = ctypes.c_void_p
+    d = P(256)  # never dereferenced: validation fails first
+    cams = (_lib.GsCamera * 3)(_cam(), _cam(), _cam())
+    pre = lambda cs=cams, views=3, n=10, sh=None, rgb=d, out=d: gs.gs_preprocess_views(
+        ctypes.cast(cs, P) if cs is not None else None, views, n, d, d, d, d, sh, 0, rgb, out, d, d, d, 0, None)
+    assert pre(cs=None) == _lib.GS_ERR_INVALID
+    for bad in (0, 33):
+        assert pre(views=bad) == _lib.GS_ERR_INVALID and b"n_views" in gs.gs_last_error()
+    odd = (_lib.GsCamera * 2)(_cam(), _cam(width=80))
+    assert pre(cs=odd, views=2) == _lib.GS_ERR_INVALID  # one size for the whole stack
+    assert b"camera 1" in gs.gs_last_error()
+    assert pre(n=-1) == _lib.GS_ERR_INVALID
+    assert pre(n=(1 << 24) // 3 + 1) == _lib.GS_ERR_INVALID  # the stack's records exceed GS_MAX_GAUSSIANS
+    assert pre(sh=None, rgb=None) == _lib.GS_ERR_INVALID
+    assert pre(out=P(264)) == _lib.GS_ERR_INVALID
+    assert pre(n=0) == _lib.GS_OK  # nothing to do
+    c = _cam()
+    need = ctypes.c_size_t(0)
+    assert gs.gs_bin_and_sort_views_async(ctypes.byref(c), 3, 10, None, None, None, None, None, 100, None,
+                                          ctypes.byref(need), None, 0, None) == _lib.GS_OK and need.value > 0
+    one = ctypes.c_size_t(0)
+    assert gs.gs_bin_and_sort(ctypes.byref(c), 30, None, None, None, None, 100, None, ctypes.byref(one),
+                              None, None) == _lib.GS_OK
+    assert one.value == need.value  # the scratch of n_views n splats
+    big = _cam(width=16384, height=16384)  # 2^20 tiles per view
+    assert gs.gs_bin_and_sort_views_async(ctypes.byref(big), 32, 10, None, None, None, None, None, 100, None,
+                                          ctypes.byref(need), None, 0, None) == _lib.GS_ERR_INVALID
+    assert b"2^24 tiles" in gs.gs_last_error()
+    assert gs.gs_bin_and_sort_views_async(ctypes.byref(c), 0, 10, None, None, None, None, None, 100, None,
+                                          ctypes.byref(need), None, 0, None) == _lib.GS_ERR_INVALID
