@@ -143,13 +143,15 @@ def bench_views(args):
     torch.cuda.synchronize()
 
     if args.batch == "stack":
-        # the 16 views as bands of one stacked frame: one launch sequence per step
+        # the 16 views as bands of stacked frames: --streams stacks, one launch sequence each
         ref_all = torch.stack(refs)
 
-        def loss_grad(image, out):
-            out.copy_(image).sub_(ref_all).sign_()
+        def loss_grad(first, image, out):
+            out.copy_(image).sub_(ref_all[first:first + image.shape[0]]).sign_()
 
-        batch = gs.ViewStack(cams, sc, capacity=int(E_max * n_views * 1.25) + 1024, device=dev)
+        per_stack = -(-n_views // max(1, min(args.streams, n_views)))
+        batch = gs.ViewStack(cams, sc, capacity=int(E_max * per_stack * 1.25) + 1024, device=dev,
+                             streams=args.streams)
     else:
         def loss_grad(i, image, out):
             out.copy_(image).sub_(refs[i]).sign_()
@@ -188,7 +190,7 @@ def bench_views(args):
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(1e3 * graph_s, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"cfg4: {WORKLOADS['cfg4']}", "n_gaussians": sc.n, "views_per_step": n_views,
-                   "batch": args.batch, "streams": args.streams if args.batch == "streams" else 1,
+                   "batch": args.batch, "streams": args.streams,
                    "backward": args.backward,
                    "width": 400, "height": 400, "entries_total": int(sum(E)) if isinstance(E, list) else int(E)},
         "secondary": {"eager_frames_per_s": round(n_views / eager_s, 3),
@@ -209,8 +211,8 @@ def main():
                     help="backward compositing over 256-entry chunks of each list (from the forward's "
                          "checkpoints) or over whole lists (results agree to float32 rounding)")
     ap.add_argument("--batch", choices=("stack", "streams"), default="stack",
-                    help="cfg4: the 16 views as bands of one stacked frame (one launch sequence), or one "
-                         "launch sequence per view spread over --streams streams")
+                    help="cfg4: the 16 views as bands of --streams stacked frames (one launch sequence "
+                         "per stack), or one launch sequence per view spread over --streams streams")
     ap.add_argument("--streams", type=int, default=4,
                     help="cfg4: streams the 16 views are spread over (fork/join inside the graph)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,

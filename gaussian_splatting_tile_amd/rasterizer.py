@@ -672,33 +672,16 @@ class ViewBatch:
         return E
 
 
-class ViewStack:
-    """A batch of views of one size composited as one frame: view v is the
-    band of tile rows [v TY, v TY + TY) of a stacked tile grid, so each stage
-    (one preprocess for all cameras, one binning, one ranges call, one
-    forward, one backward) is a single launch sequence over the whole batch
-    instead of one per view. Images are [V, 3, H, W], per-pixel buffers
-    [V, H, W], splat records and their gradients [V*n, ...] (view v's at
-    v*n + g). No host synchronisation; `check()` reports an overflow of
-    `capacity` (the batch then renders the background).
+class _StackGroup:
+    """The buffers and launch sequence of one stack of views (see ViewStack)."""
 
-    loss_grad(image, out): writes dL/dI ([V, 3, H, W]) from the rendered
-    images; enqueued between the forward and the backward.
-    """
-
-    def __init__(self, cams, scene: "Scene", capacity: int, device="cuda", bg=(0.0, 0.0, 0.0),
-                 tile_test: int = 0, scheduled=None):
-        self.device = torch.device(device)
-        self.scene, self.bg, self.tile_test = scene, bg, int(tile_test)
-        self.cams = list(cams)
-        self.V = V = len(self.cams)
-        W, H = int(self.cams[0]["width"]), int(self.cams[0]["height"])
-        if any(int(c["width"]) != W or int(c["height"]) != H for c in self.cams):
-            raise ValueError("a view stack needs cameras of one size")
-        self.c = camera(self.cams[0])  # the size of one view
+    def __init__(self, cams, scene, capacity, device, tile_test, scheduled, fwd, dL, grads, first):
+        self.cams, self.scene, self.tile_test, self.first = cams, scene, tile_test, first
+        V = self.V = len(cams)
+        self.c = camera(cams[0])  # the size of one view
         n = scene.n
-        TX, TY = tiles_xy(self.cams[0])
-        f32, i32, dev = torch.float32, torch.int32, self.device
+        TX, TY = tiles_xy(cams[0])
+        f32, i32, dev = torch.float32, torch.int32, device
         self.bins = BinBuffers(dev, capacity)
         self.bins.scratch_for(self.c, V * n)
         self.pre = dict(xy_depth=torch.empty((V * n, 4), dtype=f32, device=dev),
@@ -714,6 +697,57 @@ class ViewStack:
             scheduled = V * TX * TY < SCHEDULED_FORWARD_MAX_TILES
         self.part = (torch.empty((part_bytes(self.c, capacity, V),), dtype=torch.uint8, device=dev)
                      if scheduled else None)
+        sl = slice(first, first + V)
+        self.fwd = {k: t[sl] for k, t in fwd.items()}
+        self.dL_dimage = dL[sl]
+        self.grads = {k: t[first * n:(first + V) * n] for k, t in grads.items()}
+
+    def enqueue(self, bg, loss_grad):
+        sc, V, c = self.scene, self.V, self.c
+        preprocess_views(self.cams, sc.means, sc.scales, sc.quats, sc.opacity, sc.sh, sc.sh_degree, sc.rgb,
+                         out=self.pre, tile_test=self.tile_test)
+        keys, pl = bin_and_sort_views_async(c, V, self.pre["xy_depth"], self.pre["tiles_touched"], self.bins,
+                                            conic_op=self.pre["conic_op"], tile_test=self.tile_test)
+        tile_ranges_async(c, self.bins, out=self.ranges, order=self.order, chunks=self.chunks, n_views=V)
+        composite_fwd(c, self.ranges, pl, self.pre["xy_depth"], self.pre["conic_op"], self.pre["rgb"], bg,
+                      out=self.fwd, order=self.order, ckpt=self.ckpt, capacity=self.bins.capacity,
+                      chunks=self.chunks if self.part is not None else None, part=self.part, n_views=V)
+        if loss_grad is not None:
+            loss_grad(self.first, self.fwd["image"], self.dL_dimage)
+        composite_bwd(c, V * sc.n, self.ranges, pl, self.pre["xy_depth"], self.pre["conic_op"], self.pre["rgb"],
+                      self.fwd["final_T"], self.fwd["n_contrib"], self.dL_dimage, bg, out=self.grads,
+                      chunks=self.chunks, image=self.fwd["image"], ckpt=self.ckpt, capacity=self.bins.capacity,
+                      n_views=V)
+
+
+class ViewStack:
+    """A batch of views of one size composited as stacked frames: in a stack,
+    view v is the band of tile rows [v TY, v TY + TY) of one tile grid, so
+    each stage (one preprocess for all its cameras, one binning, one ranges
+    call, one forward, one backward) is a single launch sequence over the
+    stack instead of one per view. With streams > 1 the batch is cut into
+    that many stacks, each on its own stream (the stages of one fill the
+    gaps between those of another). Images are [V, 3, H, W], per-pixel
+    buffers [V, H, W], splat records' gradients [V*n, ...] (view v's at
+    v*n + g). No host synchronisation; `check()` reports an overflow of a
+    stack's `capacity` entries (that stack then renders the background).
+
+    loss_grad(first, image, out): writes dL/dI of views first, first + 1,
+    ... (out and image are [k, 3, H, W] slices of the batch) from their
+    images; enqueued between each stack's forward and backward.
+    """
+
+    def __init__(self, cams, scene: "Scene", capacity: int, device="cuda", bg=(0.0, 0.0, 0.0),
+                 tile_test: int = 0, scheduled=None, streams: int = 1):
+        self.device = torch.device(device)
+        self.scene, self.bg = scene, bg
+        cams = list(cams)
+        self.V = V = len(cams)
+        W, H = int(cams[0]["width"]), int(cams[0]["height"])
+        if any(int(c["width"]) != W or int(c["height"]) != H for c in cams):
+            raise ValueError("a view stack needs cameras of one size")
+        S = max(1, min(int(streams), V))
+        n, f32, i32, dev = scene.n, torch.float32, torch.int32, self.device
         self.fwd = dict(image=torch.empty((V, 3, H, W), dtype=f32, device=dev),
                         final_T=torch.empty((V, H, W), dtype=f32, device=dev),
                         n_contrib=torch.empty((V, H, W), dtype=i32, device=dev))
@@ -721,26 +755,30 @@ class ViewStack:
         self.grads = dict(grad_mean2d=torch.empty((V * n, 2), dtype=f32, device=dev),
                           grad_conic_op=torch.empty((V * n, 4), dtype=f32, device=dev),
                           grad_rgb=torch.empty((V * n, 4), dtype=f32, device=dev))
+        bounds = [round(i * V / S) for i in range(S + 1)]
+        self.groups = [_StackGroup(cams[bounds[i]:bounds[i + 1]], scene, capacity, dev, int(tile_test), scheduled,
+                                   self.fwd, self.dL_dimage, self.grads, bounds[i]) for i in range(S)]
+        # default-priority streams for every stack but the first, which runs on the caller's
+        self.streams = [torch.cuda.Stream(device=dev) for _ in range(S - 1)]
         self.graph = None
 
     def enqueue(self, loss_grad=None):
-        """Enqueue the batch on the current stream: preprocess, binning, ranges and
-        schedule, forward, loss_grad (if given), backward. Nothing waits on the host."""
-        sc, V, c = self.scene, self.V, self.c
-        preprocess_views(self.cams, sc.means, sc.scales, sc.quats, sc.opacity, sc.sh, sc.sh_degree, sc.rgb,
-                         out=self.pre, tile_test=self.tile_test)
-        keys, pl = bin_and_sort_views_async(c, V, self.pre["xy_depth"], self.pre["tiles_touched"], self.bins,
-                                            conic_op=self.pre["conic_op"], tile_test=self.tile_test)
-        tile_ranges_async(c, self.bins, out=self.ranges, order=self.order, chunks=self.chunks, n_views=V)
-        composite_fwd(c, self.ranges, pl, self.pre["xy_depth"], self.pre["conic_op"], self.pre["rgb"], self.bg,
-                      out=self.fwd, order=self.order, ckpt=self.ckpt, capacity=self.bins.capacity,
-                      chunks=self.chunks if self.part is not None else None, part=self.part, n_views=V)
-        if loss_grad is not None:
-            loss_grad(self.fwd["image"], self.dL_dimage)
-        composite_bwd(c, V * sc.n, self.ranges, pl, self.pre["xy_depth"], self.pre["conic_op"], self.pre["rgb"],
-                      self.fwd["final_T"], self.fwd["n_contrib"], self.dL_dimage, self.bg, out=self.grads,
-                      chunks=self.chunks, image=self.fwd["image"], ckpt=self.ckpt, capacity=self.bins.capacity,
-                      n_views=V)
+        """Enqueue the batch on the current stream (forked over the stacks' streams and
+        joined back): per stack preprocess, binning, ranges and schedule, forward,
+        loss_grad (if given), backward. Nothing waits on the host."""
+        main = torch.cuda.current_stream(self.device)
+        if self.streams:
+            fork = torch.cuda.Event()
+            fork.record(main)
+            for s in self.streams:
+                s.wait_event(fork)
+        for i, grp in enumerate(self.groups):
+            with torch.cuda.stream(self.streams[i - 1] if i else main):
+                grp.enqueue(self.bg, loss_grad)
+        for s in self.streams:
+            join = torch.cuda.Event()
+            join.record(s)
+            main.wait_event(join)
 
     def capture(self, loss_grad=None, warmup: int = 1):
         """Record enqueue(loss_grad) as one HIP graph (after `warmup` eager runs on a side
@@ -762,12 +800,13 @@ class ViewStack:
             raise RuntimeError("ViewStack.replay: capture() first")
         self.graph.replay()
 
-    def entries(self) -> int:
-        """Entries of the whole batch after the last run (waits for the stream)."""
-        return self.bins.entries()
+    def entries(self):
+        """Entries of each stack after the last run (waits for the stream)."""
+        return [g.bins.entries() for g in self.groups]
 
-    def check(self) -> int:
+    def check(self):
         E = self.entries()
-        if E > self.bins.capacity:
-            raise GsError(_lib.GS_ERR_CAPACITY, f"the batch's {E} entries exceed the capacity {self.bins.capacity}")
+        over = [(i, e) for i, (e, g) in enumerate(zip(E, self.groups)) if e > g.bins.capacity]
+        if over:
+            raise GsError(_lib.GS_ERR_CAPACITY, f"stacks over capacity (stack, entries): {over}")
         return E

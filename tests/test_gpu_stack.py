@@ -4,8 +4,9 @@ view alone: the records of every view bit-exact (gs_preprocess_views), each
 tile's list bit-exact (the stack's value v n + g is the view's Gaussian g),
 the image and n_contrib to the forward bar, the gradients to the backward
 bar; a HIP graph of the batch replays the eager run. Sizes: the training
-shape (400 x 400, a multiple of the tile) and a ragged one (100 x 75, whose
-bands end in rows outside the image).
+shape (400 x 400, a multiple of the tile) as one stack, and a ragged one
+(100 x 75, whose bands end in rows outside the image) cut into two stacks on
+two streams.
 """
 import sys
 
@@ -25,18 +26,25 @@ def say(*a):
 
 
 def _check_stack(orc, stack, scene_np, cams, dLdI):
-    """Each view of the stack against the oracle on that view alone."""
+    """Each view of every stack of the batch against the oracle on that view alone."""
     import torch
-    n = scene_np["n"]
     torch.cuda.synchronize()
-    E = stack.check()
-    pre = {k: to_np(v) for k, v in stack.pre.items()}
-    keys = to_np(stack.bins.keys)[:E].view(np.uint64)
-    pl = to_np(stack.bins.point_list)[:E].view(np.uint32)
-    ranges = to_np(stack.ranges).view(np.uint32)
-    TXY = ranges.shape[0] // len(cams)
+    E_all = stack.check()
+    for grp, E in zip(stack.groups, E_all):
+        _check_group(orc, stack, grp, E, scene_np, cams, dLdI)
+
+
+def _check_group(orc, stack, grp, E, scene_np, cams, dLdI):
+    n = scene_np["n"]
+    pre = {k: to_np(v) for k, v in grp.pre.items()}
+    keys = to_np(grp.bins.keys)[:E].view(np.uint64)
+    pl = to_np(grp.bins.point_list)[:E].view(np.uint32)
+    ranges = to_np(grp.ranges).view(np.uint32)
+    TXY = ranges.shape[0] // grp.V
     E_sum = 0
-    for v, cam in enumerate(cams):
+    for v in range(grp.V):
+        cam = cams[grp.first + v]
+        vb = grp.first + v  # the view's place in the batch
         o = oracle_forward(orc, cam, scene_np)
         sl = slice(v * n, (v + 1) * n)
         for k in ("xy_depth", "conic_op", "rgb", "tiles_touched"):
@@ -54,17 +62,17 @@ def _check_stack(orc, stack, scene_np, cams, dLdI):
                 raise AssertionError(f"view {v} tile {t}: list differs")
             assert (keys[r[t, 0]:r[t, 1]] >> np.uint64(32) == np.uint64(v * TXY + t)).all()
         E_sum += int(L.sum())
-        g = dict(image=to_np(stack.fwd["image"][v]), final_T=to_np(stack.fwd["final_T"][v]),
-                 n_contrib=to_np(stack.fwd["n_contrib"][v]).view(np.uint32))
+        g = dict(image=to_np(stack.fwd["image"][vb]), final_T=to_np(stack.fwd["final_T"][vb]),
+                 n_contrib=to_np(stack.fwd["n_contrib"][vb]).view(np.uint32))
         compare_forward(g, o)
-        ob = oracle_backward(orc, cam, scene_np, o, dLdI[v])
-        gg = {k: to_np(t[sl]).astype(np.float64) for k, t in stack.grads.items()}
+        ob = oracle_backward(orc, cam, scene_np, o, dLdI[vb])
+        gg = {k: to_np(t[vb * n:(vb + 1) * n]).astype(np.float64) for k, t in stack.grads.items()}
         compare_gradients(gg, ob)
     assert E_sum == E
 
 
-@pytest.mark.parametrize("size", [(400, 400), (100, 75)])
-def test_view_stack_matches_each_view(orc, size):
+@pytest.mark.parametrize("size,streams", [((400, 400), 1), ((100, 75), 2)])
+def test_view_stack_matches_each_view(orc, size, streams):
     import torch
     import gaussian_splatting_tile_amd as gs
     W, H = size
@@ -77,19 +85,20 @@ def test_view_stack_matches_each_view(orc, size):
         cam.update(width=W, height=H, fx=np.float32(cam["fx"] * s), fy=np.float32(cam["fy"] * s),
                    cx=np.float32(W / 2), cy=np.float32(H / 2))
         cams.append(cam)
-    say(f"[stack] {V} views {W}x{H}")
+    say(f"[stack] {V} views {W}x{H} as {streams} stack(s)")
     sc = gs.Scene.from_numpy(scene_np)
     rng = np.random.default_rng(5)
     dLdI = rng.standard_normal((V, 3, H, W)).astype(np.float32)
     dL = torch.from_numpy(dLdI).cuda()
-    stack = gs.ViewStack(cams, sc, capacity=V * (1 << 20))
-    stack.enqueue(lambda image, out: out.copy_(dL))
+    stack = gs.ViewStack(cams, sc, capacity=V * (1 << 20), streams=streams)
+    loss = lambda first, image, out: out.copy_(dL[first:first + out.shape[0]])
+    stack.enqueue(loss)
     _check_stack(orc, stack, scene_np, cams, dLdI)
     say(f"[stack] {W}x{H}: every view matches the oracle")
     # one HIP graph of the batch replays the eager run
     eager = {k: to_np(t).copy() for k, t in stack.fwd.items()}
     eg = {k: to_np(t).astype(np.float64) for k, t in stack.grads.items()}
-    stack.capture(lambda image, out: out.copy_(dL))
+    stack.capture(loss)
     for rep in range(2):
         stack.fwd["image"].fill_(float("nan"))
         for t in stack.grads.values():
