@@ -6,7 +6,7 @@ the image and n_contrib to the forward bar, the gradients to the backward
 bar; a HIP graph of the batch replays the eager run. Sizes: the training
 shape (400 x 400, a multiple of the tile) as one stack, and a ragged one
 (100 x 75, whose bands end in rows outside the image) cut into two stacks on
-two streams.
+two streams, and into four stacks of one view each.
 """
 import sys
 
@@ -71,7 +71,7 @@ def _check_group(orc, stack, grp, E, scene_np, cams, dLdI):
     assert E_sum == E
 
 
-@pytest.mark.parametrize("size,streams", [((400, 400), 1), ((100, 75), 2)])
+@pytest.mark.parametrize("size,streams", [((400, 400), 1), ((100, 75), 2), ((100, 75), 4)])
 def test_view_stack_matches_each_view(orc, size, streams):
     import torch
     import gaussian_splatting_tile_amd as gs
