@@ -341,9 +341,10 @@ gs_status gs_tile_ranges_async(const gs_camera* cam, const uint64_t* keys, const
  *   keys, ranges, tile_order  as gs_tile_ranges / gs_tile_ranges_async
  *   capacity    length of keys; n_entries <= capacity when n_entries_dev is
  *               NULL
- *   chunks      out uint32 [4 + 4 (TX*TY + ceil(capacity / 256))], 16-byte
- *               aligned, or NULL: the work items of gs_composite_fwd_ex and
- *               gs_composite_bwd_ex.
+ *   chunks      out uint32 [4 + 4 * (TX * TY * n_views + ceil(capacity / 256))],
+ *               16-byte aligned, or NULL: the work items of
+ *               gs_composite_fwd_ex and gs_composite_bwd_ex (the compositing
+ *               launches read up to that many items, one per workgroup).
  *               chunks[0] = the item count; words 1-3 unused; from word 4,
  *               for each item, (tile, k, list start, L). When the lists
  *               average more than 256 entries (E > 256 TX TY), every list
@@ -494,7 +495,7 @@ size_t gs_composite_part_bytes(const gs_camera* cam, int32_t n_views, int64_t ca
  *             counts the records of the whole stack)
  *   chunks    the schedule gs_tile_ranges_ex wrote for this frame's ranges
  *   capacity  as gs_composite_fwd_ex (the same value)
- *   image     [3][H][W] the image gs_composite_fwd_ex wrote
+ *   image     [n_views][3][H][W] the image gs_composite_fwd_ex wrote
  *   ckpt      the checkpoints gs_composite_fwd_ex wrote in the same frame
  *             (may be NULL only when capacity is 0)
  * Other arguments as gs_composite_bwd; every input must come from the same
@@ -533,8 +534,8 @@ gs_status gs_appearance_fwd(const gs_camera* cam, int32_t n, const float* means,
 
 /* ---------------------------------------------------------------------
  * gs_appearance_bwd - gradients of gs_appearance_fwd ("rigel" README,
- * "Appearance MLP": latents get their gradient directly, view directions
- * are constants). With g = dL/drgb:
+ * "Appearance MLP": the latents receive a gradient, the view direction is
+ * held constant). With g = dL/drgb:
  *   dy = g s (1 - s);  dz = (W2^T dy) on the active units (z > 0), else 0;
  *   dL/dlatent = W1[:, :L]^T dz;  dW2 = sum dy h^T;  db2 = sum dy;
  *   dW1 = sum dz x^T;  db1 = sum dz  (sums over all n Gaussians).

@@ -84,6 +84,8 @@ def lib():
         for name in ("orc_composite_bwd_f32", "orc_composite_bwd_f64"):
             getattr(_lib, name).restype = None
             getattr(_lib, name).argtypes = [ctypes.POINTER(Camera), ctypes.c_int32] + [P] * 12
+        _lib.orc_composite_bwd_mass_f32.restype = None
+        _lib.orc_composite_bwd_mass_f32.argtypes = [ctypes.POINTER(Camera), ctypes.c_int32] + [P] * 15
         _lib.orc_constants.restype = None
         _lib.orc_constants.argtypes = [P]
         _lib.orc_sh_basis.restype = None
@@ -283,8 +285,10 @@ def composite_fwd(cam: dict, ranges, point_list, xy_depth, conic_op, rgb, bg=(0.
 
 
 def composite_bwd(cam: dict, n: int, ranges, point_list, xy_depth, conic_op, rgb, final_T,
-                  n_contrib, dL_dimage, bg=(0.0, 0.0, 0.0), dtype=np.float32):
-    """Returns dict grad_mean2d [n,2], grad_conic_op [n,4], grad_rgb [n,4] (float64)."""
+                  n_contrib, dL_dimage, bg=(0.0, 0.0, 0.0), dtype=np.float32, mass=False):
+    """Returns dict grad_mean2d [n,2], grad_conic_op [n,4], grad_rgb [n,4] (float64).
+    With mass (float32 only), also mass_mean2d, mass_conic_op, mass_rgb: per
+    element, the sum over pixels of the magnitudes of its terms."""
     ranges = _c(ranges, np.uint32)
     point_list = _c(point_list, np.uint32)
     n_contrib = _c(n_contrib, np.uint32)
@@ -293,11 +297,19 @@ def composite_bwd(cam: dict, n: int, ranges, point_list, xy_depth, conic_op, rgb
     bg = _c(bg, dtype)
     out = dict(grad_mean2d=np.zeros((n, 2), np.float64), grad_conic_op=np.zeros((n, 4), np.float64),
                grad_rgb=np.zeros((n, 4), np.float64))
-    fn = lib().orc_composite_bwd_f32 if dtype == np.float32 else lib().orc_composite_bwd_f64
     c = make_camera(cam)
-    fn(ctypes.byref(c), n, _p(ranges), _p(point_list), _p(xy_depth), _p(conic_op), _p(rgb), _p(bg),
-       _p(final_T), _p(n_contrib), _p(dL_dimage), _p(out["grad_mean2d"]), _p(out["grad_conic_op"]),
-       _p(out["grad_rgb"]))
+    args = [ctypes.byref(c), n, _p(ranges), _p(point_list), _p(xy_depth), _p(conic_op), _p(rgb), _p(bg),
+            _p(final_T), _p(n_contrib), _p(dL_dimage), _p(out["grad_mean2d"]), _p(out["grad_conic_op"]),
+            _p(out["grad_rgb"])]
+    if mass:
+        assert dtype == np.float32, "the term magnitudes are taken of the float32 backward"
+        for k, w in (("mass_mean2d", 2), ("mass_conic_op", 4), ("mass_rgb", 4)):
+            out[k] = np.zeros((n, w), np.float64)
+            args.append(_p(out[k]))
+        lib().orc_composite_bwd_mass_f32(*args)
+        return out
+    fn = lib().orc_composite_bwd_f32 if dtype == np.float32 else lib().orc_composite_bwd_f64
+    fn(*args)
     return out
 
 

@@ -879,17 +879,32 @@ void composite_fwd(const orc_camera* cam, const uint32_t* ranges, const uint32_t
 // dL/dpower = a dL/da feed dA, dB, dC, du, dv. Summed over pixels in double.
 // Outputs: grad_mean2d [n][2], grad_conic_op [n][4] (dA, dB, dC, dopacity),
 // grad_rgb [n][4] (last slot 0). They are overwritten.
+// Optionally (mass_* non-NULL) also the per-element sum over pixels of the
+// magnitudes of the terms each gradient is summed from, the scale against
+// which a float32 sum with cancellation is judged.
 template <typename F>
 void composite_bwd(const orc_camera* cam, int32_t n, const uint32_t* ranges,
                    const uint32_t* point_list, const F* xy_depth, const F* conic_op,
                    const F* rgb, const F* bg, const F* final_T, const uint32_t* n_contrib,
                    const F* dL_dimage, double* grad_mean2d, double* grad_conic_op,
-                   double* grad_rgb) {
+                   double* grad_rgb, double* mass_mean2d = nullptr, double* mass_conic_op = nullptr,
+                   double* mass_rgb = nullptr) {
     const int Wd = cam->width, Hd = cam->height, TX = tiles_x(cam);
     const F alpha_min = (F)ALPHA_MIN, alpha_max = (F)ALPHA_MAX;
     std::fill(grad_mean2d, grad_mean2d + 2 * (size_t)n, 0.0);
     std::fill(grad_conic_op, grad_conic_op + 4 * (size_t)n, 0.0);
     std::fill(grad_rgb, grad_rgb + 4 * (size_t)n, 0.0);
+    const bool mass = mass_mean2d && mass_conic_op && mass_rgb;
+    if (mass) {
+        std::fill(mass_mean2d, mass_mean2d + 2 * (size_t)n, 0.0);
+        std::fill(mass_conic_op, mass_conic_op + 4 * (size_t)n, 0.0);
+        std::fill(mass_rgb, mass_rgb + 4 * (size_t)n, 0.0);
+    }
+    // adds a term to a gradient element (and its magnitude to the mass)
+    auto add = [&](double* grad, double* m, size_t i, F term) {
+        grad[i] += (double)term;
+        if (mass) m[i] += std::fabs((double)term);
+    };
     for (int y = 0; y < Hd; ++y) {
         for (int x = 0; x < Wd; ++x) {
             const int tile = (y / TILE) * TX + (x / TILE);
@@ -912,7 +927,7 @@ void composite_bwd(const orc_camera* cam, int32_t n, const uint32_t* ranges,
                 const F Tj = T / ((F)1 - a);
                 F dL_da = 0;
                 for (int ch = 0; ch < 3; ++ch) {
-                    grad_rgb[4 * (size_t)g + ch] += (double)(a * Tj * gpix[ch]);
+                    add(grad_rgb, mass_rgb, 4 * (size_t)g + ch, a * Tj * gpix[ch]);
                     dL_da = dL_da + gpix[ch] * (c[ch] - B[ch]);
                 }
                 dL_da = dL_da * Tj;
@@ -920,12 +935,12 @@ void composite_bwd(const orc_camera* cam, int32_t n, const uint32_t* ranges,
                 T = Tj;
                 if (a_raw > alpha_max) continue;  // saturated: no gradient to o, conic, mean
                 const F dp = a * dL_da;
-                grad_conic_op[4 * (size_t)g + 3] += (double)(G * dL_da);
-                grad_conic_op[4 * (size_t)g + 0] += (double)((F)(-0.5) * dx * dx * dp);
-                grad_conic_op[4 * (size_t)g + 1] += (double)(-dx * dy * dp);
-                grad_conic_op[4 * (size_t)g + 2] += (double)((F)(-0.5) * dy * dy * dp);
-                grad_mean2d[2 * (size_t)g + 0] += (double)((co[0] * dx + co[1] * dy) * dp);
-                grad_mean2d[2 * (size_t)g + 1] += (double)((co[1] * dx + co[2] * dy) * dp);
+                add(grad_conic_op, mass_conic_op, 4 * (size_t)g + 3, G * dL_da);
+                add(grad_conic_op, mass_conic_op, 4 * (size_t)g + 0, (F)(-0.5) * dx * dx * dp);
+                add(grad_conic_op, mass_conic_op, 4 * (size_t)g + 1, -dx * dy * dp);
+                add(grad_conic_op, mass_conic_op, 4 * (size_t)g + 2, (F)(-0.5) * dy * dy * dp);
+                add(grad_mean2d, mass_mean2d, 2 * (size_t)g + 0, (co[0] * dx + co[1] * dy) * dp);
+                add(grad_mean2d, mass_mean2d, 2 * (size_t)g + 1, (co[1] * dx + co[2] * dy) * dp);
             }
         }
     }
@@ -958,6 +973,18 @@ void orc_composite_bwd_f32(const orc_camera* cam, int32_t n, const uint32_t* ran
                            double* grad_conic_op, double* grad_rgb) {
     composite_bwd<float>(cam, n, ranges, point_list, xy_depth, conic_op, rgb, bg, final_T,
                          n_contrib, dL_dimage, grad_mean2d, grad_conic_op, grad_rgb);
+}
+
+// orc_composite_bwd_f32 plus the per-element term magnitudes (mass_*,
+// laid out as the gradients).
+void orc_composite_bwd_mass_f32(const orc_camera* cam, int32_t n, const uint32_t* ranges,
+                                const uint32_t* point_list, const float* xy_depth, const float* conic_op,
+                                const float* rgb, const float* bg, const float* final_T,
+                                const uint32_t* n_contrib, const float* dL_dimage, double* grad_mean2d,
+                                double* grad_conic_op, double* grad_rgb, double* mass_mean2d,
+                                double* mass_conic_op, double* mass_rgb) {
+    composite_bwd<float>(cam, n, ranges, point_list, xy_depth, conic_op, rgb, bg, final_T, n_contrib,
+                         dL_dimage, grad_mean2d, grad_conic_op, grad_rgb, mass_mean2d, mass_conic_op, mass_rgb);
 }
 
 void orc_composite_bwd_f64(const orc_camera* cam, int32_t n, const uint32_t* ranges,

@@ -267,6 +267,25 @@ def test_chunked_composite_validates_before_launch(gs):
     assert rng(views=33) == _lib.GS_ERR_INVALID and b"n_views" in gs.gs_last_error()
 
 
+def test_header_chunk_schedule_size_matches_binding():
+    """The size gs.h states for the chunk schedule of gs_tile_ranges_ex, read
+    from the header and evaluated, equals what the binding allocates, for
+    single views and view stacks (the compositing launches index up to that
+    many items)."""
+    import math
+    import re
+    from gaussian_splatting_tile_amd.rasterizer import chunk_words
+    text = open(os.path.join(ROOT, "include", "gs.h")).read()
+    m = re.search(r"\*\s+chunks\s+out uint32 \[(.+?)\],", text)
+    assert m, "chunk schedule size not found in gs.h"
+    expr = m.group(1)
+    for (W, H, views, cap) in [(64, 64, 1, 1000), (400, 400, 4, 2_560_000), (100, 75, 16, 12345),
+                               (1920, 1080, 1, 1_600_000), (33, 17, 32, 0)]:
+        TX, TY = -(-W // 16), -(-H // 16)
+        want = eval(expr, {"__builtins__": {}}, dict(TX=TX, TY=TY, n_views=views, capacity=cap, ceil=math.ceil))
+        assert want == chunk_words(dict(width=W, height=H), cap, views), (W, H, views, cap)
+
+
 def test_view_stack_validates_before_launch(gs):
     """gs_preprocess_views and gs_bin_and_sort_views_async check the stack
     (camera count and sizes, the splat total, the tile count) before any

@@ -59,7 +59,7 @@ def test_ellipse_backward_parity(orc):
     scene, cam, dLdI = synth.config_scene("cfg2")
     o = orc.render_fwd(cam, scene, tile_test=1)
     ob = orc.composite_bwd(cam, scene["n"], o["ranges"], o["point_list"], o["xy_depth"], o["conic_op"], o["rgb"],
-                           o["final_T"], o["n_contrib"], dLdI)
+                           o["final_T"], o["n_contrib"], dLdI, mass=True)
     g, out, sc = _gpu_forward(cam, scene, 1)
     grads = gpu_backward(cam, sc, out, dLdI)
     say("[ellipse cfg2 bwd]", compare_gradients(grads, ob))
@@ -84,7 +84,7 @@ def test_ellipse_small_and_ragged(orc):
             g[k] = g[k].view(np.uint32)
         assert_preprocess_equal(g, o)
         assert_binning_equal(g, o)
-        compare_forward(g, o)
+        compare_forward(g, o, (0.1, 0.2, 0.3))
 
 
 def test_ellipse_async_views_match_blocking(orc):

@@ -76,7 +76,7 @@ def test_graph_replays_match_eager_and_oracle(orc, streams):
     compare_forward(g0, o)
     dLdI = to_np(batch.views[0]["dL_dimage"])
     ob = orc.composite_bwd(cams[0], scene_np["n"], o["ranges"], o["point_list"], o["xy_depth"], o["conic_op"],
-                           o["rgb"], o["final_T"], o["n_contrib"], dLdI)
+                           o["rgb"], o["final_T"], o["n_contrib"], dLdI, mass=True)
     rep = compare_gradients(g0, ob)
     say(f"[graph] view 0 vs oracle {rep}")
 

@@ -130,7 +130,7 @@ def test_ragged_and_sh_degrees(orc, W, H, n, deg):
     g, out, sc, _ = gpu_forward(cam, scene, bg=bg, capacity=64)  # forces the capacity retry
     assert_preprocess_equal(g, ofwd)
     assert_binning_equal(g, ofwd)
-    compare_forward(g, ofwd)
+    compare_forward(g, ofwd, bg)
     dLdI = synth.upstream_gradient(n, W, H)
     obwd = oracle_backward(orc, cam, scene, ofwd, dLdI, bg)
     compare_gradients(gpu_backward(cam, sc, out, dLdI, bg), obwd)
@@ -254,7 +254,7 @@ def test_chunked_backward_at_list_boundaries(orc):
     obwd = oracle_backward(orc, cam, scene, ofwd, dLdI, bg)
     g, out, sc, _ = gpu_forward(cam, scene, bg=bg)
     assert_binning_equal(g, ofwd)
-    compare_forward(g, ofwd)
+    compare_forward(g, ofwd, bg)
     compare_gradients(gpu_backward(cam, sc, out, dLdI, bg), obwd)
     compare_gradients(gpu_backward(cam, sc, out, dLdI, bg, chunked=True), obwd)
 
@@ -272,7 +272,7 @@ def test_chunked_backward_at_list_boundaries(orc):
     dL1 = synth.upstream_gradient(8, 16, 16)
     ob1 = oracle_backward(orc, cam1, opaque, o1, dL1, bg)
     g1, out1, sc1, _ = gpu_forward(cam1, opaque, bg=bg)
-    compare_forward(g1, o1)
+    compare_forward(g1, o1, bg)
     compare_gradients(gpu_backward(cam1, sc1, out1, dL1, bg, chunked=True), ob1)
 
 
