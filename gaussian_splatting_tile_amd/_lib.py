@@ -18,7 +18,7 @@ EXPORTS = ("gs_constants", "gs_last_error", "gs_version", "gs_preprocess", "gs_p
            "gs_bin_and_sort_async", "gs_tile_ranges", "gs_tile_ranges_async", "gs_composite_fwd",
            "gs_composite_bwd", "gs_composite_fwd_ex", "gs_composite_part_bytes", "gs_composite_bwd_ex", "gs_tile_ranges_ex",
            "gs_preprocess_views", "gs_bin_and_sort_views_async", "gs_appearance_fwd",
-           "gs_appearance_bwd")
+           "gs_appearance_bwd", "gs_bin_and_sort_async_noalloc")
 
 
 class GsCamera(ctypes.Structure):
@@ -86,6 +86,8 @@ def load() -> ctypes.CDLL:
     lib.gs_composite_part_bytes.argtypes = [CAM, I32, I64]
     lib.gs_preprocess_views.restype = ctypes.c_int
     lib.gs_preprocess_views.argtypes = [P, I32, I32, P, P, P, P, P, I32, P, P, P, P, P, U32, P]
+    lib.gs_bin_and_sort_async_noalloc.restype = ctypes.c_int
+    lib.gs_bin_and_sort_async_noalloc.argtypes = [CAM, I32, P, P, P, P, P, I64, P, U32, P]
     lib.gs_bin_and_sort_views_async.restype = ctypes.c_int
     lib.gs_bin_and_sort_views_async.argtypes = [CAM, I32, I32, P, P, P, P, P, I64, P,
                                                 ctypes.POINTER(ctypes.c_size_t), P, U32, P]

@@ -4,9 +4,17 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "gs_internal.h"
+
+// The binning workspace of gs_bin_and_sort_async_noalloc: one fixed array
+// per GPU, which each device holds from the library's load on it until the
+// process ends. In host code this name is only a stand-in for the symbol;
+// its device address on the current device comes from hipGetSymbolAddress
+// (static_scratch below), and only that address is ever passed to kernels.
+static __device__ __align__(256) unsigned char scratch[GS_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -294,6 +302,71 @@ gs_status gs_bin_and_sort_async(const gs_camera* cam, int32_t n, const float* xy
                                 uint64_t* n_entries_dev, void* stream) {
     return gs_bin_and_sort_async_ex(cam, n, xy_depth, nullptr, tiles_touched, keys, point_list, capacity,
                                     scratch, scratch_bytes, n_entries_dev, GS_TILES_SQUARE, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Device address of `scratch` on each device, looked up on the first
+// no-allocation call made with that device current.
+constexpr int kMaxDevices = 64;
+std::mutex g_static_mu;
+void* g_static_ptr[kMaxDevices] = {};
+
+gs_status static_scratch(void** out) {
+    int dev = -1;
+    if (gs_status e = hip_check(hipGetDevice(&dev), "hipGetDevice")) return e;
+    if (dev < 0 || dev >= kMaxDevices) return fail(GS_ERR_INVALID, "device %d outside [0, %d)", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_static_mu);
+    if (!g_static_ptr[dev]) {
+        void* p = nullptr;
+        if (gs_status e = hip_check(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)"))
+            return e;
+        if (!p || ((uintptr_t)p & 255)) return fail(GS_ERR_HIP, "static workspace has no 256-byte aligned address");
+        g_static_ptr[dev] = p;
+    }
+    *out = g_static_ptr[dev];
+    return GS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gs_status gs_bin_and_sort_async_noalloc(const gs_camera* cam, int32_t n, const float* xy_depth,
+                                        const float* conic_op, const uint32_t* tiles_touched, uint64_t* keys,
+                                        uint32_t* point_list, int64_t capacity, uint64_t* n_entries_dev,
+                                        uint32_t flags, void* stream) {
+    g_last_error.clear();
+    const char* fn = "gs_bin_and_sort_async_noalloc";
+    gs::BinScratch s{};
+    bool query = false;
+    size_t need = 0;
+    // the size first (no device call): arguments and the workspace this call needs
+    if (gs_status e = bin_args(fn, cam, n, xy_depth, tiles_touched, keys, point_list, capacity, nullptr, &need,
+                               &query, &s))
+        return e;
+    if (need > (size_t)GS_NOALLOC_SCRATCH_BYTES)
+        return fail(GS_ERR_INVALID,
+                    "%s: n = %d and capacity = %lld need %zu bytes of workspace, more than the fixed %zu; "
+                    "use gs_bin_and_sort_async_ex with a caller-owned workspace",
+                    fn, n, (long long)capacity, need, (size_t)GS_NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    if (gs_status e = static_scratch(&ws)) return e;
+    size_t have = GS_NOALLOC_SCRATCH_BYTES;
+    if (gs_status e = bin_args(fn, cam, n, xy_depth, tiles_touched, keys, point_list, capacity, ws, &have, &query,
+                               &s))
+        return e;
+    if (gs_status e = tile_test_args(fn, n, conic_op, flags)) return e;
+    if (!n_entries_dev || ((uintptr_t)n_entries_dev & 7))
+        return fail(GS_ERR_INVALID, "%s: n_entries_dev must be an 8-byte aligned device pointer", fn);
+    hipStream_t st = (hipStream_t)stream;
+    if (n == 0) return hip_check(gs::launch_fill_u32((uint32_t*)n_entries_dev, 2, 0u, st), "entry count clear");
+    return hip_check(gs::launch_bin_and_sort(*cam, 1, n, (const float4*)xy_depth, (const float4*)conic_op,
+                                             tiles_touched, keys, point_list, (uint32_t)capacity, s, n_entries_dev,
+                                             flags, st),
+                     "bin_and_sort launch");
 }
 
 namespace {

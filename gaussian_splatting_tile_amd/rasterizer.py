@@ -272,6 +272,25 @@ def bin_and_sort_async(cam, xy_depth, tiles_touched, buffers: BinBuffers, stream
     return buffers.keys, buffers.point_list
 
 
+def bin_and_sort_async_noalloc(cam, xy_depth, tiles_touched, keys, point_list, n_entries_dev, stream=None,
+                               conic_op=None, tile_test=0):
+    """gs_bin_and_sort_async_noalloc: as bin_and_sort_async, into the caller's keys (int64
+    [capacity]) and point_list (int32 [capacity]), with the library's fixed workspace instead
+    of a scratch buffer. E lands in n_entries_dev (int64 [1]). Calls that overlap on one GPU
+    race on that workspace."""
+    c = _cam(cam)
+    n = int(tiles_touched.shape[0])
+    capacity = int(keys.numel())
+    if point_list.numel() != capacity:
+        raise ValueError("keys and point_list must have the same length")
+    _lib.check(_lib.load().gs_bin_and_sort_async_noalloc(
+        ctypes.byref(c), n, _ptr(xy_depth, torch.float32, "xy_depth"), _ptr(conic_op, torch.float32, "conic_op"),
+        _ptr(tiles_touched, torch.int32, "tiles_touched"), _ptr(keys, torch.int64, "keys"),
+        _ptr(point_list, torch.int32, "point_list"), capacity, _ptr(n_entries_dev, torch.int64, "n_entries_dev"),
+        int(tile_test), _stream(stream)))
+    return keys, point_list
+
+
 def _check_chunks(chunks, cam, capacity, n_views=1):
     need = chunk_words(cam, capacity, n_views)
     if chunks.dtype != torch.int32 or chunks.numel() < need:

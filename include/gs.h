@@ -287,6 +287,37 @@ gs_status gs_bin_and_sort_async_ex(const gs_camera* cam, int32_t n, const float*
                                    int64_t capacity, void* scratch, size_t* scratch_bytes,
                                    uint64_t* n_entries_dev, uint32_t flags, void* stream);
 
+/* ---------------------------------------------------------------------
+ * gs_bin_and_sort_async_noalloc - gs_bin_and_sort_async_ex for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the same work, order,
+ * results and flags, with the binning workspace taken from a fixed array
+ * inside the library instead of a caller-owned scratch buffer.
+ *
+ * The array holds GS_NOALLOC_SCRATCH_BYTES (128 MiB) on every GPU the
+ * library is loaded on, for the life of the process; its address on the
+ * current device is looked up on the first call made with that device
+ * current. A call whose workspace (the scratch size gs_bin_and_sort_async
+ * reports for the same n and capacity) exceeds it returns GS_ERR_INVALID,
+ * with a message, before anything is enqueued: about n = 1M Gaussians with
+ * capacity = 5M entries fits. The call allocates nothing (no hipMalloc, no
+ * hipFree) and needs no cleared memory: every word of the workspace that a
+ * kernel reads was written earlier in the same call.
+ *
+ * All calls on one GPU share that GPU's array, which keeps the last call's
+ * contents: two such calls that overlap on one GPU (on different streams,
+ * or from different threads without ordering) race and corrupt each other's
+ * results. Order them on one stream, or use gs_bin_and_sort_async_ex.
+ *
+ *   cam, n, xy_depth, conic_op, tiles_touched, keys, point_list, capacity,
+ *   n_entries_dev, flags, stream: as gs_bin_and_sort_async_ex
+ * ------------------------------------------------------------------- */
+#define GS_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+gs_status gs_bin_and_sort_async_noalloc(const gs_camera* cam, int32_t n, const float* xy_depth,
+                                        const float* conic_op, const uint32_t* tiles_touched, uint64_t* keys,
+                                        uint32_t* point_list, int64_t capacity, uint64_t* n_entries_dev,
+                                        uint32_t flags, void* stream);
+
 /* gs_bin_and_sort_views_async - gs_bin_and_sort_async_ex over a stack of
  * n_views views (see gs_preprocess_views): xy_depth, conic_op and
  * tiles_touched hold n_views n records, view v's at v n + g; an entry's
