@@ -55,13 +55,34 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(name: str, min_seconds: float = 10.0, max_frames: int = 8):
-    """Time the oracle (single thread, as it stands) on whole frames of the
-    same workload, forward and backward, repeating the frame until about
-    min_seconds of CPU work have been timed."""
+def cpu_model() -> str:
+    """The host CPU's model name, from /proc/cpuinfo."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_threads() -> int:
+    """Host threads for the threaded oracle run: the CPUs this process may
+    use, capped by OMP_NUM_THREADS when it is set."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    try:
+        n = min(n, int(os.environ.get("OMP_NUM_THREADS", n)))
+    except ValueError:
+        pass
+    return max(1, n)
+
+
+def _oracle_frames(name: str, min_seconds: float, max_frames: int):
     import oracle
     import synth
     scene, cam, dLdI = synth.config_scene(name)
+    if dLdI is None:
+        dLdI = synth.upstream_gradient(3001, cam["width"], cam["height"])
     frames, total = 0, 0.0
     while frames < max_frames and (frames == 0 or total < min_seconds):
         t0 = time.perf_counter()
@@ -70,10 +91,32 @@ def cpu_baseline(name: str, min_seconds: float = 10.0, max_frames: int = 8):
                              fwd["conic_op"], fwd["rgb"], fwd["final_T"], fwd["n_contrib"], dLdI)
         total += time.perf_counter() - t0
         frames += 1
+    return frames, total
+
+
+def cpu_baseline(name: str, min_seconds: float = 10.0, max_frames: int = 8):
+    """Time the oracle (as it stands) on whole frames of the same workload,
+    forward and backward: single-threaded (the reported value), repeating the
+    frame until about min_seconds of CPU work have been timed; then its
+    threaded run (the preprocess and compositing over all host threads the
+    process may use; the binning and sort stay single-threaded) for about
+    half that time."""
+    import oracle
+    frames, total = _oracle_frames(name, min_seconds, max_frames)
+    threads = oracle_threads()
+    try:
+        oracle.set_threads(threads)
+        mframes, mtotal = _oracle_frames(name, min_seconds / 2, 4 * max_frames)
+    finally:
+        oracle.set_threads(1)
     return {"value": round(frames / total, 4), "unit": "frames/s", "cores": 1, "kind": "oracle",
             "sample": f"{frames} full {name} frame(s) (preprocess, bin, sort, ranges, forward and "
                       f"backward compositing), single-threaded, {total:.2f} s in total",
-            "seconds": round(total, 3)}
+            "seconds": round(total, 3), "cpu_model": cpu_model(),
+            "threaded": {"value": round(mframes / mtotal, 4), "unit": "frames/s", "threads": threads,
+                         "sample": f"{mframes} full {name} frame(s), preprocess and compositing over "
+                                   f"{threads} threads (OpenMP), {mtotal:.2f} s in total",
+                         "seconds": round(mtotal, 3)}}
 
 
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "k_composite_bwd_cfg2_hbm_traffic.md")
@@ -340,7 +383,8 @@ def main():
     stage_ms = {}
     for i, s in enumerate(STAGES):
         vals = [m[i].elapsed_time(m[i + 1]) for m in staged]
-        stage_ms[s] = float(np.median(vals)), float(np.mean(vals))
+        stage_ms[s] = (float(np.median(vals)), float(np.mean(vals)), float(np.percentile(vals, 10)),
+                       float(np.percentile(vals, 90)))
     # The same frames with the ellipse tile test (identical image, shorter
     # lists): timed the same way, reported as a secondary figure.
     for _ in range(args.warmup):
@@ -426,6 +470,7 @@ def main():
                    "evals_fwd": evals_fwd, "evals_bwd": evals_bwd},
         "pixel_splat_evals_per_s": round((evals_fwd + evals_bwd) * fps, 1),
         "stage_ms_median": {s: round(v[0], 4) for s, v in stage_ms.items()},
+        "stage_ms_p10_p90": {s: [round(v[2], 4), round(v[3], 4)] for s, v in stage_ms.items()},
         "timed_kernel_ms_mean": {"composite_fwd": round(fwd_s * 1e3, 4),
                                  "composite_bwd": round(bwd_s * 1e3, 4)},
         "roofline": {"bound": "alu", "kernel": "k_composite_bwd<true>" if chunked else "k_composite_bwd<false>",

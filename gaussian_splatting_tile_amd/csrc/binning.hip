@@ -595,56 +595,112 @@ __device__ __forceinline__ uint32_t heavy_first_key(uint32_t len) {
     return 255u - min(255u, 1u + 16u * (uint32_t)msb + frac);
 }
 
+// Length of tile t's run, with ranges[t] checked against the sorted keys:
+// ranges are written only at run boundaries (k_ranges), so a tile without
+// entries in this frame holds whatever an earlier frame left; its range is
+// taken as empty unless start < end <= E and keys[start] names the tile.
+__device__ __forceinline__ uint2 checked_range(uint2 r, const uint64_t* __restrict__ keys, uint32_t E, int t) {
+    const bool ok = r.x < r.y && r.y <= E && (uint32_t)(keys[r.x] >> 32) == (uint32_t)t;
+    return ok ? r : make_uint2(0u, 0u);
+}
+
+// The tile ranges' clean-up and the compositing schedules. Every tile's
+// range is checked (checked_range) and empty ones are set to (0, 0).
 // order = the tiles in descending order of list length (by class; the
 // order within a class is unspecified). chunks = the work items of the
 // scheduled compositing after a count (padded to 16 bytes), each (tile,
 // chunk index, list start, list length). When the lists average more than
-// one chunk (E > kChunk tiles) every list longer than a chunk is cut into
-// kChunk-entry chunks, in descending order of the list length from the
-// chunk's start to the list's end: the front chunks of the longest lists
-// first, since a pixel that stops early leaves the later chunks of its list
-// little to do; shorter lists (empty ones too) are whole items, placed by
-// their length in the same order. Otherwise the
-// tiles alone give a launch enough workgroups, and every list is one item
-// (chunk index kWholeList), in the order of `order`. One
-// workgroup of 1024 threads: class histograms, exclusive scans, scatter
-// through per-class cursors. order and chunks may be NULL.
-__global__ __launch_bounds__(1024) void k_tile_order(const uint32_t* __restrict__ ranges, int n_tiles,
-                                                     const uint64_t* __restrict__ total, uint32_t n_entries,
-                                                     uint32_t capacity, uint32_t* __restrict__ order,
-                                                     uint32_t* __restrict__ chunks) {
-    constexpr int kSweep = 8;  // tiles per thread per sweep, their ranges loaded together
-    __shared__ uint32_t s_hist[2][kRadix];  // tiles, chunks per class; then the class cursors
+// one chunk (E > kChunk tiles), every list longer than a chunk is cut into
+// kChunk-entry chunks and shorter ones (empty ones too) are whole items
+// (chunk index kWholeList); otherwise every list is a whole item. Items
+// come in descending order of the list length from the item's start to the
+// list's end: the front chunks of the longest lists first, since a pixel
+// that stops early leaves the later chunks of its list little to do. order
+// and chunks may be NULL (then only the ranges are cleaned).
+//
+// One workgroup of 1024 threads, each over the same kSweep tiles per sweep
+// in both passes: class histograms, exclusive scans, then placement through
+// per-class cursors. Empty tiles, often the largest class, go last in the
+// order of a block scan of per-thread counts. (Bumping the LDS counters once
+// per run of equal classes in a wave, or spreading the work over several
+// workgroups that each count every tile, measured slower.)
+constexpr int kOrderThreads = 1024;
+
+__global__ __launch_bounds__(kOrderThreads) void k_tile_schedule(uint32_t* __restrict__ ranges, int n_tiles,
+                                                                 const uint64_t* __restrict__ keys,
+                                                                 const uint64_t* __restrict__ total,
+                                                                 uint32_t n_entries, uint32_t capacity,
+                                                                 uint32_t* __restrict__ order,
+                                                                 uint32_t* __restrict__ chunks) {
+    constexpr int kSweep = 8;                             // tiles per thread per sweep, loaded together
+    constexpr int kSweepTiles = kOrderThreads * kSweep;
+    __shared__ uint32_t s_hist[2][kRadix];  // non-empty tiles, their chunk items per class; then the cursors
     __shared__ uint32_t s_wsum[2][kRadix / 64];
-    const int tid = threadIdx.x, lane = tid & 63;
-    const uint2* const r2 = reinterpret_cast<const uint2*>(ranges);
+    __shared__ uint32_t s_esum[kOrderThreads / 64];
+    __shared__ uint32_t s_items[2];  // non-empty tiles, their items
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint2* const r2 = reinterpret_cast<uint2*>(ranges);
     const uint32_t E = total ? usable_entries(total, capacity) : n_entries;
-    const bool split = chunks && (uint64_t)E > (uint64_t)kChunk * (uint64_t)n_tiles;
-    const bool by_tile = order || (chunks && !split);  // the tile classes are needed
+    // lists longer than `cut` become chunks: every list of more than a chunk
+    // when the lists average more than one, else none (the tiles alone then
+    // give a compositing launch enough workgroups; cutting the longest lists
+    // too measured slower)
+    const uint32_t cut = (uint64_t)E > (uint64_t)kChunk * (uint64_t)n_tiles ? (uint32_t)kChunk : 0xFFFFFFFFu;
+    const bool split = chunks != nullptr;  // the items, by the classes of the chunks
+    const bool by_tile = order != nullptr;  // the tile classes
+    const bool sched = order || chunks;
+    uint4* const items = chunks ? reinterpret_cast<uint4*>(chunks + 4) : nullptr;
     if (tid < 2 * kRadix) (&s_hist[0][0])[tid] = 0u;
     __syncthreads();
-    for (int base = 0; base < n_tiles; base += 1024 * kSweep) {
-        uint2 r[kSweep];
+    // 1. check every range; count the classes of the non-empty tiles and of
+    //    their chunk items, and this thread's empty tiles
+    uint2 r[kSweep];
+    uint32_t empties = 0;
+    for (int base = 0; base < n_tiles; base += kSweepTiles) {
 #pragma unroll
         for (int k = 0; k < kSweep; ++k) {
-            const int t = base + k * 1024 + tid;
+            const int t = base + k * kOrderThreads + tid;
             r[k] = t < n_tiles ? r2[t] : make_uint2(0u, 0u);
         }
 #pragma unroll
         for (int k = 0; k < kSweep; ++k) {
-            const int t = base + k * 1024 + tid;
+            const int t = base + k * kOrderThreads + tid;
+            const uint2 c = checked_range(r[k], keys, E, t);
+            if (t < n_tiles && (c.x != r[k].x || c.y != r[k].y)) r2[t] = c;  // an empty tile: (0, 0)
+            r[k] = c;
+        }
+        if (!sched) continue;
+#pragma unroll
+        for (int k = 0; k < kSweep; ++k) {
+            const int t = base + k * kOrderThreads + tid;
             const uint32_t len = r[k].y - r[k].x;
-            if (by_tile && t < n_tiles) atomicAdd(&s_hist[0][heavy_first_key(len)], 1u);
-            if (split && t < n_tiles) {
-                if (len <= (uint32_t)kChunk)  // one chunk at most: a whole item
+            if (t >= n_tiles) continue;
+            if (len == 0u) {
+                ++empties;
+                continue;
+            }
+            if (by_tile) atomicAdd(&s_hist[0][heavy_first_key(len)], 1u);
+            if (split) {
+                // a list up to the cut length is one item; a longer one has
+                // one per chunk, classed by the length from the chunk on
+                if (len <= cut)
                     atomicAdd(&s_hist[1][heavy_first_key(len)], 1u);
                 else
                     for (uint32_t at = 0; at < len; at += kChunk) atomicAdd(&s_hist[1][heavy_first_key(len - at)], 1u);
             }
         }
     }
-    __syncthreads();
-    // waves 0..3 scan the tile classes, waves 4..7 the chunk classes
+    if (!sched) return;
+    __syncthreads();  // every count of step 1 is in
+    // 2. class starts (exclusive scans); the empty tiles follow all others in
+    //    the order of an exclusive block scan of the per-thread counts
+    uint32_t einc = empties;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = (uint32_t)__shfl_up((int)einc, off, 64);
+        if (lane >= off) einc += y;
+    }
+    if (lane == 63) s_esum[wave] = einc;
     const int which = tid >> 8, cls = tid & (kRadix - 1), w4 = (tid >> 6) & 3;
     uint32_t h = 0, incl = 0;
     if (tid < 2 * kRadix) {
@@ -658,42 +714,66 @@ __global__ __launch_bounds__(1024) void k_tile_order(const uint32_t* __restrict_
         if (lane == 63) s_wsum[which][w4] = incl;
     }
     __syncthreads();
+    uint32_t erank = einc - empties, etot = 0;  // this thread's first empty tile among the empty ones
+    for (int w = 0; w < kOrderThreads / 64; ++w) {
+        erank += w < wave ? s_esum[w] : 0u;
+        etot += s_esum[w];
+    }
     if (tid < 2 * kRadix) {
-        uint32_t pre = 0;
-        for (int w = 0; w < w4; ++w) pre += s_wsum[which][w];
+        uint32_t pre = 0, all = 0;
+        for (int w = 0; w < 4; ++w) {
+            pre += w < w4 ? s_wsum[which][w] : 0u;
+            all += s_wsum[which][w];
+        }
         s_hist[which][cls] = pre + incl - h;  // now the class cursors
-        // the item count: every chunk and empty list, or every tile
-        if (chunks && tid == (split ? 2 * kRadix - 1 : kRadix - 1)) chunks[0] = pre + incl;
+        if (cls == 0) s_items[which] = all;
     }
     __syncthreads();
-    uint4* const items = chunks ? reinterpret_cast<uint4*>(chunks + 4) : nullptr;
-    for (int base = 0; base < n_tiles; base += 1024 * kSweep) {
-        uint2 r[kSweep];
+    // the empty tiles come after every other tile and item
+    const uint32_t filled_tiles = (uint32_t)n_tiles - etot, filled_items = split ? s_items[1] : filled_tiles;
+    // 3. placement (a single sweep keeps its checked ranges in registers).
+    //    Positions stay below the tile count and the schedule's length by
+    //    construction; the guards keep a write inside the buffers regardless.
+    const uint32_t max_items = (uint32_t)n_tiles + (capacity + (uint32_t)kChunk - 1u) / (uint32_t)kChunk;
+    auto put_order = [&](uint32_t pos, uint32_t t) {
+        if (order && pos < (uint32_t)n_tiles) order[pos] = t;
+    };
+    auto put_item = [&](uint32_t pos, uint4 it) {
+        if (pos < max_items) items[pos] = it;
+    };
+    for (int base = 0; base < n_tiles; base += kSweepTiles) {
+        if (n_tiles > kSweepTiles) {
 #pragma unroll
-        for (int k = 0; k < kSweep; ++k) {
-            const int t = base + k * 1024 + tid;
-            r[k] = t < n_tiles ? r2[t] : make_uint2(0u, 0u);
+            for (int k = 0; k < kSweep; ++k) {
+                const int t = base + k * kOrderThreads + tid;
+                r[k] = t < n_tiles ? r2[t] : make_uint2(0u, 0u);  // already checked
+            }
         }
 #pragma unroll
         for (int k = 0; k < kSweep; ++k) {
-            const int t = base + k * 1024 + tid;
+            const int t = base + k * kOrderThreads + tid;
+            if (t >= n_tiles) continue;
             const uint32_t start = r[k].x, len = r[k].y - r[k].x;
-            if (by_tile && t < n_tiles) {
-                const uint32_t pos = atomicAdd(&s_hist[0][heavy_first_key(len)], 1u);
-                if (order) order[pos] = (uint32_t)t;
-                if (chunks && !split) items[pos] = make_uint4((uint32_t)t, kWholeList, start, len);
+            if (len == 0u) {
+                const uint32_t rank = erank++;
+                put_order(filled_tiles + rank, (uint32_t)t);
+                if (chunks) put_item(filled_items + rank, make_uint4((uint32_t)t, kWholeList, 0u, 0u));
+                continue;
             }
-            if (split && t < n_tiles) {
-                if (len <= (uint32_t)kChunk)
-                    items[atomicAdd(&s_hist[1][heavy_first_key(len)], 1u)] =
-                        make_uint4((uint32_t)t, kWholeList, start, len);
+            if (by_tile) put_order(atomicAdd(&s_hist[0][heavy_first_key(len)], 1u), (uint32_t)t);
+            if (split) {
+                if (len <= cut)
+                    put_item(atomicAdd(&s_hist[1][heavy_first_key(len)], 1u),
+                             make_uint4((uint32_t)t, kWholeList, start, len));
                 else
                     for (uint32_t at = 0, b = 0; at < len; at += kChunk, ++b)
-                        items[atomicAdd(&s_hist[1][heavy_first_key(len - at)], 1u)] =
-                            make_uint4((uint32_t)t, b, start, len);
+                        put_item(atomicAdd(&s_hist[1][heavy_first_key(len - at)], 1u),
+                                 make_uint4((uint32_t)t, b, start, len));
             }
         }
     }
+    // the item count: every chunk item and empty list, or every tile
+    if (chunks && tid == 0) chunks[0] = filled_items + etot;
 }
 
 int tile_pass_count(int tile_bits) { return (tile_bits + 7) / 8; }
@@ -832,16 +912,14 @@ hipError_t launch_fill_u32(uint32_t* p, size_t words, uint32_t v, hipStream_t st
 hipError_t launch_tile_ranges(const uint64_t* keys, uint32_t n_entries, const uint64_t* n_dev, uint32_t capacity,
                               int n_tiles, uint32_t* ranges, uint32_t* tile_order, uint32_t* chunks,
                               hipStream_t stream) {
-    // clear every tile (empty tiles keep (0, 0)), then mark the run boundaries
-    const size_t words = 2 * (size_t)n_tiles;
-    hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, stream,
-                       ranges, words, 0u);
+    // mark the run boundaries, then check every tile's range against the keys
+    // (empty tiles become (0, 0)) and build the schedules
     const uint32_t grid_n = n_dev ? capacity : n_entries;
     if (grid_n > 0)
         hipLaunchKernelGGL(k_ranges, dim3((grid_n + 255) / 256), dim3(256), 0, stream, keys, n_entries, n_dev,
                            capacity, ranges);
-    if (tile_order || chunks)
-        hipLaunchKernelGGL(k_tile_order, dim3(1), dim3(1024), 0, stream, (const uint32_t*)ranges, n_tiles, n_dev,
+    if (n_tiles > 0)
+        hipLaunchKernelGGL(k_tile_schedule, dim3(1), dim3(kOrderThreads), 0, stream, ranges, n_tiles, keys, n_dev,
                            n_entries, capacity, tile_order, chunks);
     return hipGetLastError();
 }

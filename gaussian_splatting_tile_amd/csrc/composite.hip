@@ -36,13 +36,14 @@
 //    160k-Gaussian 1080p scene).
 //  * Backward: per splat, each wave sums nine per-pixel terms over its 16-lane
 //    rows with DPP adds (skipped when no lane contributed) into LDS; the
-//    terms are the colour gradient, dL/do, and the moments of dL/dpower
-//    (dx, dy, dx^2, dx dy, dy^2 times it), from which the conic and mean
-//    gradients follow once per (splat, tile). Splats are staged 128 at a time
+//    terms are the colour gradient, dL/dpower and its moments (dx, dy, dx^2,
+//    dx dy, dy^2 times it), from which the conic, mean and opacity gradients
+//    follow once per (splat, tile) (alpha = o G unclamped, so dL/do is the
+//    sum of dL/dpower over o). Splats are staged 128 at a time
 //    and walked in 32-splat batches; after each batch all
 //    256 threads finish it (one output per thread), summing only the
-//    partials of waves that wrote them (a per-wave batch stamp replaces
-//    clearing the partials); one global atomic per value per tile entry
+//    partials of waves that wrote them (each wave keeps a mask of the slots
+//    it wrote, so the partials need no clearing); one global atomic per value per tile entry
 //    lands in the per-Gaussian gradient.
 //  * Culling is per 4 x 4 pixel block (see block_mask), exact up to a
 //    rounding bound, so a skipped (splat, block) pair changes no result.
@@ -565,7 +566,7 @@ __global__ __launch_bounds__(256) void k_composite_bwd(
     __shared__ float4 s_aux[kBwdStage];    // b, Gaussian id, -, -: one address with the two above
     __shared__ uint32_t s_live[kBwdStage];
     __shared__ __align__(16) float s_part[kBwdBatch][9][kParts];  // per-row partial sums
-    __shared__ float s_epoch[4][kBwdBatch];  // batch (as int bits) whose partials of slot k wave w wrote last
+    __shared__ uint32_t s_wmask[4];  // the batch's slots whose partials wave w wrote (bit k: slot k)
     __shared__ uint32_t s_maxnc[4];
 
     int tile;
@@ -604,12 +605,12 @@ __global__ __launch_bounds__(256) void k_composite_bwd(
     const int py = ty * kTile + 8 * (wave >> 1) + (lane >> 3);
     const uint32_t qblocks = quadrant_blocks(wave);
     // the one LDS store per (splat, wave): lane j <= 8 of each row writes its
-    // row's sum of term j, lane 9 of row 0 the wave's batch stamp
+    // row's sum of term j; which slots a wave wrote is kept in s_wmask
     const int j16 = lane & 15;
-    const bool store_lane = j16 <= 8 || lane == 9;
-    float* const store_base = lane == 9 ? &s_epoch[wave][0]
-                                        : &s_part[0][min(j16, 8)][(wave * 4 + (lane >> 4)) ^ part_swizzle(j16)];
-    const int store_stride = lane == 9 ? 1 : 9 * kParts;
+    const int my_term = min(j16, 8);
+    const bool store_lane = j16 <= 8;
+    float* const store_base = &s_part[0][my_term][(wave * 4 + (lane >> 4)) ^ part_swizzle(my_term)];
+    constexpr int store_stride = 9 * kParts;
     const bool inside = px < W && py < H;
     const float fx = (float)px, fy = (float)py;
     // g.R: the upstream gradient dotted with the radiance from behind the
@@ -637,7 +638,6 @@ __global__ __launch_bounds__(256) void k_composite_bwd(
                                 __builtin_fmaf(g1, image[plane + p] - ck.z, g0 * (image[p] - ck.y)));
         }
     }
-    if (tid < 4 * kBwdBatch) (&s_epoch[0][0])[tid] = __int_as_float(-1);
 
     // per-wave and per-tile maximum of n_contrib
     uint32_t wmax = nc;
@@ -648,7 +648,6 @@ __global__ __launch_bounds__(256) void k_composite_bwd(
     const int maxnc = (int)max(max(s_maxnc[0], s_maxnc[1]), max(s_maxnc[2], s_maxnc[3]));
     const int wave_maxnc = (int)wmax;
 
-    int batch = 0;
     for (int send = min(maxnc, hi_item); send > lo; send -= kBwdStage) {  // rounds, back to front
         const int sstart = send - kBwdStage > lo ? send - kBwdStage : lo;
         __syncthreads();  // the previous round is fully consumed
@@ -662,7 +661,7 @@ __global__ __launch_bounds__(256) void k_composite_bwd(
             s_aux[tid] = make_float4(c.z, __uint_as_float(g), 0.0f, 0.0f);
             s_live[tid] = block_mask(co, xy.x, xy.y, tx * kTile, ty * kTile);
         }
-        for (int bend = send; bend > sstart; bend -= kBwdBatch, ++batch) {  // batches of the round
+        for (int bend = send; bend > sstart; bend -= kBwdBatch) {  // batches of the round
             const int bstart = bend - kBwdBatch > sstart ? bend - kBwdBatch : sstart;
             const int cnt = bend - bstart;
             const int off = bstart - sstart;  // staging slot of this batch's slot 0
@@ -670,8 +669,11 @@ __global__ __launch_bounds__(256) void k_composite_bwd(
 
             // live splats of this wave below its largest n_contrib, walked back to front
             static_assert(kBwdBatch <= 64, "one 64-bit live mask");
-            uint64_t mk = __ballot(lane < cnt && bstart + lane < wave_maxnc && (s_live[off + lane] & qblocks) != 0u);
+            const int ls = min(off + lane, kBwdStage - 1);  // (lanes past cnt read a valid slot, unused)
+            uint64_t mk = __ballot(lane < cnt && bstart + lane < wave_maxnc && (s_live[ls] & qblocks) != 0u);
             const int ncb = (int)nc - bstart;  // this lane uses slot k only if k < ncb
+            static_assert(kBwdBatch <= 32, "one 32-bit mask of stored slots");
+            uint32_t stored = 0u;  // slots whose partials this wave wrote (wave-uniform)
             // Two splats per step: their alphas are independent, so the second's
             // exponential and reciprocal overlap the first's updates, and the two
             // reductions interleave. A launch lasts as long as its heaviest tiles,
@@ -691,63 +693,68 @@ __global__ __launch_bounds__(256) void k_composite_bwd(
                 float G1, oG1, alpha1, G2, oG2, alpha2;
                 splat_alpha(co1.x, co1.y, co1.z, co1.w, dx1, dy1, G1, oG1, alpha1);
                 splat_alpha(co2.x, co2.y, co2.z, co2.w, dx2, dy2, G2, oG2, alpha2);
-                const float rinv1 = __builtin_amdgcn_rcpf(1.0f - alpha1);
-                const float rinv2 = __builtin_amdgcn_rcpf(1.0f - alpha2);
-                float t1[9], t2[9];
-                // branch-free: lanes past their n_contrib or below the floor add nothing
+                // branch-free: a lane past its n_contrib or below the floor
+                // takes alpha 0, so T / (1 - 0) = T exactly and it adds nothing
                 const bool use1 = k1 < ncb && alpha1 >= kAlphaMin;
                 const bool use2 = two && k2 < ncb && alpha2 >= kAlphaMin;
-                const uint64_t u1 = __ballot(k1 < ncb && alpha1 >= kAlphaMin);
-                const uint64_t u2 = two ? __ballot(k2 < ncb && alpha2 >= kAlphaMin) : 0ull;
-                auto step = [&](const float4& co, const float4& xc, float cb, float dx, float dy, float G, float oG,
-                                float alpha, float rinv, bool use, float* d) {
+                const float a1 = use1 ? alpha1 : 0.0f, a2 = use2 ? alpha2 : 0.0f;
+                const float rinv1 = __builtin_amdgcn_rcpf(1.0f - a1);
+                const float rinv2 = __builtin_amdgcn_rcpf(1.0f - a2);
+                float t1[9], t2[9];
+                const uint64_t u1 = __builtin_amdgcn_ballot_w64(a1 != 0.0f);  // use1 (alpha >= 1/255 > 0)
+                const uint64_t u2 = __builtin_amdgcn_ballot_w64(a2 != 0.0f);
+                auto step = [&](const float4& xc, float cb, float dx, float dy, float oG, float a, float rinv,
+                                float* d) {
                     const float Tj = T * rinv;  // transmittance in front of the splat
-                    const float a = use ? alpha : 0.0f;
                     const float w = a * Tj;
                     d[6] = w * g0;
                     d[7] = w * g1;
                     d[8] = w * g2;
                     const float gc = __builtin_fmaf(g2, cb, __builtin_fmaf(g1, xc.w, g0 * xc.z));  // g.c
-                    const float dL_da = __builtin_fmaf(-rinv, gR, Tj * gc);
-                    gR = __builtin_fmaf(w, gc, gR);  // exact no-op at w = 0
-                    T = use ? Tj : T;
-                    // unsaturated alpha = o G: dL/do = G dL/da, dL/dpower = o G dL/da
-                    const bool geo = use && oG <= kAlphaMax;
-                    d[5] = geo ? G * dL_da : 0.0f;
-                    const float dp = co.w * d[5];
-                    // moments of dL/dpower; the conic is applied once per splat afterwards
-                    d[0] = dx * dp;        // dx dp
-                    d[1] = dy * dp;        // dy dp
-                    d[2] = dx * d[0];      // dx^2 dp
-                    d[3] = dy * d[0];      // dx dy dp
-                    d[4] = dy * d[1];      // dy^2 dp
+                    const float wgc = w * gc;
+                    // dL/dpower = alpha dL/dalpha = w (g.c) - alpha / (1 - alpha) (g.R),
+                    // zero through a saturated alpha (o G > 0.99)
+                    float dp = __builtin_fmaf(-(a * rinv), gR, wgc);
+                    dp = oG <= kAlphaMax ? dp : 0.0f;
+                    gR += wgc;  // exact no-op at a = 0
+                    T = Tj;
+                    // dL/dpower and its moments; with alpha = o G unclamped,
+                    // dL/do = sum G dL/dalpha = (sum dL/dpower) / o, and the conic
+                    // and mean gradients follow from the moments once per splat
+                    d[5] = dp;
+                    d[0] = dx * dp;    // dx dp
+                    d[1] = dy * dp;    // dy dp
+                    d[2] = dx * d[0];  // dx^2 dp
+                    d[3] = dy * d[0];  // dx dy dp
+                    d[4] = dy * d[1];  // dy^2 dp
                 };
-                step(co1, xc1, cb1, dx1, dy1, G1, oG1, alpha1, rinv1, use1, t1);
-                step(co2, xc2, cb2, dx2, dy2, G2, oG2, alpha2, rinv2, use2, t2);
+                step(xc1, cb1, dx1, dy1, oG1, a1, rinv1, t1);
+                step(xc2, cb2, dx2, dy2, oG2, a2, rinv2, t2);
                 if ((u1 | u2) != 0ull) {
                     const float r1 = transpose_row_sum9(t1[0], t1[1], t1[2], t1[3], t1[4], t1[5], t1[6], t1[7], t1[8],
                                                         lane_b0, lane_b1, lane_b2, lane_b3);
                     const float r2 = transpose_row_sum9(t2[0], t2[1], t2[2], t2[3], t2[4], t2[5], t2[6], t2[7], t2[8],
                                                         lane_b0, lane_b1, lane_b2, lane_b3);
-                    const float v1 = lane == 9 ? __int_as_float(batch) : r1;
-                    const float v2 = lane == 9 ? __int_as_float(batch) : r2;
                     if (store_lane) {
-                        if (u1 != 0ull) store_base[k1 * store_stride] = v1;
-                        if (u2 != 0ull) store_base[k2 * store_stride] = v2;
+                        if (u1 != 0ull) store_base[k1 * store_stride] = r1;
+                        if (u2 != 0ull) store_base[k2 * store_stride] = r2;
                     }
+                    stored |= (u1 != 0ull ? 1u << k1 : 0u) | (u2 != 0ull ? 1u << k2 : 0u);
                 }
             }
+            if (lane == 0) s_wmask[wave] = stored;
             __syncthreads();
             // all 256 threads: splat slot k = tid % 32, one output group per
             // thread (tid / 32): the mean pair, dA, dB, dC, dopacity, r, g, b.
             // Only the partials of waves that wrote slot k in this batch count.
-            //   d(u, v) = (A Sx + B Sy, B Sx + C Sy); dA = -Sxx / 2; dB = -Sxy; dC = -Syy / 2
+            //   d(u, v) = (A Sx + B Sy, B Sx + C Sy); dA = -Sxx / 2; dB = -Sxy; dC = -Syy / 2;
+            //   do = S / o (S the sum of dL/dpower)
             {
                 const int k = tid & (kBwdBatch - 1), grp = tid >> 5;
                 if (k < cnt) {
                     uint32_t wm = 0u;
     #pragma unroll
-                    for (int w = 0; w < 4; ++w) wm |= (__float_as_int(s_epoch[w][k]) == batch ? 1u : 0u) << w;
+                    for (int w = 0; w < 4; ++w) wm |= ((s_wmask[w] >> k) & 1u) << w;
                     if (wm != 0u) {
                         const uint32_t g = __float_as_uint(s_aux[off + k].y);
                         // term t of wave w sits in slots 4 w' .. 4 w' + 3, w' = w ^ part_swizzle(t) / 4
@@ -769,9 +776,11 @@ __global__ __launch_bounds__(256) void k_composite_bwd(
                             const float A = -2.0f * co.x, C = -2.0f * co.z;  // exact
                             atomic_add_nz(grad_mean2d + 2 * (size_t)g, A * Sx + co.y * Sy);
                             atomic_add_nz(grad_mean2d + 2 * (size_t)g + 1, co.y * Sx + C * Sy);
-                        } else if (grp <= 4) {
-                            const float scale = grp == 2 ? -1.0f : (grp == 4 ? 1.0f : -0.5f);
+                        } else if (grp <= 3) {
+                            const float scale = grp == 2 ? -1.0f : -0.5f;
                             atomic_add_nz(grad_conic_op + 4 * (size_t)g + (grp - 1), scale * term_sum(grp + 1));
+                        } else if (grp == 4) {  // dL/do = (sum dL/dpower) / o
+                            atomic_add_nz(grad_conic_op + 4 * (size_t)g + 3, term_sum(5) / s_conic[off + k].w);
                         } else {
                             atomic_add_nz(grad_rgb + 4 * (size_t)g + (grp - 5), term_sum(grp + 1));
                         }

@@ -378,16 +378,14 @@ gs_status gs_tile_ranges_async(const gs_camera* cam, const uint64_t* keys, const
  *               launches read up to that many items, one per workgroup).
  *               chunks[0] = the item count; words 1-3 unused; from word 4,
  *               for each item, (tile, k, list start, L). When the lists
- *               average more than 256 entries (E > 256 TX TY), every list
- *               longer than 256 is cut into ceil(L / 256) chunks, chunk k
- *               covering list positions [256 k, min(256 k + 256, L)), and
- *               every shorter list (empty ones too) is one item with
- *               k = 0xffffffff (the whole list); items come in descending
- *               order of L - 256 k, the list length from the item on
- *               (classes as tile_order's; k = 0 for whole lists). Otherwise
- *               the tiles alone give the compositing enough workgroups:
- *               every list is one item with k = 0xffffffff, in tile_order's
- *               order.
+ *               average more than 256 entries (E > 256 TX TY n_views),
+ *               every list longer than 256 is cut into ceil(L / 256)
+ *               chunks, chunk k covering list positions [256 k,
+ *               min(256 k + 256, L)), and every shorter list (empty ones
+ *               too) is one item with k = 0xffffffff (the whole list);
+ *               otherwise every list is one such item. Items come in
+ *               descending order of L - 256 k, the list length from the item
+ *               on (classes as tile_order's; k = 0 for whole lists).
  * ------------------------------------------------------------------- */
 gs_status gs_tile_ranges_ex(const gs_camera* cam, int32_t n_views, const uint64_t* keys, int64_t n_entries,
                             const uint64_t* n_entries_dev, int64_t capacity, uint32_t* ranges,

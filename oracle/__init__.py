@@ -26,7 +26,7 @@ TILE = 16
 
 def build(verbose: bool = False) -> str:
     """Compile liboracle.so with the host compiler. Returns its path."""
-    cmd = ["g++", "-O2", "-std=c++17", "-ffp-contract=off", "-fno-fast-math",
+    cmd = ["g++", "-O2", "-std=c++17", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
            "-fPIC", "-shared", "-Wall", "-o", _LIB + ".tmp", _SRC]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -86,6 +86,8 @@ def lib():
             getattr(_lib, name).argtypes = [ctypes.POINTER(Camera), ctypes.c_int32] + [P] * 12
         _lib.orc_composite_bwd_mass_f32.restype = None
         _lib.orc_composite_bwd_mass_f32.argtypes = [ctypes.POINTER(Camera), ctypes.c_int32] + [P] * 15
+        _lib.orc_set_threads.restype = ctypes.c_int
+        _lib.orc_set_threads.argtypes = [ctypes.c_int32]
         _lib.orc_constants.restype = None
         _lib.orc_constants.argtypes = [P]
         _lib.orc_sh_basis.restype = None
@@ -113,6 +115,12 @@ def _p(a):
 
 def _c(a, dtype):
     return np.ascontiguousarray(a, dtype=dtype)
+
+
+def set_threads(threads: int) -> int:
+    """Threads the preprocess and the compositing use (1, the default: the
+    canonical single-threaded run). Returns the number set."""
+    return int(lib().orc_set_threads(int(threads)))
 
 
 def tiles_xy(cam: dict):

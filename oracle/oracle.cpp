@@ -31,6 +31,18 @@
 #include <cstring>
 #include <vector>
 
+#include <omp.h>
+
+// Threads used by the preprocess and the compositing (orc_set_threads).
+// At 1, the default, every loop runs in the order written below. Above 1
+// the preprocess (per Gaussian) and the forward (per pixel row) split
+// independent iterations over threads, so their outputs are identical; the
+// backward gives each thread its own partial gradients over a block of
+// rows and sums them in thread order, so its sums differ from the
+// single-threaded ones by double rounding only. Used to time the oracle on
+// all host cores; the pins run single-threaded.
+static int g_threads = 1;
+
 extern "C" {
 
 // World-to-camera pinhole camera. p_cam = R p + t, R row-major; +z forward,
@@ -557,6 +569,7 @@ int orc_preprocess_ex(const orc_camera* cam, int32_t n, const float* means,
     const int TX = tiles_x(cam), TY = tiles_y(cam);
     const int n_coef = sh ? (sh_degree + 1) * (sh_degree + 1) : 0;
 
+#pragma omp parallel for schedule(static) num_threads(g_threads) if (g_threads > 1)
     for (int g = 0; g < n; ++g) {
         float* o_xy = xy_depth + 4 * (size_t)g;
         float* o_co = conic_op + 4 * (size_t)g;
@@ -835,6 +848,7 @@ void composite_fwd(const orc_camera* cam, const uint32_t* ranges, const uint32_t
                    F* image, F* final_T, uint32_t* n_contrib, uint32_t* n_examined) {
     const int Wd = cam->width, Hd = cam->height, TX = tiles_x(cam);
     const F alpha_min = (F)ALPHA_MIN, alpha_max = (F)ALPHA_MAX, t_stop = (F)T_STOP;
+#pragma omp parallel for schedule(dynamic, 4) num_threads(g_threads) if (g_threads > 1)
     for (int y = 0; y < Hd; ++y) {
         for (int x = 0; x < Wd; ++x) {
             const int tile = (y / TILE) * TX + (x / TILE);
@@ -866,46 +880,23 @@ void composite_fwd(const orc_camera* cam, const uint32_t* ranges, const uint32_t
     }
 }
 
-// Backward of composite_fwd: walk each pixel's list back to front from
-// n_contrib - 1, undoing T_j = T_{j+1} / (1 - a_j) from final_T and carrying
-// the colour behind the current splat (starting from the background).
-//   [rigel] "Backward": suffix accumulation, T recovery, n_contrib skip;
-//     "Deliberate differences": zero gradient through a saturated alpha.
-//   [learn-gs] "The next live problem": the tile walk in reverse,
-//     reconstructing each T_i from the end state.
-// Per splat j with colour c, alpha a (unclamped a_raw = o G), and upstream
-// pixel gradient g:  dL/dc = a T_j g;  dL/da = T_j sum_ch g_ch (c_ch - B_ch),
-// where B is the colour behind j; when a_raw <= 0.99, dL/do = G dL/da and
-// dL/dpower = a dL/da feed dA, dB, dC, du, dv. Summed over pixels in double.
-// Outputs: grad_mean2d [n][2], grad_conic_op [n][4] (dA, dB, dC, dopacity),
-// grad_rgb [n][4] (last slot 0). They are overwritten.
-// Optionally (mass_* non-NULL) also the per-element sum over pixels of the
-// magnitudes of the terms each gradient is summed from, the scale against
-// which a float32 sum with cancellation is judged.
+// The backward's walk over pixel rows [y0, y1), adding each term to the
+// given gradient arrays (and its magnitude to mass_* when those are given).
 template <typename F>
-void composite_bwd(const orc_camera* cam, int32_t n, const uint32_t* ranges,
-                   const uint32_t* point_list, const F* xy_depth, const F* conic_op,
-                   const F* rgb, const F* bg, const F* final_T, const uint32_t* n_contrib,
-                   const F* dL_dimage, double* grad_mean2d, double* grad_conic_op,
-                   double* grad_rgb, double* mass_mean2d = nullptr, double* mass_conic_op = nullptr,
-                   double* mass_rgb = nullptr) {
+void composite_bwd_rows(const orc_camera* cam, const uint32_t* ranges, const uint32_t* point_list,
+                        const F* xy_depth, const F* conic_op, const F* rgb, const F* bg, const F* final_T,
+                        const uint32_t* n_contrib, const F* dL_dimage, int y0, int y1, double* grad_mean2d,
+                        double* grad_conic_op, double* grad_rgb, double* mass_mean2d, double* mass_conic_op,
+                        double* mass_rgb) {
     const int Wd = cam->width, Hd = cam->height, TX = tiles_x(cam);
     const F alpha_min = (F)ALPHA_MIN, alpha_max = (F)ALPHA_MAX;
-    std::fill(grad_mean2d, grad_mean2d + 2 * (size_t)n, 0.0);
-    std::fill(grad_conic_op, grad_conic_op + 4 * (size_t)n, 0.0);
-    std::fill(grad_rgb, grad_rgb + 4 * (size_t)n, 0.0);
     const bool mass = mass_mean2d && mass_conic_op && mass_rgb;
-    if (mass) {
-        std::fill(mass_mean2d, mass_mean2d + 2 * (size_t)n, 0.0);
-        std::fill(mass_conic_op, mass_conic_op + 4 * (size_t)n, 0.0);
-        std::fill(mass_rgb, mass_rgb + 4 * (size_t)n, 0.0);
-    }
     // adds a term to a gradient element (and its magnitude to the mass)
     auto add = [&](double* grad, double* m, size_t i, F term) {
         grad[i] += (double)term;
         if (mass) m[i] += std::fabs((double)term);
     };
-    for (int y = 0; y < Hd; ++y) {
+    for (int y = y0; y < y1; ++y) {
         for (int x = 0; x < Wd; ++x) {
             const int tile = (y / TILE) * TX + (x / TILE);
             const uint32_t start = ranges[2 * tile];
@@ -946,9 +937,71 @@ void composite_bwd(const orc_camera* cam, int32_t n, const uint32_t* ranges,
     }
 }
 
+// Backward of composite_fwd: walk each pixel's list back to front from
+// n_contrib - 1, undoing T_j = T_{j+1} / (1 - a_j) from final_T and carrying
+// the colour behind the current splat (starting from the background).
+//   [rigel] "Backward": suffix accumulation, T recovery, n_contrib skip;
+//     "Deliberate differences": zero gradient through a saturated alpha.
+//   [learn-gs] "The next live problem": the tile walk in reverse,
+//     reconstructing each T_i from the end state.
+// Per splat j with colour c, alpha a (unclamped a_raw = o G), and upstream
+// pixel gradient g:  dL/dc = a T_j g;  dL/da = T_j sum_ch g_ch (c_ch - B_ch),
+// where B is the colour behind j; when a_raw <= 0.99, dL/do = G dL/da and
+// dL/dpower = a dL/da feed dA, dB, dC, du, dv. Summed over pixels in double.
+// Outputs: grad_mean2d [n][2], grad_conic_op [n][4] (dA, dB, dC, dopacity),
+// grad_rgb [n][4] (last slot 0). They are overwritten.
+// Optionally (mass_* non-NULL) also the per-element sum over pixels of the
+// magnitudes of the terms each gradient is summed from, the scale against
+// which a float32 sum with cancellation is judged.
+template <typename F>
+void composite_bwd(const orc_camera* cam, int32_t n, const uint32_t* ranges,
+                   const uint32_t* point_list, const F* xy_depth, const F* conic_op,
+                   const F* rgb, const F* bg, const F* final_T, const uint32_t* n_contrib,
+                   const F* dL_dimage, double* grad_mean2d, double* grad_conic_op,
+                   double* grad_rgb, double* mass_mean2d = nullptr, double* mass_conic_op = nullptr,
+                   double* mass_rgb = nullptr) {
+    const int Hd = cam->height;
+    const bool mass = mass_mean2d && mass_conic_op && mass_rgb;
+    double* outs[6] = {grad_mean2d, grad_conic_op, grad_rgb, mass_mean2d, mass_conic_op, mass_rgb};
+    const size_t len[6] = {2 * (size_t)n, 4 * (size_t)n, 4 * (size_t)n, 2 * (size_t)n, 4 * (size_t)n,
+                           4 * (size_t)n};
+    for (int k = 0; k < (mass ? 6 : 3); ++k) std::fill(outs[k], outs[k] + len[k], 0.0);
+    const int T = std::max(1, std::min(g_threads, Hd));
+    if (T == 1) {
+        composite_bwd_rows<F>(cam, ranges, point_list, xy_depth, conic_op, rgb, bg, final_T, n_contrib, dL_dimage,
+                              0, Hd, grad_mean2d, grad_conic_op, grad_rgb, mass_mean2d, mass_conic_op, mass_rgb);
+        return;
+    }
+    // thread t: rows [t Hd / T, (t + 1) Hd / T) into its own arrays, summed in thread order
+    const size_t per = 10 * (size_t)n;
+    std::vector<double> part((size_t)T * per * (mass ? 2 : 1), 0.0);
+#pragma omp parallel for schedule(static, 1) num_threads(T)
+    for (int t = 0; t < T; ++t) {
+        double* b = part.data() + (size_t)t * per * (mass ? 2 : 1);
+        double* m = mass ? b + per : nullptr;
+        composite_bwd_rows<F>(cam, ranges, point_list, xy_depth, conic_op, rgb, bg, final_T, n_contrib, dL_dimage,
+                              (int)((int64_t)t * Hd / T), (int)((int64_t)(t + 1) * Hd / T), b, b + 2 * (size_t)n,
+                              b + 6 * (size_t)n, m, m ? m + 2 * (size_t)n : nullptr, m ? m + 6 * (size_t)n : nullptr);
+    }
+    for (int t = 0; t < T; ++t) {
+        const double* b = part.data() + (size_t)t * per * (mass ? 2 : 1);
+        for (int k = 0; k < (mass ? 6 : 3); ++k) {
+            const double* src = b + (k >= 3 ? per : 0) + (k % 3 == 0 ? 0 : (k % 3 == 1 ? 2 * (size_t)n : 6 * (size_t)n));
+            for (size_t i = 0; i < len[k]; ++i) outs[k][i] += src[i];
+        }
+    }
+}
+
 }  // namespace
 
 extern "C" {
+
+// Threads for the preprocess and the compositing (see g_threads); values
+// below 1 mean 1. Returns the number set.
+int orc_set_threads(int32_t threads) {
+    g_threads = std::max(1, (int)threads);
+    return g_threads;
+}
 
 void orc_composite_fwd_f32(const orc_camera* cam, const uint32_t* ranges, const uint32_t* point_list,
                            const float* xy_depth, const float* conic_op, const float* rgb,

@@ -392,27 +392,26 @@ def _chunk_class(L):
 
 
 def _check_chunk_schedule(chunks, ranges):
-    """chunks: the schedule words; ranges [T, 2]. If the lists average more
-    than 256 entries: every (tile, k) with k < ceil(L / 256) of each list
-    longer than 256 exactly once and every other tile once as a whole item,
-    in non-increasing class of L - 256 k (k = 0 for whole items, empty tiles
-    last); else every tile once as a whole item, in non-increasing class of
-    L. Returns whether it split."""
+    """chunks: the schedule words; ranges [T, 2]. With the cut length C = 256
+    when the lists average more than 256 entries, else no cut: every
+    (tile, k) with k < ceil(L / 256) of each list longer than C exactly once
+    and every other tile once as a whole item, in non-increasing class of
+    L - 256 k (k = 0 for whole items, empty tiles last). Returns C (None:
+    no cut)."""
     L = ranges[:, 1].astype(np.int64) - ranges[:, 0]
+    cut = 256 if L.sum() > 256 * len(L) else None
+    if cut is None:
+        cut_len = np.iinfo(np.int64).max
+    else:
+        cut_len = cut
     count = int(chunks[0])
     items4 = chunks[4:4 + 4 * count].reshape(count, 4).astype(np.int64)
-    assert np.array_equal(items4[:, 2], ranges[items4[:, 0], 0])
+    assert np.array_equal(items4[:, 2], np.where(L[items4[:, 0]] > 0, ranges[items4[:, 0], 0], 0))
     assert np.array_equal(items4[:, 3], L[items4[:, 0]])
     whole = items4[:, 1] == 0xFFFFFFFF
-    if L.sum() <= 256 * len(L):
-        assert whole.all()
-        assert np.array_equal(np.sort(items4[:, 0]), np.arange(len(L)))
-        cls = np.where(L[items4[:, 0]] == 0, -1, _chunk_class(L[items4[:, 0]]))
-        assert (np.diff(cls) <= 0).all()
-        return False
-    nch = np.where(L > 256, (L + 255) // 256, 0)
-    assert count == int(nch.sum()) + int((L <= 256).sum()), (count, int(nch.sum()))
-    assert np.array_equal(np.sort(items4[whole, 0]), np.nonzero(L <= 256)[0])
+    nch = np.where(L > cut_len, (L + 255) // 256, 0)
+    assert count == int(nch.sum()) + int((L <= cut_len).sum()), (count, int(nch.sum()))
+    assert np.array_equal(np.sort(items4[whole, 0]), np.nonzero(L <= cut_len)[0])
     items = items4[~whole, :2]
     want = np.concatenate([np.stack([np.full(k, t), np.arange(k)], 1) for t, k in enumerate(nch) if k] or
                           [np.zeros((0, 2), np.int64)])
@@ -422,7 +421,7 @@ def _check_chunk_schedule(chunks, ranges):
     assert (rest[~whole] > 0).all()
     cls = np.where(rest == 0, -1, _chunk_class(np.maximum(rest, 1)))
     assert (np.diff(cls) <= 0).all()
-    return True
+    return cut
 
 
 def test_chunk_schedule_covers_every_chunk(orc):
@@ -433,11 +432,11 @@ def test_chunk_schedule_covers_every_chunk(orc):
     import gaussian_splatting_tile_amd as gs
     import torch
     from gpu_helpers import to_np
-    for name, split in (("cfg2", False), ("cfg3", True)):
+    for name, cut in (("cfg2", None), ("cfg3", 256)):
         say(f"[{name}] schedule")
         scene, cam, _, ofwd, _ = workload(orc, name)
         g, out, sc, r = gpu_forward(cam, scene, capacity=1 << 23)
-        assert _check_chunk_schedule(to_np(out["chunks"]).view(np.uint32), g["ranges"]) == split
+        assert _check_chunk_schedule(to_np(out["chunks"]).view(np.uint32), g["ranges"]) == cut
         c = gs.camera(cam)
         for capacity in (g["n_entries"] + 5000, g["n_entries"] - 1):
             bins = gs.BinBuffers(torch.device("cuda"), capacity)
@@ -448,8 +447,47 @@ def test_chunk_schedule_covers_every_chunk(orc):
             rg = to_np(ranges).view(np.uint32)
             if capacity >= g["n_entries"]:
                 assert np.array_equal(rg, g["ranges"])
-                assert _check_chunk_schedule(to_np(chunks).view(np.uint32), rg) == split
+                assert _check_chunk_schedule(to_np(chunks).view(np.uint32), rg) == cut
             else:
                 # every list empty: one whole item per tile
                 assert not rg.any()
-                assert _check_chunk_schedule(to_np(chunks).view(np.uint32), rg) is False
+                assert _check_chunk_schedule(to_np(chunks).view(np.uint32), rg) is None
+
+
+def test_ranges_ignore_stale_buffer_contents(orc):
+    """The ranges call writes only run boundaries and then checks every tile's
+    range against the sorted keys, so whatever the buffer held before (random
+    words, another frame's ranges, those ranges shuffled over the tiles) the
+    result is the oracle's, empty tiles (0, 0), with the same schedules."""
+    import gaussian_splatting_tile_amd as gs
+    import torch
+    from gpu_helpers import to_np
+    scene, cam, _, ofwd, _ = workload(orc, "cfg1")
+    g, out, sc, r = gpu_forward(cam, scene, capacity=1 << 21)
+    E = g["n_entries"]
+    c = gs.camera(cam)
+    n_tiles = ofwd["ranges"].shape[0]
+    big = synth.look_at_camera((0.3, 0.2, -3.0), (0, 0, 0), cam["width"], cam["height"], 500.0, 500.0)
+    other = orc.render_fwd(big, scene)["ranges"].astype(np.int64)
+    rng = np.random.default_rng(5)
+    fills = {"random words": rng.integers(0, 2**31, (n_tiles, 2)),
+             "another frame": other,
+             "shuffled own ranges": ofwd["ranges"].astype(np.int64)[rng.permutation(n_tiles)],
+             "own ranges reversed": ofwd["ranges"].astype(np.int64)[:, ::-1].copy()}
+    ref_order = None
+    for what, fill in fills.items():
+        ranges = torch.from_numpy(fill.astype(np.uint32).view(np.int32)).cuda()
+        order = torch.full((n_tiles,), -1, dtype=torch.int32, device="cuda")
+        chunks = torch.full((gs.chunk_words(cam, int(out["keys"].numel())),), -1, dtype=torch.int32, device="cuda")
+        gs.tile_ranges(c, out["keys"], E, out=ranges, order=order, chunks=chunks)
+        torch.cuda.synchronize()
+        rg = to_np(ranges).view(np.uint32)
+        assert_bits_equal(rg, ofwd["ranges"], f"ranges over {what}")
+        od = to_np(order).view(np.uint32).astype(np.int64)
+        assert np.array_equal(np.sort(od), np.arange(n_tiles)), what
+        _check_chunk_schedule(to_np(chunks).view(np.uint32), rg)
+        # plain call (no schedules): only the check of the ranges runs
+        ranges2 = torch.from_numpy(fill.astype(np.uint32).view(np.int32)).cuda()
+        gs.tile_ranges(c, out["keys"], E, out=ranges2)
+        torch.cuda.synchronize()
+        assert_bits_equal(to_np(ranges2).view(np.uint32), ofwd["ranges"], f"plain ranges over {what}")

@@ -163,3 +163,33 @@ def test_matches_brute_force(orc, seed):
     same = out["n_contrib"] == nc
     np.testing.assert_allclose(out["image"][:, same], img[:, same], atol=2e-6)
     np.testing.assert_allclose(out["final_T"][same], T[same], atol=2e-6)
+
+
+def test_threaded_oracle_matches_single_threaded(orc):
+    """The oracle's multi-threaded run (used to time it on all host cores)
+    gives the single-threaded preprocess, binning and forward outputs bit for
+    bit (independent Gaussians and pixel rows), and the backward to double
+    rounding (per-thread partial sums added in thread order)."""
+    import synth
+    cam = synth.look_at_camera((0.3, -0.2, -4.0), (0.0, 0.0, 0.0), 257, 129, 150.0, 150.0)
+    scene = synth.random_scene(3000, 17, cam, sh_degree=2, spread=1.3)
+    dLdI = synth.upstream_gradient(9, 257, 129)
+    bg = (0.1, 0.2, 0.3)
+    outs = {}
+    try:
+        for threads in (1, 5):
+            assert orc.set_threads(threads) == threads
+            f = orc.render_fwd(cam, scene, bg=bg)
+            b = orc.composite_bwd(cam, scene["n"], f["ranges"], f["point_list"], f["xy_depth"], f["conic_op"],
+                                  f["rgb"], f["final_T"], f["n_contrib"], dLdI, bg=bg, mass=True)
+            outs[threads] = (f, b)
+    finally:
+        orc.set_threads(1)
+    (f1, b1), (f5, b5) = outs[1], outs[5]
+    assert f1["keys"].size > 10000
+    for k in ("xy_depth", "conic_op", "rgb", "tiles_touched", "keys", "point_list", "ranges", "image", "final_T",
+              "n_contrib", "n_examined"):
+        assert np.array_equal(np.asarray(f1[k]).view(np.uint8), np.asarray(f5[k]).view(np.uint8)), k
+    for k in b1:
+        ref = b1[k]
+        assert np.abs(b5[k] - ref).max() <= 1e-12 * max(np.abs(ref).max(), 1e-300), k
