@@ -121,27 +121,67 @@ def cpu_baseline(name: str, min_seconds: float = 10.0, max_frames: int = 8):
 
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "k_composite_bwd_cfg2_hbm_traffic.md")
 KERNEL_SOURCE = os.path.join(ROOT, "gaussian_splatting_tile_amd", "csrc", "composite.hip")
+BIN_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "bin_and_sort_cfg2_hbm_traffic.md")
+BIN_SOURCE = os.path.join(ROOT, "gaussian_splatting_tile_amd", "csrc", "binning.hip")
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per launch of the backward compositing kernel, from the
-    committed rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE, each
-    scaled by what the counter reads for a copy of known size). None when
-    the summary is missing, covers another workload, or was taken on a
-    different version of the kernel source."""
+def _summary_figure(summary: str, source: str, workload: str, field: str):
+    """One machine-readable figure (`- field: `value``) of a committed
+    rocprofv3 counter summary, or None when the summary is missing, covers
+    another workload, or was taken on a different version of the source it
+    names by hash."""
     import hashlib
     try:
-        text = open(TRAFFIC_SUMMARY).read()
-        src = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+        text = open(summary).read()
+        src = hashlib.sha256(open(source, "rb").read()).hexdigest()
     except OSError:
         return None
     fields = dict(re.findall(r"^- (\w+): `([^`]*)`", text, flags=re.M))
     if fields.get("workload") != workload or fields.get("source_sha256") != src:
         return None
     try:
-        return float(fields["hbm_bytes_per_launch"])
+        return float(fields[field])
     except (KeyError, ValueError):
         return None
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the backward compositing kernel, from the
+    committed counter summary (FETCH_SIZE and WRITE_SIZE, each scaled by what
+    the counter reads for a copy of known size)."""
+    return _summary_figure(TRAFFIC_SUMMARY, KERNEL_SOURCE, workload, "hbm_bytes_per_launch")
+
+
+def measured_binning_traffic(workload: str):
+    """HBM bytes of one gs_bin_and_sort_async call (every kernel it launches,
+    square spans), from the committed counter summary, scaled as above."""
+    return _summary_figure(BIN_TRAFFIC_SUMMARY, BIN_SOURCE, workload, "hbm_bytes_per_call")
+
+
+def sort_dup_bytes(n: int, E: int, TX: int, TY: int) -> int:
+    """Bytes the binning of this design must move at the least: per splat,
+    its depth read (4 B) and key/id pair written (8 B), four 8-bit passes
+    over the pairs (16 B each), the tile count read and entry offset written
+    in the last pass (8 B), and the duplication's reads (record 16 B, offset
+    and id 8 B); per entry, the (key, id) written by the duplication (12 B)
+    and every 8-bit pass over the tile-id bits (12 B read, 12 B written)."""
+    tile_bits = max(1, (TX * TY - 1).bit_length())
+    passes = -(-tile_bits // 8)
+    return n * (4 + 8 + 4 * 16 + 8 + 24) + E * (12 + 24 * passes)
+
+
+def sort_dup_record(n, E, TX, TY, seconds, counter_bytes):
+    """The binning against the HBM roofline: algorithmic bytes (above) and,
+    when a current counter summary exists, the measured HBM bytes, each over
+    the stage's median time."""
+    alg = sort_dup_bytes(n, E, TX, TY)
+    rec = {"ms": round(seconds * 1e3, 4), "alg_bytes": alg, "alg_GBps": round(alg / seconds / 1e9, 1),
+           "alg_frac": round(alg / seconds / PEAK_HBM, 4), "counter_bytes": None, "counter_GBps": None,
+           "counter_frac": None}
+    if counter_bytes:
+        rec.update(counter_bytes=int(counter_bytes), counter_GBps=round(counter_bytes / seconds / 1e9, 1),
+                   counter_frac=round(counter_bytes / seconds / PEAK_HBM, 4))
+    return rec
 
 
 def copy_calibration(mib: int, repeats: int = 3):
@@ -483,6 +523,8 @@ def main():
             "composite_fwd_tflops": round(evals_fwd * FLOPS_PER_FWD_EVAL / fwd_s / 1e12, 4),
             "composite_fwd_frac": round(evals_fwd * FLOPS_PER_FWD_EVAL / fwd_s / PEAK_FP32_VECTOR, 5),
             "entries_per_s": round(E / sort_s, 1),
+            "sort_dup": sort_dup_record(n, E, TX, TY, stage_ms["bin_and_sort"][0] * 1e-3,
+                                        measured_binning_traffic(args.workload)),
             "ellipse_tile_test_frames_per_s": round(ellipse_fps, 3),
             "ellipse_tile_test_n_entries": E_ellipse,
             "preprocess_bwd_ms": round(pbwd_s * 1e3, 4),

@@ -5,7 +5,9 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libgs.so")
+# GS_LIB_PATH names another build of the same sources (the host-sanitized
+# one of the CPU tests); the default is the in-tree library.
+LIB_PATH = os.environ.get("GS_LIB_PATH") or os.path.join(_HERE, "libgs.so")
 
 GS_OK, GS_ERR_INVALID, GS_ERR_CAPACITY, GS_ERR_OVERFLOW, GS_ERR_HIP = range(5)
 GS_TILES_SQUARE, GS_TILES_ELLIPSE = 0, 1

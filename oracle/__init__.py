@@ -19,7 +19,11 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.cpp")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# GS_ORACLE_LIB names a prebuilt copy of oracle.cpp (the sanitized build of
+# the CPU tests), used as it is; otherwise the in-tree liboracle.so is
+# rebuilt whenever oracle.cpp is newer.
+_LIB_OVERRIDE = os.environ.get("GS_ORACLE_LIB")
+_LIB = _LIB_OVERRIDE or os.path.join(_HERE, "liboracle.so")
 
 TILE = 16
 
@@ -59,7 +63,7 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        if not _LIB_OVERRIDE and (not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC)):
             build()
         _lib = ctypes.CDLL(_LIB)
         P = ctypes.c_void_p

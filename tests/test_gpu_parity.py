@@ -335,6 +335,64 @@ def test_async_overflow_renders_background(orc):
         assert (res["image"][ch] == np.float32(bg[ch])).all()
 
 
+@pytest.mark.parametrize("extra", [0, 1])
+def test_entry_count_at_the_32_bit_limit(orc, extra):
+    """Splats that each cover the whole 1920x1080 grid (120 x 68 = 8160 tiles):
+    n = floor(2^32 / 8160) of them give E = 2^32 - 256, which still fits in 32
+    bits (GS_ERR_CAPACITY against a capacity of 1); one more gives
+    E = 2^32 + 7904 (GS_ERR_OVERFLOW). Both report the exact E, which the
+    oracle's 64-bit scan of its own tile counts fixes, and neither writes an
+    entry; the asynchronous call leaves E in n_entries_dev and the ranges
+    then stay empty."""
+    import ctypes
+
+    import gaussian_splatting_tile_amd as gs
+    import torch
+    from gaussian_splatting_tile_amd import _lib
+    W, H = 1920, 1080
+    cam = synth.look_at_camera((0.0, 0.0, -4.0), (0.0, 0.0, 0.0), W, H, 1100.0, 1100.0)
+    n = (1 << 32) // 8160 + extra
+    say(f"[entry count limit n={n}]")
+    scene = synth.random_scene(n, 77, cam, scale_lo=20.0, scale_hi=40.0, depth_lo=2.0, depth_hi=3.0, spread=0.1)
+    opre = orc.preprocess(cam, scene)
+    assert (opre["tiles_touched"] == 8160).all(), "every splat must cover the whole grid"
+    _, E = orc.exclusive_scan(opre["tiles_touched"])
+    assert E == n * 8160 and (E >= 1 << 32) == bool(extra)
+
+    sc = gs.Scene.from_numpy(scene)
+    pre = gs.preprocess(cam, sc.means, sc.scales, sc.quats, sc.opacity, sc.sh, sc.sh_degree, sc.rgb)
+    xy_depth, tt = pre["xy_depth"], pre["tiles_touched"]
+    assert_bits_equal(tt.cpu().numpy().view(np.uint32), opre["tiles_touched"], "tiles_touched")
+
+    lib = _lib.load()
+    c = gs.camera(cam)
+    keys = torch.full((1,), -1, dtype=torch.int64, device="cuda")
+    plist = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    need = ctypes.c_size_t(0)
+    assert lib.gs_bin_and_sort(ctypes.byref(c), n, None, None, None, None, 1, None, ctypes.byref(need),
+                               None, None) == _lib.GS_OK
+    scratch = torch.empty((need.value,), dtype=torch.uint8, device="cuda")
+    n_entries = ctypes.c_int64(-1)
+    st = lib.gs_bin_and_sort(ctypes.byref(c), n, ctypes.c_void_p(xy_depth.data_ptr()),
+                             ctypes.c_void_p(tt.data_ptr()), ctypes.c_void_p(keys.data_ptr()),
+                             ctypes.c_void_p(plist.data_ptr()), 1, ctypes.c_void_p(scratch.data_ptr()),
+                             ctypes.byref(need), ctypes.byref(n_entries), None)
+    want = _lib.GS_ERR_OVERFLOW if extra else _lib.GS_ERR_CAPACITY
+    assert st == want, (_lib.STATUS_NAMES.get(st), lib.gs_last_error())
+    assert n_entries.value == E
+    torch.cuda.synchronize()
+    assert int(keys.item()) == -1 and int(plist.item()) == -1
+
+    bins = gs.BinBuffers(torch.device("cuda"), capacity=1)
+    bins.keys.fill_(-1)
+    bins.point_list.fill_(-1)
+    gs.bin_and_sort_async(c, xy_depth, tt, bins)
+    ranges = gs.tile_ranges_async(c, bins)
+    assert bins.entries() == E
+    assert not ranges.any()
+    assert int(bins.keys.item()) == -1 and int(bins.point_list.item()) == -1
+
+
 def test_async_empty_scene():
     import gaussian_splatting_tile_amd as gs
     import torch
