@@ -574,16 +574,43 @@ __global__ void k_fill_u32(uint32_t* __restrict__ p, size_t n, uint32_t v) {
     if (i < n) p[i] = v;
 }
 
-// Run boundaries of the sorted tile ids. The count is n, or the usable
-// entries (*total, capacity) when total is given.
+// Every tile's range from the sorted tile ids: a run's first entry writes
+// its start, its last entry its end; the tiles between two runs, before the
+// first and after the last get (0, 0). Each lane that ends a run (and the
+// first entry, for the tiles before it) names the gap of empty tiles that
+// follows, and its wave clears every such gap 64 tiles at a time. With at
+// least one entry every tile of the n_tiles is written; with none,
+// k_tile_schedule clears them. The count is n, or the usable entries
+// (*total, capacity) when total is given.
 __global__ void k_ranges(const uint64_t* __restrict__ keys, uint32_t n, const uint64_t* __restrict__ total,
-                         uint32_t capacity, uint32_t* __restrict__ ranges) {
+                         uint32_t capacity, uint32_t n_tiles, uint32_t* __restrict__ ranges) {
     const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+    const int lane = threadIdx.x & 63;
     if (total) n = usable_entries(total, capacity);
-    if (i >= n) return;
-    const uint32_t t = (uint32_t)(keys[i] >> 32);
-    if (i == 0 || (uint32_t)(keys[i - 1] >> 32) != t) ranges[2 * (size_t)t] = i;
-    if (i == n - 1 || (uint32_t)(keys[i + 1] >> 32) != t) ranges[2 * (size_t)t + 1] = i + 1;
+    uint2* const r2 = reinterpret_cast<uint2*>(ranges);
+    uint32_t g0 = 0, g1 = 0, h1 = 0;  // empty tiles [g0, g1) after this run; [0, h1) before the first
+    if (i < n) {
+        const uint32_t t = (uint32_t)(keys[i] >> 32);
+        if (i == 0) h1 = min(t, n_tiles);
+        if (i == 0 || (uint32_t)(keys[i - 1] >> 32) != t) ranges[2 * (size_t)t] = i;
+        const uint32_t next = i == n - 1 ? n_tiles : (uint32_t)(keys[i + 1] >> 32);
+        if (next != t) {
+            ranges[2 * (size_t)t + 1] = i + 1;
+            g0 = t + 1;
+            g1 = min(next, n_tiles);
+        }
+    }
+    // the whole wave clears each named gap (every lane takes part, in range or not)
+    for (int pass = 0; pass < 2; ++pass) {
+        const uint32_t lo = pass ? g0 : 0u, hi = pass ? g1 : h1;
+        uint64_t m = __ballot(hi > lo);
+        while (m) {
+            const int l = __ffsll((unsigned long long)m) - 1;
+            m &= m - 1;
+            const uint32_t a = (uint32_t)__shfl((int)lo, l, 64), b = (uint32_t)__shfl((int)hi, l, 64);
+            for (uint32_t u = a + (uint32_t)lane; u < b; u += 64) r2[u] = make_uint2(0u, 0u);
+        }
+    }
 }
 
 // Sort class of a tile for heaviest-first scheduling: 255 - (1 + 16 log2
@@ -595,17 +622,9 @@ __device__ __forceinline__ uint32_t heavy_first_key(uint32_t len) {
     return 255u - min(255u, 1u + 16u * (uint32_t)msb + frac);
 }
 
-// Length of tile t's run, with ranges[t] checked against the sorted keys:
-// ranges are written only at run boundaries (k_ranges), so a tile without
-// entries in this frame holds whatever an earlier frame left; its range is
-// taken as empty unless start < end <= E and keys[start] names the tile.
-__device__ __forceinline__ uint2 checked_range(uint2 r, const uint64_t* __restrict__ keys, uint32_t E, int t) {
-    const bool ok = r.x < r.y && r.y <= E && (uint32_t)(keys[r.x] >> 32) == (uint32_t)t;
-    return ok ? r : make_uint2(0u, 0u);
-}
-
-// The tile ranges' clean-up and the compositing schedules. Every tile's
-// range is checked (checked_range) and empty ones are set to (0, 0).
+// The compositing schedules, from ranges that k_ranges wrote for every
+// tile; with no usable entries (E = 0, or E > capacity), when k_ranges
+// wrote nothing, every range is set to (0, 0) here instead.
 // order = the tiles in descending order of list length (by class; the
 // order within a class is unspecified). chunks = the work items of the
 // scheduled compositing after a count (padded to 16 bytes), each (tile,
@@ -616,7 +635,7 @@ __device__ __forceinline__ uint2 checked_range(uint2 r, const uint64_t* __restri
 // come in descending order of the list length from the item's start to the
 // list's end: the front chunks of the longest lists first, since a pixel
 // that stops early leaves the later chunks of its list little to do. order
-// and chunks may be NULL (then only the ranges are cleaned).
+// and chunks may be NULL.
 //
 // One workgroup of 1024 threads, each over the same kSweep tiles per sweep
 // in both passes: class histograms, exclusive scans, then placement through
@@ -627,7 +646,6 @@ __device__ __forceinline__ uint2 checked_range(uint2 r, const uint64_t* __restri
 constexpr int kOrderThreads = 1024;
 
 __global__ __launch_bounds__(kOrderThreads) void k_tile_schedule(uint32_t* __restrict__ ranges, int n_tiles,
-                                                                 const uint64_t* __restrict__ keys,
                                                                  const uint64_t* __restrict__ total,
                                                                  uint32_t n_entries, uint32_t capacity,
                                                                  uint32_t* __restrict__ order,
@@ -660,14 +678,8 @@ __global__ __launch_bounds__(kOrderThreads) void k_tile_schedule(uint32_t* __res
 #pragma unroll
         for (int k = 0; k < kSweep; ++k) {
             const int t = base + k * kOrderThreads + tid;
-            r[k] = t < n_tiles ? r2[t] : make_uint2(0u, 0u);
-        }
-#pragma unroll
-        for (int k = 0; k < kSweep; ++k) {
-            const int t = base + k * kOrderThreads + tid;
-            const uint2 c = checked_range(r[k], keys, E, t);
-            if (t < n_tiles && (c.x != r[k].x || c.y != r[k].y)) r2[t] = c;  // an empty tile: (0, 0)
-            r[k] = c;
+            r[k] = t < n_tiles && E > 0u ? r2[t] : make_uint2(0u, 0u);
+            if (t < n_tiles && E == 0u) r2[t] = r[k];
         }
         if (!sched) continue;
 #pragma unroll
@@ -746,7 +758,7 @@ __global__ __launch_bounds__(kOrderThreads) void k_tile_schedule(uint32_t* __res
 #pragma unroll
             for (int k = 0; k < kSweep; ++k) {
                 const int t = base + k * kOrderThreads + tid;
-                r[k] = t < n_tiles ? r2[t] : make_uint2(0u, 0u);  // already checked
+                r[k] = t < n_tiles && E > 0u ? r2[t] : make_uint2(0u, 0u);
             }
         }
 #pragma unroll
@@ -917,9 +929,9 @@ hipError_t launch_tile_ranges(const uint64_t* keys, uint32_t n_entries, const ui
     const uint32_t grid_n = n_dev ? capacity : n_entries;
     if (grid_n > 0)
         hipLaunchKernelGGL(k_ranges, dim3((grid_n + 255) / 256), dim3(256), 0, stream, keys, n_entries, n_dev,
-                           capacity, ranges);
+                           capacity, (uint32_t)n_tiles, ranges);
     if (n_tiles > 0)
-        hipLaunchKernelGGL(k_tile_schedule, dim3(1), dim3(kOrderThreads), 0, stream, ranges, n_tiles, keys, n_dev,
+        hipLaunchKernelGGL(k_tile_schedule, dim3(1), dim3(kOrderThreads), 0, stream, ranges, n_tiles, n_dev,
                            n_entries, capacity, tile_order, chunks);
     return hipGetLastError();
 }
