@@ -31,6 +31,8 @@ if ROOT not in sys.path:
 
 METRIC = "fwd+bwd frames/s @160k Gaussians 1920x1080; pixel-splat evals/s vs VALU peak"
 WORKLOADS = {
+    "cfg0": "1,000 Gaussians on a jittered unit sphere, precomputed RGB, 64x64, forward + backward with "
+            "dL/dI ~ N(0,1)",
     "cfg2": "160,000-Gaussian procedural scene (60% sphere shell, 20% helix, 20% checkered plane), "
             "SH degree 3, 1920x1080, fx=fy=1100, forward + backward with dL/dI ~ N(0,1)",
     "cfg3": "1,000,000-Gaussian dense-overdraw scene (80% thick shell, 20% cube), SH degree 3, "
@@ -78,20 +80,35 @@ def oracle_threads() -> int:
 
 
 def _oracle_frames(name: str, min_seconds: float, max_frames: int):
+    """Whole frames of the workload through the oracle, stage by stage:
+    (frames, total seconds, median ms per stage)."""
+    import numpy as np
+
     import oracle
     import synth
     scene, cam, dLdI = synth.config_scene(name)
     if dLdI is None:
         dLdI = synth.upstream_gradient(3001, cam["width"], cam["height"])
     frames, total = 0, 0.0
+    stage = {s: [] for s in STAGES}
     while frames < max_frames and (frames == 0 or total < min_seconds):
-        t0 = time.perf_counter()
-        fwd = oracle.render_fwd(cam, scene)
-        oracle.composite_bwd(cam, scene["n"], fwd["ranges"], fwd["point_list"], fwd["xy_depth"],
-                             fwd["conic_op"], fwd["rgb"], fwd["final_T"], fwd["n_contrib"], dLdI)
-        total += time.perf_counter() - t0
+        t = [time.perf_counter()]
+        pre = oracle.preprocess(cam, scene)
+        t.append(time.perf_counter())
+        keys, point_list = oracle.bin_and_sort(cam, pre["xy_depth"], pre["tiles_touched"])
+        t.append(time.perf_counter())
+        ranges = oracle.tile_ranges(cam, keys)
+        t.append(time.perf_counter())
+        fwd = oracle.composite_fwd(cam, ranges, point_list, pre["xy_depth"], pre["conic_op"], pre["rgb"])
+        t.append(time.perf_counter())
+        oracle.composite_bwd(cam, scene["n"], ranges, point_list, pre["xy_depth"], pre["conic_op"], pre["rgb"],
+                             fwd["final_T"], fwd["n_contrib"], dLdI)
+        t.append(time.perf_counter())
+        for i, s in enumerate(STAGES):
+            stage[s].append(1e3 * (t[i + 1] - t[i]))
+        total += t[-1] - t[0]
         frames += 1
-    return frames, total
+    return frames, total, {s: round(float(np.median(v)), 3) for s, v in stage.items()}
 
 
 def cpu_baseline(name: str, min_seconds: float = 10.0, max_frames: int = 8):
@@ -102,21 +119,21 @@ def cpu_baseline(name: str, min_seconds: float = 10.0, max_frames: int = 8):
     process may use; the binning and sort stay single-threaded) for about
     half that time."""
     import oracle
-    frames, total = _oracle_frames(name, min_seconds, max_frames)
+    frames, total, stage_ms = _oracle_frames(name, min_seconds, max_frames)
     threads = oracle_threads()
     try:
         oracle.set_threads(threads)
-        mframes, mtotal = _oracle_frames(name, min_seconds / 2, 4 * max_frames)
+        mframes, mtotal, mstage_ms = _oracle_frames(name, min_seconds / 2, 4 * max_frames)
     finally:
         oracle.set_threads(1)
     return {"value": round(frames / total, 4), "unit": "frames/s", "cores": 1, "kind": "oracle",
             "sample": f"{frames} full {name} frame(s) (preprocess, bin, sort, ranges, forward and "
                       f"backward compositing), single-threaded, {total:.2f} s in total",
-            "seconds": round(total, 3), "cpu_model": cpu_model(),
+            "seconds": round(total, 3), "stage_ms_median": stage_ms, "cpu_model": cpu_model(),
             "threaded": {"value": round(mframes / mtotal, 4), "unit": "frames/s", "threads": threads,
                          "sample": f"{mframes} full {name} frame(s), preprocess and compositing over "
                                    f"{threads} threads (OpenMP), {mtotal:.2f} s in total",
-                         "seconds": round(mtotal, 3)}}
+                         "seconds": round(mtotal, 3), "stage_ms_median": mstage_ms}}
 
 
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "k_composite_bwd_cfg2_hbm_traffic.md")
@@ -318,7 +335,11 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
     if args.workload == "cfg4":
-        print(json.dumps(bench_views(args)), flush=True)
+        result = bench_views(args)
+        if not args.no_cpu_baseline:
+            log("[bench] timing the oracle on the host (cpu_baseline, one 400x400 view per frame)")
+            result["cpu_baseline"] = cpu_baseline("cfg4")
+        print(json.dumps(result), flush=True)
         return
     if args.copy_calibration_mib > 0:
         copy_calibration(args.copy_calibration_mib)
@@ -358,6 +379,10 @@ def main():
     chunked = args.backward == "chunked"
     ckpt = torch.empty((gs.ckpt_rows(bins.capacity), 4), dtype=f32, device=dev) if chunked else None
     chunks = torch.empty((gs.chunk_words(cam, bins.capacity),), dtype=i32, device=dev) if chunked else None
+    # the forward over the chunk schedule on small tile grids with long lists,
+    # as the Rasterizer chooses it
+    sched_fwd = chunked and gs.scheduled_forward(cam) and E > 256 * TX * TY
+    part = torch.empty((gs.part_bytes(cam, bins.capacity),), dtype=torch.uint8, device=dev) if sched_fwd else None
     gs.tile_ranges(cam, keys, E, out=ranges)
     probe = gs.composite_fwd(cam, ranges, pl, pre["xy_depth"], pre["conic_op"], pre["rgb"],
                              with_examined=True)
@@ -386,7 +411,7 @@ def main():
         gs.tile_ranges_async(c, bins, out=ranges, order=order, chunks=chunks)
         mark(True)
         gs.composite_fwd(c, ranges, p, pre["xy_depth"], pre["conic_op"], pre["rgb"], out=fwd, order=order,
-                         ckpt=ckpt, capacity=bins.capacity)
+                         ckpt=ckpt, capacity=bins.capacity, chunks=chunks if sched_fwd else None, part=part)
         mark(True)
         gs.composite_bwd(c, n, ranges, p, pre["xy_depth"], pre["conic_op"], pre["rgb"],
                          fwd["final_T"], fwd["n_contrib"], dLdI, out=grads, order=order, chunks=chunks,
@@ -506,6 +531,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: {WORKLOADS[args.workload]}", "tile_order": args.tile_order,
                    "backward": args.backward,
+                   "forward": "chunk schedule" if sched_fwd else "whole lists",
                    "n_gaussians": n, "width": W, "height": H, "n_entries": E,
                    "evals_fwd": evals_fwd, "evals_bwd": evals_bwd},
         "pixel_splat_evals_per_s": round((evals_fwd + evals_bwd) * fps, 1),

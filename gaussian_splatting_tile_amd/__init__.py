@@ -9,10 +9,10 @@ from ._lib import EXPORTS, GsError, LIB_PATH
 from .rasterizer import (appearance_bwd, appearance_fwd, appearance_params, BinBuffers, Rasterizer, Scene, bin_and_sort, bin_and_sort_async, camera, chunk_words, ckpt_rows, part_bytes,
                          composite_bwd, composite_fwd, constants, preprocess, preprocess_bwd, tile_ranges,
                          tile_ranges_async, tiles_xy, version, ViewBatch, ViewStack, preprocess_views,
-                         bin_and_sort_views_async)
+                         bin_and_sort_views_async, scheduled_forward)
 
 __all__ = ["appearance_bwd", "appearance_fwd", "appearance_params", "EXPORTS", "GsError", "LIB_PATH", "BinBuffers", "Rasterizer", "Scene", "bin_and_sort",
            "bin_and_sort_async", "camera", "chunk_words", "ckpt_rows", "part_bytes", "composite_bwd", "composite_fwd", "constants", "preprocess",
            "preprocess_bwd",
            "tile_ranges", "tile_ranges_async", "tiles_xy", "version", "ViewBatch", "ViewStack",
-           "preprocess_views", "bin_and_sort_views_async"]
+           "preprocess_views", "bin_and_sort_views_async", "scheduled_forward"]
