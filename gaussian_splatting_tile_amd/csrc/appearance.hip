@@ -41,7 +41,6 @@ namespace {
 
 constexpr int kAppThreads = 128;
 constexpr int kAppPitch = kAppThreads + 4;  // LDS row pitch (floats): 16-byte rows, 4 banks apart
-constexpr int kMaxIn = GS_APP_MAX_LATENT + 3;
 
 __device__ __forceinline__ void view_dir(const gs_camera& cam, const float* __restrict__ means, size_t N, int g,
                                          float& dx, float& dy, float& dz) {
@@ -54,8 +53,9 @@ __device__ __forceinline__ void view_dir(const gs_camera& cam, const float* __re
 
 // The weights in LDS, laid out for 16-byte reads: W1 input-major
 // (w1t[j][i], units padded to a multiple of 4, so four units of one input
-// are one read), W1 unit-major (w1r[i][j], inputs padded to a multiple of
-// 4), b1, W2 unit-major (w2t[i] = (W2[0][i], W2[1][i], W2[2][i], 0)) and b2.
+// are one read), W1 unit-major (w1r[i][j]), b1, W2 unit-major
+// (w2t[i] = (W2[0][i], W2[1][i], W2[2][i], 0)) and b2. Inputs are padded to
+// K4, a multiple of 4, in both W1 layouts; the padding is zero.
 struct AppLds {
     float* w1t;
     float* w1r;
@@ -66,13 +66,13 @@ struct AppLds {
 };
 __host__ __device__ inline int app_lds_floats(int L, int H) {
     const int K = L + 3, H4 = (H + 3) & ~3, K4 = (K + 3) & ~3;
-    return K * H4 + H * K4 + H4 + 4 * H + 4;
+    return K4 * H4 + H * K4 + H4 + 4 * H + 4;
 }
 __device__ __forceinline__ AppLds app_lds(float* base, int L, int H) {
     const int K = L + 3, H4 = (H + 3) & ~3, K4 = (K + 3) & ~3;
     AppLds w;
     w.w1t = base;
-    w.w1r = w.w1t + K * H4;
+    w.w1r = w.w1t + K4 * H4;
     w.b1 = w.w1r + H * K4;
     w.w2t = reinterpret_cast<float4*>(w.b1 + H4);
     w.b2 = reinterpret_cast<float*>(w.w2t + H);
@@ -111,57 +111,63 @@ __device__ __forceinline__ float sigmoid(float y) { return 1.0f / (1.0f + __expf
 // padding): z_i = b1_i + W1[i][0] x_0 + W1[i][1] x_1 + ..., each summed in
 // input order with separate multiply and add; the four sums are
 // interleaved, their weights of one input read as one float4.
-__device__ __forceinline__ void hidden4(const AppLds& w, int K, int i0, const float* x, float z[4]) {
+//
+// KP = K4 / 4: the inputs past K are zero with zero weights, so each adds an
+// exact zero after the real terms and z is unchanged (a fixed trip count
+// lets every loop unroll without per-input branches).
+template <int KP>
+__device__ __forceinline__ void hidden4(const AppLds& w, int i0, const float* x, float z[4]) {
     const float4 b = *reinterpret_cast<const float4*>(w.b1 + i0);
     z[0] = b.x;
     z[1] = b.y;
     z[2] = b.z;
     z[3] = b.w;
 #pragma unroll
-    for (int j = 0; j < kMaxIn; ++j)
-        if (j < K) {
-            const float4 c = *reinterpret_cast<const float4*>(w.w1t + j * w.H4 + i0);
-            z[0] = z[0] + c.x * x[j];
-            z[1] = z[1] + c.y * x[j];
-            z[2] = z[2] + c.z * x[j];
-            z[3] = z[3] + c.w * x[j];
-        }
+    for (int j = 0; j < 4 * KP; ++j) {
+        const float4 c = *reinterpret_cast<const float4*>(w.w1t + j * w.H4 + i0);
+        z[0] = z[0] + c.x * x[j];
+        z[1] = z[1] + c.y * x[j];
+        z[2] = z[2] + c.z * x[j];
+        z[3] = z[3] + c.w * x[j];
+    }
 }
 
-// The inputs of Gaussian g: its latent, then the unit view direction.
+// The inputs of Gaussian g: its latent, then the unit view direction,
+// then zeros up to 4 KP.
+template <int KP>
 __device__ __forceinline__ void inputs(const gs_camera& cam, const float* __restrict__ means,
-                                       const float* __restrict__ latent, size_t N, int L, int g, float x[kMaxIn]) {
+                                       const float* __restrict__ latent, size_t N, int L, int g, float x[4 * KP]) {
 #pragma unroll
-    for (int j = 0; j < kMaxIn; ++j) x[j] = j < L ? latent[(size_t)j * N + g] : 0.0f;
+    for (int j = 0; j < 4 * KP; ++j) x[j] = j < L ? latent[(size_t)j * N + g] : 0.0f;
     float d0, d1, d2;
     view_dir(cam, means, N, g, d0, d1, d2);
 #pragma unroll
-    for (int j = 0; j < kMaxIn; ++j) {
+    for (int j = 0; j < 4 * KP; ++j) {
         if (j == L) x[j] = d0;
         if (j == L + 1) x[j] = d1;
         if (j == L + 2) x[j] = d2;
     }
 }
 
+template <int KP>
 __global__ __launch_bounds__(kAppThreads) void k_appearance_fwd(const gs_camera cam, const int n,
                                                                 const float* __restrict__ means,
                                                                 const float* __restrict__ latent, const int L,
                                                                 const int H, const float* __restrict__ weights,
                                                                 float* __restrict__ rgb) {
     extern __shared__ float s_w[];
-    const int K = L + 3;
     stage_weights(weights, L, H, s_w);
     __syncthreads();
     const int g = blockIdx.x * blockDim.x + threadIdx.x;
     if (g >= n) return;
     const size_t N = (size_t)n;
     const AppLds w = app_lds(s_w, L, H);
-    float x[kMaxIn];
-    inputs(cam, means, latent, N, L, g, x);
+    float x[4 * KP];
+    inputs<KP>(cam, means, latent, N, L, g, x);
     float y0 = w.b2[0], y1 = w.b2[1], y2 = w.b2[2];
     for (int i0 = 0; i0 < H; i0 += 4) {
         float z[4];
-        hidden4(w, K, i0, x, z);
+        hidden4<KP>(w, i0, x, z);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int i = i0 + u;
@@ -207,8 +213,19 @@ __device__ __forceinline__ float row_dot(const float* a, const float* b) {
     return (acc.x + acc.y) + (acc.z + acc.w);
 }
 
+// Slot of workgroup b among nb in the partials. Workgroups go round-robin
+// over the eight XCDs (b mod 8), each with its own L2; slots are handed out
+// per XCD in contiguous blocks, so the 4-byte partials that fill one cache
+// line come from a single L2 instead of eight (each of which would write
+// back its own copy of the partly written line). A bijection on [0, nb).
+__device__ __forceinline__ int xcd_slot(int b, int nb) {
+    const int x = b & 7, k = b >> 3, q = nb >> 3, r = nb & 7;
+    return x * q + min(x, r) + k;
+}
+
 // Per-Gaussian backward plus the workgroup's partial weight gradients
-// (partials [P][gridDim.x]: each weight's partials contiguous).
+// (partials [P][gridDim.x]: each weight's partials contiguous, in slot order).
+template <int KP>
 __global__ __launch_bounds__(kAppThreads) void k_appearance_bwd(
     const gs_camera cam, const int n, const float* __restrict__ means, const float* __restrict__ latent,
     const int L, const int H, const float* __restrict__ weights, const float* __restrict__ grad_rgb,
@@ -224,20 +241,20 @@ __global__ __launch_bounds__(kAppThreads) void k_appearance_bwd(
     const int g = blockIdx.x * blockDim.x + t;
     const bool valid = g < n;
     const size_t N = (size_t)n;
-    float* const out = partials + blockIdx.x;  // weight p's partial at out[p * gridDim.x]
+    float* const out = partials + xcd_slot((int)blockIdx.x, (int)gridDim.x);  // weight p's at out[p * gridDim.x]
     const size_t ps = gridDim.x;
 
     // 1. forward again: hidden activations to rows [0, H), the sigmoid-input
     //    gradients dy = g s (1 - s) to rows H .. H + 2; the active set as bits
-    float x[kMaxIn];
+    float x[4 * KP];
     uint64_t active = 0;
     float e0 = 0.0f, e1 = 0.0f, e2 = 0.0f;
     if (valid) {
-        inputs(cam, means, latent, N, L, g, x);
+        inputs<KP>(cam, means, latent, N, L, g, x);
         float y0 = w.b2[0], y1 = w.b2[1], y2 = w.b2[2];
         for (int i0 = 0; i0 < H; i0 += 4) {
             float z[4];
-            hidden4(w, K, i0, x, z);
+            hidden4<KP>(w, i0, x, z);
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int i = i0 + u;
@@ -272,9 +289,10 @@ __global__ __launch_bounds__(kAppThreads) void k_appearance_bwd(
     // 3. through the hidden layer: dz = (W2^T dy) on the active units, to
     //    rows [0, H); the latents' gradients; the inputs to rows H .. H + K - 1
     if (valid) {
-        float gl[kMaxIn];
+        // gradients of every input (those past the latents are discarded)
+        float gl[4 * KP];
 #pragma unroll
-        for (int j = 0; j < kMaxIn; ++j) gl[j] = 0.0f;
+        for (int j = 0; j < 4 * KP; ++j) gl[j] = 0.0f;
         for (int i = 0; i < H; ++i) {
             const float4 v = w.w2t[i];
             const float dh = v.x * e0 + v.y * e1 + v.z * e2;
@@ -282,17 +300,16 @@ __global__ __launch_bounds__(kAppThreads) void k_appearance_bwd(
             s_tile[i * kAppPitch + t] = dz;
             const float4* row = reinterpret_cast<const float4*>(w.w1r + i * w.K4);
 #pragma unroll
-            for (int j4 = 0; j4 < kMaxIn; j4 += 4)
-                if (j4 < L) {
-                    const float4 c = row[j4 / 4];
-                    gl[j4] += c.x * dz;
-                    if (j4 + 1 < L) gl[j4 + 1] += c.y * dz;
-                    if (j4 + 2 < L) gl[j4 + 2] += c.z * dz;
-                    if (j4 + 3 < L) gl[j4 + 3] += c.w * dz;
-                }
+            for (int j4 = 0; j4 < KP; ++j4) {
+                const float4 c = row[j4];
+                gl[4 * j4] += c.x * dz;
+                gl[4 * j4 + 1] += c.y * dz;
+                gl[4 * j4 + 2] += c.z * dz;
+                gl[4 * j4 + 3] += c.w * dz;
+            }
         }
 #pragma unroll
-        for (int j = 0; j < kMaxIn; ++j) {
+        for (int j = 0; j < 4 * KP; ++j) {
             if (j < L) grad_latent[(size_t)j * N + g] = gl[j];
             if (j < K) s_tile[(H + j) * kAppPitch + t] = x[j];
         }
@@ -307,8 +324,9 @@ __global__ __launch_bounds__(kAppThreads) void k_appearance_bwd(
     }
 }
 
-// grad_weights[p] = sum over workgroups b of partials[p][b], b in order:
-// one workgroup per weight, a strided sum per thread, then a fixed tree.
+// grad_weights[p] = sum over the slots b of partials[p][b], in a fixed
+// order: one workgroup per weight, a strided sum per thread, then a fixed
+// tree.
 __global__ __launch_bounds__(256) void k_appearance_reduce(const float* __restrict__ partials, int nblk, int P,
                                                           float* __restrict__ grad_weights) {
     __shared__ float s_sum[256];
@@ -325,6 +343,36 @@ __global__ __launch_bounds__(256) void k_appearance_reduce(const float* __restri
     if (t == 0) grad_weights[p] = s_sum[0];
 }
 
+// The kernels for KP = ceil((L + 3) / 4), 1 .. 8, chosen at launch.
+template <int KP>
+hipError_t appearance_fwd_kp(const gs_camera& cam, int n, const float* means, const float* latent, int L, int H,
+                             const float* weights, float* rgb, hipStream_t stream) {
+    const size_t lds = (size_t)app_lds_floats(L, H) * sizeof(float);
+    hipLaunchKernelGGL(k_appearance_fwd<KP>, dim3((n + kAppThreads - 1) / kAppThreads), dim3(kAppThreads), lds,
+                       stream, cam, n, means, latent, L, H, weights, rgb);
+    return hipGetLastError();
+}
+
+template <int KP>
+hipError_t appearance_bwd_kp(const gs_camera& cam, int n, const float* means, const float* latent, int L, int H,
+                             const float* weights, const float* grad_rgb, float* grad_latent, float* grad_weights,
+                             float* partials, hipStream_t stream) {
+    const int P = H * (L + 3) + 4 * H + 3;
+    const int nblk = (n + kAppThreads - 1) / kAppThreads;
+    const int K = L + 3;
+    const size_t lds = (size_t)((H + std::max(3, K)) * kAppPitch + app_lds_floats(L, H)) * sizeof(float);
+    if (lds > 65536) {  // up to 68 KB at 29 latents and 64 units
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_appearance_bwd<KP>),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(k_appearance_bwd<KP>, dim3(nblk), dim3(kAppThreads), lds, stream, cam, n, means, latent, L,
+                       H, weights, grad_rgb, grad_latent, partials);
+    hipLaunchKernelGGL(k_appearance_reduce, dim3(P), dim3(256), 0, stream, (const float*)partials, nblk, P,
+                       grad_weights);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 int appearance_params(int L, int H) { return H * (L + 3) + 4 * H + 3; }
@@ -337,30 +385,39 @@ size_t appearance_bwd_scratch(int n, int L, int H) {
 hipError_t launch_appearance_fwd(const gs_camera& cam, int n, const float* means, const float* latent, int L,
                                  int H, const float* weights, float* rgb, hipStream_t stream) {
     if (n <= 0) return hipSuccess;
-    const size_t lds = (size_t)app_lds_floats(L, H) * sizeof(float);
-    hipLaunchKernelGGL(k_appearance_fwd, dim3((n + kAppThreads - 1) / kAppThreads), dim3(kAppThreads), lds, stream,
-                       cam, n, means, latent, L, H, weights, rgb);
-    return hipGetLastError();
+#define GS_FWD_CALL(KP) appearance_fwd_kp<KP>(cam, n, means, latent, L, H, weights, rgb, stream)
+    switch ((L + 3 + 3) / 4) {
+        case 1: return GS_FWD_CALL(1);
+        case 2: return GS_FWD_CALL(2);
+        case 3: return GS_FWD_CALL(3);
+        case 4: return GS_FWD_CALL(4);
+        case 5: return GS_FWD_CALL(5);
+        case 6: return GS_FWD_CALL(6);
+        case 7: return GS_FWD_CALL(7);
+        case 8: return GS_FWD_CALL(8);
+        default: return hipErrorInvalidValue;
+    }
+#undef GS_FWD_CALL
 }
 
 hipError_t launch_appearance_bwd(const gs_camera& cam, int n, const float* means, const float* latent, int L,
                                  int H, const float* weights, const float* grad_rgb, float* grad_latent,
                                  float* grad_weights, float* partials, hipStream_t stream) {
-    const int P = appearance_params(L, H);
-    if (n <= 0) return launch_fill_u32((uint32_t*)grad_weights, (size_t)P, 0u, stream);  // 0.0f bits
-    const int nblk = (n + kAppThreads - 1) / kAppThreads;
-    const int K = L + 3;
-    const size_t lds = (size_t)((H + std::max(3, K)) * kAppPitch + app_lds_floats(L, H)) * sizeof(float);
-    if (lds > 65536) {  // up to 68 KB at 29 latents and 64 units
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_appearance_bwd),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
+    if (n <= 0) return launch_fill_u32((uint32_t*)grad_weights, (size_t)appearance_params(L, H), 0u, stream);
+#define GS_BWD_CALL(KP) \
+    appearance_bwd_kp<KP>(cam, n, means, latent, L, H, weights, grad_rgb, grad_latent, grad_weights, partials, stream)
+    switch ((L + 3 + 3) / 4) {
+        case 1: return GS_BWD_CALL(1);
+        case 2: return GS_BWD_CALL(2);
+        case 3: return GS_BWD_CALL(3);
+        case 4: return GS_BWD_CALL(4);
+        case 5: return GS_BWD_CALL(5);
+        case 6: return GS_BWD_CALL(6);
+        case 7: return GS_BWD_CALL(7);
+        case 8: return GS_BWD_CALL(8);
+        default: return hipErrorInvalidValue;
     }
-    hipLaunchKernelGGL(k_appearance_bwd, dim3(nblk), dim3(kAppThreads), lds, stream, cam, n, means, latent, L, H,
-                       weights, grad_rgb, grad_latent, partials);
-    hipLaunchKernelGGL(k_appearance_reduce, dim3(P), dim3(256), 0, stream, (const float*)partials, nblk, P,
-                       grad_weights);
-    return hipGetLastError();
+#undef GS_BWD_CALL
 }
 
 }  // namespace gs
