@@ -57,7 +57,7 @@
 //    per workgroup at 1080p: the backward's last 70 of 245 us then ran on
 //    under 5% of the workgroup slots).
 //  * Long lists in chunks. With a work schedule from the ranges call (see
-//    k_tile_order) a workgroup takes one 256-entry chunk of a list instead
+//    k_tile_schedule) a workgroup takes one 256-entry chunk of a list instead
 //    of the whole list, so a long list is walked by several workgroups at
 //    once. The forward stores each pixel's (T, C) at every 256-entry
 //    boundary; a backward chunk starts a pixel that composited past its end

@@ -74,6 +74,30 @@ def test_appearance_parity(L, H, n):
     say(f"[appearance L={L} H={H} n={n}] rgb err {err:.2e} {rep}")
 
 
+@pytest.mark.parametrize("L,H", [(1, 1), (5, 7), (9, 16), (13, 33), (17, 20), (21, 64), (25, 3), (29, 64),
+                                 (3, 9), (12, 1)])
+def test_appearance_every_input_width(L, H):
+    """The kernels are specialised on the input count L + 3 rounded up to a
+    multiple of 4 (1..8 groups of four): every specialisation, with exact
+    and padded widths, odd hidden widths and a ragged last workgroup."""
+    import torch
+    import gaussian_splatting_tile_amd as gs
+    n = 1000 + 37 * L + H
+    cam = synth.view_camera(4001, 4.0, 300, 200, 300.0)
+    means, latent, w, g = _inputs(7 * L + H, n, L, H)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    rgb = gs.appearance_fwd(cam, t(means), t(latent), t(w), H)
+    out = gs.appearance_bwd(cam, t(means), t(latent), t(w), H, t(g))
+    torch.cuda.synchronize()
+    o_rgb, _ = app.forward(cam, means, latent, w, L, H)
+    err = np.abs(to_np(rgb) - o_rgb).max()
+    assert err <= 1e-5, err
+    o_lat, o_w = app.backward(cam, means, latent, w, L, H, g)
+    rep = _check(to_np(out["grad_latent"]).astype(np.float64), to_np(out["grad_weights"]).astype(np.float64),
+                 o_lat, o_w, L, H)
+    say(f"[appearance width L={L} H={H} n={n}] rgb err {err:.2e} {rep}")
+
+
 def test_appearance_through_the_rasterizer(orc):
     """MLP colours -> preprocess(rgb_in) -> render -> backward ->
     preprocess_bwd (grad_rgb_in) -> appearance_bwd, against the same chain
