@@ -64,8 +64,17 @@ constexpr int kSortThreads = 256;
 constexpr int kSortWaves = kSortThreads / 64;
 constexpr int kEntryItems = 8;                          // entry keys per lane
 constexpr int kEntryTile = kSortThreads * kEntryItems;  // entries per workgroup
-constexpr int kGaussItems = 2;                          // splat keys per lane
-constexpr int kGaussTile = kSortThreads * kGaussItems;  // splats per workgroup
+// Splat keys per lane in the depth passes: 2 for small frames (enough
+// workgroups to spread the latency-bound passes), 8 from kGaussBigN splats
+// on (fewer, fuller workgroups: the per-workgroup scans and staging are
+// amortised over four times the keys).
+constexpr int kGaussItems = 2;
+constexpr int kGaussItemsBig = 8;
+#ifndef GS_DEPTH_BIG_N
+#define GS_DEPTH_BIG_N (1 << 19)
+#endif
+constexpr int kGaussBigN = GS_DEPTH_BIG_N;
+constexpr int kGaussTile = kSortThreads * kGaussItems;  // splats per workgroup (the smaller tile: scratch bound)
 constexpr int kRadix = 256;
 constexpr int kGaussPasses = 4;                         // 32 depth bits
 constexpr int kMaxTilePasses = 3;                       // up to 24 tile-id bits
@@ -264,6 +273,7 @@ __global__ __launch_bounds__(kDupThreads) void k_duplicate(
 
 // Depth keys of the splats (culled ones last), the identity permutation and
 // the per-tile counts of the first depth pass's digit.
+template <int ITEMS>
 __global__ __launch_bounds__(kSortThreads) void k_depth_keys(const float4* __restrict__ xy_depth,
                                                              const uint32_t* __restrict__ tiles_touched,
                                                              int n, uint32_t* __restrict__ keys,
@@ -273,9 +283,9 @@ __global__ __launch_bounds__(kSortThreads) void k_depth_keys(const float4* __res
     const int tid = threadIdx.x, lane = tid & 63;
     s_hist[tid] = 0;
     __syncthreads();
-    const int base = blockIdx.x * kGaussTile;
+    const int base = blockIdx.x * (kSortThreads * ITEMS);
 #pragma unroll
-    for (int i = 0; i < kGaussItems; ++i) {
+    for (int i = 0; i < ITEMS; ++i) {
         const int g = base + i * kSortThreads + tid;
         const bool valid = g < n;
         uint32_t key = 0xFFFFFFFFu;
@@ -839,15 +849,14 @@ size_t bin_scratch_layout(int n, int64_t capacity, BinScratch* out, void* base) 
     return off;
 }
 
-hipError_t launch_bin_and_sort(const gs_camera& cam, int n_views, int n, const float4* xy_depth,
-                               const float4* conic_op, const uint32_t* tiles_touched, uint64_t* keys,
-                               uint32_t* values, uint32_t capacity, const BinScratch& s, uint64_t* n_dev,
-                               uint32_t flags, hipStream_t stream) {
-    // 1. stable depth order of the splats (culled last) into gv[0]; the last
-    // pass also scans tiles_touched in that order: offsets, first_owner, E
-    const unsigned nbg = (unsigned)((n + kGaussTile - 1) / kGaussTile);
-    const unsigned nbe = (capacity + kEntryTile - 1) / kEntryTile;
-    hipLaunchKernelGGL(k_depth_keys, dim3(nbg), dim3(kSortThreads), 0, stream, xy_depth, tiles_touched, n,
+// The stable depth order of the n splats (culled last) into s.gv[0], with
+// the scan of their tile counts in that order riding on the last pass
+// (offsets, first_owner, E to s.total and *n_dev), ITEMS keys per lane.
+template <int ITEMS>
+void launch_depth_sort(int n, const float4* xy_depth, const uint32_t* tiles_touched, const BinScratch& s,
+                       unsigned nbe, uint64_t* n_dev, hipStream_t stream) {
+    const unsigned nbg = (unsigned)((n + kSortThreads * ITEMS - 1) / (kSortThreads * ITEMS));
+    hipLaunchKernelGGL(k_depth_keys<ITEMS>, dim3(nbg), dim3(kSortThreads), 0, stream, xy_depth, tiles_touched, n,
                        s.gk[0], s.gv[0], s.gauss_counts);
     const DepthScanArgs none{};
     const DepthScanArgs scan{tiles_touched, s.tt_prefix, s.tt_hist, s.offsets, s.first_owner, nbe, s.total, n_dev};
@@ -856,26 +865,39 @@ hipError_t launch_bin_and_sort(const gs_camera& cam, int n_views, int n, const f
         const bool last = p == kGaussPasses - 1;
         uint32_t* cnt = s.gauss_counts + (size_t)p * kRadix * nbg;
         if (last)
-            hipLaunchKernelGGL((k_count_digits<uint32_t, kGaussItems, true>), dim3(nbg), dim3(kSortThreads), 0,
+            hipLaunchKernelGGL((k_count_digits<uint32_t, ITEMS, true>), dim3(nbg), dim3(kSortThreads), 0,
                                stream, s.gk[src], (uint32_t)n, (const uint64_t*)nullptr, 0u, 8 * p, cnt,
                                (const uint32_t*)s.gv[src], tiles_touched, s.tt_counts);
         else if (p > 0)
-            hipLaunchKernelGGL((k_count_digits<uint32_t, kGaussItems, false>), dim3(nbg), dim3(kSortThreads), 0,
+            hipLaunchKernelGGL((k_count_digits<uint32_t, ITEMS, false>), dim3(nbg), dim3(kSortThreads), 0,
                                stream, s.gk[src], (uint32_t)n, (const uint64_t*)nullptr, 0u, 8 * p, cnt,
                                (const uint32_t*)nullptr, (const uint32_t*)nullptr, (uint32_t*)nullptr);
         hipLaunchKernelGGL(k_count_scan, dim3(kRadix), dim3(kScanThreads), 0, stream, cnt, (int)nbg, (int)nbg,
-                           (const uint64_t*)nullptr, 0u, kGaussTile, s.gauss_hist + p * kRadix,
+                           (const uint64_t*)nullptr, 0u, kSortThreads * ITEMS, s.gauss_hist + p * kRadix,
                            last ? (const uint32_t*)s.tt_counts : nullptr, last ? s.tt_prefix : nullptr,
                            last ? s.tt_hist : nullptr);
         if (last)
-            hipLaunchKernelGGL((k_radix_pass<uint32_t, kGaussItems, true>), dim3(nbg), dim3(kSortThreads), 0,
+            hipLaunchKernelGGL((k_radix_pass<uint32_t, ITEMS, true>), dim3(nbg), dim3(kSortThreads), 0,
                                stream, s.gk[src], s.gv[src], (uint32_t)n, (const uint64_t*)nullptr, 0u, 8 * p,
                                s.gauss_hist + p * kRadix, cnt, s.gk[dst], s.gv[dst], scan);
         else
-            hipLaunchKernelGGL((k_radix_pass<uint32_t, kGaussItems, false>), dim3(nbg), dim3(kSortThreads), 0,
+            hipLaunchKernelGGL((k_radix_pass<uint32_t, ITEMS, false>), dim3(nbg), dim3(kSortThreads), 0,
                                stream, s.gk[src], s.gv[src], (uint32_t)n, (const uint64_t*)nullptr, 0u, 8 * p,
                                s.gauss_hist + p * kRadix, cnt, s.gk[dst], s.gv[dst], none);
     }
+}
+
+hipError_t launch_bin_and_sort(const gs_camera& cam, int n_views, int n, const float4* xy_depth,
+                               const float4* conic_op, const uint32_t* tiles_touched, uint64_t* keys,
+                               uint32_t* values, uint32_t capacity, const BinScratch& s, uint64_t* n_dev,
+                               uint32_t flags, hipStream_t stream) {
+    // 1. stable depth order of the splats (culled last) into gv[0]; the last
+    // pass also scans tiles_touched in that order: offsets, first_owner, E
+    const unsigned nbe = (capacity + kEntryTile - 1) / kEntryTile;
+    if (n >= kGaussBigN)
+        launch_depth_sort<kGaussItemsBig>(n, xy_depth, tiles_touched, s, nbe, n_dev, stream);
+    else
+        launch_depth_sort<kGaussItems>(n, xy_depth, tiles_touched, s, nbe, n_dev, stream);
     // 2. duplication and the stable sort on the tile-id bits. Grids cover the
     // capacity; the kernels read E and do nothing when it exceeds capacity.
     if (nbe == 0) return hipGetLastError();
