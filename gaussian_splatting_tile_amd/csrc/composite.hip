@@ -340,13 +340,16 @@ __device__ __forceinline__ void fwd_walk(int cnt, uint32_t pos0, int wave, int l
             }
 #pragma unroll
             for (int i = 0; i < kIlpF; ++i) {
-                // branch-free update; stopped lanes, sentinels and alphas below the floor change nothing
+                // branch-free update; stopped lanes, sentinels and alphas below
+                // the floor change nothing (w = 0). T (1 - alpha) is taken as
+                // T - alpha T, the weight already at hand: one instruction
+                // instead of three, within an ulp of the product.
                 const bool use = T >= kTStop && alpha[i] >= kAlphaMin;
                 const float w = use ? alpha[i] * T : 0.0f;
                 C0 = __builtin_fmaf(xc[i].z, w, C0);
                 C1 = __builtin_fmaf(xc[i].w, w, C1);
                 C2 = __builtin_fmaf(cb[i], w, C2);
-                T = use ? T * (1.0f - alpha[i]) : T;
+                T = T - w;
                 lastl = use ? e[i] : lastl;
             }
         }
@@ -383,7 +386,7 @@ __device__ __forceinline__ size_t part_row(uint32_t start, uint32_t len, uint32_
 // local T, and its per-pixel (T, C, last) land in part / part_last for
 // k_composite_fwd_resolve, which writes the outputs of its pixels.
 template <bool kItems>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) void k_composite_fwd(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(7, 7))) void k_composite_fwd(
     const int W, const int H, const int TX, const int TYb, const uint32_t* __restrict__ ranges,
     const uint32_t* __restrict__ point_list, const float4* __restrict__ xy_depth,
     const float4* __restrict__ conic_op, const float4* __restrict__ rgb, const float3 bg,
@@ -488,7 +491,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
 // is composited again through the chunk from (T_in, C), splat by splat as
 // the whole-list walk does, stopping where that walk stops; if not and this
 // is the list's last chunk, the combined state is final.
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) void k_composite_fwd_resolve(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(7, 7))) void k_composite_fwd_resolve(
     const int W, const int H, const int TX, const int TYb, const uint32_t* __restrict__ point_list,
     const float4* __restrict__ xy_depth, const float4* __restrict__ conic_op, const float4* __restrict__ rgb,
     const float3 bg, float* __restrict__ image, float* __restrict__ final_T, uint32_t* __restrict__ n_contrib,
