@@ -234,6 +234,63 @@ def _tile_confined_scene(cam, counts, opacity, seed):
                 rgb=rng.uniform(0, 1, (3, n)).astype(np.float32), sh=None, sh_degree=0)
 
 
+def _block_confined_scene(cam, counts, seed, opacity=(0.02, 0.15)):
+    """counts[(bx, by)] splats centred within 0.25 px of the centre of 4 x 4
+    pixel block (bx, by) of the top-left 16 x 16 tile, small and faint enough
+    (projected sigma <= 0.62 px with the 0.3 px^2 dilation, opacity <= 0.15:
+    alpha >= 1/255 within 1.8 px) to reach no pixel outside that block;
+    depths in [1, 1.5]."""
+    rng = np.random.default_rng(seed)
+    fx, cx, cy = float(cam["fx"]), float(cam["cx"]), float(cam["cy"])
+    cols = []
+    for (bx, by), k in sorted(counts.items()):
+        z = rng.uniform(1.0, 1.5, k)
+        u = 4 * bx + 1.5 + rng.uniform(-0.25, 0.25, k)
+        v = 4 * by + 1.5 + rng.uniform(-0.25, 0.25, k)
+        cols.append(np.stack([(u - cx) * z / fx, (v - cy) * z / fx, z]))
+    means = np.concatenate(cols, axis=1).astype(np.float32)
+    n = means.shape[1]
+    perm = rng.permutation(n)  # blocks interleaved in index order too
+    return dict(n=n, means=np.ascontiguousarray(means[:, perm]), scales=np.full((3, n), 0.006, np.float32),
+                quats=np.tile(np.float32([[1], [0], [0], [0]]), (1, n)),
+                opacity=rng.uniform(*opacity, n).astype(np.float32),
+                rgb=rng.uniform(0, 1, (3, n)).astype(np.float32), sh=None, sh_degree=0)
+
+
+@pytest.mark.parametrize("case", ["uneven", "one_block"])
+def test_forward_quarters_with_uneven_lists(orc, case):
+    """The forward walks, per 16-lane quarter (one 4 x 4 block), only the
+    splats that reach its block. One tile whose sixteen blocks get very
+    different counts (0 to 300, around multiples of the three-splat step,
+    of 64 and of the 256-splat batch), so within a wave one quarter runs
+    out or stops long before another; and one whose splats all sit in a
+    single block. Forward and both backward forms against the oracle."""
+    if case == "uneven":
+        ks = [0, 1, 2, 3, 5, 63, 64, 65, 130, 255, 256, 257, 300, 7, 0, 11]
+        counts = {(b % 4, b // 4): k for b, k in enumerate(ks) if k}
+    else:
+        counts = {(2, 1): 700}
+    cam = _sheet_camera(32, 32)
+    scene = _block_confined_scene(cam, counts, seed=len(counts) + 41)
+    say(f"[block-confined {case}: n={scene['n']}]")
+    bg = (0.1, 0.2, 0.3)
+    ofwd = oracle_forward(orc, cam, scene, bg)
+    assert ofwd["keys"].shape[0] >= scene["n"]  # every splat listed (some in two tiles)
+    g, out, sc, _ = gpu_forward(cam, scene, bg=bg)
+    assert_binning_equal(g, ofwd)
+    compare_forward(g, ofwd, bg)
+    # every pixel outside the loaded blocks of tile (0, 0) keeps the background
+    img = np.asarray(g["image"])
+    mask = np.zeros((32, 32), bool)
+    for (bx, by) in counts:
+        mask[4 * by:4 * by + 4, 4 * bx:4 * bx + 4] = True
+    np.testing.assert_array_equal(img[:, ~mask], np.broadcast_to(np.float32(bg)[:, None], (3, int((~mask).sum()))))
+    dLdI = synth.upstream_gradient(scene["n"] + 7, 32, 32)
+    obwd = oracle_backward(orc, cam, scene, ofwd, dLdI, bg)
+    compare_gradients(gpu_backward(cam, sc, out, dLdI, bg), obwd)
+    compare_gradients(gpu_backward(cam, sc, out, dLdI, bg, chunked=True), obwd)
+
+
 def test_chunked_backward_at_list_boundaries(orc):
     """The chunked backward on lists of 512 (a multiple of the chunk), 257 and
     255 entries, the last tile ragged (40 px wide), and on a one-tile image
