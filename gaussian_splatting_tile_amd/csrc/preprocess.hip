@@ -194,7 +194,8 @@ __device__ __forceinline__ void project_splat(const gs_camera& cam, const In& in
     } while (false);
 }
 
-// Inputs read from the SoA arrays where they are needed.
+// Inputs read from the SoA arrays where the projection needs them: a
+// culled Gaussian never loads its SH rows.
 struct GlobalIn {
     const float* __restrict__ means;
     const float* __restrict__ scales;
@@ -211,7 +212,7 @@ struct GlobalIn {
     __device__ float rgb(int c) const { return rgbs[c * n + g]; }
 };
 
-// Inputs held in registers, read once for every camera of a stack.
+// One Gaussian's inputs, held in registers (see load_inputs).
 struct RegIn {
     float m[3], s[3], q[4], o, c[48];
     __device__ float mean(int i) const { return m[i]; }
@@ -222,6 +223,38 @@ struct RegIn {
     __device__ float rgb(int i) const { return c[i]; }
 };
 
+template <int R>
+__device__ __forceinline__ void load_rows(float* c, const float* __restrict__ src, int n, int g) {
+#pragma unroll
+    for (int row = 0; row < R; ++row) c[row] = src[(size_t)row * n + g];
+}
+
+// Every input of Gaussian g, loaded at once: the loads are independent, so
+// issuing them together costs one memory round trip instead of one per group
+// of values as the projection reaches them (the SH coefficients alone are
+// sixteen groups). One straight run of loads per SH degree.
+__device__ __forceinline__ void load_inputs(RegIn& in, int n, int g, const float* __restrict__ means,
+                                            const float* __restrict__ scales, const float* __restrict__ quats,
+                                            const float* __restrict__ opacity, const float* __restrict__ sh,
+                                            int n_coef, const float* __restrict__ rgb_in) {
+    load_rows<3>(in.m, means, n, g);
+    load_rows<3>(in.s, scales, n, g);
+    load_rows<4>(in.q, quats, n, g);
+    in.o = opacity[g];
+    if (!sh) load_rows<3>(in.c, rgb_in, n, g);
+    else if (n_coef == 16) load_rows<48>(in.c, sh, n, g);
+    else if (n_coef == 9) load_rows<27>(in.c, sh, n, g);
+    else if (n_coef == 4) load_rows<12>(in.c, sh, n, g);
+    else load_rows<3>(in.c, sh, n, g);
+}
+
+// Splats per launch below which the single-camera projection loads every
+// input up front: too few waves to hide one wave's chain of memory round
+// trips (1080p / 160k: 14.5 -> 13.2 us). Above it the launch is bandwidth-
+// bound and loading where needed skips culled Gaussians' SH rows.
+constexpr int kUpfrontMaxN = 1 << 19;
+
+template <bool kUpfront>
 __global__ __launch_bounds__(256) void k_preprocess(
     const gs_camera cam, const int n, const float* __restrict__ means,
     const float* __restrict__ scales, const float* __restrict__ quats,
@@ -230,10 +263,16 @@ __global__ __launch_bounds__(256) void k_preprocess(
     float4* __restrict__ rgb_out, uint32_t* __restrict__ tiles_touched, const uint32_t flags) {
     const int g = blockIdx.x * blockDim.x + threadIdx.x;
     if (g >= n) return;
-    const GlobalIn in{means, scales, quats, opacity, sh, rgb_in, (size_t)n, (size_t)g};
     float4 o_xy, o_co, o_rgb;
     uint32_t count;
-    project_splat(cam, in, sh != nullptr, n_coef, flags, o_xy, o_co, o_rgb, count);
+    if (kUpfront) {
+        RegIn in;
+        load_inputs(in, n, g, means, scales, quats, opacity, sh, n_coef, rgb_in);
+        project_splat(cam, in, sh != nullptr, n_coef, flags, o_xy, o_co, o_rgb, count);
+    } else {
+        const GlobalIn in{means, scales, quats, opacity, sh, rgb_in, (size_t)n, (size_t)g};
+        project_splat(cam, in, sh != nullptr, n_coef, flags, o_xy, o_co, o_rgb, count);
+    }
     xy_depth[g] = o_xy;
     conic_op[g] = o_co;
     rgb_out[g] = o_rgb;
@@ -251,22 +290,7 @@ __global__ __launch_bounds__(256) void k_preprocess_views(
     const int g = blockIdx.x * blockDim.x + threadIdx.x;
     if (g >= n) return;
     RegIn in;
-#pragma unroll
-    for (int c = 0; c < 3; ++c) {
-        in.m[c] = means[(size_t)c * n + g];
-        in.s[c] = scales[(size_t)c * n + g];
-    }
-#pragma unroll
-    for (int c = 0; c < 4; ++c) in.q[c] = quats[(size_t)c * n + g];
-    in.o = opacity[g];
-    if (sh) {
-#pragma unroll
-        for (int row = 0; row < 48; ++row)
-            in.c[row] = row < 3 * n_coef ? sh[(size_t)row * n + g] : 0.0f;
-    } else {
-#pragma unroll
-        for (int c = 0; c < 3; ++c) in.c[c] = rgb_in[(size_t)c * n + g];
-    }
+    load_inputs(in, n, g, means, scales, quats, opacity, sh, n_coef, rgb_in);
     for (int v = 0; v < cams.n; ++v) {
         float4 o_xy, o_co, o_rgb;
         uint32_t count;
@@ -290,8 +314,12 @@ hipError_t launch_preprocess(const gs_camera& cam, int n, const float* means, co
     if (n <= 0) return hipSuccess;
     const int n_coef = sh ? (sh_degree + 1) * (sh_degree + 1) : 0;
     const int blocks = (n + 255) / 256;
-    hipLaunchKernelGGL(k_preprocess, dim3(blocks), dim3(256), 0, stream, cam, n, means, scales,
-                       quats, opacity, sh, n_coef, rgb_in, xy_depth, conic_op, rgb, tiles_touched, flags);
+    if (n <= kUpfrontMaxN)
+        hipLaunchKernelGGL(k_preprocess<true>, dim3(blocks), dim3(256), 0, stream, cam, n, means, scales,
+                           quats, opacity, sh, n_coef, rgb_in, xy_depth, conic_op, rgb, tiles_touched, flags);
+    else
+        hipLaunchKernelGGL(k_preprocess<false>, dim3(blocks), dim3(256), 0, stream, cam, n, means, scales,
+                           quats, opacity, sh, n_coef, rgb_in, xy_depth, conic_op, rgb, tiles_touched, flags);
     return hipGetLastError();
 }
 

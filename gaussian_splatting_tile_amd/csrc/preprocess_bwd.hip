@@ -18,6 +18,8 @@
 // branches are decided from x/z and y/z evaluated with the operation order
 // of the preprocess kernel (bit-identical, so the branch is the one the
 // forward took).
+#include <type_traits>
+
 #include "gs_internal.h"
 
 namespace gs {
@@ -52,12 +54,34 @@ __global__ __launch_bounds__(256) void k_preprocess_bwd(
     float gq0 = 0.f, gq1 = 0.f, gq2 = 0.f, gq3 = 0.f;
     float gop = 0.f;
     float dc0 = 0.f, dc1 = 0.f, dc2 = 0.f;   // dL/dcolour
-    const bool visible = tiles_touched[g] != 0u;
     float dirx = 0.f, diry = 0.f, dirz = 0.f;
+
+    // Every input first, in one batch of independent loads (one memory
+    // round trip instead of one per group of values as the math reaches
+    // them); a culled Gaussian's values are loaded but not used. One
+    // straight run of loads per SH degree (rows past it are not read).
+    const bool visible = tiles_touched[g] != 0u;
+    const float mx = means[g], my = means[N + g], mz = means[2 * N + g];
+    const float q0 = quats[g], q1 = quats[N + g], q2 = quats[2 * N + g], q3 = quats[3 * N + g];
+    const float s[3] = {scales[g], scales[N + g], scales[2 * N + g]};
+    const float4 gco = grad_conic_op[g];
+    const float2 guv = grad_mean2d[g];
+    const float4 gcol = grad_rgb[g];
+    float shv[48];
+    if (sh != nullptr) {
+        const int rows = n_coef == 16 ? 48 : n_coef == 9 ? 27 : n_coef == 4 ? 12 : 3;
+        auto load = [&](auto R) {
+#pragma unroll
+            for (int row = 0; row < decltype(R)::value; ++row) shv[row] = sh[(size_t)row * N + g];
+        };
+        if (rows == 48) load(std::integral_constant<int, 48>{});
+        else if (rows == 27) load(std::integral_constant<int, 27>{});
+        else if (rows == 12) load(std::integral_constant<int, 12>{});
+        else load(std::integral_constant<int, 3>{});
+    }
 
     if (visible) {
         const float* W = cam.R;
-        const float mx = means[g], my = means[N + g], mz = means[2 * N + g];
         // Camera space and the clamp decision, in the preprocess's order.
         const float px = ((W[0] * mx + W[1] * my) + W[2] * mz) + cam.t[0];
         const float py = ((W[3] * mx + W[4] * my) + W[5] * mz) + cam.t[1];
@@ -76,7 +100,6 @@ __global__ __launch_bounds__(256) void k_preprocess_bwd(
         const float J11 = fy * iz, J12 = -fy * yj * iz2;
 
         // Normalised quaternion and R(q).
-        const float q0 = quats[g], q1 = quats[N + g], q2 = quats[2 * N + g], q3 = quats[3 * N + g];
         const float qn = sqrtf(q0 * q0 + q1 * q1 + q2 * q2 + q3 * q3);
         const float iq = 1.0f / qn;
         const float w = q0 * iq, x = q1 * iq, y = q2 * iq, z = q3 * iq;
@@ -84,7 +107,6 @@ __global__ __launch_bounds__(256) void k_preprocess_bwd(
         R[0][0] = 1.f - 2.f * (y * y + z * z); R[0][1] = 2.f * (x * y - w * z); R[0][2] = 2.f * (x * z + w * y);
         R[1][0] = 2.f * (x * y + w * z); R[1][1] = 1.f - 2.f * (x * x + z * z); R[1][2] = 2.f * (y * z - w * x);
         R[2][0] = 2.f * (x * z - w * y); R[2][1] = 2.f * (y * z + w * x); R[2][2] = 1.f - 2.f * (x * x + y * y);
-        const float s[3] = {scales[g], scales[N + g], scales[2 * N + g]};
         float M[3][3];
 #pragma unroll
         for (int i = 0; i < 3; ++i)
@@ -116,8 +138,6 @@ __global__ __launch_bounds__(256) void k_preprocess_bwd(
         const float id2 = 1.0f / (det * det);
 
         // Inverse 2x2: conic (A, B, C) = (c, -b, a) / det.
-        const float4 gco = grad_conic_op[g];
-        const float2 guv = grad_mean2d[g];
         const float ga = (-c * c * gco.x + b * c * gco.y - b * b * gco.z) * id2;
         const float gb = (2.f * b * c * gco.x - (a * c + b * b) * gco.y + 2.f * a * b * gco.z) * id2;
         const float gc = (-b * b * gco.x + a * b * gco.y - a * a * gco.z) * id2;
@@ -193,7 +213,6 @@ __global__ __launch_bounds__(256) void k_preprocess_bwd(
         gq2 = (hy - y * rad) * iq;
         gq3 = (hz - z * rad) * iq;
 
-        const float4 gcol = grad_rgb[g];
         dc0 = gcol.x;
         dc1 = gcol.y;
         dc2 = gcol.z;
@@ -233,10 +252,10 @@ __global__ __launch_bounds__(256) void k_preprocess_bwd(
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
             if (k < n_coef) {
-                // a culled Gaussian's colour gradient is zero: skip its loads
-                const float s0 = visible ? sh[(size_t)(3 * k + 0) * N + g] : 0.f;
-                const float s1 = visible ? sh[(size_t)(3 * k + 1) * N + g] : 0.f;
-                const float s2 = visible ? sh[(size_t)(3 * k + 2) * N + g] : 0.f;
+                // a culled Gaussian's colour gradient is zero
+                const float s0 = visible ? shv[3 * k + 0] : 0.f;
+                const float s1 = visible ? shv[3 * k + 1] : 0.f;
+                const float s2 = visible ? shv[3 * k + 2] : 0.f;
                 e[k] = dc0 * s0 + dc1 * s1 + dc2 * s2;
                 grad_sh[(size_t)(3 * k + 0) * N + g] = dc0 * Y[k];
                 grad_sh[(size_t)(3 * k + 1) * N + g] = dc1 * Y[k];
@@ -260,8 +279,7 @@ __global__ __launch_bounds__(256) void k_preprocess_bwd(
               kY3d * (6.f * zz - 3.f * xx - 3.f * yy) * e[12] - kY3c * 8.f * x * z * e[13] +
               kY3e * (xx - yy) * e[14];
         if (visible) {
-            const float vx = means[g] - cam.campos[0], vy = means[N + g] - cam.campos[1],
-                        vz = means[2 * N + g] - cam.campos[2];
+            const float vx = mx - cam.campos[0], vy = my - cam.campos[1], vz = mz - cam.campos[2];
             const float ivn = 1.0f / sqrtf(vx * vx + vy * vy + vz * vz);
             const float rd = x * dx + y * dy + z * dz;
             gm0 += (dx - x * rd) * ivn;
