@@ -596,14 +596,25 @@ __global__ void k_ranges(const uint64_t* __restrict__ keys, uint32_t n, const ui
                          uint32_t capacity, uint32_t n_tiles, uint32_t* __restrict__ ranges) {
     const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
     const int lane = threadIdx.x & 63;
+    // The tile ids (high words) of entries i - 1, i and i + 1, loaded at once
+    // and before the entry count is known, within the keys buffer (capacity
+    // entries when the count comes from the device, else n); entries at or
+    // past the count are not used.
+    const uint32_t bound = total ? capacity : n;
+    const uint32_t* const khi = reinterpret_cast<const uint32_t*>(keys) + 1;
+    uint32_t tp = 0, t = 0, tn = 0;
+    if (i < bound) {
+        tp = khi[2 * (size_t)(i > 0 ? i - 1 : 0)];
+        t = khi[2 * (size_t)i];
+        tn = khi[2 * (size_t)(i + 1 < bound ? i + 1 : i)];
+    }
     if (total) n = usable_entries(total, capacity);
     uint2* const r2 = reinterpret_cast<uint2*>(ranges);
     uint32_t g0 = 0, g1 = 0, h1 = 0;  // empty tiles [g0, g1) after this run; [0, h1) before the first
     if (i < n) {
-        const uint32_t t = (uint32_t)(keys[i] >> 32);
         if (i == 0) h1 = min(t, n_tiles);
-        if (i == 0 || (uint32_t)(keys[i - 1] >> 32) != t) ranges[2 * (size_t)t] = i;
-        const uint32_t next = i == n - 1 ? n_tiles : (uint32_t)(keys[i + 1] >> 32);
+        if (i == 0 || tp != t) ranges[2 * (size_t)t] = i;
+        const uint32_t next = i == n - 1 ? n_tiles : tn;
         if (next != t) {
             ranges[2 * (size_t)t + 1] = i + 1;
             g0 = t + 1;
@@ -685,11 +696,19 @@ __global__ __launch_bounds__(kOrderThreads) void k_tile_schedule(uint32_t* __res
     uint2 r[kSweep];
     uint32_t empties = 0;
     for (int base = 0; base < n_tiles; base += kSweepTiles) {
+        if (E > 0u) {  // (E is uniform) the sweep's ranges in one batch of loads
 #pragma unroll
-        for (int k = 0; k < kSweep; ++k) {
-            const int t = base + k * kOrderThreads + tid;
-            r[k] = t < n_tiles && E > 0u ? r2[t] : make_uint2(0u, 0u);
-            if (t < n_tiles && E == 0u) r2[t] = r[k];
+            for (int k = 0; k < kSweep; ++k) {
+                const int t = base + k * kOrderThreads + tid;
+                r[k] = t < n_tiles ? r2[t] : make_uint2(0u, 0u);
+            }
+        } else {  // no usable entries: every range becomes (0, 0)
+#pragma unroll
+            for (int k = 0; k < kSweep; ++k) {
+                const int t = base + k * kOrderThreads + tid;
+                r[k] = make_uint2(0u, 0u);
+                if (t < n_tiles) r2[t] = r[k];
+            }
         }
         if (!sched) continue;
 #pragma unroll
