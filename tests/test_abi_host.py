@@ -47,6 +47,26 @@ def test_library_exports_every_declared_symbol(gs):
         assert hasattr(gs, name)
 
 
+def declared_arity():
+    """Parameter count of every function include/gs.h declares."""
+    src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    out = {}
+    for m in re.finditer(r"\b(gs_[a-z_0-9]+)\s*\(([^;{]*?)\)\s*;", src):
+        params = m.group(2).strip()
+        out[m.group(1)] = 0 if params in ("", "void") else params.count(",") + 1
+    return out
+
+
+def test_binding_argument_counts_match_header(gs):
+    """Every ctypes declaration passes as many arguments as the C prototype
+    takes (a missing trailing pointer would shift the stream argument)."""
+    arity = declared_arity()
+    assert sorted(arity) == declared_functions()
+    for name, n in arity.items():
+        assert len(getattr(gs, name).argtypes) == n, name
+
+
 def test_constants_match_oracle(gs, orc):
     import gaussian_splatting_tile_amd as pkg
     np.testing.assert_array_equal(pkg.constants(), orc.constants())
