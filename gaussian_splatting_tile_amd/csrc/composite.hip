@@ -258,7 +258,8 @@ __device__ __forceinline__ void fwd_stage(uint32_t base, uint32_t end, int tid, 
         s_xyc[tid] = make_float4(xy.x, xy.y, c.x, c.y);
         s_bl[tid] = make_float4(c.z, __uint_as_float(block_mask(co, xy.x, xy.y, x0, y0)), 0.0f, 0.0f);
     } else {
-        s_bl[tid] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        // a slot past the end is never walked: only its (empty) block bits are read
+        reinterpret_cast<float*>(s_bl + tid)[1] = 0.0f;
     }
 }
 
