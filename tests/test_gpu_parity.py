@@ -137,6 +137,63 @@ def test_ragged_and_sh_degrees(orc, W, H, n, deg):
     compare_gradients(gpu_backward(cam, sc, out, dLdI, bg, chunked=True), obwd)
 
 
+def _sweep_case(seed):
+    """A seeded random (camera, scene, background, tile test) drawn over the
+    edges of the path: ragged image sizes down to one pixel, SH degrees 0-3
+    or direct colours, means from behind the near plane to far away and up
+    to three frames off-screen, scales from sub-pixel to larger than the
+    image with random anisotropy, opacities at the 1/255 floor, ordinary, or
+    saturating at 0.99, and either tile test."""
+    rng = np.random.default_rng(7000 + seed)
+    W = [1, 7, 16, 17, 31, 64, 97, 160, 255, 333][seed % 10]
+    H = [1, 5, 16, 23, 48, 100, 129, 200, 257][(4 * seed) % 9]
+    while True:
+        eye = rng.normal(0.0, 1.0, 3)
+        eye *= rng.uniform(2.5, 6.0) / np.linalg.norm(eye)
+        target = rng.normal(0.0, 0.3, 3)
+        d = (target - eye) / np.linalg.norm(target - eye)
+        if abs(d[1]) < 0.9:  # the camera's up vector is +y
+            break
+    f = float(rng.uniform(0.5, 2.0)) * max(W, H)
+    cam = synth.look_at_camera(tuple(eye), tuple(target), W, H, f, f * float(rng.uniform(0.8, 1.25)))
+    n = int(rng.choice([1, 5, 60, 500, 2000, 4000]))
+    deg = [None, 0, 1, 2, 3][seed % 5]
+    scale_lo, scale_hi = [(0.001, 0.01), (0.01, 0.3), (0.001, 1.0), (0.2, 2.0)][int(rng.integers(4))]
+    op_lo, op_hi = [(0.002, 0.01), (0.05, 0.99), (0.9, 1.0)][int(rng.integers(3))]
+    depth_lo = float(rng.choice([0.05, 0.5, 1.0]))
+    scene = synth.random_scene(n, 7000 + seed, cam, sh_degree=deg, scale_lo=scale_lo, scale_hi=scale_hi,
+                               op_lo=op_lo, op_hi=op_hi, depth_lo=depth_lo,
+                               depth_hi=depth_lo + float(rng.uniform(0.5, 8.0)),
+                               spread=float(rng.choice([0.5, 1.2, 3.0])))
+    bg = tuple(float(x) for x in rng.uniform(0.0, 1.0, 3))
+    return cam, scene, bg, int(rng.integers(2)), dict(W=W, H=H, n=n, deg=deg, scales=(scale_lo, scale_hi),
+                                                       opacity=(op_lo, op_hi), depth_lo=depth_lo)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_scene_sweep(orc, seed):
+    """Every stage against the oracle on a seeded random case (see
+    _sweep_case): preprocess and binning bit-exact, the forward (whole lists
+    and over the chunk schedule) and both backward forms within the bar."""
+    import gaussian_splatting_tile_amd as gs
+    cam, scene, bg, tile_test, desc = _sweep_case(seed)
+    say(f"[sweep {seed}] tile_test={tile_test} {desc}")
+    ofwd = orc.render_fwd(cam, scene, bg=bg, tile_test=tile_test)
+    rast = gs.Rasterizer(capacity=64, tile_test=tile_test)  # small: forces the capacity retry
+    g, out, sc, _ = gpu_forward(cam, scene, bg=bg, rast=rast)
+    assert_preprocess_equal(g, ofwd)
+    assert_binning_equal(g, ofwd)
+    rep = compare_forward(g, ofwd, bg)
+    say(f"[sweep {seed}] E={g['n_entries']} {rep}")
+    dLdI = synth.upstream_gradient(seed + 11, cam["width"], cam["height"])
+    obwd = oracle_backward(orc, cam, scene, ofwd, dLdI, bg)
+    compare_gradients(gpu_backward(cam, sc, out, dLdI, bg), obwd)
+    compare_gradients(gpu_backward(cam, sc, out, dLdI, bg, chunked=True), obwd)
+    g2, out2, sc2, _ = gpu_forward(cam, scene, bg=bg, rast=rast, scheduled=True)
+    compare_forward(g2, ofwd, bg)
+    compare_gradients(gpu_backward(cam, sc2, out2, dLdI, bg, chunked=True), obwd)
+
+
 def test_empty_and_fully_culled(orc):
     import gaussian_splatting_tile_amd as gs
     import torch
