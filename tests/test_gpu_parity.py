@@ -194,6 +194,30 @@ def test_random_scene_sweep(orc, seed):
     compare_gradients(gpu_backward(cam, sc2, out2, dLdI, bg, chunked=True), obwd)
 
 
+def test_depth_order_with_a_large_tie_cluster(orc):
+    """100,000 splats of which all but 2,048 (those at indices j N / 2048)
+    share one depth, the others spread in front and behind: one run of about
+    98,000 equal depth keys, spread over every workgroup of every depth pass,
+    must come out in index order among spread keys, as the oracle's stable
+    sort puts them."""
+    n, W, H = 100_000, 256, 256
+    cam = synth.look_at_camera((0.0, 0.0, -4.0), (0.0, 0.0, 0.0), W, H, 200.0, 200.0)
+    rng = np.random.default_rng(17)
+    sampled = (np.arange(2048, dtype=np.int64) * n) // 2048
+    z = np.full(n, 1.0, np.float64)  # world z: depth 5 from the camera
+    z[sampled] = rng.uniform(-2.0, 4.0, sampled.size)
+    xy = rng.uniform(-0.55, 0.55, (2, n)) * (z + 4.0)  # inside the frame at each depth
+    scene = synth.random_scene(n, 18, cam, scale_lo=0.002, scale_hi=0.006)
+    scene["means"] = np.ascontiguousarray(np.stack([xy[0], xy[1], z]).astype(np.float32))
+    ofwd = oracle_forward(orc, cam, scene)
+    depth = ofwd["xy_depth"][2] if ofwd["xy_depth"].shape[0] == 4 else ofwd["xy_depth"][:, 2]
+    say(f"[tie cluster] E={ofwd['keys'].shape[0]} distinct depths={np.unique(depth).size}")
+    g, out, sc, _ = gpu_forward(cam, scene, capacity=1 << 20)
+    assert_preprocess_equal(g, ofwd)
+    assert_binning_equal(g, ofwd)
+    compare_forward(g, ofwd)
+
+
 def test_empty_and_fully_culled(orc):
     import gaussian_splatting_tile_amd as gs
     import torch
