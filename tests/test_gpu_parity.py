@@ -11,7 +11,7 @@ import pytest
 import synth
 from gpu_helpers import (assert_binning_equal, assert_bits_equal, assert_preprocess_equal,
                          compare_forward, compare_gradients, gpu_backward, gpu_forward,
-                         oracle_backward, oracle_forward)
+                         oracle_backward, oracle_forward, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -216,6 +216,47 @@ def test_depth_order_with_a_large_tie_cluster(orc):
     assert_preprocess_equal(g, ofwd)
     assert_binning_equal(g, ofwd)
     compare_forward(g, ofwd)
+
+
+def test_alpha_floor_decisions_match_exactly(orc):
+    """The compositing kernels decide alpha >= 1/255 on the oracle's number
+    (the correctly rounded exponential near the floor): single splats over
+    one 16 x 16 tile, opacities chosen so that many pixels' alpha lies
+    within a few ulp of the floor. n_contrib must match the oracle on every
+    pixel, and T and the image to float32 rounding."""
+    import math
+    import torch
+    import gaussian_splatting_tile_amd as gs
+    cam = synth.look_at_camera((0, 0, -4), (0, 0, 0), 16, 16, 16.0, 16.0)
+    rng = np.random.default_rng(23)
+    dev = torch.device("cuda")
+    ranges = torch.tensor([[0, 1]], dtype=torch.int32, device=dev)
+    point_list = torch.zeros((1,), dtype=torch.int32, device=dev)
+    near = 0
+    for case in range(300):
+        u, v = rng.uniform(2.0, 14.0, 2)
+        A, C = np.exp(rng.uniform(np.log(0.02), np.log(1.0), 2))
+        B = rng.uniform(-0.8, 0.8) * math.sqrt(A * C)
+        # an opacity that puts the floor crossing at a random pixel's power
+        px, py = rng.integers(0, 16, 2)
+        dx, dy = px - u, py - v
+        power = -0.5 * (A * dx * dx + C * dy * dy) - B * dx * dy
+        o = min(1.0, (1.0 / 255.0) / math.exp(power) * (1.0 + rng.uniform(-3e-7, 3e-7)))
+        xy = np.array([[u, v, 5.0, 20.0]], np.float32)
+        co = np.array([[A, B, C, o]], np.float32)
+        rgb = np.array([[0.2, 0.5, 0.8, 0.0]], np.float32)
+        ref = orc.composite_fwd(cam, np.array([[0, 1]], np.uint32), np.array([0], np.uint32), xy, co, rgb)
+        out = gs.composite_fwd(cam, ranges, point_list, torch.from_numpy(xy).to(dev), torch.from_numpy(co).to(dev),
+                               torch.from_numpy(rgb).to(dev))
+        torch.cuda.synchronize()
+        nc = to_np(out["n_contrib"]).view(np.uint32)
+        np.testing.assert_array_equal(nc, ref["n_contrib"], err_msg=f"case {case}")
+        np.testing.assert_allclose(to_np(out["final_T"]), ref["final_T"], rtol=0, atol=2e-7)
+        np.testing.assert_allclose(to_np(out["image"]), ref["image"], rtol=0, atol=2e-7)
+        a = ref["final_T"]
+        near += int((np.abs((1.0 - a[a < 1]) * 255.0 - 1.0) < 1e-5).sum())
+    say(f"[alpha floor] pixels with alpha within 1e-5 of 1/255: {near}")
+    assert near >= 50  # the cases do probe the floor
 
 
 def test_empty_and_fully_culled(orc):
