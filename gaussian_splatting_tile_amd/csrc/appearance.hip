@@ -327,7 +327,7 @@ __global__ __launch_bounds__(kAppThreads) void k_appearance_bwd(
 // grad_weights[p] = sum over the slots b of partials[p][b], in a fixed
 // order: one workgroup per weight, a strided sum per thread, then a fixed
 // tree.
-__global__ __launch_bounds__(256) void k_appearance_reduce(const float* __restrict__ partials, int nblk, int P,
+__global__ __launch_bounds__(256) void k_appearance_reduce(const float* __restrict__ partials, int nblk,
                                                           float* __restrict__ grad_weights) {
     __shared__ float s_sum[256];
     const int p = blockIdx.x, t = threadIdx.x;
@@ -368,7 +368,7 @@ hipError_t appearance_bwd_kp(const gs_camera& cam, int n, const float* means, co
     }
     hipLaunchKernelGGL(k_appearance_bwd<KP>, dim3(nblk), dim3(kAppThreads), lds, stream, cam, n, means, latent, L,
                        H, weights, grad_rgb, grad_latent, partials);
-    hipLaunchKernelGGL(k_appearance_reduce, dim3(P), dim3(256), 0, stream, (const float*)partials, nblk, P,
+    hipLaunchKernelGGL(k_appearance_reduce, dim3(P), dim3(256), 0, stream, (const float*)partials, nblk,
                        grad_weights);
     return hipGetLastError();
 }
